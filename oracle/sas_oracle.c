@@ -1,0 +1,506 @@
+/*
+ * SAS gated block-sparse attention -- plain CPU oracle, fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: it exists so that tests, the smoke check and the CPU
+ * baseline leg of the benchmark can check the HIP library against a slow,
+ * obviously correct restatement of the method.  It shares no code, header,
+ * table or constant with the HIP library.
+ *
+ * Sources (the pages on "SAS: Simple Attention Sparsification via End-to-End
+ * Optimization of Context Ranking", arXiv 2609.13141):
+ *   [R]  dimensionstp.github.io review: 1-1 (dense and block-sparse attention
+ *        equations), 1-2 (hard Top-K equation), 2-1 (g = phi(s), g0 = 1,
+ *        broadcast), 2-2 (inner log-gate equation and the softmax/log identity),
+ *        3-3 (softmax gate activation), 3-5 (sparse scope), 3-6 (fused kernel,
+ *        backward keeps the selector gradient), 3-7 (decode path steps 1-4).
+ *   [P]  papers.paperslantern.ai paper text: section 3 (standard attention,
+ *        scaling factor omitted, block partition, Top-K selected index set),
+ *        section 4 (current block singled out and unbiased, gate broadcast,
+ *        gate-position/activation/scope design elements), ablation results
+ *        (inner gate gradient "relative signal", normaliser shared by the
+ *        historical blocks and not applied to the current block, invariance
+ *        to a global shift of the scores).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - logits are z = scale * q.k + log g; the gate itself is not scaled.
+ *   - GATE_HIST (mode 0, the pages' reading): g = softmax over the history
+ *     blocks j < i only, the current block keeps log g = 0.
+ *     GATE_ALL (mode 1): softmax over j <= i, current block included.
+ *   - the normaliser runs over every causal history candidate; the Top-K then
+ *     keeps a subset, so kept gates sum to at most 1.
+ *   - budget Kb counts the current block; k = min(Kb - 1, i) history blocks.
+ *   - Top-K on the stored fp32 logits, larger first, lower index on ties
+ *     (-0 and +0 compare equal).
+ *   - a token attends to keys u <= t inside its own block (self included).
+ *   - all-(-inf) normaliser sets give log g = -inf (gate 0).
+ *   - decode: cache length L counts the query's own token; the current block
+ *     is cur = (L-1)/b and may be partial; block summaries exist for j < cur.
+ *   - decode scores are computed in fp32 in one fixed order so that both
+ *     sides take the Top-K decision on identical values:
+ *       kbar[j][e] = (((k0 + k1) + k2) + ... + k63) / 64        (fp32, in order)
+ *       qbar[e]    = (((q0 + q1) + ... + q_{G-1})) / G          (fp32, in order)
+ *       A          = fmaf(qbar[e], kbar[j][e], A)  for e = 0..d-1 (fp32)
+ *       s_j        = A / sqrtf(d)                                (fp32)
+ *
+ * Layouts (all row-major, C order):
+ *   q, o, dq        [T][hq][d]        k, v, dk, dv   [T][hkv][d]
+ *   lse             [hq][T]           logits         [hkv][QB][ld]
+ *   sel_idx, sel_lg, dlg              [hkv][QB][Kb]  gate_lse [hkv][QB]
+ * where T = cu_seqlens[nseq], QB = sum over sequences of ceil(len / b), and a
+ * row r = g * QB + (first query block of the sequence) + i.
+ * sel_idx of a row: the kept history blocks ascending, then the current
+ * block i, then -1 padding (with log gate -inf).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_GATE_HIST 0
+#define ORACLE_GATE_ALL 1
+
+static int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+/* Prefix sums of query blocks per sequence; returns the total. */
+static int query_block_offsets(int nseq, const int32_t *cu, int blk, int *cuqb) {
+  cuqb[0] = 0;
+  for (int s = 0; s < nseq; ++s) cuqb[s + 1] = cuqb[s] + ceil_div(cu[s + 1] - cu[s], blk);
+  return cuqb[nseq];
+}
+
+static int seq_of_qblock(int nseq, const int *cuqb, int Q) {
+  int s = 0;
+  while (s + 1 < nseq && cuqb[s + 1] <= Q) ++s;
+  return s;
+}
+
+int sas_oracle_num_qblocks(int nseq, const int32_t *cu, int blk) {
+  int *cuqb = (int *)malloc(sizeof(int) * (nseq + 1));
+  int n = query_block_offsets(nseq, cu, blk, cuqb);
+  free(cuqb);
+  return n;
+}
+
+/*
+ * One gate row ([R] 2-1 g = phi(s) with g0 = 1, 3-3 softmax activation;
+ * [P] section 4 current block unbiased; [R] 1-2 I = TopK(s, K)).
+ * s: the row's scores for blocks 0..i (s[i] read only in GATE_ALL mode).
+ */
+static void gate_row(const float *s, int i, int Kb, int mode, int32_t *idx, double *lg,
+                     double *lse_out, unsigned char *chosen) {
+  int nn = (mode == ORACLE_GATE_ALL) ? i + 1 : i; /* size of the normaliser set */
+  double lse = -INFINITY;
+  if (nn > 0) {
+    double m = -INFINITY;
+    for (int j = 0; j < nn; ++j)
+      if ((double)s[j] > m) m = (double)s[j];
+    if (m != -INFINITY) {
+      double acc = 0.0;
+      for (int j = 0; j < nn; ++j) acc += exp((double)s[j] - m);
+      lse = m + log(acc);
+    }
+  }
+  *lse_out = lse;
+
+  /* Hard Top-K over the history blocks: repeatedly take the largest score,
+   * the lowest index winning ties.  Quadratic, which is fine here. */
+  int k = Kb - 1 < i ? Kb - 1 : i;
+  memset(chosen, 0, (size_t)(i > 0 ? i : 1));
+  for (int t = 0; t < k; ++t) {
+    int best = -1;
+    for (int j = 0; j < i; ++j) {
+      if (chosen[j]) continue;
+      if (best < 0 || s[j] > s[best]) best = j;
+    }
+    chosen[best] = 1;
+  }
+  int pos = 0;
+  for (int j = 0; j < i; ++j) {
+    if (!chosen[j]) continue;
+    idx[pos] = j;
+    lg[pos] = (lse == -INFINITY) ? -INFINITY : (double)s[j] - lse;
+    ++pos;
+  }
+  idx[pos] = i;
+  if (mode == ORACLE_GATE_ALL)
+    lg[pos] = (lse == -INFINITY) ? -INFINITY : (double)s[i] - lse;
+  else
+    lg[pos] = 0.0;
+  ++pos;
+  for (; pos < Kb; ++pos) {
+    idx[pos] = -1;
+    lg[pos] = -INFINITY;
+  }
+}
+
+int sas_oracle_gate_topk(int nseq, const int32_t *cu, int blk, int hkv, int Kb, int mode,
+                         const float *logits, int64_t ld, int32_t *sel_idx, double *sel_lg,
+                         double *gate_lse) {
+  if (nseq <= 0 || blk <= 0 || hkv <= 0 || Kb < 1) return -1;
+  int *cuqb = (int *)malloc(sizeof(int) * (nseq + 1));
+  int QB = query_block_offsets(nseq, cu, blk, cuqb);
+  int maxi = 0;
+  for (int s = 0; s < nseq; ++s)
+    if (cuqb[s + 1] - cuqb[s] > maxi) maxi = cuqb[s + 1] - cuqb[s];
+  if (ld < maxi) {
+    free(cuqb);
+    return -2;
+  }
+  long nrows = (long)hkv * QB;
+#pragma omp parallel
+  {
+    unsigned char *chosen = (unsigned char *)malloc((size_t)maxi + 1);
+#pragma omp for schedule(dynamic, 8)
+    for (long r = 0; r < nrows; ++r) {
+      int Q = (int)(r % QB);
+      int s = seq_of_qblock(nseq, cuqb, Q);
+      int i = Q - cuqb[s];
+      gate_row(logits + r * ld, i, Kb, mode, sel_idx + r * Kb, sel_lg + r * Kb, gate_lse + r,
+               chosen);
+    }
+    free(chosen);
+  }
+  free(cuqb);
+  return 0;
+}
+
+/* Gate + Top-K for one row given its scores directly (decode rows). */
+int sas_oracle_gate_row(const float *scores, int i, int Kb, int mode, int32_t *idx, double *lg,
+                        double *lse) {
+  unsigned char *chosen = (unsigned char *)malloc((size_t)i + 1);
+  gate_row(scores, i, Kb, mode, idx, lg, lse, chosen);
+  free(chosen);
+  return 0;
+}
+
+/*
+ * The attended key list of one query token ([R] 1-1 block-sparse equation,
+ * 2-2 inner log gate, 2-1 broadcast of a block's gate to its tokens;
+ * [P] section 3 union of the selected blocks).  Fills u[] (global key rows)
+ * and slot[] (index into the row's selection) and returns the count.
+ */
+static int attended_keys(const int32_t *idx, int Kb, int i, int blk, int seq_start, int seq_len,
+                         int t_local, int *u, int *slot) {
+  int n = 0;
+  for (int sl = 0; sl < Kb; ++sl) {
+    int j = idx[sl];
+    if (j < 0) continue;
+    int lo = j * blk, hi = lo + blk;
+    if (hi > seq_len) hi = seq_len;
+    if (j == i && hi > t_local + 1) hi = t_local + 1; /* causal inside the current block */
+    for (int p = lo; p < hi; ++p) {
+      u[n] = seq_start + p;
+      slot[n] = sl;
+      ++n;
+    }
+  }
+  return n;
+}
+
+static double dot_dd(const double *a, const double *b, int d) {
+  double acc = 0.0;
+  for (int e = 0; e < d; ++e) acc += a[e] * b[e];
+  return acc;
+}
+
+/*
+ * Forward ([R] 2-2: o = softmax(q K_S^T + log g_S) V_S, with the scale the
+ * paper text says it omits for brevity restored).  Rows whose row_mask entry
+ * is 0 are skipped (row_mask may be NULL: every row).
+ */
+int sas_oracle_fwd(int nseq, const int32_t *cu, int blk, int hq, int hkv, int d, int Kb,
+                   double scale, const double *q, const double *k, const double *v,
+                   const int32_t *sel_idx, const double *sel_lg, const unsigned char *row_mask,
+                   double *o, double *lse) {
+  if (hq % hkv) return -1;
+  int G = hq / hkv;
+  int *cuqb = (int *)malloc(sizeof(int) * (nseq + 1));
+  int QB = query_block_offsets(nseq, cu, blk, cuqb);
+  int T = cu[nseq];
+  long nrows = (long)hkv * QB;
+  int maxkeys = Kb * blk;
+#pragma omp parallel
+  {
+    int *u = (int *)malloc(sizeof(int) * maxkeys);
+    int *slot = (int *)malloc(sizeof(int) * maxkeys);
+    double *z = (double *)malloc(sizeof(double) * maxkeys);
+#pragma omp for schedule(dynamic, 1)
+    for (long r = 0; r < nrows; ++r) {
+      if (row_mask && !row_mask[r]) continue;
+      int g = (int)(r / QB), Q = (int)(r % QB);
+      int s = seq_of_qblock(nseq, cuqb, Q);
+      int i = Q - cuqb[s];
+      int start = cu[s], len = cu[s + 1] - cu[s];
+      const int32_t *idx = sel_idx + r * Kb;
+      const double *lg = sel_lg + r * Kb;
+      for (int tl = i * blk; tl < (i + 1) * blk && tl < len; ++tl) {
+        int t = start + tl;
+        int n = attended_keys(idx, Kb, i, blk, start, len, tl, u, slot);
+        for (int hh = 0; hh < G; ++hh) {
+          int h = g * G + hh;
+          const double *qt = q + ((long)t * hq + h) * d;
+          double m = -INFINITY;
+          for (int a = 0; a < n; ++a) {
+            z[a] = scale * dot_dd(qt, k + ((long)u[a] * hkv + g) * d, d) + lg[slot[a]];
+            if (z[a] > m) m = z[a];
+          }
+          double den = 0.0;
+          for (int a = 0; a < n; ++a) den += exp(z[a] - m);
+          double *ot = o + ((long)t * hq + h) * d;
+          for (int e = 0; e < d; ++e) ot[e] = 0.0;
+          for (int a = 0; a < n; ++a) {
+            double p = exp(z[a] - m) / den;
+            const double *vu = v + ((long)u[a] * hkv + g) * d;
+            for (int e = 0; e < d; ++e) ot[e] += p * vu[e];
+          }
+          lse[(long)h * T + t] = m + log(den);
+        }
+      }
+    }
+    free(u);
+    free(slot);
+    free(z);
+  }
+  free(cuqb);
+  return 0;
+}
+
+/*
+ * Backward: the gradients of the forward above with respect to q, k, v and
+ * the per-block log gate, written out by the chain rule (the pages state
+ * that the backward keeps the selector gradient, [R] 3-6, and describe the
+ * inner gate's gradient as P_gated (dP - D) style "relative signal", [P]
+ * ablation results):
+ *   P_tu  = softmax_u(z_t)          D_t   = sum_e dO_te o_te
+ *   dP_tu = dO_t . v_u              dS_tu = P_tu (dP_tu - D_t)
+ *   dq_t  = scale sum_u dS_tu k_u   dk_u  = scale sum_t dS_tu q_t
+ *   dv_u  = sum_t P_tu dO_t         dlg_r,slot = sum over the row's tokens,
+ *                                    heads and the slot's keys of dS_tu
+ * row_mask selects the rows whose dq / dlg are produced; kblk_mask (indexed
+ * like rows: [hkv][QB]) selects the key blocks whose dk / dv are produced,
+ * accumulated over every row that attends to them.  NULL masks mean all.
+ * Every output is overwritten (zero where not produced).
+ */
+int sas_oracle_bwd(int nseq, const int32_t *cu, int blk, int hq, int hkv, int d, int Kb,
+                   double scale, const double *q, const double *k, const double *v,
+                   const double *dO, const int32_t *sel_idx, const double *sel_lg,
+                   const unsigned char *row_mask, const unsigned char *kblk_mask, double *dq,
+                   double *dk, double *dv, double *dlg) {
+  if (hq % hkv) return -1;
+  int G = hq / hkv;
+  int *cuqb = (int *)malloc(sizeof(int) * (nseq + 1));
+  int QB = query_block_offsets(nseq, cu, blk, cuqb);
+  int T = cu[nseq];
+  memset(dq, 0, sizeof(double) * (size_t)T * hq * d);
+  memset(dk, 0, sizeof(double) * (size_t)T * hkv * d);
+  memset(dv, 0, sizeof(double) * (size_t)T * hkv * d);
+  memset(dlg, 0, sizeof(double) * (size_t)hkv * QB * Kb);
+  int maxkeys = Kb * blk;
+  long npairs = (long)hkv * nseq;
+  /* Key rows of one (kv head, sequence) are touched only by that pair's rows,
+   * so pairs are independent. */
+#pragma omp parallel
+  {
+    int *u = (int *)malloc(sizeof(int) * maxkeys);
+    int *slot = (int *)malloc(sizeof(int) * maxkeys);
+    double *z = (double *)malloc(sizeof(double) * maxkeys);
+    double *P = (double *)malloc(sizeof(double) * maxkeys);
+    double *ot = (double *)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 1)
+    for (long pr = 0; pr < npairs; ++pr) {
+      int g = (int)(pr / nseq), s = (int)(pr % nseq);
+      int start = cu[s], len = cu[s + 1] - cu[s];
+      int nb = cuqb[s + 1] - cuqb[s];
+      for (int i = 0; i < nb; ++i) {
+        long r = (long)g * QB + cuqb[s] + i;
+        const int32_t *idx = sel_idx + r * Kb;
+        const double *lg = sel_lg + r * Kb;
+        int want_row = row_mask ? row_mask[r] : 1;
+        int want_keys = 0;
+        for (int sl = 0; sl < Kb; ++sl) {
+          if (idx[sl] < 0) continue;
+          if (!kblk_mask || kblk_mask[(long)g * QB + cuqb[s] + idx[sl]]) want_keys = 1;
+        }
+        if (!want_row && !want_keys) continue;
+        for (int tl = i * blk; tl < (i + 1) * blk && tl < len; ++tl) {
+          int t = start + tl;
+          int n = attended_keys(idx, Kb, i, blk, start, len, tl, u, slot);
+          for (int hh = 0; hh < G; ++hh) {
+            int h = g * G + hh;
+            const double *qt = q + ((long)t * hq + h) * d;
+            const double *dOt = dO + ((long)t * hq + h) * d;
+            double m = -INFINITY;
+            for (int a = 0; a < n; ++a) {
+              z[a] = scale * dot_dd(qt, k + ((long)u[a] * hkv + g) * d, d) + lg[slot[a]];
+              if (z[a] > m) m = z[a];
+            }
+            double den = 0.0;
+            for (int a = 0; a < n; ++a) den += exp(z[a] - m);
+            for (int e = 0; e < d; ++e) ot[e] = 0.0;
+            for (int a = 0; a < n; ++a) {
+              P[a] = exp(z[a] - m) / den;
+              const double *vu = v + ((long)u[a] * hkv + g) * d;
+              for (int e = 0; e < d; ++e) ot[e] += P[a] * vu[e];
+            }
+            double D = 0.0;
+            for (int e = 0; e < d; ++e) D += dOt[e] * ot[e];
+            for (int a = 0; a < n; ++a) {
+              const double *ku = k + ((long)u[a] * hkv + g) * d;
+              const double *vu = v + ((long)u[a] * hkv + g) * d;
+              double dP = dot_dd(dOt, vu, d);
+              double dS = P[a] * (dP - D);
+              if (want_row) {
+                double *dqt = dq + ((long)t * hq + h) * d;
+                for (int e = 0; e < d; ++e) dqt[e] += scale * dS * ku[e];
+                dlg[r * Kb + slot[a]] += dS;
+              }
+              int kb = idx[slot[a]];
+              if (!kblk_mask || kblk_mask[(long)g * QB + cuqb[s] + kb]) {
+                double *dku = dk + ((long)u[a] * hkv + g) * d;
+                double *dvu = dv + ((long)u[a] * hkv + g) * d;
+                for (int e = 0; e < d; ++e) {
+                  dku[e] += scale * dS * qt[e];
+                  dvu[e] += P[a] * dOt[e];
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    free(u);
+    free(slot);
+    free(z);
+    free(P);
+    free(ot);
+  }
+  free(cuqb);
+  return 0;
+}
+
+/*
+ * Gate backward: d logits from d log g through the softmax normaliser
+ * ([R] 2-1 g = phi(s); [P] ablation results: the normaliser is shared by all
+ * historical blocks).  With p_m = exp(log g_m) over the normaliser set N:
+ *   d s_m = [m kept] dlg_m - p_m * sum over kept j of dlg_j     (m in N)
+ * GATE_HIST: N = {0..i-1}, the current slot carries no gradient.
+ * GATE_ALL:  N = {0..i}, the current block counts as kept.
+ * Columns outside N get 0.  Rows are recomputed from the logits.
+ */
+int sas_oracle_gate_bwd(int nseq, const int32_t *cu, int blk, int hkv, int Kb, int mode,
+                        const float *logits, int64_t ld, const int32_t *sel_idx,
+                        const double *dlg, double *dlogits) {
+  int *cuqb = (int *)malloc(sizeof(int) * (nseq + 1));
+  int QB = query_block_offsets(nseq, cu, blk, cuqb);
+  long nrows = (long)hkv * QB;
+#pragma omp parallel for schedule(dynamic, 8)
+  for (long r = 0; r < nrows; ++r) {
+    int Q = (int)(r % QB);
+    int s = seq_of_qblock(nseq, cuqb, Q);
+    int i = Q - cuqb[s];
+    const float *sr = logits + r * ld;
+    double *out = dlogits + r * ld;
+    for (long c = 0; c < ld; ++c) out[c] = 0.0;
+    int nn = (mode == ORACLE_GATE_ALL) ? i + 1 : i;
+    if (nn == 0) continue;
+    double m = -INFINITY;
+    for (int j = 0; j < nn; ++j)
+      if ((double)sr[j] > m) m = (double)sr[j];
+    if (m == -INFINITY) continue;
+    double acc = 0.0;
+    for (int j = 0; j < nn; ++j) acc += exp((double)sr[j] - m);
+    double lse = m + log(acc);
+    double tot = 0.0;
+    for (int sl = 0; sl < Kb; ++sl) {
+      int j = sel_idx[r * Kb + sl];
+      if (j < 0) continue;
+      if (j == i && mode != ORACLE_GATE_ALL) continue;
+      tot += dlg[r * Kb + sl];
+      out[j] += dlg[r * Kb + sl];
+    }
+    for (int j = 0; j < nn; ++j) out[j] -= exp((double)sr[j] - lse) * tot;
+  }
+  free(cuqb);
+  return 0;
+}
+
+/* ---------------------------------------------------------------- decode */
+
+/*
+ * Block summaries of one (sequence, kv head): the mean key of every full
+ * history block j < (L-1)/b, in the fixed fp32 order stated in the header
+ * ([R] 3-7 step 1: the selector scores cached block summaries).
+ * K: [L][d] fp32 values; kbar: [nhist][d].
+ */
+int sas_oracle_pool_keys_row(int L, int blk, int d, const float *K, float *kbar) {
+  int nhist = (L - 1) / blk;
+  for (int j = 0; j < nhist; ++j)
+    for (int e = 0; e < d; ++e) {
+      float acc = 0.0f;
+      for (int t = 0; t < blk; ++t) acc = acc + K[(long)(j * blk + t) * d + e];
+      kbar[(long)j * d + e] = acc / (float)blk;
+    }
+  return nhist;
+}
+
+/*
+ * Pooled decode scores of one (sequence, kv head): the group's mean query
+ * dotted with each summary, divided by sqrt(d), all in fp32 in the fixed
+ * order stated in the header.  q: [G][d]; kbar: [nhist][d]; scores: [nhist].
+ */
+int sas_oracle_decode_scores_row(int nhist, int d, int G, const float *q, const float *kbar,
+                                 float *scores) {
+  float *qbar = (float *)malloc(sizeof(float) * d);
+  for (int e = 0; e < d; ++e) {
+    float acc = 0.0f;
+    for (int h = 0; h < G; ++h) acc = acc + q[(long)h * d + e];
+    qbar[e] = acc / (float)G;
+  }
+  float rs = sqrtf((float)d);
+  for (int j = 0; j < nhist; ++j) {
+    float acc = 0.0f;
+    for (int e = 0; e < d; ++e) acc = fmaf(qbar[e], kbar[(long)j * d + e], acc);
+    scores[j] = acc / rs;
+  }
+  free(qbar);
+  return 0;
+}
+
+/*
+ * Decode attention of one (sequence, kv head) for its G query heads
+ * ([R] 3-7 steps 3-4): the kept history blocks (whole) plus the present
+ * tokens of the current block, log gates added per block.
+ * q: [G][d]; K, V: [L][d]; sel_idx / sel_lg: [Kb] (sel_lg NULL: no gate);
+ * o: [G][d]; lse: [G].
+ */
+int sas_oracle_decode_row(int L, int blk, int d, int G, int Kb, double scale, const double *q,
+                          const double *K, const double *V, const int32_t *sel_idx,
+                          const double *sel_lg, double *o, double *lse) {
+  int cur = (L - 1) / blk;
+  int maxkeys = Kb * blk;
+  int *u = (int *)malloc(sizeof(int) * maxkeys);
+  int *slot = (int *)malloc(sizeof(int) * maxkeys);
+  double *z = (double *)malloc(sizeof(double) * maxkeys);
+  int n = attended_keys(sel_idx, Kb, cur, blk, 0, L, L - 1, u, slot);
+  for (int h = 0; h < G; ++h) {
+    double m = -INFINITY;
+    for (int a = 0; a < n; ++a) {
+      z[a] = scale * dot_dd(q + (long)h * d, K + (long)u[a] * d, d) +
+             (sel_lg ? sel_lg[slot[a]] : 0.0);
+      if (z[a] > m) m = z[a];
+    }
+    double den = 0.0;
+    for (int a = 0; a < n; ++a) den += exp(z[a] - m);
+    for (int e = 0; e < d; ++e) o[(long)h * d + e] = 0.0;
+    for (int a = 0; a < n; ++a) {
+      double p = exp(z[a] - m) / den;
+      for (int e = 0; e < d; ++e) o[(long)h * d + e] += p * V[(long)u[a] * d + e];
+    }
+    lse[h] = m + log(den);
+  }
+  free(u);
+  free(slot);
+  free(z);
+  return n;
+}

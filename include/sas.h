@@ -1,0 +1,225 @@
+/*
+ * sas.h -- C ABI of the MI355X (gfx950) library for SAS gated block-sparse
+ * attention ("SAS: Simple Attention Sparsification via End-to-End
+ * Optimization of Context Ranking", arXiv 2609.13141).
+ *
+ * The method (as the pages on it describe it):
+ *   - a selector scores every history block of 64 tokens; the scores are
+ *     turned into gates by a softmax over the history blocks while the
+ *     always-kept current block keeps gate 1 (dimensionstp.github.io review,
+ *     section 2-1 "g = phi(s), g0 = 1" and 3-3; paperslantern paper text,
+ *     section 4);
+ *   - a hard Top-K keeps the budgeted history blocks (review section 1-2);
+ *   - attention runs on the kept blocks only, with log(gate) added to every
+ *     logit of the block: o = softmax(q K_S^T + log g_S) V_S (review
+ *     section 2-2; block-sparse form: paper text section 3);
+ *   - the backward returns dQ/dK/dV and the per-block log-gate gradient,
+ *     through which the language-model loss reaches the selector (review
+ *     section 3-6; paper text, ablation results);
+ *   - decode scores cached block summaries, takes the Top-K per query group,
+ *     and attends to the kept blocks of a (paged) KV cache (review 3-7).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers unless the name ends in _host.
+ *     The caller owns all memory; the library never allocates, frees or
+ *     synchronises.  Every call is asynchronous on `stream` (a hipStream_t,
+ *     NULL = the default stream); pointers must stay valid until the stream
+ *     reaches the work.
+ *   - Arguments are checked on the host before anything is launched.  On a
+ *     failed check nothing is launched, no output is touched and a negative
+ *     sas_status is returned; sas_last_error() then describes the failure
+ *     (thread-local).  A launch failure returns SAS_ERR_HIP.
+ *   - Contents of device arrays (selection indices, page ids, sequence
+ *     lengths) are not re-checked against their host copies; indices out of
+ *     range are skipped by the kernels, NaN inputs give unspecified values.
+ *   - Layouts are row-major and contiguous; tensors must be 16-byte aligned.
+ *     block = 64 tokens; head_dim in {64, 128}; hq a multiple of hkv, and the
+ *     query heads h of one KV head g are h = g*G .. g*G+G-1 (G = hq/hkv).
+ *   - Varlen ("packed") tensors: tokens of all sequences back to back,
+ *     cu_seqlens[s] = first token of sequence s.  Query block i of sequence s
+ *     covers tokens [cu_seqlens[s] + 64 i, min(+64, cu_seqlens[s+1])).
+ *     A row is one (kv head g, query block): row = g * total_qblocks +
+ *     cu_qblocks[s] + i.
+ *   - Selections: sel_idx [rows][budget_blocks] int32 holds the kept history
+ *     blocks in ascending order, then the current block, then -1 padding;
+ *     sel_loggate has the same shape and holds log(gate) per entry
+ *     (-inf on padding).
+ *   - Results are deterministic: identical inputs give bit-identical outputs.
+ */
+#ifndef SAS_H_
+#define SAS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sas_status;
+
+#define SAS_OK 0
+#define SAS_ERR_NULL (-1)        /* a required pointer is NULL */
+#define SAS_ERR_SHAPE (-2)       /* sizes are inconsistent */
+#define SAS_ERR_DTYPE (-3)       /* unknown dtype code */
+#define SAS_ERR_ALIGN (-4)       /* a tensor is not 16-byte aligned */
+#define SAS_ERR_UNSUPPORTED (-5) /* head_dim / block / group size not supported */
+#define SAS_ERR_WORKSPACE (-6)   /* workspace missing or too small */
+#define SAS_ERR_HIP (-7)         /* the HIP runtime reported an error */
+
+#define SAS_BF16 0
+#define SAS_F32 1
+
+/* Gate normaliser.  SAS_GATE_HIST is the pages' reading: softmax over the
+ * history blocks j < i, the current block keeps log gate 0 (review section
+ * 2-1, g0 = 1; paper text: the normaliser is not applied to the current
+ * block).  SAS_GATE_ALL normalises over j <= i, the current block included. */
+#define SAS_GATE_HIST 0
+#define SAS_GATE_ALL 1
+
+#define SAS_KV_CONTIGUOUS 0 /* cache [batch][hkv][max_seqlen][head_dim] */
+#define SAS_KV_PAGED 1      /* cache [num_pages][hkv][64][head_dim] + page table */
+
+/* A packed variable-length training / prefill problem. */
+typedef struct sas_problem {
+  int32_t num_seqs;
+  int32_t total_tokens;    /* T = cu_seqlens[num_seqs] */
+  int32_t total_qblocks;   /* QB = sum over sequences of ceil(len / 64) */
+  int32_t hq, hkv;         /* query heads, key/value heads */
+  int32_t head_dim;        /* 64 or 128 */
+  int32_t block;           /* 64 */
+  int32_t budget_blocks;   /* Kb: kept blocks per row, current block included */
+  int32_t dtype;           /* q, k, v: SAS_BF16 or SAS_F32 */
+  int32_t out_dtype;       /* o (and dO in sas_bwd): SAS_BF16 or SAS_F32 */
+  float scale;             /* softmax scale on q.k (the gate is not scaled) */
+  const int32_t *cu_seqlens;       /* device [num_seqs + 1] */
+  const int32_t *cu_qblocks;       /* device [num_seqs + 1] */
+  const int32_t *cu_seqlens_host;  /* host copies of the two arrays above */
+  const int32_t *cu_qblocks_host;
+} sas_problem;
+
+/* A single-token decode problem over a KV cache. */
+typedef struct sas_decode_problem {
+  int32_t batch;
+  int32_t hq, hkv, head_dim, block, budget_blocks;
+  int32_t dtype;           /* q and caches: SAS_BF16 */
+  int32_t out_dtype;       /* o: SAS_BF16 or SAS_F32 */
+  int32_t layout;          /* SAS_KV_CONTIGUOUS or SAS_KV_PAGED */
+  int32_t max_seqlen;      /* contiguous: cache capacity per (batch, kv head) */
+  int32_t max_pages;       /* paged: row stride of page_table */
+  int32_t num_pages;       /* paged: physical pages in the cache */
+  int32_t nblk_stride;     /* summaries: row stride (>= largest history count) */
+  float scale;
+  const int32_t *seqlens;       /* device [batch]: cache length L, query token included */
+  const int32_t *seqlens_host;  /* host copy */
+  const int32_t *page_table;    /* device [batch][max_pages] (paged only) */
+} sas_decode_problem;
+
+/*
+ * sas_gate_topk -- gate + hard Top-K for every training row (review 1-2,
+ * 2-1, 3-3; paper text section 4).
+ *   logits      [hkv][total_qblocks][ld] fp32: column j = key block j of the
+ *               row's own sequence; only columns j < i (and j = i in
+ *               SAS_GATE_ALL) are read.  ld >= the longest sequence's blocks.
+ *   gate_mode   SAS_GATE_HIST or SAS_GATE_ALL.
+ *   sel_idx     out [rows][Kb] int32; sel_loggate out [rows][Kb] fp32;
+ *   gate_lse    out [rows] fp32: log of the gate normaliser (-inf when empty).
+ * Top-K compares the stored fp32 logits: larger first, lower index on ties,
+ * -0 equal to +0.  k = min(Kb - 1, i) history blocks are kept.
+ */
+sas_status sas_gate_topk(const sas_problem *p, const float *logits, int64_t ld,
+                         int32_t gate_mode, int32_t *sel_idx, float *sel_loggate,
+                         float *gate_lse, void *stream);
+
+/*
+ * sas_fwd -- gated block-sparse attention forward (review 2-2, 3-6).
+ *   q [T][hq][d], k/v [T][hkv][d] in p->dtype; o [T][hq][d] in p->out_dtype;
+ *   lse out [hq][T] fp32, natural-log row log-sum-exp of the gated logits.
+ * Token t of query block i attends the kept history blocks whole and the
+ * keys u <= t of block i; logit = scale * q.k + sel_loggate of the block.
+ */
+sas_status sas_fwd(const sas_problem *p, const void *q, const void *k, const void *v,
+                   const int32_t *sel_idx, const float *sel_loggate, void *o, float *lse,
+                   void *stream);
+
+/*
+ * sas_bwd -- gradients of sas_fwd (review 3-6; paper text, ablation results).
+ *   o and dO in p->out_dtype; lse from sas_fwd.
+ *   dq [T][hq][d], dk/dv [T][hkv][d], d_loggate [rows][Kb]: fp32 outputs,
+ *   overwritten (d_loggate padding slots are 0).  d_loggate holds
+ *   sum over the row's tokens, its G heads and the block's keys of
+ *   dS = P (dP - D), the gradient of the loss with respect to log(gate).
+ *   workspace: device scratch of at least sas_bwd_workspace_size(p) bytes.
+ */
+size_t sas_bwd_workspace_size(const sas_problem *p);
+sas_status sas_bwd(const sas_problem *p, const void *q, const void *k, const void *v,
+                   const void *o, const void *dO, const float *lse, const int32_t *sel_idx,
+                   const float *sel_loggate, float *dq, float *dk, float *dv,
+                   float *d_loggate, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sas_gate_bwd -- selector-logit gradient from the log-gate gradient through
+ * the gate softmax (review 2-1; paper text, ablation results: the normaliser
+ * is shared by all history blocks):
+ *   d s_m = [m kept] dlg_m - exp(s_m - gate_lse) * sum over kept j of dlg_j
+ * for m in the normaliser set; other columns (up to ld) are written 0.
+ * In SAS_GATE_HIST the current block's slot carries no gradient.
+ *   d_logits out [hkv][total_qblocks][ld] fp32.
+ */
+sas_status sas_gate_bwd(const sas_problem *p, const float *logits, int64_t ld,
+                        int32_t gate_mode, const int32_t *sel_idx, const float *gate_lse,
+                        const float *d_loggate, float *d_logits, void *stream);
+
+/*
+ * sas_pool_keys -- cached block summaries for decode (review 3-7 step 1):
+ * the mean key of each full history block j < (L_b - 1) / 64, summed in
+ * token order in fp32 and divided by 64.
+ *   k_cache in p->layout; ksum out [batch][hkv][head_dim][nblk_stride] fp32.
+ */
+sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, float *ksum,
+                         void *stream);
+
+/*
+ * sas_decode_select -- decode-time selection (review 3-7 steps 1-2; GQA
+ * groups share one selection): per (batch b, kv head g) row,
+ *   qbar_e = (q_{gG} + ... + q_{gG+G-1})_e / G   (fp32, heads in order)
+ *   s_j    = (fmaf chain over e of qbar_e * ksum_je) / sqrtf(head_dim)
+ * then the gate + Top-K of sas_gate_topk with i = (L_b - 1) / 64 and
+ * SAS_GATE_HIST.  q [batch][hq][d] bf16.
+ *   sel_idx / sel_loggate out [batch*hkv][Kb]; gate_lse out [batch*hkv];
+ *   scores out [batch][hkv][nblk_stride] fp32 (the pooled scores).
+ */
+sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const float *ksum,
+                             float *scores, int32_t *sel_idx, float *sel_loggate,
+                             float *gate_lse, void *stream);
+
+/*
+ * sas_decode -- block-sparse decode attention (review 3-7 steps 3-4) for
+ * the newest token of every sequence: each of the G query heads of (b, g)
+ * attends the kept history blocks and the present tokens of the current
+ * block, log gates added per block (sel_loggate NULL: no gate).  Work is
+ * split over kept blocks and merged with a log-sum-exp combine.
+ *   q [batch][hq][d] bf16; o out [batch][hq][d] in p->out_dtype;
+ *   lse out [batch][hq] fp32 or NULL.
+ *   workspace: at least sas_decode_workspace_size(p) bytes.
+ */
+size_t sas_decode_workspace_size(const sas_decode_problem *p);
+sas_status sas_decode(const sas_decode_problem *p, const void *q, const void *k_cache,
+                      const void *v_cache, const int32_t *sel_idx, const float *sel_loggate,
+                      void *o, float *lse, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Static description of a status code. */
+const char *sas_status_string(sas_status s);
+/* Detail of the last failed call on this thread ("" if none). */
+const char *sas_last_error(void);
+/* ABI version of this header: bumped on any incompatible change. */
+int32_t sas_abi_version(void);
+
+#define SAS_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAS_H_ */

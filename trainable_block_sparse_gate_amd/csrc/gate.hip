@@ -1,0 +1,254 @@
+// Gate + hard Top-K (forward) and the gate backward, one workgroup per row.
+//
+// Forward (dimensionstp.github.io review, sections 1-2, 2-1 and 3-3;
+// paperslantern paper text, section 4): per row with current block i,
+//   lse      = log sum_{j in N} exp(s_j),  N = {j < i} (or {j <= i})
+//   log g_j  = s_j - lse,  the current block keeps log g = 0 in the first mode
+//   kept     = the min(Kb-1, i) largest s_j over j < i, lower j on ties.
+// The Top-K threshold is found with an exact radix select over 32-bit
+// order-preserving keys of the fp32 scores (4 passes of 8 bits, LDS
+// histograms); the kept blocks are then emitted in index order with a
+// workgroup-wide ballot scan, so the result is unique and deterministic.
+//
+// Backward (review section 2-1; paper text, ablation results, where the
+// normaliser is shared by every history block):
+//   d s_m = [m kept] dlg_m - exp(s_m - lse) * sum over kept j of dlg_j.
+#include "sas_device.h"
+#include "sas_launch.h"
+
+namespace sas {
+
+constexpr int kGateThreads = 256;
+constexpr int kGateWaves = kGateThreads / kWave;
+
+__device__ inline uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;  // -0 sorts with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Workgroup reductions / scans through a small LDS scratch.
+__device__ inline float block_max(float x, float *red) {
+  x = wave_max(x);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x % kWave) == 0) red[w] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int k = 1; k < kGateWaves; ++k) r = fmaxf(r, red[k]);
+  return r;
+}
+
+__device__ inline float block_sum(float x, float *red) {
+  x = wave_sum(x);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x % kWave) == 0) red[w] = x;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int k = 0; k < kGateWaves; ++k) r += red[k];  // fixed order: deterministic
+  return r;
+}
+
+// Exclusive prefix count of `flag` over the workgroup in thread order, and
+// the total.
+__device__ inline int block_scan_flag(bool flag, int &total, int *cnt) {
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const uint64_t m = __ballot(flag);
+  const int below = __popcll(m & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (lane == 0) cnt[w] = __popcll(m);
+  __syncthreads();
+  int off = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < kGateWaves; ++k) {
+    if (k < w) off += cnt[k];
+    total += cnt[k];
+  }
+  return off + below;
+}
+
+__device__ inline void row_geometry(const GateParams &p, int r, int &i) {
+  if (p.decode) {
+    const int b = r / p.hkv;
+    i = (p.seqlens[b] - 1) / kBlock;
+  } else {
+    const int Q = r % p.QB;
+    const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, Q);
+    i = Q - p.cu_qblocks[s];
+  }
+}
+
+__global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
+  __shared__ float red[kGateWaves];
+  __shared__ int cnt[kGateWaves];
+  __shared__ int hist[256];
+  __shared__ int s_bin, s_rem;
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  int i;
+  row_geometry(p, r, i);
+  const float *srow = p.scores + (long)r * p.ld;
+  const int nn = (p.mode == 1) ? i + 1 : i;
+  const int k = min(p.Kb - 1, i);
+
+  // Normaliser.
+  float mx = -INFINITY;
+  for (int j = tid; j < nn; j += kGateThreads) mx = fmaxf(mx, srow[j]);
+  mx = block_max(mx, red);
+  float sum = 0.f;
+  if (mx != -INFINITY)
+    for (int j = tid; j < nn; j += kGateThreads) sum += expf(srow[j] - mx);
+  sum = block_sum(sum, red);
+  const float lse = (nn == 0 || mx == -INFINITY) ? -INFINITY : mx + logf(sum);
+
+  // Exact k-th largest key (radix select), unless every candidate is kept.
+  const bool keep_all = (k == i);
+  uint32_t prefix = 0u, pmask = 0u;
+  int remaining = k;
+  if (!keep_all && k > 0) {
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hist[tid] = 0;
+      __syncthreads();
+      for (int j = tid; j < i; j += kGateThreads) {
+        const uint32_t key = order_key(srow[j]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        const int lane = tid;
+        // lane owns bins 4*lane .. 4*lane+3; suffix sums run from the top bin
+        const int c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                  c3 = hist[4 * lane + 3];
+        const int local = c0 + c1 + c2 + c3;
+        int incl = local;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int y = __shfl_down(incl, o);
+          if (lane + o < kWave) incl += y;
+        }
+        int cum = incl - local;  // keys in bins above this lane's four
+        const int cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+        for (int x = 3; x >= 0; --x) {
+          if (cum < remaining && cum + cs[x] >= remaining) {
+            s_bin = 4 * lane + x;
+            s_rem = remaining - cum;
+          }
+          cum += cs[x];
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_bin << shift;
+      pmask |= 255u << shift;
+      remaining = s_rem;
+      __syncthreads();
+    }
+  }
+
+  // Emit kept blocks in index order: keys above the threshold, plus the
+  // first `remaining` keys equal to it.
+  int32_t *oidx = p.sel_idx + (long)r * p.Kb;
+  float *olg = p.sel_lg + (long)r * p.Kb;
+  int base = 0, eq_base = 0;
+  if (k > 0) {
+    for (int c0 = 0; c0 < i; c0 += kGateThreads) {
+      const int j = c0 + tid;
+      const bool valid = j < i;
+      const float sj = valid ? srow[j] : 0.f;
+      const uint32_t key = order_key(sj);
+      const bool eq = valid && !keep_all && key == prefix;
+      int eq_tot;
+      const int eq_rank = eq_base + block_scan_flag(eq, eq_tot, cnt);
+      const bool take = valid && (keep_all || key > prefix || (eq && eq_rank < remaining));
+      int take_tot;
+      const int pos = base + block_scan_flag(take, take_tot, cnt);
+      if (take) {
+        oidx[pos] = j;
+        olg[pos] = (lse == -INFINITY) ? -INFINITY : sj - lse;
+      }
+      base += take_tot;
+      eq_base += eq_tot;
+    }
+  }
+  if (tid == 0) {
+    oidx[k] = i;
+    olg[k] = (p.mode == 1) ? ((lse == -INFINITY) ? -INFINITY : srow[i] - lse) : 0.f;
+    p.gate_lse[r] = lse;
+  }
+  for (int x = k + 1 + tid; x < p.Kb; x += kGateThreads) {
+    oidx[x] = -1;
+    olg[x] = -INFINITY;
+  }
+}
+
+hipError_t launch_gate_topk(const GateParams &p, hipStream_t stream) {
+  if (p.nrows == 0) return hipSuccess;
+  hipLaunchKernelGGL(gate_topk_kernel, dim3(p.nrows), dim3(kGateThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kGateThreads) void gate_bwd_kernel(GateBwdParams p) {
+  __shared__ int s_j[kMaxBudget];
+  __shared__ float s_d[kMaxBudget];
+  __shared__ int s_n;
+  __shared__ float s_tot;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int Q = r % p.QB;
+  const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, Q);
+  const int i = Q - p.cu_qblocks[s];
+  const int nn = (p.mode == 1) ? i + 1 : i;
+  const float lse = p.gate_lse[r];
+  const int32_t *sel = p.sel_idx + (long)r * p.Kb;
+  const float *dlg = p.dlg + (long)r * p.Kb;
+  if (tid == 0) {
+    // kept entries that carry a gradient, ascending by block index
+    int n = 0;
+    float tot = 0.f;
+    for (int sl = 0; sl < p.Kb; ++sl) {
+      const int j = sel[sl];
+      if (j < 0 || j > i || (j == i && p.mode != 1)) continue;
+      s_j[n] = j;
+      s_d[n] = dlg[sl];
+      tot += dlg[sl];
+      ++n;
+    }
+    s_n = n;
+    s_tot = tot;
+  }
+  __syncthreads();
+  const int n = s_n;
+  const float tot = s_tot;
+  const float *srow = p.logits + (long)r * p.ld;
+  float *out = p.dlogits + (long)r * p.ld;
+  for (long c = tid; c < p.ld; c += kGateThreads) {
+    float val = 0.f;
+    if (c < nn && lse != -INFINITY) {
+      val = -expf(srow[c] - lse) * tot;
+      int lo = 0, hi = n - 1;
+      while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_j[mid] == c) {
+          val += s_d[mid];
+          break;
+        }
+        if (s_j[mid] < c) lo = mid + 1; else hi = mid - 1;
+      }
+    }
+    out[c] = val;
+  }
+}
+
+hipError_t launch_gate_bwd(const GateBwdParams &p, hipStream_t stream) {
+  if (p.nrows == 0) return hipSuccess;
+  hipLaunchKernelGGL(gate_bwd_kernel, dim3(p.nrows), dim3(kGateThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sas

@@ -1,0 +1,247 @@
+// C ABI of the SAS library: argument checks on the host, then launches.
+// Every check runs before any HIP call, so a rejected call touches nothing.
+#include "../../include/sas.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "sas_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sas_status fail(sas_status code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+sas_status ok() {
+  g_last_error.clear();
+  return SAS_OK;
+}
+
+sas_status from_hip(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(SAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+// Checks shared by every varlen entry point; fills the largest per-sequence
+// block count.
+sas_status check_problem(const sas_problem *p, int *max_blocks) {
+  REQUIRE(p, SAS_ERR_NULL, "problem is NULL");
+  REQUIRE(p->block == 64, SAS_ERR_UNSUPPORTED, "block must be 64 (got %d)", p->block);
+  REQUIRE(p->head_dim == 64 || p->head_dim == 128, SAS_ERR_UNSUPPORTED,
+          "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  REQUIRE(p->hq > 0 && p->hkv > 0, SAS_ERR_SHAPE, "head counts must be positive");
+  REQUIRE(p->hq % p->hkv == 0, SAS_ERR_SHAPE, "hq (%d) is not a multiple of hkv (%d)", p->hq,
+          p->hkv);
+  REQUIRE(p->budget_blocks >= 1 && p->budget_blocks <= sas::kMaxBudget, SAS_ERR_UNSUPPORTED,
+          "budget_blocks must be in [1, %d] (got %d)", sas::kMaxBudget, p->budget_blocks);
+  REQUIRE(p->dtype == SAS_BF16 || p->dtype == SAS_F32, SAS_ERR_DTYPE, "unknown dtype %d",
+          p->dtype);
+  REQUIRE(p->out_dtype == SAS_BF16 || p->out_dtype == SAS_F32, SAS_ERR_DTYPE,
+          "unknown out_dtype %d", p->out_dtype);
+  REQUIRE(!(p->dtype == SAS_F32 && p->out_dtype == SAS_BF16), SAS_ERR_UNSUPPORTED,
+          "fp32 inputs need an fp32 output");
+  REQUIRE(std::isfinite(p->scale), SAS_ERR_SHAPE, "scale is not finite");
+  REQUIRE(p->num_seqs >= 1, SAS_ERR_SHAPE, "num_seqs must be >= 1");
+  REQUIRE(p->cu_seqlens && p->cu_qblocks, SAS_ERR_NULL, "cu_seqlens / cu_qblocks is NULL");
+  REQUIRE(p->cu_seqlens_host && p->cu_qblocks_host, SAS_ERR_NULL,
+          "host copies of cu_seqlens / cu_qblocks are required");
+  REQUIRE(p->cu_seqlens_host[0] == 0 && p->cu_qblocks_host[0] == 0, SAS_ERR_SHAPE,
+          "cu_seqlens[0] and cu_qblocks[0] must be 0");
+  int mb = 0;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int len = p->cu_seqlens_host[s + 1] - p->cu_seqlens_host[s];
+    REQUIRE(len >= 0, SAS_ERR_SHAPE, "cu_seqlens decreases at sequence %d", s);
+    const int nb = (len + 63) / 64;
+    REQUIRE(p->cu_qblocks_host[s + 1] - p->cu_qblocks_host[s] == nb, SAS_ERR_SHAPE,
+            "cu_qblocks[%d..%d] does not match ceil(len / 64) = %d", s, s + 1, nb);
+    if (nb > mb) mb = nb;
+  }
+  REQUIRE(p->cu_seqlens_host[p->num_seqs] == p->total_tokens, SAS_ERR_SHAPE,
+          "total_tokens (%d) != cu_seqlens[num_seqs] (%d)", p->total_tokens,
+          p->cu_seqlens_host[p->num_seqs]);
+  REQUIRE(p->cu_qblocks_host[p->num_seqs] == p->total_qblocks, SAS_ERR_SHAPE,
+          "total_qblocks (%d) != cu_qblocks[num_seqs] (%d)", p->total_qblocks,
+          p->cu_qblocks_host[p->num_seqs]);
+  if (max_blocks) *max_blocks = mb;
+  return SAS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sas_abi_version(void) { return SAS_ABI_VERSION; }
+
+const char *sas_status_string(sas_status s) {
+  switch (s) {
+    case SAS_OK: return "ok";
+    case SAS_ERR_NULL: return "a required pointer is NULL";
+    case SAS_ERR_SHAPE: return "inconsistent sizes";
+    case SAS_ERR_DTYPE: return "unknown dtype";
+    case SAS_ERR_ALIGN: return "tensor not 16-byte aligned";
+    case SAS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SAS_ERR_WORKSPACE: return "workspace missing or too small";
+    case SAS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *sas_last_error(void) { return g_last_error.c_str(); }
+
+sas_status sas_gate_topk(const sas_problem *p, const float *logits, int64_t ld,
+                         int32_t gate_mode, int32_t *sel_idx, float *sel_loggate,
+                         float *gate_lse, void *stream) {
+  int mb = 0;
+  sas_status st = check_problem(p, &mb);
+  if (st) return st;
+  REQUIRE(logits && sel_idx && sel_loggate && gate_lse, SAS_ERR_NULL,
+          "logits / sel_idx / sel_loggate / gate_lse is NULL");
+  REQUIRE(gate_mode == SAS_GATE_HIST || gate_mode == SAS_GATE_ALL, SAS_ERR_SHAPE,
+          "unknown gate_mode %d", gate_mode);
+  REQUIRE(ld >= mb && ld >= 1, SAS_ERR_SHAPE, "ld (%lld) < blocks of the longest sequence (%d)",
+          (long long)ld, mb);
+  sas::GateParams g{};
+  g.scores = logits;
+  g.ld = ld;
+  g.decode = 0;
+  g.QB = p->total_qblocks;
+  g.num_seqs = p->num_seqs;
+  g.hkv = p->hkv;
+  g.cu_qblocks = p->cu_qblocks;
+  g.Kb = p->budget_blocks;
+  g.mode = gate_mode;
+  g.sel_idx = sel_idx;
+  g.sel_lg = sel_loggate;
+  g.gate_lse = gate_lse;
+  g.nrows = p->hkv * p->total_qblocks;
+  return from_hip(sas::launch_gate_topk(g, (hipStream_t)stream), "gate_topk launch");
+}
+
+sas_status sas_fwd(const sas_problem *p, const void *q, const void *k, const void *v,
+                   const int32_t *sel_idx, const float *sel_loggate, void *o, float *lse,
+                   void *stream) {
+  sas_status st = check_problem(p, nullptr);
+  if (st) return st;
+  REQUIRE(q && k && v && sel_idx && sel_loggate && o && lse, SAS_ERR_NULL,
+          "a tensor argument of sas_fwd is NULL");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o), SAS_ERR_ALIGN,
+          "q, k, v and o must be 16-byte aligned");
+  if (p->total_qblocks == 0) return ok();
+  sas::FwdParams f{};
+  f.q = q;
+  f.k = k;
+  f.v = v;
+  f.sel_idx = sel_idx;
+  f.sel_lg = sel_loggate;
+  f.o = o;
+  f.lse = lse;
+  f.cu_seqlens = p->cu_seqlens;
+  f.cu_qblocks = p->cu_qblocks;
+  f.num_seqs = p->num_seqs;
+  f.T = p->total_tokens;
+  f.QB = p->total_qblocks;
+  f.hq = p->hq;
+  f.hkv = p->hkv;
+  f.G = p->hq / p->hkv;
+  f.Kb = p->budget_blocks;
+  f.scale_log2 = p->scale * 1.4426950408889634f;
+  return from_hip(sas::launch_fwd(f, p->dtype == SAS_BF16, p->out_dtype == SAS_BF16,
+                                  p->head_dim, (hipStream_t)stream),
+                  "fwd launch");
+}
+
+sas_status sas_gate_bwd(const sas_problem *p, const float *logits, int64_t ld,
+                        int32_t gate_mode, const int32_t *sel_idx, const float *gate_lse,
+                        const float *d_loggate, float *d_logits, void *stream) {
+  int mb = 0;
+  sas_status st = check_problem(p, &mb);
+  if (st) return st;
+  REQUIRE(logits && sel_idx && gate_lse && d_loggate && d_logits, SAS_ERR_NULL,
+          "a tensor argument of sas_gate_bwd is NULL");
+  REQUIRE(gate_mode == SAS_GATE_HIST || gate_mode == SAS_GATE_ALL, SAS_ERR_SHAPE,
+          "unknown gate_mode %d", gate_mode);
+  REQUIRE(ld >= mb && ld >= 1, SAS_ERR_SHAPE, "ld (%lld) < blocks of the longest sequence (%d)",
+          (long long)ld, mb);
+  sas::GateBwdParams g{};
+  g.logits = logits;
+  g.ld = ld;
+  g.QB = p->total_qblocks;
+  g.num_seqs = p->num_seqs;
+  g.hkv = p->hkv;
+  g.Kb = p->budget_blocks;
+  g.mode = gate_mode;
+  g.cu_qblocks = p->cu_qblocks;
+  g.sel_idx = sel_idx;
+  g.gate_lse = gate_lse;
+  g.dlg = d_loggate;
+  g.dlogits = d_logits;
+  g.nrows = p->hkv * p->total_qblocks;
+  return from_hip(sas::launch_gate_bwd(g, (hipStream_t)stream), "gate_bwd launch");
+}
+
+size_t sas_bwd_workspace_size(const sas_problem *p) {
+  (void)p;
+  return 0;
+}
+
+sas_status sas_bwd(const sas_problem *p, const void *q, const void *k, const void *v,
+                   const void *o, const void *dO, const float *lse, const int32_t *sel_idx,
+                   const float *sel_loggate, float *dq, float *dk, float *dv,
+                   float *d_loggate, void *workspace, size_t workspace_bytes, void *stream) {
+  (void)q, (void)k, (void)v, (void)o, (void)dO, (void)lse, (void)sel_idx, (void)sel_loggate;
+  (void)dq, (void)dk, (void)dv, (void)d_loggate, (void)workspace, (void)workspace_bytes;
+  (void)stream;
+  sas_status st = check_problem(p, nullptr);
+  if (st) return st;
+  return fail(SAS_ERR_UNSUPPORTED, "sas_bwd is not built yet");
+}
+
+size_t sas_decode_workspace_size(const sas_decode_problem *p) {
+  (void)p;
+  return 0;
+}
+
+sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, float *ksum,
+                         void *stream) {
+  (void)p, (void)k_cache, (void)ksum, (void)stream;
+  return fail(SAS_ERR_UNSUPPORTED, "sas_pool_keys is not built yet");
+}
+
+sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const float *ksum,
+                             float *scores, int32_t *sel_idx, float *sel_loggate,
+                             float *gate_lse, void *stream) {
+  (void)p, (void)q, (void)ksum, (void)scores, (void)sel_idx, (void)sel_loggate, (void)gate_lse;
+  (void)stream;
+  return fail(SAS_ERR_UNSUPPORTED, "sas_decode_select is not built yet");
+}
+
+sas_status sas_decode(const sas_decode_problem *p, const void *q, const void *k_cache,
+                      const void *v_cache, const int32_t *sel_idx, const float *sel_loggate,
+                      void *o, float *lse, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  (void)p, (void)q, (void)k_cache, (void)v_cache, (void)sel_idx, (void)sel_loggate, (void)o;
+  (void)lse, (void)workspace, (void)workspace_bytes, (void)stream;
+  return fail(SAS_ERR_UNSUPPORTED, "sas_decode is not built yet");
+}
+
+}  // extern "C"

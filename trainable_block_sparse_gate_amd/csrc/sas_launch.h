@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI (sas_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sas {
+
+constexpr int kMaxBudget = 256;  // largest budget_blocks a row may hold
+
+struct GateParams {
+  // Row layout: training rows (decode == 0) are r = g * QB + Q with the
+  // query block Q of sequence s at local index i = Q - cu_qblocks[s];
+  // decode rows are r = b * hkv + g with i = (seqlens[b] - 1) / 64.
+  const float *scores;
+  int64_t ld;
+  int decode;
+  int QB, num_seqs, hkv;
+  const int32_t *cu_qblocks;
+  const int32_t *seqlens;
+  int Kb, mode;
+  int32_t *sel_idx;
+  float *sel_lg;
+  float *gate_lse;
+  int nrows;
+};
+hipError_t launch_gate_topk(const GateParams &p, hipStream_t stream);
+
+struct GateBwdParams {
+  const float *logits;
+  int64_t ld;
+  int QB, num_seqs, hkv, Kb, mode;
+  const int32_t *cu_qblocks;
+  const int32_t *sel_idx;
+  const float *gate_lse;
+  const float *dlg;
+  float *dlogits;
+  int nrows;
+};
+hipError_t launch_gate_bwd(const GateBwdParams &p, hipStream_t stream);
+
+struct FwdParams {
+  const void *q, *k, *v;
+  const int32_t *sel_idx;
+  const float *sel_lg;
+  void *o;
+  float *lse;
+  const int32_t *cu_seqlens, *cu_qblocks;
+  int num_seqs, T, QB, hq, hkv, G, Kb;
+  float scale_log2;  // softmax scale * log2(e)
+};
+hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
+                      hipStream_t stream);
+
+}  // namespace sas

@@ -86,3 +86,81 @@ def test_gate_fwd_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(sel, first[0]) and torch.equal(lg, first[1])
     assert torch.equal(o, first[3]) and torch.equal(lse, first[4])
+
+
+def check_bwd(case, prob, dv, gpu, ref, mode=sas.GATE_HIST):
+    import torch
+    sel, lg, glse, o, lse = gpu
+    ridx, rlg, rlse, ro, rl = ref
+    dq, dk, dvv, dlg = sas.bwd(prob, dv["q"], dv["k"], dv["v"], o, dv["dO"], lse, sel, lg)
+    dlogits = sas.gate_bwd(prob, dv["logits"], sel, glse, dlg, mode)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, rdlg = oracle.bwd(case.cu_seqlens, case.q, case.k, case.v, case.dO, ridx,
+                                     rlg, case.budget_blocks, case.scale)
+    tol = TOL[case.dtype]
+    assert_close("dq", dq.cpu().numpy(), rdq, tol)
+    assert_close("dk", dk.cpu().numpy(), rdk, tol)
+    assert_close("dv", dvv.cpu().numpy(), rdv, tol)
+    assert_close("dlg", dlg.cpu().numpy(), rdlg, tol)
+    rdz = oracle.gate_bwd(case.cu_seqlens, case.logits, ridx, rdlg, case.hkv,
+                          case.budget_blocks, mode)
+    assert_close("d_logits", dlogits.cpu().numpy(), rdz, tol)
+    return dq, dk, dvv, dlg, dlogits
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_bwd_small(name):
+    case, prob, dv, gpu, ref = run_case(name)
+    check_bwd(case, prob, dv, gpu, ref)
+
+
+def test_bwd_all_softmax_mode():
+    case, prob, dv, gpu, ref = run_case("ragged_g4_d128", mode=sas.GATE_ALL)
+    check_bwd(case, prob, dv, gpu, ref, mode=sas.GATE_ALL)
+
+
+def test_bwd_neg_inf_logits():
+    case, prob, dv, gpu, ref = run_case("ragged_g4_d128", neg_inf_frac=0.3)
+    check_bwd(case, prob, dv, gpu, ref)
+
+
+def test_bwd_fp32_output_and_dO():
+    """o and dO in fp32 while q, k, v are bf16."""
+    case, prob, dv, gpu, ref = run_case("ragged_g4_d128", out_dtype="f32")
+    import torch
+    dv = dict(dv)
+    dv["dO"] = torch.from_numpy(case.dO).cuda()  # bf16 values held in fp32
+    check_bwd(case, prob, dv, gpu, ref)
+
+
+def test_bwd_hot_key_blocks_split_over_segments():
+    """A long sequence with a few columns boosted so that most rows keep the
+    same key blocks: those blocks are split over many segments."""
+    import torch
+    lengths, hq, hkv, d, Kb = [4096 + 37], 8, 2, 128, 8
+    case = wl.make_varlen("hot", lengths, hq, hkv, d, Kb, dtype="bf16", logit_sigma=1.0,
+                          workload_id=71, boost_frac=0.05, boost=6.0)
+    prob = sas.Varlen(lengths, hq, hkv, d, Kb)
+    dv = case_to_device(case)
+    sel, lg, glse = sas.gate_topk(prob, dv["logits"])
+    o, lse = sas.fwd(prob, dv["q"], dv["k"], dv["v"], sel, lg)
+    torch.cuda.synchronize()
+    ridx, rlg, rlse = oracle.gate_topk(case.cu_seqlens, case.logits, hkv, Kb)
+    assert np.array_equal(sel.cpu().numpy(), ridx)
+    counts = np.bincount(ridx[0][ridx[0] >= 0].ravel(), minlength=65)
+    say(f"  most-kept block count: {counts.max()}")
+    assert counts.max() > 32  # at least two segments of 32
+    ro, rl = oracle.fwd(case.cu_seqlens, case.q, case.k, case.v, ridx, rlg, Kb, case.scale)
+    assert_close("o", o.float().cpu().numpy(), ro, TOL["bf16"])
+    check_bwd(case, prob, dv, (sel, lg, glse, o, lse), (ridx, rlg, rlse, ro, rl))
+
+
+def test_bwd_deterministic():
+    import torch
+    case, prob, dv, gpu, ref = run_case("ragged_g4_d128")
+    a = check_bwd(case, prob, dv, gpu, ref)
+    sel, lg, glse, o, lse = gpu
+    b = sas.bwd(prob, dv["q"], dv["k"], dv["v"], o, dv["dO"], lse, sel, lg)
+    torch.cuda.synchronize()
+    for x, y in zip(a[:4], b):
+        assert torch.equal(x, y)

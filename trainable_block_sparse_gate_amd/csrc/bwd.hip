@@ -1,0 +1,635 @@
+// Gated block-sparse attention backward for gfx950.
+//
+// Gradients of o_t = sum_u P_tu v_u, P_t = softmax_u(scale q_t.k_u + log g),
+// which the pages say the fused kernel keeps through to the selector
+// (dimensionstp.github.io review, section 3-6; paperslantern paper text,
+// ablation results: the inner gate's gradient carries P_gated (dP - D)):
+//   D_t   = sum_e dO_te o_te            dP_tu = dO_t . v_u
+//   dS_tu = P_tu (dP_tu - D_t)          dq_t  = scale sum_u dS_tu k_u
+//   dk_u  = scale sum_t dS_tu q_t       dv_u  = sum_t P_tu dO_t
+//   dlg[row][slot] = sum over the row's tokens, its G heads and the slot's
+//                    keys of dS_tu       (the per-block log-gate gradient)
+//
+// Work split (all deterministic, no atomics on results):
+//   1. csr:    for every (kv head, key block), the (query block, slot) pairs
+//              that keep it, in query-block order (one wave per key block).
+//   2. scan:   segments of at most `seg` pairs per key block, prefix-summed.
+//   3. dq:     one workgroup per (query block, kv head) -- the forward's
+//              geometry; recomputes P from the saved lse, forms dS, and
+//              produces dq and the per-tile sums of dS (dlg).  D is first
+//              taken from the stored o (rounded to the output dtype) for dq;
+//              the exact D_t = sum_u P_tu dP_tu is accumulated over the tiles
+//              and used for dlg and, through the workspace, for dk.  dlg of a
+//              tile is sum P dP - sum_t D_t (sum over the tile of P_tu), so
+//              the rounding of o never enters the selector gradient.
+//   4. dkdv:   one workgroup per segment of a key block: K and V stay in
+//              registers, Q/dO tiles of the keeping rows stream through LDS
+//              (row-major and transposed), dK^T and dV^T accumulate in
+//              registers.  Key blocks kept by many rows are split over
+//              several segments whose partial sums
+//   5. reduce: are added in segment order.
+#include "sas_device.h"
+#include "sas_launch.h"
+#include "tile_stage.h"
+
+namespace sas {
+
+// ------------------------------------------------------------------ csr
+// One wave per x = g * QB + kb.  Rows that can keep key block j of sequence
+// s are its query blocks i >= j.
+__global__ __launch_bounds__(256) void bwd_csr_kernel(BwdParams p) {
+  const int x = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (x >= p.hkv * p.QB) return;
+  const int g = x / p.QB, kb = x % p.QB;
+  const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, kb);
+  const int q0 = p.cu_qblocks[s], nb = p.cu_qblocks[s + 1] - q0;
+  const int j = kb - q0;
+  int32_t *out = p.list + (long)x * p.max_nb;
+  int n = 0;
+  for (int i0 = j; i0 < nb; i0 += kWave) {
+    const int i = i0 + lane;
+    int slot = -1;
+    if (i < nb) {
+      const int32_t *sel = p.sel_idx + ((long)g * p.QB + q0 + i) * p.Kb;
+      for (int sl = 0; sl < p.Kb; ++sl)
+        if (sel[sl] == j) {
+          slot = sl;
+          break;
+        }
+    }
+    const uint64_t m = __ballot(slot >= 0);
+    if (slot >= 0) {
+      const int pos = n + __popcll(m & ((1ull << lane) - 1ull));
+      out[pos] = ((q0 + i) << 8) | slot;
+    }
+    n += __popcll(m);
+  }
+  if (lane == 0) p.count[x] = n;
+}
+
+// ------------------------------------------------------------------ scan
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p) {
+  __shared__ int part[kScanThreads];
+  const int n = p.hkv * p.QB;
+  const int per = (n + kScanThreads - 1) / kScanThreads;
+  const int b0 = threadIdx.x * per, b1 = min(n, b0 + per);
+  int local = 0;
+  for (int x = b0; x < b1; ++x) local += (p.count[x] + p.seg - 1) / p.seg;
+  part[threadIdx.x] = local;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    const int y = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += y;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - local;  // exclusive
+  for (int x = b0; x < b1; ++x) {
+    p.seg_off[x] = run;
+    run += (p.count[x] + p.seg - 1) / p.seg;
+  }
+  if (threadIdx.x == kScanThreads - 1) p.seg_off[n] = part[kScanThreads - 1];
+}
+
+// ------------------------------------------------------------------ dq
+template <typename T, typename TO, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
+  using M = Mfma<T>;
+  constexpr int NT = NW * kWave;
+  using KT = Tile4<T, D, NT>;  // K: row-major + transposed
+  using VT = Tile4<T, D, NT>;  // V: row-major
+  constexpr int KS = M::K, E = M::E;
+  constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
+
+  __shared__ __attribute__((aligned(16))) T Ks[kBlock * KT::ROW];
+  __shared__ __attribute__((aligned(16))) T Kt[D * KT::TROW];
+  __shared__ __attribute__((aligned(16))) T Vs[kBlock * VT::ROW];
+  __shared__ float s_F[NW][kMaxBudget];   // per tile: sum of P dP over the wave's rows
+  __shared__ int s_order[kMaxBudget];
+  __shared__ int s_n;
+  extern __shared__ float s_G[];         // [NW][Kb][64]: per tile, sum of P per query row
+
+  const T *q = static_cast<const T *>(p.q);
+  const T *kk = static_cast<const T *>(p.k);
+  const T *vv = static_cast<const T *>(p.v);
+  const TO *oo = static_cast<const TO *>(p.o);
+  const TO *dO = static_cast<const TO *>(p.dO);
+
+  const int Q = blockIdx.x;
+  const int nhc = (p.G + NW - 1) / NW;
+  const int g = blockIdx.y / nhc, hc = blockIdx.y % nhc;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int hf = lane / 32, l32 = lane % 32;
+  const int hh = hc * NW + wave;
+  const bool head_ok = hh < p.G;
+  const int h = g * p.G + (head_ok ? hh : 0);
+  const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, Q);
+  const int i = Q - p.cu_qblocks[s];
+  const int seq_start = p.cu_seqlens[s];
+  const int seq_len = p.cu_seqlens[s + 1] - seq_start;
+  const int nq = min(kBlock, seq_len - i * kBlock);
+  const long row = (long)g * p.QB + Q;
+  const int32_t *sel = p.sel_idx + row * p.Kb;
+  const float *slg = p.sel_lg + row * p.Kb;
+
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int sl = 0; sl < p.Kb; ++sl) {
+      const int j = sel[sl];
+      if (j >= 0 && j <= i) s_order[n++] = sl;
+    }
+    s_n = n;
+  }
+
+  // Q and dO as B operands (lane -> query column), D and lse per column.
+  typename M::Op qreg[2][NKS], doreg[2][NKS];
+  float Dv[2], lse2[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int ql = 32 * nt + l32;
+    const long t = seq_start + (long)i * kBlock + ql;
+    const long base = (t * p.hq + h) * D + hf * E;
+    float dacc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ql < nq) {
+        qreg[nt][ks] = lds_op<T>(q + base + ks * KS);
+        typename M::Op dv;
+        if constexpr (E == 8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float d_ = to_f32(dO[base + ks * KS + e]);
+            dacc += d_ * to_f32(oo[base + ks * KS + e]);
+            dv[e] = (T)d_;
+          }
+        } else {
+          const float d_ = to_f32(dO[base + ks * KS]);
+          dacc += d_ * to_f32(oo[base + ks * KS]);
+          dv = (T)d_;
+        }
+        doreg[nt][ks] = dv;
+      } else {
+        qreg[nt][ks] = typename M::Op{};
+        doreg[nt][ks] = typename M::Op{};
+      }
+    }
+    dacc += __shfl_xor(dacc, 32);
+    Dv[nt] = dacc;
+    lse2[nt] = INFINITY;  // padding rows: P = 0
+    if (ql < nq) lse2[nt] = p.lse[(long)h * p.T + t] * kLog2e;
+  }
+  float Eacc[2] = {0.f, 0.f};  // exact D: sum_u P dP (lane-partial)
+
+  f32x16 dqacc[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) dqacc[dt][nt] = f32x16{};
+
+  __syncthreads();
+  const int ntiles = s_n;
+  const long kstride = (long)p.hkv * D;
+  KT kst;
+  VT vst;
+  auto load_tile = [&](int it) {
+    const int j = sel[s_order[it]];
+    const long tok = seq_start + (long)j * kBlock;
+    const int nv = min(kBlock, seq_len - j * kBlock);
+    tile4_load<T, T, D, NT>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);
+    tile4_load<T, T, D, NT>(vst, vv + (tok * p.hkv + g) * D, kstride, nv);
+  };
+  if (ntiles > 0) load_tile(0);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int slot = s_order[it];
+    const int j = sel[slot];
+    const float lg2 = slg[slot] * kLog2e;
+    const bool diag = (j == i);
+    __syncthreads();
+    tile4_store_rm<T, D, NT>(kst, Ks);
+    tile4_store_tr<T, D, NT>(kst, Kt);
+    tile4_store_rm<T, D, NT>(vst, Vs);
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(it + 1);
+
+    float tile_F = 0.f;
+    float Gp[2] = {0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) sacc[nt] = pacc[nt] = f32x16{};
+      const int krow = 32 * mt + chain_key_of_row<T>(l32);
+      const T *ka = Ks + krow * KT::ROW + hf * E;
+      const T *va = Vs + krow * VT::ROW + hf * E;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const typename M::Op a = lds_op<T>(ka + ks * KS);
+        const typename M::Op b = lds_op<T>(va + ks * KS);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          sacc[nt] = M::run(a, qreg[nt][ks], sacc[nt]);
+          pacc[nt] = M::run(b, doreg[nt][ks], pacc[nt]);
+        }
+      }
+      // dS^T = P^T (dP^T - D), P^T recomputed from the saved lse
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int ql = 32 * nt + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = fast_exp2(sacc[nt][r] * p.scale_log2 + lg2 - lse2[nt]);
+          if (diag && 32 * mt + chain_slot<T>(r, hf) > ql) pr = 0.f;
+          const float pdp = pr * pacc[nt][r];
+          tile_F += pdp;
+          Eacc[nt] += pdp;
+          Gp[nt] += pr;
+          sacc[nt][r] = pdp - pr * Dv[nt];
+        }
+      }
+      // dQ^T[d][query] += K^T[d][key] dS^T[key][query] over this 32-key half
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const T *ta = Kt + (32 * dt + l32) * KT::TROW + 32 * mt + hf * E;
+#pragma unroll
+        for (int kc = 0; kc < SPT; ++kc) {
+          const typename M::Op a = lds_op<T>(ta + kc * KS);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            dqacc[dt][nt] = M::run(a, regs_op<T>(sacc[nt], kc * E), dqacc[dt][nt]);
+        }
+      }
+    }
+    tile_F = wave_sum(tile_F);
+    if (lane == 0) s_F[wave][it] = head_ok ? tile_F : 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float gsum = Gp[nt] + __shfl_xor(Gp[nt], 32);
+      if (hf == 0) s_G[(wave * p.Kb + it) * kBlock + 32 * nt + l32] = gsum;
+    }
+  }
+
+  // Exact D per query row, then dlg of each tile = sum P dP - sum_t D_t G_t.
+  float Ex[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    Ex[nt] = Eacc[nt] + __shfl_xor(Eacc[nt], 32);
+    const int ql = 32 * nt + l32;
+    if (ql < nq && hf == 0 && head_ok)
+      p.Dbuf[(long)h * p.T + seq_start + (long)i * kBlock + ql] = Ex[nt];
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    float c = 0.f;
+    if (hf == 0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) c += Ex[nt] * s_G[(wave * p.Kb + it) * kBlock + 32 * nt + l32];
+    }
+    c = wave_sum(c);
+    if (lane == 0) s_F[wave][it] = head_ok ? s_F[wave][it] - c : 0.f;
+  }
+
+  if (head_ok) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int ql = 32 * nt + l32;
+      if (ql >= nq) continue;
+      const long t = seq_start + (long)i * kBlock + ql;
+      float *dqp = p.dq + (t * p.hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = 32 * dt + d_row(4 * rg, hf);
+          *reinterpret_cast<float4 *>(dqp + d0) =
+              make_float4(dqacc[dt][nt][4 * rg] * p.scale, dqacc[dt][nt][4 * rg + 1] * p.scale,
+                          dqacc[dt][nt][4 * rg + 2] * p.scale,
+                          dqacc[dt][nt][4 * rg + 3] * p.scale);
+        }
+    }
+  }
+  __syncthreads();
+  // Per-slot log-gate gradient: heads of this workgroup summed in order.
+  float *dst = nhc == 1 ? p.dlg + row * p.Kb : p.dlg_part + ((long)hc * p.hkv * p.QB + row) * p.Kb;
+  for (int sl = threadIdx.x; sl < p.Kb; sl += NT) {
+    float val = 0.f;
+    for (int it = 0; it < ntiles; ++it)
+      if (s_order[it] == sl) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) val += s_F[w][it];
+      }
+    dst[sl] = val;
+  }
+}
+
+__global__ void bwd_dlg_sum_kernel(BwdParams p, int nhc) {
+  const long n = (long)p.hkv * p.QB * p.Kb;
+  const long x = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= n) return;
+  float v = 0.f;
+  for (int hc = 0; hc < nhc; ++hc) v += p.dlg_part[hc * n + x];
+  p.dlg[x] = v;
+}
+
+// ------------------------------------------------------------------ dk/dv
+// Workgroup of 4 waves: wave = (query half qh, key half kh).  Each wave
+// owns 32 keys (K, V as B operands in registers) and, per step, 32 of the
+// 64 query rows of one head of one keeping row.
+template <typename T, typename TO, int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+  using M = Mfma<T>;
+  constexpr int NT = 256;
+  using QT = Tile4<T, D, NT>;
+  constexpr int KS = M::K, E = M::E;
+  constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
+  constexpr int TILE_RM = kBlock * QT::ROW, TILE_TR = D * QT::TROW;
+  constexpr int LDS_T = 2 * (TILE_RM + TILE_TR);
+  constexpr int LDS_RED = 2 * 2 * NDT * 16 * kWave;  // floats: 2 waves x (dk, dv)
+  constexpr int LDS_BYTES =
+      (LDS_T * (int)sizeof(T) > LDS_RED * 4) ? LDS_T * (int)sizeof(T) : LDS_RED * 4;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) float s_lse[kBlock];
+  __shared__ __attribute__((aligned(16))) float s_D[kBlock];
+  T *Qs = reinterpret_cast<T *>(smem);
+  T *Qt = Qs + TILE_RM;
+  T *Ds = Qt + TILE_TR;
+  T *Dt = Ds + TILE_RM;
+
+  const int w = blockIdx.x;
+  const int nx = p.hkv * p.QB;
+  if (w >= p.seg_off[nx]) return;
+  int lo = 0, hi = nx - 1;  // largest x with seg_off[x] <= w
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.seg_off[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  const int x = lo;
+  const int g = x / p.QB, kb = x % p.QB;
+  const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, kb);
+  const int q0 = p.cu_qblocks[s];
+  const int j = kb - q0;
+  const int seq_start = p.cu_seqlens[s];
+  const int seq_len = p.cu_seqlens[s + 1] - seq_start;
+  const int nvalid = min(kBlock, seq_len - j * kBlock);
+  const long ktok0 = seq_start + (long)j * kBlock;
+  const int nseg = p.seg_off[x + 1] - p.seg_off[x];
+  const int seg = w - p.seg_off[x];
+  const int cnt = p.count[x];
+  const int e0 = seg * p.seg, e1 = min(cnt, e0 + p.seg);
+  const int32_t *list = p.list + (long)x * p.max_nb;
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int hf = lane / 32, l32 = lane % 32;
+  const int kh = wave % 2, qh = wave / 2;
+  const int key = 32 * kh + l32;  // this lane's key (column of S)
+
+  const T *q = static_cast<const T *>(p.q);
+  const T *kk = static_cast<const T *>(p.k);
+  const T *vv = static_cast<const T *>(p.v);
+  const TO *dO = static_cast<const TO *>(p.dO);
+
+  typename M::Op kreg[NKS], vreg[NKS];
+  {
+    const long base = ((ktok0 + key) * p.hkv + g) * D + hf * E;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (key < nvalid) {
+        kreg[ks] = lds_op<T>(kk + base + ks * KS);
+        vreg[ks] = lds_op<T>(vv + base + ks * KS);
+      } else {
+        kreg[ks] = typename M::Op{};
+        vreg[ks] = typename M::Op{};
+      }
+    }
+  }
+  f32x16 dkacc[NDT], dvacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
+
+  const int nsteps = (e1 - e0) * p.G;
+  const long qstride = (long)p.hq * D;
+  QT qst, dst;
+  float st_lse = 0.f, st_D = 0.f;
+  auto step_geom = [&](int st, int &Qrow, int &slot, int &hh) {
+    const int ent = list[e0 + st / p.G];
+    Qrow = ent >> 8;
+    slot = ent & 255;
+    hh = st % p.G;
+  };
+  auto load_step = [&](int st) {
+    int Qrow, slot, hh;
+    step_geom(st, Qrow, slot, hh);
+    const int i = Qrow - q0;
+    const int h = g * p.G + hh;
+    const long t0 = seq_start + (long)i * kBlock;
+    const int nq = min(kBlock, seq_len - i * kBlock);
+    tile4_load<T, T, D, NT>(qst, q + (t0 * p.hq + h) * D, qstride, nq);
+    tile4_load<TO, T, D, NT>(dst, dO + (t0 * p.hq + h) * D, qstride, nq);
+    if (threadIdx.x < kBlock) {
+      const bool ok = threadIdx.x < nq;
+      st_lse = ok ? p.lse[(long)h * p.T + t0 + threadIdx.x] : INFINITY;
+      st_D = ok ? p.Dbuf[(long)h * p.T + t0 + threadIdx.x] : 0.f;
+    }
+  };
+  if (nsteps > 0) load_step(0);
+
+  for (int st = 0; st < nsteps; ++st) {
+    int Qrow, slot, hh;
+    step_geom(st, Qrow, slot, hh);
+    const int i = Qrow - q0;
+    const int nq = min(kBlock, seq_len - i * kBlock);
+    const float lg2 = p.sel_lg[((long)g * p.QB + Qrow) * p.Kb + slot] * kLog2e;
+    const bool diag = (i == j);
+    __syncthreads();
+    tile4_store_rm<T, D, NT>(qst, Qs);
+    tile4_store_tr<T, D, NT>(qst, Qt);
+    tile4_store_rm<T, D, NT>(dst, Ds);
+    tile4_store_tr<T, D, NT>(dst, Dt);
+    if (threadIdx.x < kBlock) {
+      s_lse[threadIdx.x] = st_lse * kLog2e;
+      s_D[threadIdx.x] = st_D;
+    }
+    __syncthreads();
+    if (st + 1 < nsteps) load_step(st + 1);
+
+    // S[query][key] and dP[query][key] for 32 queries x this wave's 32 keys;
+    // query rows loaded in chain order so P and dS feed the next products.
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    const int qrow = 32 * qh + chain_key_of_row<T>(l32);
+    const T *qa = Qs + qrow * QT::ROW + hf * E;
+    const T *da = Ds + qrow * QT::ROW + hf * E;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      sacc = M::run(lds_op<T>(qa + ks * KS), kreg[ks], sacc);
+      pacc = M::run(lds_op<T>(da + ks * KS), vreg[ks], pacc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ql = 32 * qh + chain_slot<T>(r, hf);
+      const bool ok = ql < nq && key < nvalid && !(diag && key > ql);
+      const float pr = ok ? fast_exp2(sacc[r] * p.scale_log2 + lg2 - s_lse[ql]) : 0.f;
+      sacc[r] = pr;
+      pacc[r] = pr * (pacc[r] - s_D[ql]);
+    }
+    // dV^T[d][key] += dO^T[d][query] P[query][key];  dK^T += Q^T dS
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const T *doa = Dt + (32 * dt + l32) * QT::TROW + 32 * qh + hf * E;
+      const T *qta = Qt + (32 * dt + l32) * QT::TROW + 32 * qh + hf * E;
+#pragma unroll
+      for (int kc = 0; kc < SPT; ++kc) {
+        dvacc[dt] = M::run(lds_op<T>(doa + kc * KS), regs_op<T>(sacc, kc * E), dvacc[dt]);
+        dkacc[dt] = M::run(lds_op<T>(qta + kc * KS), regs_op<T>(pacc, kc * E), dkacc[dt]);
+      }
+    }
+  }
+
+  // Add the two query halves: waves qh = 1 hand their sums to qh = 0.
+  __syncthreads();
+  float *red = reinterpret_cast<float *>(smem);
+  if (qh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        red[((kh * 2 + 0) * NDT * 16 + dt * 16 + r) * kWave + lane] = dkacc[dt][r];
+        red[((kh * 2 + 1) * NDT * 16 + dt * 16 + r) * kWave + lane] = dvacc[dt][r];
+      }
+  }
+  __syncthreads();
+  if (qh == 1) return;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dkacc[dt][r] += red[((kh * 2 + 0) * NDT * 16 + dt * 16 + r) * kWave + lane];
+      dvacc[dt][r] += red[((kh * 2 + 1) * NDT * 16 + dt * 16 + r) * kWave + lane];
+    }
+  // Output: lane holds key `key`, 4 consecutive d per register group.
+  float *dk_out, *dv_out;
+  long kstride;
+  if (nseg == 1) {
+    if (key >= nvalid) return;
+    dk_out = p.dk + ((ktok0 + key) * p.hkv + g) * D;
+    dv_out = p.dv + ((ktok0 + key) * p.hkv + g) * D;
+  } else {
+    float *part = p.partial + (long)w * 2 * kBlock * D;
+    dk_out = part + (long)key * D;
+    dv_out = part + (long)(kBlock + key) * D;
+  }
+  (void)kstride;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * dt + d_row(4 * rg, hf);
+      *reinterpret_cast<float4 *>(dk_out + d0) =
+          make_float4(dkacc[dt][4 * rg] * p.scale, dkacc[dt][4 * rg + 1] * p.scale,
+                      dkacc[dt][4 * rg + 2] * p.scale, dkacc[dt][4 * rg + 3] * p.scale);
+      *reinterpret_cast<float4 *>(dv_out + d0) =
+          make_float4(dvacc[dt][4 * rg], dvacc[dt][4 * rg + 1], dvacc[dt][4 * rg + 2],
+                      dvacc[dt][4 * rg + 3]);
+    }
+}
+
+// ------------------------------------------------------------------ reduce
+// Key blocks split over several segments (or kept by no row): sum the
+// partials in segment order (zeros when there are none).
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int D) {
+  const int x = blockIdx.x;
+  const int nseg = p.seg_off[x + 1] - p.seg_off[x];
+  if (nseg == 1) return;
+  const int kb = x % p.QB, g = x / p.QB;
+  const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, kb);
+  const int j = kb - p.cu_qblocks[s];
+  const int seq_start = p.cu_seqlens[s];
+  const int nvalid = min(kBlock, p.cu_seqlens[s + 1] - seq_start - j * kBlock);
+  const long ktok0 = seq_start + (long)j * kBlock;
+  const int n = kBlock * D;
+  const float *part = p.partial + (long)p.seg_off[x] * 2 * n;
+  for (int e = threadIdx.x * 4; e < 2 * n; e += 256 * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sg = 0; sg < nseg; ++sg) {
+      const float4 v = *reinterpret_cast<const float4 *>(part + (long)sg * 2 * n + e);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const int which = e / n, key = (e % n) / D, d = e % D;
+    if (key >= nvalid) continue;
+    float *out = (which == 0 ? p.dk : p.dv) + ((ktok0 + key) * p.hkv + g) * D + d;
+    *reinterpret_cast<float4 *>(out) = acc;
+  }
+}
+
+// ------------------------------------------------------------------ launch
+constexpr int kLdsBytes = 160 * 1024;
+
+template <typename T, int D, int NW>
+constexpr int dq_static_lds() {
+  return (int)sizeof(T) * (2 * kBlock * Tile4<T, D, NW * 64>::ROW + D * Tile4<T, D, NW * 64>::TROW) +
+         (NW + 1) * kMaxBudget * 4 + 64;
+}
+
+template <typename T, int D, int NW>
+static size_t dq_dynamic_lds(const BwdParams &p) {
+  return sizeof(float) * NW * p.Kb * kBlock;
+}
+
+template <typename T, typename TO, int D, int NW>
+static hipError_t launch_dq_t(const BwdParams &p, hipStream_t stream) {
+  const int nhc = (p.G + NW - 1) / NW;
+  const size_t dyn = dq_dynamic_lds<T, D, NW>(p);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, TO, D, NW>), dim3(p.QB, p.hkv * nhc), dim3(NW * 64), dyn,
+                     stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nhc == 1) return e;
+  const long n = (long)p.hkv * p.QB * p.Kb;
+  hipLaunchKernelGGL(bwd_dlg_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p, nhc);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static bool dq_fits(const BwdParams &p) {
+  if (p.G >= 4) return dq_static_lds<T, D, 4>() + dq_dynamic_lds<T, D, 4>(p) <= kLdsBytes;
+  if (p.G >= 2) return dq_static_lds<T, D, 2>() + dq_dynamic_lds<T, D, 2>(p) <= kLdsBytes;
+  return dq_static_lds<T, D, 1>() + dq_dynamic_lds<T, D, 1>(p) <= kLdsBytes;
+}
+
+template <typename T, typename TO, int D>
+static hipError_t launch_bwd_d(const BwdParams &p, hipStream_t stream) {
+  if (!dq_fits<T, D>(p)) return hipErrorNotSupported;  // nothing launched
+  const int nx = p.hkv * p.QB;
+  hipLaunchKernelGGL(bwd_csr_kernel, dim3((nx + 3) / 4), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_seg_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.G >= 4)
+    e = launch_dq_t<T, TO, D, 4>(p, stream);
+  else if (p.G >= 2)
+    e = launch_dq_t<T, TO, D, 2>(p, stream);
+  else
+    e = launch_dq_t<T, TO, D, 1>(p, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, TO, D>), dim3(p.U), dim3(256), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(nx), dim3(256), 0, stream, p, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
+                      hipStream_t stream) {
+  if (dtype_bf16) {
+    if (out_bf16)
+      return head_dim == 128 ? launch_bwd_d<__bf16, __bf16, 128>(p, stream)
+                             : launch_bwd_d<__bf16, __bf16, 64>(p, stream);
+    return head_dim == 128 ? launch_bwd_d<__bf16, float, 128>(p, stream)
+                           : launch_bwd_d<__bf16, float, 64>(p, stream);
+  }
+  return head_dim == 128 ? launch_bwd_d<float, float, 128>(p, stream)
+                         : launch_bwd_d<float, float, 64>(p, stream);
+}
+
+}  // namespace sas

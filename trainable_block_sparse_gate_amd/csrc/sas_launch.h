@@ -52,4 +52,26 @@ struct FwdParams {
 hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
                       hipStream_t stream);
 
+struct BwdParams {
+  const void *q, *k, *v, *o, *dO;
+  const float *lse;
+  const int32_t *sel_idx;
+  const float *sel_lg;
+  float *dq, *dk, *dv, *dlg;
+  const int32_t *cu_seqlens, *cu_qblocks;
+  int num_seqs, T, QB, hq, hkv, G, Kb, max_nb;
+  float scale, scale_log2;
+  // workspace carve-up
+  float *Dbuf;       // [hq][T]      rowsum(dO * o)
+  int32_t *list;     // [hkv*QB][max_nb]  (query block << 8 | slot) per key block
+  int32_t *count;    // [hkv*QB]
+  int32_t *seg_off;  // [hkv*QB + 1] prefix sum of segments per key block
+  float *dlg_part;   // [nhc][hkv*QB][Kb] when a row's heads span workgroups
+  float *partial;    // [U][2][64][D] partial dK / dV of split key blocks
+  int seg;           // keeping rows per segment
+  int U;             // upper bound on the number of segments (dk/dv grid)
+};
+hipError_t launch_bwd(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
+                      hipStream_t stream);
+
 }  // namespace sas

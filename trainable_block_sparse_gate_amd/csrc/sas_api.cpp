@@ -302,32 +302,153 @@ sas_status sas_bwd(const sas_problem *p, const void *q, const void *k, const voi
   return from_hip(e, "bwd launch");
 }
 
+namespace {
+
+sas_status check_decode(const sas_decode_problem *p) {
+  REQUIRE(p, SAS_ERR_NULL, "decode problem is NULL");
+  REQUIRE(p->block == 64, SAS_ERR_UNSUPPORTED, "block must be 64 (got %d)", p->block);
+  REQUIRE(p->head_dim == 64 || p->head_dim == 128, SAS_ERR_UNSUPPORTED,
+          "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  REQUIRE(p->batch >= 1, SAS_ERR_SHAPE, "batch must be >= 1");
+  REQUIRE(p->hq > 0 && p->hkv > 0 && p->hq % p->hkv == 0, SAS_ERR_SHAPE,
+          "hq (%d) must be a positive multiple of hkv (%d)", p->hq, p->hkv);
+  const int G = p->hq / p->hkv;
+  REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, SAS_ERR_UNSUPPORTED,
+          "decode supports query groups of 1, 2, 4 or 8 heads (got %d)", G);
+  REQUIRE(p->budget_blocks >= 1 && p->budget_blocks <= sas::kMaxBudget, SAS_ERR_UNSUPPORTED,
+          "budget_blocks must be in [1, %d] (got %d)", sas::kMaxBudget, p->budget_blocks);
+  REQUIRE(p->dtype == SAS_BF16, SAS_ERR_DTYPE, "decode takes bf16 q and caches");
+  REQUIRE(p->out_dtype == SAS_BF16 || p->out_dtype == SAS_F32, SAS_ERR_DTYPE,
+          "unknown out_dtype %d", p->out_dtype);
+  REQUIRE(p->layout == SAS_KV_CONTIGUOUS || p->layout == SAS_KV_PAGED, SAS_ERR_SHAPE,
+          "unknown layout %d", p->layout);
+  REQUIRE(std::isfinite(p->scale), SAS_ERR_SHAPE, "scale is not finite");
+  REQUIRE(p->seqlens && p->seqlens_host, SAS_ERR_NULL, "seqlens (device and host) required");
+  int maxL = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    REQUIRE(p->seqlens_host[b] >= 1, SAS_ERR_SHAPE, "seqlens[%d] = %d < 1", b,
+            p->seqlens_host[b]);
+    if (p->seqlens_host[b] > maxL) maxL = p->seqlens_host[b];
+  }
+  if (p->layout == SAS_KV_CONTIGUOUS) {
+    REQUIRE(p->max_seqlen >= maxL, SAS_ERR_SHAPE, "max_seqlen (%d) < longest sequence (%d)",
+            p->max_seqlen, maxL);
+  } else {
+    REQUIRE(p->page_table, SAS_ERR_NULL, "paged layout needs a page table");
+    REQUIRE(p->max_pages >= (maxL + 63) / 64, SAS_ERR_SHAPE,
+            "max_pages (%d) < pages of the longest sequence (%d)", p->max_pages,
+            (maxL + 63) / 64);
+    REQUIRE(p->num_pages >= 1, SAS_ERR_SHAPE, "num_pages must be >= 1");
+  }
+  REQUIRE(p->nblk_stride >= 1 && p->nblk_stride >= (maxL - 1) / 64, SAS_ERR_SHAPE,
+          "nblk_stride (%d) < history blocks of the longest sequence (%d)", p->nblk_stride,
+          (maxL - 1) / 64);
+  return SAS_OK;
+}
+
+sas::DecodeParams decode_params(const sas_decode_problem *p) {
+  sas::DecodeParams d{};
+  d.seqlens = p->seqlens;
+  d.page_table = p->page_table;
+  d.paged = p->layout == SAS_KV_PAGED;
+  d.max_pages = p->max_pages;
+  d.max_seqlen = p->max_seqlen;
+  d.batch = p->batch;
+  d.hq = p->hq;
+  d.hkv = p->hkv;
+  d.D = p->head_dim;
+  d.Kb = p->budget_blocks;
+  d.nblk_stride = p->nblk_stride;
+  d.sqrt_d = sqrtf((float)p->head_dim);
+  d.scale_log2 = p->scale * 1.4426950408889634f;
+  d.out_bf16 = p->out_dtype == SAS_BF16;
+  // split-K: enough workgroups to cover the chip several times over
+  const int rows = p->batch * p->hkv;
+  int nsplit = (2048 + rows - 1) / rows;
+  if (nsplit > p->budget_blocks) nsplit = p->budget_blocks;
+  if (nsplit < 1) nsplit = 1;
+  d.per_split = (p->budget_blocks + nsplit - 1) / nsplit;
+  d.nsplit = (p->budget_blocks + d.per_split - 1) / d.per_split;
+  return d;
+}
+
+size_t decode_ws_bytes(const sas_decode_problem *p) {
+  const sas::DecodeParams d = decode_params(p);
+  return sizeof(float) * (size_t)p->batch * p->hkv * d.nsplit * (p->hq / p->hkv) *
+         (p->head_dim + 2);
+}
+
+}  // namespace
+
 size_t sas_decode_workspace_size(const sas_decode_problem *p) {
-  (void)p;
-  return 0;
+  if (check_decode(p) != SAS_OK) return 0;
+  return decode_ws_bytes(p);
 }
 
 sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, float *ksum,
                          void *stream) {
-  (void)p, (void)k_cache, (void)ksum, (void)stream;
-  return fail(SAS_ERR_UNSUPPORTED, "sas_pool_keys is not built yet");
+  sas_status st = check_decode(p);
+  if (st) return st;
+  REQUIRE(k_cache && ksum, SAS_ERR_NULL, "k_cache / ksum is NULL");
+  REQUIRE(aligned16(k_cache), SAS_ERR_ALIGN, "k_cache must be 16-byte aligned");
+  sas::DecodeParams d = decode_params(p);
+  d.k = k_cache;
+  d.ksum = ksum;
+  return from_hip(sas::launch_pool_keys(d, (hipStream_t)stream), "pool_keys launch");
 }
 
 sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const float *ksum,
                              float *scores, int32_t *sel_idx, float *sel_loggate,
                              float *gate_lse, void *stream) {
-  (void)p, (void)q, (void)ksum, (void)scores, (void)sel_idx, (void)sel_loggate, (void)gate_lse;
-  (void)stream;
-  return fail(SAS_ERR_UNSUPPORTED, "sas_decode_select is not built yet");
+  sas_status st = check_decode(p);
+  if (st) return st;
+  REQUIRE(q && ksum && scores && sel_idx && sel_loggate && gate_lse, SAS_ERR_NULL,
+          "a tensor argument of sas_decode_select is NULL");
+  sas::DecodeParams d = decode_params(p);
+  d.q = q;
+  d.ksum = const_cast<float *>(ksum);
+  d.scores = scores;
+  hipError_t e = sas::launch_pooled_scores(d, (hipStream_t)stream);
+  if (e != hipSuccess) return from_hip(e, "pooled scores launch");
+  sas::GateParams g{};
+  g.scores = scores;
+  g.ld = p->nblk_stride;
+  g.decode = 1;
+  g.hkv = p->hkv;
+  g.seqlens = p->seqlens;
+  g.Kb = p->budget_blocks;
+  g.mode = SAS_GATE_HIST;
+  g.sel_idx = sel_idx;
+  g.sel_lg = sel_loggate;
+  g.gate_lse = gate_lse;
+  g.nrows = p->batch * p->hkv;
+  return from_hip(sas::launch_gate_topk(g, (hipStream_t)stream), "decode gate_topk launch");
 }
 
 sas_status sas_decode(const sas_decode_problem *p, const void *q, const void *k_cache,
                       const void *v_cache, const int32_t *sel_idx, const float *sel_loggate,
                       void *o, float *lse, void *workspace, size_t workspace_bytes,
                       void *stream) {
-  (void)p, (void)q, (void)k_cache, (void)v_cache, (void)sel_idx, (void)sel_loggate, (void)o;
-  (void)lse, (void)workspace, (void)workspace_bytes, (void)stream;
-  return fail(SAS_ERR_UNSUPPORTED, "sas_decode is not built yet");
+  sas_status st = check_decode(p);
+  if (st) return st;
+  REQUIRE(q && k_cache && v_cache && sel_idx && o, SAS_ERR_NULL,
+          "q, k_cache, v_cache, sel_idx and o are required");
+  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(o),
+          SAS_ERR_ALIGN, "q, caches and o must be 16-byte aligned");
+  const size_t need = decode_ws_bytes(p);
+  REQUIRE(workspace && workspace_bytes >= need, SAS_ERR_WORKSPACE,
+          "workspace has %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
+  REQUIRE(aligned16(workspace), SAS_ERR_ALIGN, "workspace must be 16-byte aligned");
+  sas::DecodeParams d = decode_params(p);
+  d.q = q;
+  d.k = k_cache;
+  d.v = v_cache;
+  d.sel_idx = sel_idx;
+  d.sel_lg = sel_loggate;
+  d.o = o;
+  d.lse = lse;
+  d.partial = static_cast<float *>(workspace);
+  return from_hip(sas::launch_decode_attend(d, (hipStream_t)stream), "decode launch");
 }
 
 }  // extern "C"

@@ -74,4 +74,26 @@ struct BwdParams {
 hipError_t launch_bwd(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
                       hipStream_t stream);
 
+struct DecodeParams {
+  const void *q, *k, *v;       // q [batch][hq][D]; caches in either layout
+  const int32_t *seqlens;      // [batch]
+  const int32_t *page_table;   // [batch][max_pages] when paged
+  int paged, max_pages, max_seqlen;
+  int batch, hq, hkv, D, Kb, nblk_stride;
+  float *ksum;                 // [batch][hkv][D][nblk_stride]
+  float *scores;               // [batch][hkv][nblk_stride]
+  float sqrt_d;                // sqrtf(D), for the pooled score
+  const int32_t *sel_idx;      // [batch*hkv][Kb]
+  const float *sel_lg;         // [batch*hkv][Kb] or NULL
+  void *o;                     // [batch][hq][D]
+  float *lse;                  // [batch][hq] or NULL
+  float scale_log2;
+  int out_bf16;
+  int nsplit, per_split;       // split-K geometry
+  float *partial;              // [batch*hkv][nsplit][G][D + 2]
+};
+hipError_t launch_pool_keys(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_pooled_scores(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_attend(const DecodeParams &p, hipStream_t stream);
+
 }  // namespace sas

@@ -158,6 +158,27 @@ sas_status sas_bwd(const sas_problem *p, const void *q, const void *k, const voi
                    float *d_loggate, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The three phases sas_bwd runs, in this order on one workspace (a caller
+ * may time them or place them on its own streams, keeping the order):
+ *   sas_bwd_prepare  lists, for every (kv head, key block), the (query
+ *                    block, slot) pairs that keep it, in query-block order.
+ *   sas_bwd_dq       dq and d_loggate; also stores in the workspace the
+ *                    exact row term D_t = sum_u P_tu dP_tu that dk needs.
+ *   sas_bwd_dkdv     dk and dv; reads the lists and D_t written above.
+ * budget_blocks is limited by LDS in sas_bwd_dq (SAS_ERR_UNSUPPORTED when
+ * it does not fit: at most about 100 blocks at head_dim 128 in bf16).
+ */
+sas_status sas_bwd_prepare(const sas_problem *p, const int32_t *sel_idx, void *workspace,
+                           size_t workspace_bytes, void *stream);
+sas_status sas_bwd_dq(const sas_problem *p, const void *q, const void *k, const void *v,
+                      const void *o, const void *dO, const float *lse, const int32_t *sel_idx,
+                      const float *sel_loggate, float *dq, float *d_loggate, void *workspace,
+                      size_t workspace_bytes, void *stream);
+sas_status sas_bwd_dkdv(const sas_problem *p, const void *q, const void *k, const void *v,
+                        const void *dO, const float *lse, const float *sel_loggate, float *dk,
+                        float *dv, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * sas_gate_bwd -- selector-logit gradient from the log-gate gradient through
  * the gate softmax (review 2-1; paper text, ablation results: the normaliser
  * is shared by all history blocks):

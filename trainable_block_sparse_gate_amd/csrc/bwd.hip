@@ -26,8 +26,9 @@
 //              registers, Q/dO tiles of the keeping rows stream through LDS
 //              (row-major and transposed), dK^T and dV^T accumulate in
 //              registers.  Key blocks kept by many rows are split over
-//              several segments whose partial sums
-//   5. reduce: are added in segment order.
+//              several segments; each writes a partial sum and the last one
+//              to finish adds all of them in segment order, so the result
+//              does not depend on which workgroup finishes last.
 #include "sas_device.h"
 #include "sas_launch.h"
 #include "tile_stage.h"
@@ -76,8 +77,13 @@ __global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p)
   const int n = p.hkv * p.QB;
   const int per = (n + kScanThreads - 1) / kScanThreads;
   const int b0 = threadIdx.x * per, b1 = min(n, b0 + per);
+  // every key block gets at least one segment (a block no row keeps then
+  // simply writes zeros)
   int local = 0;
-  for (int x = b0; x < b1; ++x) local += (p.count[x] + p.seg - 1) / p.seg;
+  for (int x = b0; x < b1; ++x) {
+    local += max(1, (p.count[x] + p.seg - 1) / p.seg);
+    p.done[x] = 0;
+  }
   part[threadIdx.x] = local;
   __syncthreads();
   for (int o = 1; o < kScanThreads; o <<= 1) {
@@ -89,7 +95,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p)
   int run = part[threadIdx.x] - local;  // exclusive
   for (int x = b0; x < b1; ++x) {
     p.seg_off[x] = run;
-    run += (p.count[x] + p.seg - 1) / p.seg;
+    run += max(1, (p.count[x] + p.seg - 1) / p.seg);
   }
   if (threadIdx.x == kScanThreads - 1) p.seg_off[n] = part[kScanThreads - 1];
 }
@@ -500,65 +506,62 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       }
   }
   __syncthreads();
-  if (qh == 1) return;
+  if (qh == 0) {
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dkacc[dt][r] += red[((kh * 2 + 0) * NDT * 16 + dt * 16 + r) * kWave + lane];
-      dvacc[dt][r] += red[((kh * 2 + 1) * NDT * 16 + dt * 16 + r) * kWave + lane];
+      for (int r = 0; r < 16; ++r) {
+        dkacc[dt][r] += red[((kh * 2 + 0) * NDT * 16 + dt * 16 + r) * kWave + lane];
+        dvacc[dt][r] += red[((kh * 2 + 1) * NDT * 16 + dt * 16 + r) * kWave + lane];
+      }
+    // lane holds key `key`, 4 consecutive d per register group
+    float *dk_out, *dv_out;
+    bool write = true;
+    if (nseg == 1) {
+      write = key < nvalid;
+      dk_out = p.dk + ((ktok0 + key) * p.hkv + g) * D;
+      dv_out = p.dv + ((ktok0 + key) * p.hkv + g) * D;
+    } else {
+      float *part = p.partial + (long)w * 2 * kBlock * D;
+      dk_out = part + (long)key * D;
+      dv_out = part + (long)(kBlock + key) * D;
     }
-  // Output: lane holds key `key`, 4 consecutive d per register group.
-  float *dk_out, *dv_out;
-  long kstride;
-  if (nseg == 1) {
-    if (key >= nvalid) return;
-    dk_out = p.dk + ((ktok0 + key) * p.hkv + g) * D;
-    dv_out = p.dv + ((ktok0 + key) * p.hkv + g) * D;
-  } else {
-    float *part = p.partial + (long)w * 2 * kBlock * D;
-    dk_out = part + (long)key * D;
-    dv_out = part + (long)(kBlock + key) * D;
+    if (write) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = 32 * dt + d_row(4 * rg, hf);
+          *reinterpret_cast<float4 *>(dk_out + d0) =
+              make_float4(dkacc[dt][4 * rg] * p.scale, dkacc[dt][4 * rg + 1] * p.scale,
+                          dkacc[dt][4 * rg + 2] * p.scale, dkacc[dt][4 * rg + 3] * p.scale);
+          *reinterpret_cast<float4 *>(dv_out + d0) =
+              make_float4(dvacc[dt][4 * rg], dvacc[dt][4 * rg + 1], dvacc[dt][4 * rg + 2],
+                          dvacc[dt][4 * rg + 3]);
+        }
+    }
   }
-  (void)kstride;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = 32 * dt + d_row(4 * rg, hf);
-      *reinterpret_cast<float4 *>(dk_out + d0) =
-          make_float4(dkacc[dt][4 * rg] * p.scale, dkacc[dt][4 * rg + 1] * p.scale,
-                      dkacc[dt][4 * rg + 2] * p.scale, dkacc[dt][4 * rg + 3] * p.scale);
-      *reinterpret_cast<float4 *>(dv_out + d0) =
-          make_float4(dvacc[dt][4 * rg], dvacc[dt][4 * rg + 1], dvacc[dt][4 * rg + 2],
-                      dvacc[dt][4 * rg + 3]);
-    }
-}
-
-// ------------------------------------------------------------------ reduce
-// Key blocks split over several segments (or kept by no row): sum the
-// partials in segment order (zeros when there are none).
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int D) {
-  const int x = blockIdx.x;
-  const int nseg = p.seg_off[x + 1] - p.seg_off[x];
   if (nseg == 1) return;
-  const int kb = x % p.QB, g = x / p.QB;
-  const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, kb);
-  const int j = kb - p.cu_qblocks[s];
-  const int seq_start = p.cu_seqlens[s];
-  const int nvalid = min(kBlock, p.cu_seqlens[s + 1] - seq_start - j * kBlock);
-  const long ktok0 = seq_start + (long)j * kBlock;
+
+  // Split key block: the last segment to finish adds the partials in order.
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomicAdd(&p.done[x], 1) == nseg - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
   const int n = kBlock * D;
-  const float *part = p.partial + (long)p.seg_off[x] * 2 * n;
+  const float *part0 = p.partial + (long)p.seg_off[x] * 2 * n;
   for (int e = threadIdx.x * 4; e < 2 * n; e += 256 * 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int sg = 0; sg < nseg; ++sg) {
-      const float4 v = *reinterpret_cast<const float4 *>(part + (long)sg * 2 * n + e);
+      const float4 v = *reinterpret_cast<const float4 *>(part0 + (long)sg * 2 * n + e);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
-    const int which = e / n, key = (e % n) / D, d = e % D;
-    if (key >= nvalid) continue;
-    float *out = (which == 0 ? p.dk : p.dv) + ((ktok0 + key) * p.hkv + g) * D + d;
+    const int which = e / n, kk2 = (e % n) / D, d = e % D;
+    if (kk2 >= nvalid) continue;
+    float *out = (which == 0 ? p.dk : p.dv) + ((ktok0 + kk2) * p.hkv + g) * D + d;
     *reinterpret_cast<float4 *>(out) = acc;
   }
 }
@@ -597,39 +600,58 @@ static bool dq_fits(const BwdParams &p) {
   return dq_static_lds<T, D, 1>() + dq_dynamic_lds<T, D, 1>(p) <= kLdsBytes;
 }
 
-template <typename T, typename TO, int D>
-static hipError_t launch_bwd_d(const BwdParams &p, hipStream_t stream) {
-  if (!dq_fits<T, D>(p)) return hipErrorNotSupported;  // nothing launched
+hipError_t launch_bwd_prepare(const BwdParams &p, hipStream_t stream) {
   const int nx = p.hkv * p.QB;
   hipLaunchKernelGGL(bwd_csr_kernel, dim3((nx + 3) / 4), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_seg_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (p.G >= 4)
-    e = launch_dq_t<T, TO, D, 4>(p, stream);
-  else if (p.G >= 2)
-    e = launch_dq_t<T, TO, D, 2>(p, stream);
-  else
-    e = launch_dq_t<T, TO, D, 1>(p, stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, TO, D>), dim3(p.U), dim3(256), 0, stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(nx), dim3(256), 0, stream, p, D);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
-                      hipStream_t stream) {
+template <typename T, typename TO, int D>
+static hipError_t launch_dq_d(const BwdParams &p, hipStream_t stream) {
+  if (!dq_fits<T, D>(p)) return hipErrorNotSupported;  // nothing launched
+  if (p.G >= 4) return launch_dq_t<T, TO, D, 4>(p, stream);
+  if (p.G >= 2) return launch_dq_t<T, TO, D, 2>(p, stream);
+  return launch_dq_t<T, TO, D, 1>(p, stream);
+}
+
+hipError_t launch_bwd_dq(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
+                         hipStream_t stream) {
   if (dtype_bf16) {
     if (out_bf16)
-      return head_dim == 128 ? launch_bwd_d<__bf16, __bf16, 128>(p, stream)
-                             : launch_bwd_d<__bf16, __bf16, 64>(p, stream);
-    return head_dim == 128 ? launch_bwd_d<__bf16, float, 128>(p, stream)
-                           : launch_bwd_d<__bf16, float, 64>(p, stream);
+      return head_dim == 128 ? launch_dq_d<__bf16, __bf16, 128>(p, stream)
+                             : launch_dq_d<__bf16, __bf16, 64>(p, stream);
+    return head_dim == 128 ? launch_dq_d<__bf16, float, 128>(p, stream)
+                           : launch_dq_d<__bf16, float, 64>(p, stream);
   }
-  return head_dim == 128 ? launch_bwd_d<float, float, 128>(p, stream)
-                         : launch_bwd_d<float, float, 64>(p, stream);
+  return head_dim == 128 ? launch_dq_d<float, float, 128>(p, stream)
+                         : launch_dq_d<float, float, 64>(p, stream);
+}
+
+bool bwd_dq_supported(const BwdParams &p, int dtype_bf16, int head_dim) {
+  if (dtype_bf16) return head_dim == 128 ? dq_fits<__bf16, 128>(p) : dq_fits<__bf16, 64>(p);
+  return head_dim == 128 ? dq_fits<float, 128>(p) : dq_fits<float, 64>(p);
+}
+
+template <typename T, typename TO, int D>
+static hipError_t launch_dkdv_t(const BwdParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, TO, D>), dim3(p.U), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
+                           hipStream_t stream) {
+  if (dtype_bf16) {
+    if (out_bf16)
+      return head_dim == 128 ? launch_dkdv_t<__bf16, __bf16, 128>(p, stream)
+                             : launch_dkdv_t<__bf16, __bf16, 64>(p, stream);
+    return head_dim == 128 ? launch_dkdv_t<__bf16, float, 128>(p, stream)
+                           : launch_dkdv_t<__bf16, float, 64>(p, stream);
+  }
+  return head_dim == 128 ? launch_dkdv_t<float, float, 128>(p, stream)
+                         : launch_dkdv_t<float, float, 64>(p, stream);
 }
 
 }  // namespace sas

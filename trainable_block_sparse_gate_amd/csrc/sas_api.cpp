@@ -204,7 +204,7 @@ namespace {
 constexpr int kSeg = 32;  // keeping rows per dk/dv segment
 
 struct BwdLayout {
-  size_t off_D, off_list, off_count, off_segoff, off_dlgpart, off_partial, total;
+  size_t off_D, off_list, off_count, off_segoff, off_done, off_dlgpart, off_partial, total;
   int U, nhc, max_nb;
 };
 
@@ -217,17 +217,58 @@ BwdLayout bwd_layout(const sas_problem *p, int max_nb) {
   const int nw = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
   L.nhc = (G + nw - 1) / nw;
   L.max_nb = max_nb > 0 ? max_nb : 1;
+  // segments: sum over key blocks of max(1, ceil(count / kSeg)), count <= kept entries
   L.U = (int)((nx * p->budget_blocks + kSeg - 1) / kSeg + nx);
   size_t off = 0;
   L.off_D = off;        off = align256(off + sizeof(float) * (size_t)p->hq * p->total_tokens);
   L.off_list = off;     off = align256(off + sizeof(int32_t) * nx * L.max_nb);
   L.off_count = off;    off = align256(off + sizeof(int32_t) * nx);
   L.off_segoff = off;   off = align256(off + sizeof(int32_t) * (nx + 1));
+  L.off_done = off;     off = align256(off + sizeof(int32_t) * nx);
   L.off_dlgpart = off;
   if (L.nhc > 1) off = align256(off + sizeof(float) * L.nhc * nx * p->budget_blocks);
   L.off_partial = off;  off = align256(off + sizeof(float) * (size_t)L.U * 2 * 64 * p->head_dim);
   L.total = off;
   return L;
+}
+
+// Checks shared by the backward phases; fills the kernel parameters.
+sas_status bwd_setup(const sas_problem *p, void *workspace, size_t workspace_bytes,
+                     sas::BwdParams *b) {
+  int mb = 0;
+  sas_status st = check_problem(p, &mb);
+  if (st) return st;
+  REQUIRE(p->total_qblocks < (1 << 23), SAS_ERR_UNSUPPORTED,
+          "total_qblocks must be below 2^23 (got %d)", p->total_qblocks);
+  const BwdLayout L = bwd_layout(p, mb);
+  REQUIRE(workspace, SAS_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", L.total);
+  REQUIRE(workspace_bytes >= L.total, SAS_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+          workspace_bytes, L.total);
+  REQUIRE(aligned16(workspace), SAS_ERR_ALIGN, "workspace must be 16-byte aligned");
+  char *ws = static_cast<char *>(workspace);
+  *b = sas::BwdParams{};
+  b->cu_seqlens = p->cu_seqlens;
+  b->cu_qblocks = p->cu_qblocks;
+  b->num_seqs = p->num_seqs;
+  b->T = p->total_tokens;
+  b->QB = p->total_qblocks;
+  b->hq = p->hq;
+  b->hkv = p->hkv;
+  b->G = p->hq / p->hkv;
+  b->Kb = p->budget_blocks;
+  b->max_nb = L.max_nb;
+  b->scale = p->scale;
+  b->scale_log2 = p->scale * 1.4426950408889634f;
+  b->Dbuf = reinterpret_cast<float *>(ws + L.off_D);
+  b->list = reinterpret_cast<int32_t *>(ws + L.off_list);
+  b->count = reinterpret_cast<int32_t *>(ws + L.off_count);
+  b->seg_off = reinterpret_cast<int32_t *>(ws + L.off_segoff);
+  b->done = reinterpret_cast<int32_t *>(ws + L.off_done);
+  b->dlg_part = reinterpret_cast<float *>(ws + L.off_dlgpart);
+  b->partial = reinterpret_cast<float *>(ws + L.off_partial);
+  b->seg = kSeg;
+  b->U = L.U;
+  return SAS_OK;
 }
 
 }  // namespace
@@ -238,29 +279,33 @@ size_t sas_bwd_workspace_size(const sas_problem *p) {
   return bwd_layout(p, mb).total;
 }
 
-sas_status sas_bwd(const sas_problem *p, const void *q, const void *k, const void *v,
-                   const void *o, const void *dO, const float *lse, const int32_t *sel_idx,
-                   const float *sel_loggate, float *dq, float *dk, float *dv,
-                   float *d_loggate, void *workspace, size_t workspace_bytes, void *stream) {
-  int mb = 0;
-  sas_status st = check_problem(p, &mb);
+sas_status sas_bwd_prepare(const sas_problem *p, const int32_t *sel_idx, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  sas::BwdParams b;
+  sas_status st = bwd_setup(p, workspace, workspace_bytes, &b);
   if (st) return st;
-  REQUIRE(q && k && v && o && dO && lse && sel_idx && sel_loggate && dq && dk && dv &&
-              d_loggate,
-          SAS_ERR_NULL, "a tensor argument of sas_bwd is NULL");
-  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(dO) &&
-              aligned16(dq) && aligned16(dk) && aligned16(dv),
-          SAS_ERR_ALIGN, "q, k, v, o, dO, dq, dk and dv must be 16-byte aligned");
-  REQUIRE(p->total_qblocks < (1 << 23), SAS_ERR_UNSUPPORTED,
-          "total_qblocks must be below 2^23 (got %d)", p->total_qblocks);
-  const BwdLayout L = bwd_layout(p, mb);
-  REQUIRE(workspace, SAS_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", L.total);
-  REQUIRE(workspace_bytes >= L.total, SAS_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
-          workspace_bytes, L.total);
-  REQUIRE(aligned16(workspace), SAS_ERR_ALIGN, "workspace must be 16-byte aligned");
+  REQUIRE(sel_idx, SAS_ERR_NULL, "sel_idx is NULL");
   if (p->total_qblocks == 0) return ok();
-  char *ws = static_cast<char *>(workspace);
-  sas::BwdParams b{};
+  b.sel_idx = sel_idx;
+  return from_hip(sas::launch_bwd_prepare(b, (hipStream_t)stream), "bwd prepare launch");
+}
+
+sas_status sas_bwd_dq(const sas_problem *p, const void *q, const void *k, const void *v,
+                      const void *o, const void *dO, const float *lse, const int32_t *sel_idx,
+                      const float *sel_loggate, float *dq, float *d_loggate, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  sas::BwdParams b;
+  sas_status st = bwd_setup(p, workspace, workspace_bytes, &b);
+  if (st) return st;
+  REQUIRE(q && k && v && o && dO && lse && sel_idx && sel_loggate && dq && d_loggate,
+          SAS_ERR_NULL, "a tensor argument of sas_bwd_dq is NULL");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(dO) &&
+              aligned16(dq),
+          SAS_ERR_ALIGN, "q, k, v, o, dO and dq must be 16-byte aligned");
+  REQUIRE(sas::bwd_dq_supported(b, p->dtype == SAS_BF16, p->head_dim), SAS_ERR_UNSUPPORTED,
+          "budget_blocks %d too large for the backward's LDS at this head_dim / dtype",
+          p->budget_blocks);
+  if (p->total_qblocks == 0) return ok();
   b.q = q;
   b.k = k;
   b.v = v;
@@ -270,36 +315,60 @@ sas_status sas_bwd(const sas_problem *p, const void *q, const void *k, const voi
   b.sel_idx = sel_idx;
   b.sel_lg = sel_loggate;
   b.dq = dq;
+  b.dlg = d_loggate;
+  return from_hip(sas::launch_bwd_dq(b, p->dtype == SAS_BF16, p->out_dtype == SAS_BF16,
+                                     p->head_dim, (hipStream_t)stream),
+                  "bwd dq launch");
+}
+
+sas_status sas_bwd_dkdv(const sas_problem *p, const void *q, const void *k, const void *v,
+                        const void *dO, const float *lse, const float *sel_loggate, float *dk,
+                        float *dv, void *workspace, size_t workspace_bytes, void *stream) {
+  sas::BwdParams b;
+  sas_status st = bwd_setup(p, workspace, workspace_bytes, &b);
+  if (st) return st;
+  REQUIRE(q && k && v && dO && lse && sel_loggate && dk && dv, SAS_ERR_NULL,
+          "a tensor argument of sas_bwd_dkdv is NULL");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(dO) && aligned16(dk) &&
+              aligned16(dv),
+          SAS_ERR_ALIGN, "q, k, v, dO, dk and dv must be 16-byte aligned");
+  if (p->total_qblocks == 0) return ok();
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.dO = dO;
+  b.lse = lse;
+  b.sel_lg = sel_loggate;
   b.dk = dk;
   b.dv = dv;
-  b.dlg = d_loggate;
-  b.cu_seqlens = p->cu_seqlens;
-  b.cu_qblocks = p->cu_qblocks;
-  b.num_seqs = p->num_seqs;
-  b.T = p->total_tokens;
-  b.QB = p->total_qblocks;
-  b.hq = p->hq;
-  b.hkv = p->hkv;
-  b.G = p->hq / p->hkv;
-  b.Kb = p->budget_blocks;
-  b.max_nb = L.max_nb;
-  b.scale = p->scale;
-  b.scale_log2 = p->scale * 1.4426950408889634f;
-  b.Dbuf = reinterpret_cast<float *>(ws + L.off_D);
-  b.list = reinterpret_cast<int32_t *>(ws + L.off_list);
-  b.count = reinterpret_cast<int32_t *>(ws + L.off_count);
-  b.seg_off = reinterpret_cast<int32_t *>(ws + L.off_segoff);
-  b.dlg_part = reinterpret_cast<float *>(ws + L.off_dlgpart);
-  b.partial = reinterpret_cast<float *>(ws + L.off_partial);
-  b.seg = kSeg;
-  b.U = L.U;
-  const hipError_t e = sas::launch_bwd(b, p->dtype == SAS_BF16, p->out_dtype == SAS_BF16,
-                                       p->head_dim, (hipStream_t)stream);
-  if (e == hipErrorNotSupported)
-    return fail(SAS_ERR_UNSUPPORTED,
-                "budget_blocks %d too large for the backward's LDS at this head_dim / dtype",
-                p->budget_blocks);
-  return from_hip(e, "bwd launch");
+  return from_hip(sas::launch_bwd_dkdv(b, p->dtype == SAS_BF16, p->out_dtype == SAS_BF16,
+                                       p->head_dim, (hipStream_t)stream),
+                  "bwd dkdv launch");
+}
+
+sas_status sas_bwd(const sas_problem *p, const void *q, const void *k, const void *v,
+                   const void *o, const void *dO, const float *lse, const int32_t *sel_idx,
+                   const float *sel_loggate, float *dq, float *dk, float *dv,
+                   float *d_loggate, void *workspace, size_t workspace_bytes, void *stream) {
+  sas::BwdParams b;
+  sas_status st = bwd_setup(p, workspace, workspace_bytes, &b);
+  if (st) return st;
+  REQUIRE(q && k && v && o && dO && lse && sel_idx && sel_loggate && dq && dk && dv &&
+              d_loggate,
+          SAS_ERR_NULL, "a tensor argument of sas_bwd is NULL");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(dO) &&
+              aligned16(dq) && aligned16(dk) && aligned16(dv),
+          SAS_ERR_ALIGN, "q, k, v, o, dO, dq, dk and dv must be 16-byte aligned");
+  REQUIRE(sas::bwd_dq_supported(b, p->dtype == SAS_BF16, p->head_dim), SAS_ERR_UNSUPPORTED,
+          "budget_blocks %d too large for the backward's LDS at this head_dim / dtype",
+          p->budget_blocks);
+  st = sas_bwd_prepare(p, sel_idx, workspace, workspace_bytes, stream);
+  if (st) return st;
+  st = sas_bwd_dq(p, q, k, v, o, dO, lse, sel_idx, sel_loggate, dq, d_loggate, workspace,
+                  workspace_bytes, stream);
+  if (st) return st;
+  return sas_bwd_dkdv(p, q, k, v, dO, lse, sel_loggate, dk, dv, workspace, workspace_bytes,
+                      stream);
 }
 
 namespace {

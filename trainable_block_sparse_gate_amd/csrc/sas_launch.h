@@ -68,11 +68,16 @@ struct BwdParams {
   int32_t *seg_off;  // [hkv*QB + 1] prefix sum of segments per key block
   float *dlg_part;   // [nhc][hkv*QB][Kb] when a row's heads span workgroups
   float *partial;    // [U][2][64][D] partial dK / dV of split key blocks
+  int32_t *done;     // [hkv*QB] finished segments per key block
   int seg;           // keeping rows per segment
   int U;             // upper bound on the number of segments (dk/dv grid)
 };
-hipError_t launch_bwd(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
-                      hipStream_t stream);
+hipError_t launch_bwd_prepare(const BwdParams &p, hipStream_t stream);
+bool bwd_dq_supported(const BwdParams &p, int dtype_bf16, int head_dim);
+hipError_t launch_bwd_dq(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
+                         hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
+                           hipStream_t stream);
 
 struct DecodeParams {
   const void *q, *k, *v;       // q [batch][hq][D]; caches in either layout

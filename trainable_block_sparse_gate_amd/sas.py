@@ -22,7 +22,8 @@ STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTY
           -7: "SAS_ERR_HIP"}
 
 # Every symbol the header declares (checked by the CPU tests).
-EXPORTS = ["sas_gate_topk", "sas_fwd", "sas_bwd_workspace_size", "sas_bwd", "sas_gate_bwd",
+EXPORTS = ["sas_gate_topk", "sas_fwd", "sas_bwd_workspace_size", "sas_bwd", "sas_bwd_prepare",
+           "sas_bwd_dq", "sas_bwd_dkdv", "sas_gate_bwd",
            "sas_pool_keys", "sas_decode_select", "sas_decode_workspace_size", "sas_decode",
            "sas_status_string", "sas_last_error", "sas_abi_version"]
 
@@ -77,6 +78,9 @@ def lib():
             "sas_fwd": [P, vp, vp, vp, vp, vp, vp, vp, vp],
             "sas_bwd_workspace_size": [P],
             "sas_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "sas_bwd_prepare": [P, vp, vp, sz, vp],
+            "sas_bwd_dq": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "sas_bwd_dkdv": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "sas_gate_bwd": [P, vp, i64, i32, vp, vp, vp, vp, vp],
             "sas_pool_keys": [DP, vp, vp, vp],
             "sas_decode_select": [DP, vp, vp, vp, vp, vp, vp, vp],
@@ -148,23 +152,28 @@ class Varlen:
         return torch.bfloat16 if d == "bf16" else torch.float32
 
 
-def gate_topk(prob: Varlen, logits, mode=GATE_HIST):
+def gate_topk(prob: Varlen, logits, mode=GATE_HIST, out=None):
     """sas_gate_topk -> (sel_idx int32 [hkv,QB,Kb], sel_loggate f32, gate_lse f32)."""
     import torch
     dev = logits.device
-    sel = torch.empty((prob.hkv, prob.QB, prob.Kb), dtype=torch.int32, device=dev)
-    lg = torch.empty((prob.hkv, prob.QB, prob.Kb), dtype=torch.float32, device=dev)
-    lse = torch.empty((prob.hkv, prob.QB), dtype=torch.float32, device=dev)
+    if out is None:
+        out = (torch.empty((prob.hkv, prob.QB, prob.Kb), dtype=torch.int32, device=dev),
+               torch.empty((prob.hkv, prob.QB, prob.Kb), dtype=torch.float32, device=dev),
+               torch.empty((prob.hkv, prob.QB), dtype=torch.float32, device=dev))
+    sel, lg, lse = out
     _check(lib().sas_gate_topk(prob.ref, _ptr(logits), logits.shape[-1], mode, _ptr(sel),
                                _ptr(lg), _ptr(lse), _stream()))
     return sel, lg, lse
 
 
-def fwd(prob: Varlen, q, k, v, sel_idx, sel_lg):
+def fwd(prob: Varlen, q, k, v, sel_idx, sel_lg, out=None):
     """sas_fwd -> (o [T,hq,d] in the output dtype, lse f32 [hq,T])."""
     import torch
-    o = torch.empty((prob.T, prob.hq, prob.d), dtype=prob.torch_dtype("out"), device=q.device)
-    lse = torch.empty((prob.hq, prob.T), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = (torch.empty((prob.T, prob.hq, prob.d), dtype=prob.torch_dtype("out"),
+                           device=q.device),
+               torch.empty((prob.hq, prob.T), dtype=torch.float32, device=q.device))
+    o, lse = out
     _check(lib().sas_fwd(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(sel_idx), _ptr(sel_lg),
                          _ptr(o), _ptr(lse), _stream()))
     return o, lse
@@ -191,10 +200,34 @@ def bwd(prob: Varlen, q, k, v, o, dO, lse, sel_idx, sel_lg, workspace=None):
     return dq, dk, dv, dlg
 
 
-def gate_bwd(prob: Varlen, logits, sel_idx, gate_lse, dlg, mode=GATE_HIST):
+def bwd_phases(prob: Varlen, q, k, v, o, dO, lse, sel_idx, sel_lg, out, workspace,
+               marks=None):
+    """sas_bwd_prepare, sas_bwd_dq and sas_bwd_dkdv into preallocated
+    outputs out = (dq, dk, dv, dlg).  `marks`, if given, is called with a
+    phase name before each phase and with "end" after the last (used to
+    record timing events between phases)."""
+    dq, dk, dv, dlg = out
+    L, st, ws, n = lib(), _stream(), _ptr(workspace), workspace.numel()
+    if marks:
+        marks("prepare")
+    _check(L.sas_bwd_prepare(prob.ref, _ptr(sel_idx), ws, n, st))
+    if marks:
+        marks("dq")
+    _check(L.sas_bwd_dq(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                        _ptr(sel_idx), _ptr(sel_lg), _ptr(dq), _ptr(dlg), ws, n, st))
+    if marks:
+        marks("dkdv")
+    _check(L.sas_bwd_dkdv(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse),
+                          _ptr(sel_lg), _ptr(dk), _ptr(dv), ws, n, st))
+    if marks:
+        marks("end")
+
+
+def gate_bwd(prob: Varlen, logits, sel_idx, gate_lse, dlg, mode=GATE_HIST, out=None):
     """sas_gate_bwd -> d_logits f32, shaped like logits."""
     import torch
-    out = torch.empty(logits.shape, dtype=torch.float32, device=logits.device)
+    if out is None:
+        out = torch.empty(logits.shape, dtype=torch.float32, device=logits.device)
     _check(lib().sas_gate_bwd(prob.ref, _ptr(logits), logits.shape[-1], mode, _ptr(sel_idx),
                               _ptr(gate_lse), _ptr(dlg), _ptr(out), _stream()))
     return out
@@ -242,16 +275,18 @@ def pool_keys(prob: Decode, k_cache):
     return ksum
 
 
-def decode_select(prob: Decode, q, ksum):
+def decode_select(prob: Decode, q, ksum, out=None):
     """sas_decode_select -> (sel_idx, sel_loggate, gate_lse, scores)."""
     import torch
     dev = q.device
     rows = prob.batch * prob.hkv
-    scores = torch.empty((prob.batch, prob.hkv, prob.nblk_stride), dtype=torch.float32,
-                         device=dev)
-    sel = torch.empty((rows, prob.Kb), dtype=torch.int32, device=dev)
-    lg = torch.empty((rows, prob.Kb), dtype=torch.float32, device=dev)
-    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    if out is None:
+        out = (torch.empty((rows, prob.Kb), dtype=torch.int32, device=dev),
+               torch.empty((rows, prob.Kb), dtype=torch.float32, device=dev),
+               torch.empty((rows,), dtype=torch.float32, device=dev),
+               torch.empty((prob.batch, prob.hkv, prob.nblk_stride), dtype=torch.float32,
+                           device=dev))
+    sel, lg, lse, scores = out
     _check(lib().sas_decode_select(prob.ref, _ptr(q), _ptr(ksum), _ptr(scores), _ptr(sel),
                                    _ptr(lg), _ptr(lse), _stream()))
     return sel, lg, lse, scores
@@ -261,14 +296,16 @@ def decode_workspace_bytes(prob: Decode):
     return int(lib().sas_decode_workspace_size(prob.ref))
 
 
-def decode(prob: Decode, q, k_cache, v_cache, sel_idx, sel_lg, workspace=None):
+def decode(prob: Decode, q, k_cache, v_cache, sel_idx, sel_lg, workspace=None, out=None):
     """sas_decode -> (o [B,hq,d], lse f32 [B,hq])."""
     import torch
     dev = q.device
-    o = torch.empty((prob.batch, prob.hq, prob.d),
-                    dtype=torch.bfloat16 if prob.out_dtype == "bf16" else torch.float32,
-                    device=dev)
-    lse = torch.empty((prob.batch, prob.hq), dtype=torch.float32, device=dev)
+    if out is None:
+        out = (torch.empty((prob.batch, prob.hq, prob.d),
+                           dtype=torch.bfloat16 if prob.out_dtype == "bf16" else torch.float32,
+                           device=dev),
+               torch.empty((prob.batch, prob.hq), dtype=torch.float32, device=dev))
+    o, lse = out
     nbytes = decode_workspace_bytes(prob)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)

@@ -342,27 +342,32 @@ __global__ void bwd_dlg_sum_kernel(BwdParams p, int nhc) {
 // ------------------------------------------------------------------ dk/dv
 // Workgroup of 4 waves: wave = (query half qh, key half kh).  Each wave
 // owns 32 keys (K, V as B operands in registers) and, per step, 32 of the
-// 64 query rows of one head of one keeping row.
+// 64 query rows of one head of one keeping row.  Q and dO tiles are double
+// buffered in LDS (row-major only) with the step after next in flight from
+// memory; the products that contract over query rows read their operands
+// transposed straight from the row-major tiles.
+constexpr int kSegMax = 64;  // entries per segment the kernel can hold
+
 template <typename T, typename TO, int D>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   using M = Mfma<T>;
   constexpr int NT = 256;
-  using QT = Tile4<T, D, NT>;
+  constexpr int PAD = sizeof(T) == 2 ? 16 : 4;
+  using RT = RowTile<T, D, NT, PAD>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
-  constexpr int TILE_RM = kBlock * QT::ROW, TILE_TR = D * QT::TROW;
-  constexpr int LDS_T = 2 * (TILE_RM + TILE_TR);
+  constexpr int TILE = kBlock * RT::ROW;          // elements per tile
+  constexpr int LDS_T = 2 * 2 * TILE;             // {Q, dO} x 2 buffers
   constexpr int LDS_RED = 2 * 2 * NDT * 16 * kWave;  // floats: 2 waves x (dk, dv)
   constexpr int LDS_BYTES =
       (LDS_T * (int)sizeof(T) > LDS_RED * 4) ? LDS_T * (int)sizeof(T) : LDS_RED * 4;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
-  __shared__ __attribute__((aligned(16))) float s_lse[kBlock];
-  __shared__ __attribute__((aligned(16))) float s_D[kBlock];
-  T *Qs = reinterpret_cast<T *>(smem);
-  T *Qt = Qs + TILE_RM;
-  T *Ds = Qt + TILE_TR;
-  T *Dt = Ds + TILE_RM;
+  __shared__ __attribute__((aligned(16))) float s_lse[2][kBlock];
+  __shared__ __attribute__((aligned(16))) float s_D[2][kBlock];
+  __shared__ int s_ent[kSegMax];
+  __shared__ float s_lg[kSegMax];
+  __shared__ int s_last;
 
   const int w = blockIdx.x;
   const int nx = p.hkv * p.QB;
@@ -385,17 +390,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int seg = w - p.seg_off[x];
   const int cnt = p.count[x];
   const int e0 = seg * p.seg, e1 = min(cnt, e0 + p.seg);
-  const int32_t *list = p.list + (long)x * p.max_nb;
+  const int nent = max(0, e1 - e0);
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int hf = lane / 32, l32 = lane % 32;
   const int kh = wave % 2, qh = wave / 2;
   const int key = 32 * kh + l32;  // this lane's key (column of S)
 
+  if (threadIdx.x < nent) {
+    const int ent = p.list[(long)x * p.max_nb + e0 + threadIdx.x];
+    s_ent[threadIdx.x] = ent;
+    s_lg[threadIdx.x] = p.sel_lg[((long)g * p.QB + (ent >> 8)) * p.Kb + (ent & 255)] * kLog2e;
+  }
+
   const T *q = static_cast<const T *>(p.q);
   const T *kk = static_cast<const T *>(p.k);
   const T *vv = static_cast<const T *>(p.v);
   const TO *dO = static_cast<const TO *>(p.dO);
+  T *tiles = reinterpret_cast<T *>(smem);  // [buf][Q | dO][64][ROW]
 
   typename M::Op kreg[NKS], vreg[NKS];
   {
@@ -415,58 +427,64 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
 
-  const int nsteps = (e1 - e0) * p.G;
+  const int G = p.G;
+  const int nsteps = nent * G;
   const long qstride = (long)p.hq * D;
-  QT qst, dst;
+  RT qst, dst;
   float st_lse = 0.f, st_D = 0.f;
-  auto step_geom = [&](int st, int &Qrow, int &slot, int &hh) {
-    const int ent = list[e0 + st / p.G];
-    Qrow = ent >> 8;
-    slot = ent & 255;
-    hh = st % p.G;
-  };
+  __syncthreads();  // s_ent / s_lg visible
+
   auto load_step = [&](int st) {
-    int Qrow, slot, hh;
-    step_geom(st, Qrow, slot, hh);
-    const int i = Qrow - q0;
-    const int h = g * p.G + hh;
+    const int ent = s_ent[st / G];
+    const int i = (ent >> 8) - q0;
+    const int h = g * G + st % G;
     const long t0 = seq_start + (long)i * kBlock;
     const int nq = min(kBlock, seq_len - i * kBlock);
-    tile4_load<T, T, D, NT>(qst, q + (t0 * p.hq + h) * D, qstride, nq);
-    tile4_load<TO, T, D, NT>(dst, dO + (t0 * p.hq + h) * D, qstride, nq);
+    rowtile_load<T, T, D, NT, PAD>(qst, q + (t0 * p.hq + h) * D, qstride, nq);
+    rowtile_load<TO, T, D, NT, PAD>(dst, dO + (t0 * p.hq + h) * D, qstride, nq);
     if (threadIdx.x < kBlock) {
       const bool ok = threadIdx.x < nq;
-      st_lse = ok ? p.lse[(long)h * p.T + t0 + threadIdx.x] : INFINITY;
+      st_lse = ok ? p.lse[(long)h * p.T + t0 + threadIdx.x] * kLog2e : INFINITY;
       st_D = ok ? p.Dbuf[(long)h * p.T + t0 + threadIdx.x] : 0.f;
     }
   };
-  if (nsteps > 0) load_step(0);
-
-  for (int st = 0; st < nsteps; ++st) {
-    int Qrow, slot, hh;
-    step_geom(st, Qrow, slot, hh);
-    const int i = Qrow - q0;
-    const int nq = min(kBlock, seq_len - i * kBlock);
-    const float lg2 = p.sel_lg[((long)g * p.QB + Qrow) * p.Kb + slot] * kLog2e;
-    const bool diag = (i == j);
-    __syncthreads();
-    tile4_store_rm<T, D, NT>(qst, Qs);
-    tile4_store_tr<T, D, NT>(qst, Qt);
-    tile4_store_rm<T, D, NT>(dst, Ds);
-    tile4_store_tr<T, D, NT>(dst, Dt);
+  auto store_step = [&](int b) {
+    rowtile_store<T, D, NT, PAD>(qst, tiles + (2 * b + 0) * TILE);
+    rowtile_store<T, D, NT, PAD>(dst, tiles + (2 * b + 1) * TILE);
     if (threadIdx.x < kBlock) {
-      s_lse[threadIdx.x] = st_lse * kLog2e;
-      s_D[threadIdx.x] = st_D;
+      s_lse[b][threadIdx.x] = st_lse;
+      s_D[b][threadIdx.x] = st_D;
     }
-    __syncthreads();
-    if (st + 1 < nsteps) load_step(st + 1);
+  };
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(0);
+    if (nsteps > 1) load_step(1);
+  }
+  __syncthreads();
+
+  // Per step: compute from one buffer, then store the next step's tile
+  // (loaded one step earlier) into the other buffer, issue the loads of the
+  // step after that, and barrier.  No LDS write of a wave is in flight while
+  // its transposed reads (ds_read_b64_tr_b16) issue: with writes pending,
+  // those reads returned wrong data on gfx950.
+  for (int st = 0; st < nsteps; ++st) {
+    const int b = st & 1;
+
+    const int e = st / G;
+    const int i = (s_ent[e] >> 8) - q0;
+    const int nq = min(kBlock, seq_len - i * kBlock);
+    const float lg2 = s_lg[e];
+    const bool diag = (i == j);
+    const T *Qs = tiles + (2 * b + 0) * TILE;
+    const T *Ds = tiles + (2 * b + 1) * TILE;
 
     // S[query][key] and dP[query][key] for 32 queries x this wave's 32 keys;
     // query rows loaded in chain order so P and dS feed the next products.
     f32x16 sacc = f32x16{}, pacc = f32x16{};
     const int qrow = 32 * qh + chain_key_of_row<T>(l32);
-    const T *qa = Qs + qrow * QT::ROW + hf * E;
-    const T *da = Ds + qrow * QT::ROW + hf * E;
+    const T *qa = Qs + qrow * RT::ROW + hf * E;
+    const T *da = Ds + qrow * RT::ROW + hf * E;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       sacc = M::run(lds_op<T>(qa + ks * KS), kreg[ks], sacc);
@@ -476,25 +494,28 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     for (int r = 0; r < 16; ++r) {
       const int ql = 32 * qh + chain_slot<T>(r, hf);
       const bool ok = ql < nq && key < nvalid && !(diag && key > ql);
-      const float pr = ok ? fast_exp2(sacc[r] * p.scale_log2 + lg2 - s_lse[ql]) : 0.f;
+      const float pr = ok ? fast_exp2(sacc[r] * p.scale_log2 + lg2 - s_lse[b][ql]) : 0.f;
       sacc[r] = pr;
-      pacc[r] = pr * (pacc[r] - s_D[ql]);
+      pacc[r] = pr * (pacc[r] - s_D[b][ql]);
     }
     // dV^T[d][key] += dO^T[d][query] P[query][key];  dK^T += Q^T dS
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const T *doa = Dt + (32 * dt + l32) * QT::TROW + 32 * qh + hf * E;
-      const T *qta = Qt + (32 * dt + l32) * QT::TROW + 32 * qh + hf * E;
 #pragma unroll
       for (int kc = 0; kc < SPT; ++kc) {
-        dvacc[dt] = M::run(lds_op<T>(doa + kc * KS), regs_op<T>(sacc, kc * E), dvacc[dt]);
-        dkacc[dt] = M::run(lds_op<T>(qta + kc * KS), regs_op<T>(pacc, kc * E), dkacc[dt]);
+        const int kq = 32 * qh + kc * KS;
+        dvacc[dt] = M::run(lds_op_rows<T>(Ds, RT::ROW, kq, 32 * dt), regs_op<T>(sacc, kc * E),
+                           dvacc[dt]);
+        dkacc[dt] = M::run(lds_op_rows<T>(Qs, RT::ROW, kq, 32 * dt), regs_op<T>(pacc, kc * E),
+                           dkacc[dt]);
       }
     }
+    if (st + 1 < nsteps) store_step(b ^ 1);
+    if (st + 2 < nsteps) load_step(st + 2);
+    __syncthreads();
   }
 
   // Add the two query halves: waves qh = 1 hand their sums to qh = 0.
-  __syncthreads();
   float *red = reinterpret_cast<float *>(smem);
   if (qh == 1) {
 #pragma unroll
@@ -544,7 +565,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   if (nseg == 1) return;
 
   // Split key block: the last segment to finish adds the partials in order.
-  __shared__ int s_last;
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) s_last = (atomicAdd(&p.done[x], 1) == nseg - 1);

@@ -1,6 +1,6 @@
 // C ABI of the SAS library: argument checks on the host, then launches.
 // Every check runs before any HIP call, so a rejected call touches nothing.
-#include "../../include/sas.h"
+#include "sas.h"
 
 #include <hip/hip_runtime.h>
 
@@ -201,7 +201,7 @@ sas_status sas_gate_bwd(const sas_problem *p, const float *logits, int64_t ld,
 
 namespace {
 
-constexpr int kSeg = 32;  // keeping rows per dk/dv segment
+constexpr int kSeg = 32;  // keeping rows per dk/dv segment (at most 64)
 
 struct BwdLayout {
   size_t off_D, off_list, off_count, off_segoff, off_done, off_dlgpart, off_partial, total;

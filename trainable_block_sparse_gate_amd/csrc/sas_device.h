@@ -66,6 +66,39 @@ __device__ __host__ constexpr inline int chain_key_of_row(int m) {
 }
 
 // ---------------------------------------------------------------------------
+// MFMA operand that contracts over the ROWS of a row-major LDS tile X[k][m]
+// (row stride ld elements): lane l receives X[kb + h*E + e][mb + l % 32],
+// e = 0..E-1, h = l / 32 -- the k-contiguous layout both A and B operands
+// use.  For bf16 this is two ds_read_b64_tr_b16: within each 16-lane group,
+// output lane j, element e comes from source lane 4e + j/4, element j % 4,
+// so a source lane s that points at row kb + s/4, columns 4(s%4)..+3 of its
+// group's 16 columns hands every output lane four consecutive rows of one
+// column.  Groups: lanes 16g..16g+15 cover columns 16(g%2)..+15 and rows
+// 8(g/2)..+7 (two reads of four rows).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) short lds_short;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <typename T>
+__device__ inline typename Mfma<T>::Op lds_op_rows(const T *X, int ld, int kb, int mb) {
+  const int lane = threadIdx.x % kWave;
+  if constexpr (sizeof(T) == 2) {
+    const int g = lane / 16, s = lane % 16;
+    const int row = kb + 8 * (g / 2) + s / 4;
+    const int col = mb + 16 * (g % 2) + 4 * (s % 4);
+    const lds_short *base = (const lds_short *)((const T *)X + row * ld + col);
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)base);
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + 4 * ld));
+    const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+  } else {
+    return X[(kb + lane / 32) * ld + mb + lane % 32];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Conversions
 // ---------------------------------------------------------------------------
 __device__ inline float to_f32(__bf16 x) { return (float)x; }

@@ -94,6 +94,48 @@ __device__ inline void tile4_store_tr(const Tile4<T, D, NT> &st, T *lds) {
   }
 }
 
+// Row-major staging only: 16-byte chunks (VEC elements of T), a row of D
+// elements is D / VEC chunks, consecutive threads take consecutive chunks.
+template <typename T, int D, int NT, int PAD>
+struct RowTile {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int DC = D / VEC;
+  static constexpr int TOT = kBlock * DC;
+  static constexpr int CH = (TOT + NT - 1) / NT;
+  static constexpr int ROW = D + PAD;  // LDS row stride (elements)
+  T v[CH][VEC];
+};
+
+template <typename TS, typename T, int D, int NT, int PAD>
+__device__ inline void rowtile_load(RowTile<T, D, NT, PAD> &st, const TS *base, long stride,
+                                    int nvalid) {
+  using F = RowTile<T, D, NT, PAD>;
+#pragma unroll
+  for (int it = 0; it < F::CH; ++it) {
+    const int c = threadIdx.x + it * NT;
+    const int row = c / F::DC, dc = c % F::DC;
+    if ((F::TOT % NT == 0 || c < F::TOT) && row < nvalid) {
+      load_vec<TS, T>(st.v[it], base + row * stride + dc * F::VEC, F::VEC);
+    } else {
+#pragma unroll
+      for (int e = 0; e < F::VEC; ++e) st.v[it][e] = T(0.f);
+    }
+  }
+}
+
+template <typename T, int D, int NT, int PAD>
+__device__ inline void rowtile_store(const RowTile<T, D, NT, PAD> &st, T *lds) {
+  using F = RowTile<T, D, NT, PAD>;
+#pragma unroll
+  for (int it = 0; it < F::CH; ++it) {
+    const int c = threadIdx.x + it * NT;
+    if (F::TOT % NT != 0 && c >= F::TOT) continue;
+    const int row = c / F::DC, dc = c % F::DC;
+    *reinterpret_cast<uint4 *>(lds + row * F::ROW + dc * F::VEC) =
+        *reinterpret_cast<const uint4 *>(st.v[it]);
+  }
+}
+
 template <typename T>
 __device__ inline typename Mfma<T>::Op lds_op(const T *p) {
   if constexpr (sizeof(T) == 2)

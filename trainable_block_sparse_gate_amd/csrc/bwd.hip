@@ -101,20 +101,28 @@ __global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p)
 }
 
 // ------------------------------------------------------------------ dq
+// The forward's geometry: waves are the query heads of one kv head, 64 rows
+// each, Q and dO held in registers as B operands.  K and V tiles of the kept
+// blocks are double buffered in LDS (row-major); dQ^T = K^T dS^T reads K
+// transposed with ds_read_b64_tr_b16.  Per tile: compute from one buffer,
+// then store the next tile into the other, issue the loads of the one after,
+// and barrier (no LDS write of a wave in flight while its transposed reads
+// issue).
 template <typename T, typename TO, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   using M = Mfma<T>;
   constexpr int NT = NW * kWave;
-  using KT = Tile4<T, D, NT>;  // K: row-major + transposed
-  using VT = Tile4<T, D, NT>;  // V: row-major
+  constexpr int PAD = sizeof(T) == 2 ? 16 : 4;
+  using RT = RowTile<T, D, NT, PAD>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
+  constexpr int TILE = kBlock * RT::ROW;
 
-  __shared__ __attribute__((aligned(16))) T Ks[kBlock * KT::ROW];
-  __shared__ __attribute__((aligned(16))) T Kt[D * KT::TROW];
-  __shared__ __attribute__((aligned(16))) T Vs[kBlock * VT::ROW];
-  __shared__ float s_F[NW][kMaxBudget];   // per tile: sum of P dP over the wave's rows
-  __shared__ int s_order[kMaxBudget];
+  __shared__ __attribute__((aligned(16))) T tiles[2 * 2 * TILE];  // [buf][K | V]
+  __shared__ float s_F[NW][kMaxBudget];  // per tile: sum of P dP over the wave's rows
+  __shared__ int s_slot[kMaxBudget];     // tiles in processing order
+  __shared__ int s_j[kMaxBudget];
+  __shared__ float s_lg[kMaxBudget];     // log gate * log2(e)
   __shared__ int s_n;
   extern __shared__ float s_G[];         // [NW][Kb][64]: per tile, sum of P per query row
 
@@ -138,14 +146,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   const int seq_len = p.cu_seqlens[s + 1] - seq_start;
   const int nq = min(kBlock, seq_len - i * kBlock);
   const long row = (long)g * p.QB + Q;
-  const int32_t *sel = p.sel_idx + row * p.Kb;
-  const float *slg = p.sel_lg + row * p.Kb;
 
   if (threadIdx.x == 0) {
+    const int32_t *sel = p.sel_idx + row * p.Kb;
+    const float *slg = p.sel_lg + row * p.Kb;
     int n = 0;
     for (int sl = 0; sl < p.Kb; ++sl) {
       const int j = sel[sl];
-      if (j >= 0 && j <= i) s_order[n++] = sl;
+      if (j >= 0 && j <= i) {
+        s_slot[n] = sl;
+        s_j[n] = j;
+        s_lg[n] = slg[sl] * kLog2e;
+        ++n;
+      }
     }
     s_n = n;
   }
@@ -198,47 +211,52 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   __syncthreads();
   const int ntiles = s_n;
   const long kstride = (long)p.hkv * D;
-  KT kst;
-  VT vst;
+  RT kst, vst;
   auto load_tile = [&](int it) {
-    const int j = sel[s_order[it]];
+    const int j = s_j[it];
     const long tok = seq_start + (long)j * kBlock;
     const int nv = min(kBlock, seq_len - j * kBlock);
-    tile4_load<T, T, D, NT>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);
-    tile4_load<T, T, D, NT>(vst, vv + (tok * p.hkv + g) * D, kstride, nv);
+    rowtile_load<T, T, D, NT, PAD>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);
+    rowtile_load<T, T, D, NT, PAD>(vst, vv + (tok * p.hkv + g) * D, kstride, nv);
   };
-  if (ntiles > 0) load_tile(0);
+  auto store_tile = [&](int b) {
+    rowtile_store<T, D, NT, PAD>(kst, tiles + (2 * b + 0) * TILE);
+    rowtile_store<T, D, NT, PAD>(vst, tiles + (2 * b + 1) * TILE);
+  };
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (ntiles > 1) load_tile(1);
+  }
+  __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
-    const int slot = s_order[it];
-    const int j = sel[slot];
-    const float lg2 = slg[slot] * kLog2e;
-    const bool diag = (j == i);
-    __syncthreads();
-    tile4_store_rm<T, D, NT>(kst, Ks);
-    tile4_store_tr<T, D, NT>(kst, Kt);
-    tile4_store_rm<T, D, NT>(vst, Vs);
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(it + 1);
+    const int b = it & 1;
+    const float lg2 = s_lg[it];
+    const bool diag = (s_j[it] == i);
+    const T *Ks = tiles + (2 * b + 0) * TILE;
+    const T *Vs = tiles + (2 * b + 1) * TILE;
 
     float tile_F = 0.f;
     float Gp[2] = {0.f, 0.f};
-#pragma unroll
+    // one 32-key half at a time (not unrolled: keeps both halves' live
+    // ranges from overlapping)
+#pragma unroll 1
     for (int mt = 0; mt < 2; ++mt) {
       f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) sacc[nt] = pacc[nt] = f32x16{};
       const int krow = 32 * mt + chain_key_of_row<T>(l32);
-      const T *ka = Ks + krow * KT::ROW + hf * E;
-      const T *va = Vs + krow * VT::ROW + hf * E;
+      const T *ka = Ks + krow * RT::ROW + hf * E;
+      const T *va = Vs + krow * RT::ROW + hf * E;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const typename M::Op a = lds_op<T>(ka + ks * KS);
-        const typename M::Op b = lds_op<T>(va + ks * KS);
+        const typename M::Op bb = lds_op<T>(va + ks * KS);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           sacc[nt] = M::run(a, qreg[nt][ks], sacc[nt]);
-          pacc[nt] = M::run(b, doreg[nt][ks], pacc[nt]);
+          pacc[nt] = M::run(bb, doreg[nt][ks], pacc[nt]);
         }
       }
       // dS^T = P^T (dP^T - D), P^T recomputed from the saved lse
@@ -259,10 +277,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
       // dQ^T[d][query] += K^T[d][key] dS^T[key][query] over this 32-key half
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const T *ta = Kt + (32 * dt + l32) * KT::TROW + 32 * mt + hf * E;
 #pragma unroll
         for (int kc = 0; kc < SPT; ++kc) {
-          const typename M::Op a = lds_op<T>(ta + kc * KS);
+          const typename M::Op a = lds_op_rows<T>(Ks, RT::ROW, 32 * mt + kc * KS, 32 * dt);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
             dqacc[dt][nt] = M::run(a, regs_op<T>(sacc[nt], kc * E), dqacc[dt][nt]);
@@ -276,6 +293,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
       const float gsum = Gp[nt] + __shfl_xor(Gp[nt], 32);
       if (hf == 0) s_G[(wave * p.Kb + it) * kBlock + 32 * nt + l32] = gsum;
     }
+    if (it + 1 < ntiles) store_tile(b ^ 1);
+    if (it + 2 < ntiles) load_tile(it + 2);
+    __syncthreads();
   }
 
   // Exact D per query row, then dlg of each tile = sum P dP - sum_t D_t G_t.
@@ -322,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   for (int sl = threadIdx.x; sl < p.Kb; sl += NT) {
     float val = 0.f;
     for (int it = 0; it < ntiles; ++it)
-      if (s_order[it] == sl) {
+      if (s_slot[it] == sl) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) val += s_F[w][it];
       }
@@ -591,8 +611,8 @@ constexpr int kLdsBytes = 160 * 1024;
 
 template <typename T, int D, int NW>
 constexpr int dq_static_lds() {
-  return (int)sizeof(T) * (2 * kBlock * Tile4<T, D, NW * 64>::ROW + D * Tile4<T, D, NW * 64>::TROW) +
-         (NW + 1) * kMaxBudget * 4 + 64;
+  return (int)sizeof(T) * 4 * kBlock * (D + (sizeof(T) == 2 ? 16 : 4)) +
+         (NW + 3) * kMaxBudget * 4 + 64;
 }
 
 template <typename T, int D, int NW>

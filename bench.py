@@ -180,6 +180,18 @@ def decode_bench(args, torch, sas, wl, metrics):
                           "GB/s": round(scan_gbs, 1)}}
 
 
+def calibration_copy(torch, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, run untimed so that
+    hardware-counter runs of this script see a kernel whose true HBM traffic
+    is known (nbytes read + nbytes written per launch)."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline(case, metrics):
     """The oracle as it stands, on a bounded sample of the same workload: the
     last NS query blocks of every kv head (steady state: every row keeps the
@@ -231,6 +243,7 @@ def main():
     log(f"[bench] inputs drawn in {time.perf_counter() - t0:.1f} s")
     tr = train_bench(args, torch, sas, wl, metrics, case)
     dec = None if args.no_decode else decode_bench(args, torch, sas, wl, metrics)
+    calibration_copy(torch)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, metrics)

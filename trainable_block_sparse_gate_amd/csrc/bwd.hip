@@ -510,13 +510,35 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       sacc = M::run(lds_op<T>(qa + ks * KS), kreg[ks], sacc);
       pacc = M::run(lds_op<T>(da + ks * KS), vreg[ks], pacc);
     }
+    // this lane's 16 query rows, in register order, come in four runs of 4
+    // consecutive rows: fetch their lse and D as float4s
+    // (bf16 chain order; the fp32 order interleaves, so it reads one by one)
+    float lse_r[16], D_r[16];
+    if constexpr (E == 8) {
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += 4) {
+        const int q4 = 32 * qh + chain_slot<T>(r0, hf);
+        const float4 a = *reinterpret_cast<const float4 *>(&s_lse[b][q4]);
+        const float4 c = *reinterpret_cast<const float4 *>(&s_D[b][q4]);
+        lse_r[r0] = a.x; lse_r[r0 + 1] = a.y; lse_r[r0 + 2] = a.z; lse_r[r0 + 3] = a.w;
+        D_r[r0] = c.x; D_r[r0 + 1] = c.y; D_r[r0 + 2] = c.z; D_r[r0 + 3] = c.w;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        lse_r[r] = s_lse[b][32 * qh + chain_slot<T>(r, hf)];
+        D_r[r] = s_D[b][32 * qh + chain_slot<T>(r, hf)];
+      }
+    }
+    const bool key_ok = key < nvalid;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ql = 32 * qh + chain_slot<T>(r, hf);
-      const bool ok = ql < nq && key < nvalid && !(diag && key > ql);
-      const float pr = ok ? fast_exp2(sacc[r] * p.scale_log2 + lg2 - s_lse[b][ql]) : 0.f;
+      const bool ok = key_ok && ql < nq && !(diag && key > ql);
+      const float z = ok ? sacc[r] * p.scale_log2 + lg2 - lse_r[r] : -INFINITY;
+      const float pr = fast_exp2(z);
       sacc[r] = pr;
-      pacc[r] = pr * (pacc[r] - s_D[b][ql]);
+      pacc[r] = pr * (pacc[r] - D_r[r]);
     }
     // dV^T[d][key] += dO^T[d][query] P[query][key];  dK^T += Q^T dS
 #pragma unroll

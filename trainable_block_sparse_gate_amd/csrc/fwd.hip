@@ -11,124 +11,46 @@
 //   - one workgroup per (query block, kv head): its waves are the G query
 //     heads that share the kv head (GQA), 64 query rows each, so every K/V
 //     tile staged in LDS feeds G*64 rows;
-//   - K/V tiles are gathered by kept-block index; K is stored row-major and
-//     V transposed in LDS, both padded by 16 bytes per row;
+//   - K/V tiles are gathered by kept-block index into double-buffered LDS,
+//     row-major with padded rows; the product that contracts over keys reads
+//     V transposed with ds_read_b64_tr_b16;
 //   - S^T = K Q^T on 32x32 MFMA tiles with Q held in registers, so each
 //     lane owns one query column and the softmax row statistics need a
 //     single cross-half exchange; the key order inside each tile is chosen
 //     so that the probabilities chain straight into O^T += V^T P^T;
 //   - fp32 online softmax in the log2 domain; the log gate of the tile is one
 //     scalar; the current (diagonal) block goes first so the running max is
-//     finite before any gated history tile;
-//   - the next tile's global loads are issued before the current tile's
-//     MFMAs (register staging, one LDS buffer).
+//     finite before any gated history tile; the output is rescaled only when
+//     a tile's max jumps well above the running reference;
+//   - two tiles ahead are in flight: one in LDS, one in registers.
 #include "sas_device.h"
 #include "sas_launch.h"
+#include "tile_stage.h"
 
 namespace sas {
 
-template <typename T, int D, int NW>
-struct FwdTile {
-  static constexpr int NT = NW * kWave;               // threads
-  static constexpr int VEC = 16 / sizeof(T);          // elements per 16 bytes
-  static constexpr int KROW = D + VEC;                // K row stride (elements)
-  static constexpr int VROW = kBlock + VEC;           // V^T row stride (elements)
-  static constexpr int KTOT = kBlock * D / VEC;         // 16-byte K chunks per tile
-  static constexpr int VTOT = (kBlock / 4) * (D / VEC);  // 4-key x 16-byte V chunks
-  static constexpr int KCH = (KTOT + NT - 1) / NT;       // per thread
-  static constexpr int VCH = (VTOT + NT - 1) / NT;
-};
-
-template <typename T, int D, int NW>
-struct TileStage {
-  uint4 k[FwdTile<T, D, NW>::KCH];
-  uint4 v[FwdTile<T, D, NW>::VCH][4];
-};
-
-// Global -> registers for one 64-key tile (zero past the sequence end).
-template <typename T, int D, int NW>
-__device__ inline void stage_load(TileStage<T, D, NW> &st, const T *kbase, const T *vbase,
-                                  int nvalid, int kstride) {
-  using F = FwdTile<T, D, NW>;
-  constexpr int DC = D / F::VEC;
-#pragma unroll
-  for (int it = 0; it < F::KCH; ++it) {
-    int c = threadIdx.x + it * F::NT;
-    int key = c / DC, dc = c % DC;
-    st.k[it] = (c < F::KTOT && key < nvalid)
-                   ? *reinterpret_cast<const uint4 *>(kbase + (long)key * kstride + dc * F::VEC)
-                   : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int it = 0; it < F::VCH; ++it) {
-    int c = threadIdx.x + it * F::NT;
-    int kg = c / DC, dc = c % DC;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      int key = 4 * kg + x;
-      st.v[it][x] = (c < F::VTOT && key < nvalid) ? *reinterpret_cast<const uint4 *>(vbase + (long)key * kstride +
-                                                                    dc * F::VEC)
-                                 : make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-// Registers -> LDS: K row-major, V transposed ([d][key]).
-template <typename T, int D, int NW>
-__device__ inline void stage_store(const TileStage<T, D, NW> &st, T *Ks, T *Vt) {
-  using F = FwdTile<T, D, NW>;
-  constexpr int DC = D / F::VEC;
-#pragma unroll
-  for (int it = 0; it < F::KCH; ++it) {
-    int c = threadIdx.x + it * F::NT;
-    int key = c / DC, dc = c % DC;
-    if (F::KTOT % F::NT != 0 && c >= F::KTOT) continue;
-    *reinterpret_cast<uint4 *>(Ks + key * F::KROW + dc * F::VEC) = st.k[it];
-  }
-#pragma unroll
-  for (int it = 0; it < F::VCH; ++it) {
-    int c = threadIdx.x + it * F::NT;
-    int kg = c / DC, dc = c % DC;
-    if (F::VTOT % F::NT != 0 && c >= F::VTOT) continue;
-    const T *r0 = reinterpret_cast<const T *>(&st.v[it][0]);
-    const T *r1 = reinterpret_cast<const T *>(&st.v[it][1]);
-    const T *r2 = reinterpret_cast<const T *>(&st.v[it][2]);
-    const T *r3 = reinterpret_cast<const T *>(&st.v[it][3]);
-#pragma unroll
-    for (int e = 0; e < F::VEC; ++e) {
-      T *dst = Vt + (dc * F::VEC + e) * F::VROW + 4 * kg;
-      if constexpr (sizeof(T) == 2) {
-        bf16x4 w = {r0[e], r1[e], r2[e], r3[e]};
-        *reinterpret_cast<bf16x4 *>(dst) = w;
-      } else {
-        float4 w = make_float4(r0[e], r1[e], r2[e], r3[e]);
-        *reinterpret_cast<float4 *>(dst) = w;
-      }
-    }
-  }
-}
-
-template <typename T>
-__device__ inline typename Mfma<T>::Op load_op(const T *p) {
-  if constexpr (sizeof(T) == 2)
-    return *reinterpret_cast<const bf16x8 *>(p);
-  else
-    return *p;
-}
+// Lazy rescaling: the running reference max of a query row moves only when
+// a tile's max exceeds it by more than this (log2 units), so most tiles skip
+// the O *= alpha pass; probabilities stay <= 2^kRescale, exact in fp32 sums
+// and well inside bf16 range.
+constexpr float kRescale = 8.f;
 
 template <typename T, typename TO, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   using M = Mfma<T>;
-  using F = FwdTile<T, D, NW>;
+  constexpr int NT = NW * kWave;
+  constexpr int PAD = sizeof(T) == 2 ? 16 : 4;
+  using RT = RowTile<T, D, NT, PAD>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS;          // k-steps over head_dim
   constexpr int NDT = D / 32;          // 32-row d tiles of O^T
   constexpr int NKC = kBlock / KS;     // k-steps over a 64-key tile
   constexpr int SPT = 32 / KS;         // k-steps per 32-key half tile
+  constexpr int TILE = kBlock * RT::ROW;
 
-  __shared__ __attribute__((aligned(16))) T Ks[kBlock * F::KROW];
-  __shared__ __attribute__((aligned(16))) T Vt[D * F::VROW];
-  __shared__ int s_order[kMaxBudget];
+  __shared__ __attribute__((aligned(16))) T tiles[2 * 2 * TILE];  // [buf][K | V]
+  __shared__ int s_j[kMaxBudget];
+  __shared__ float s_lg[kMaxBudget];
   __shared__ int s_n;
 
   const T *q = static_cast<const T *>(p.q);
@@ -150,16 +72,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int seq_len = p.cu_seqlens[s + 1] - seq_start;
   const int nq = min(kBlock, seq_len - i * kBlock);
   const long row = (long)g * p.QB + Q;
-  const int32_t *sel = p.sel_idx + row * p.Kb;
-  const float *slg = p.sel_lg + row * p.Kb;
 
+  // tile order: the current (diagonal) block first, so the running max is
+  // finite before any gated history tile, then the kept history blocks
   if (threadIdx.x == 0) {
+    const int32_t *sel = p.sel_idx + row * p.Kb;
+    const float *slg = p.sel_lg + row * p.Kb;
     int n = 0;
     for (int sl = 0; sl < p.Kb; ++sl)
-      if (sel[sl] == i) s_order[n++] = sl;
+      if (sel[sl] == i) {
+        s_j[n] = i;
+        s_lg[n] = slg[sl] * kLog2e;
+        ++n;
+      }
     for (int sl = 0; sl < p.Kb; ++sl) {
-      int j = sel[sl];
-      if (j >= 0 && j < i) s_order[n++] = sl;
+      const int j = sel[sl];
+      if (j >= 0 && j < i) {
+        s_j[n] = j;
+        s_lg[n] = slg[sl] * kLog2e;
+        ++n;
+      }
     }
     s_n = n;
   }
@@ -168,12 +100,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   typename M::Op qreg[2][NKS];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    int ql = 32 * nt + l32;
+    const int ql = 32 * nt + l32;
     const T *qp = q + ((long)(seq_start + i * kBlock + ql) * p.hq + h) * D + hf * E;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if (ql < nq)
-        qreg[nt][ks] = load_op<T>(qp + ks * KS);
+        qreg[nt][ks] = lds_op<T>(qp + ks * KS);
       else
         qreg[nt][ks] = typename M::Op{};
     }
@@ -189,48 +121,46 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 
   __syncthreads();
   const int ntiles = s_n;
-  const int kstride = p.hkv * D;
-
-  TileStage<T, D, NW> st;
-  auto tile_ptrs = [&](int it, const T *&kb, const T *&vb, int &nvalid, int &j) {
-    j = sel[s_order[it]];
-    long tok = seq_start + (long)j * kBlock;
-    kb = kk + (tok * p.hkv + g) * D;
-    vb = vv + (tok * p.hkv + g) * D;
-    nvalid = min(kBlock, seq_len - j * kBlock);
+  const long kstride = (long)p.hkv * D;
+  RT kst, vst;
+  auto load_tile = [&](int it) {
+    const int j = s_j[it];
+    const long tok = seq_start + (long)j * kBlock;
+    const int nv = min(kBlock, seq_len - j * kBlock);
+    rowtile_load<T, T, D, NT, PAD>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);
+    rowtile_load<T, T, D, NT, PAD>(vst, vv + (tok * p.hkv + g) * D, kstride, nv);
+  };
+  auto store_tile = [&](int b) {
+    rowtile_store<T, D, NT, PAD>(kst, tiles + (2 * b + 0) * TILE);
+    rowtile_store<T, D, NT, PAD>(vst, tiles + (2 * b + 1) * TILE);
   };
   if (ntiles > 0) {
-    const T *kb, *vb;
-    int nv, j;
-    tile_ptrs(0, kb, vb, nv, j);
-    stage_load<T, D, NW>(st, kb, vb, nv, kstride);
+    load_tile(0);
+    store_tile(0);
+    if (ntiles > 1) load_tile(1);
   }
+  __syncthreads();
 
+  // Per tile: compute from one buffer, then store the next tile into the
+  // other, issue the loads of the one after, and barrier (no LDS write of a
+  // wave in flight while its transposed reads issue).
   for (int it = 0; it < ntiles; ++it) {
-    const int slot = s_order[it];
-    const int j = sel[slot];
-    const float lg2 = slg[slot] * kLog2e;
-    const bool diag = (j == i);
-    __syncthreads();
-    stage_store<T, D, NW>(st, Ks, Vt);
-    __syncthreads();
-    if (it + 1 < ntiles) {
-      const T *kb, *vb;
-      int nv, jn;
-      tile_ptrs(it + 1, kb, vb, nv, jn);
-      stage_load<T, D, NW>(st, kb, vb, nv, kstride);
-    }
+    const int b = it & 1;
+    const float lg2 = s_lg[it];
+    const bool diag = (s_j[it] == i);
+    const T *Ks = tiles + (2 * b + 0) * TILE;
+    const T *Vs = tiles + (2 * b + 1) * TILE;
 
     // S^T[key][query] for two 32-key halves x two 32-query tiles.
     f32x16 sacc[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const T *arow = Ks + (32 * mt + chain_key_of_row<T>(l32)) * F::KROW + hf * E;
+      const T *arow = Ks + (32 * mt + chain_key_of_row<T>(l32)) * RT::ROW + hf * E;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        typename M::Op a = load_op<T>(arow + ks * KS);
+        const typename M::Op a = lds_op<T>(arow + ks * KS);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = M::run(a, qreg[nt][ks], sacc[mt][nt]);
       }
@@ -247,57 +177,50 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float z = sacc[mt][nt][r] * p.scale_log2 + lg2;
-          if (diag) {
-            int key = 32 * mt + chain_slot<T>(r, hf);
-            if (key > ql) z = -INFINITY;
-          }
+          if (diag && 32 * mt + chain_slot<T>(r, hf) > ql) z = -INFINITY;
           sacc[mt][nt][r] = z;
           mx = fmaxf(mx, z);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float alpha = fast_exp2(m_run[nt] - m_new);
+      // move the reference only on a large increase (first tile: from -inf)
+      const bool move = mx > m_run[nt] + kRescale;
+      const float m_new = move ? mx : m_run[nt];
+      const float alpha = move ? fast_exp2(m_run[nt] - m_new) : 1.f;
       float sum = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(sacc[mt][nt][r] - m_new);
+          const float pr = fast_exp2(sacc[mt][nt][r] - m_new);
           sacc[mt][nt][r] = pr;
           sum += pr;
         }
       sum += __shfl_xor(sum, 32);
       l_run[nt] = l_run[nt] * alpha + sum;
       m_run[nt] = m_new;
+      if (__builtin_amdgcn_read_exec() & __ballot(move)) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const int mt = kc / SPT, r0 = (kc % SPT) * E;
-        if constexpr (E == 8) {
-          bf16x8 b;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) b[e] = (__bf16)sacc[mt][nt][r0 + e];
-          pop[nt][kc] = b;
-        } else {
-          pop[nt][kc] = sacc[mt][nt][r0];
-        }
+          for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
       }
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) pop[nt][kc] = regs_op<T>(sacc[kc / SPT][nt], (kc % SPT) * E);
     }
 
-    // O^T[d][query] += V^T[d][key] P^T[key][query]
+    // O^T[d][query] += V^T[d][key] P^T[key][query], V read transposed
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const T *arow = Vt + (32 * dt + l32) * F::VROW + hf * E;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        typename M::Op a = load_op<T>(arow + kc * KS);
+        const typename M::Op a = lds_op_rows<T>(Vs, RT::ROW, kc * KS, 32 * dt);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = M::run(a, pop[nt][kc], oacc[dt][nt]);
       }
     }
+    if (it + 1 < ntiles) store_tile(b ^ 1);
+    if (it + 2 < ntiles) load_tile(it + 2);
+    __syncthreads();
   }
 
   if (!head_ok) return;

@@ -112,11 +112,10 @@ template <typename T, typename TO, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   using M = Mfma<T>;
   constexpr int NT = NW * kWave;
-  constexpr int PAD = sizeof(T) == 2 ? 16 : 4;
-  using RT = RowTile<T, D, NT, PAD>;
+  using RT = RowTile<T, D, NT>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
-  constexpr int TILE = kBlock * RT::ROW;
+  constexpr int TILE = RT::ELEMS;
 
   __shared__ __attribute__((aligned(16))) T tiles[2 * 2 * TILE];  // [buf][K | V]
   __shared__ float s_F[NW][kMaxBudget];  // per tile: sum of P dP over the wave's rows
@@ -216,12 +215,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
     const int j = s_j[it];
     const long tok = seq_start + (long)j * kBlock;
     const int nv = min(kBlock, seq_len - j * kBlock);
-    rowtile_load<T, T, D, NT, PAD>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);
-    rowtile_load<T, T, D, NT, PAD>(vst, vv + (tok * p.hkv + g) * D, kstride, nv);
+    rowtile_load<T, T, D, NT>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);
+    rowtile_load<T, T, D, NT>(vst, vv + (tok * p.hkv + g) * D, kstride, nv);
   };
   auto store_tile = [&](int b) {
-    rowtile_store<T, D, NT, PAD>(kst, tiles + (2 * b + 0) * TILE);
-    rowtile_store<T, D, NT, PAD>(vst, tiles + (2 * b + 1) * TILE);
+    rowtile_store<T, D, NT>(kst, tiles + (2 * b + 0) * TILE);
+    rowtile_store<T, D, NT>(vst, tiles + (2 * b + 1) * TILE);
   };
   if (ntiles > 0) {
     load_tile(0);
@@ -247,12 +246,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) sacc[nt] = pacc[nt] = f32x16{};
       const int krow = 32 * mt + chain_key_of_row<T>(l32);
-      const T *ka = Ks + krow * RT::ROW + hf * E;
-      const T *va = Vs + krow * RT::ROW + hf * E;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const typename M::Op a = lds_op<T>(ka + ks * KS);
-        const typename M::Op bb = lds_op<T>(va + ks * KS);
+        const typename M::Op a = tile_op<T, D>(Ks, krow, hf * E + ks * KS);
+        const typename M::Op bb = tile_op<T, D>(Vs, krow, hf * E + ks * KS);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           sacc[nt] = M::run(a, qreg[nt][ks], sacc[nt]);
@@ -279,7 +276,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
       for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
         for (int kc = 0; kc < SPT; ++kc) {
-          const typename M::Op a = lds_op_rows<T>(Ks, RT::ROW, 32 * mt + kc * KS, 32 * dt);
+          const typename M::Op a = tile_op_rows<T, D>(Ks, 32 * mt + kc * KS, 32 * dt);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
             dqacc[dt][nt] = M::run(a, regs_op<T>(sacc[nt], kc * E), dqacc[dt][nt]);
@@ -372,11 +369,10 @@ template <typename T, typename TO, int D>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   using M = Mfma<T>;
   constexpr int NT = 256;
-  constexpr int PAD = sizeof(T) == 2 ? 16 : 4;
-  using RT = RowTile<T, D, NT, PAD>;
+  using RT = RowTile<T, D, NT>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
-  constexpr int TILE = kBlock * RT::ROW;          // elements per tile
+  constexpr int TILE = RT::ELEMS;                 // elements per tile
   constexpr int LDS_T = 2 * 2 * TILE;             // {Q, dO} x 2 buffers
   constexpr int LDS_RED = 2 * 2 * NDT * 16 * kWave;  // floats: 2 waves x (dk, dv)
   constexpr int LDS_BYTES =
@@ -460,8 +456,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     const int h = g * G + st % G;
     const long t0 = seq_start + (long)i * kBlock;
     const int nq = min(kBlock, seq_len - i * kBlock);
-    rowtile_load<T, T, D, NT, PAD>(qst, q + (t0 * p.hq + h) * D, qstride, nq);
-    rowtile_load<TO, T, D, NT, PAD>(dst, dO + (t0 * p.hq + h) * D, qstride, nq);
+    rowtile_load<T, T, D, NT>(qst, q + (t0 * p.hq + h) * D, qstride, nq);
+    rowtile_load<TO, T, D, NT>(dst, dO + (t0 * p.hq + h) * D, qstride, nq);
     if (threadIdx.x < kBlock) {
       const bool ok = threadIdx.x < nq;
       st_lse = ok ? p.lse[(long)h * p.T + t0 + threadIdx.x] * kLog2e : INFINITY;
@@ -469,8 +465,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
   auto store_step = [&](int b) {
-    rowtile_store<T, D, NT, PAD>(qst, tiles + (2 * b + 0) * TILE);
-    rowtile_store<T, D, NT, PAD>(dst, tiles + (2 * b + 1) * TILE);
+    rowtile_store<T, D, NT>(qst, tiles + (2 * b + 0) * TILE);
+    rowtile_store<T, D, NT>(dst, tiles + (2 * b + 1) * TILE);
     if (threadIdx.x < kBlock) {
       s_lse[b][threadIdx.x] = st_lse;
       s_D[b][threadIdx.x] = st_D;
@@ -503,12 +499,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     // query rows loaded in chain order so P and dS feed the next products.
     f32x16 sacc = f32x16{}, pacc = f32x16{};
     const int qrow = 32 * qh + chain_key_of_row<T>(l32);
-    const T *qa = Qs + qrow * RT::ROW + hf * E;
-    const T *da = Ds + qrow * RT::ROW + hf * E;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      sacc = M::run(lds_op<T>(qa + ks * KS), kreg[ks], sacc);
-      pacc = M::run(lds_op<T>(da + ks * KS), vreg[ks], pacc);
+      sacc = M::run(tile_op<T, D>(Qs, qrow, hf * E + ks * KS), kreg[ks], sacc);
+      pacc = M::run(tile_op<T, D>(Ds, qrow, hf * E + ks * KS), vreg[ks], pacc);
     }
     // this lane's 16 query rows, in register order, come in four runs of 4
     // consecutive rows: fetch their lse and D as float4s
@@ -546,9 +540,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int kc = 0; kc < SPT; ++kc) {
         const int kq = 32 * qh + kc * KS;
-        dvacc[dt] = M::run(lds_op_rows<T>(Ds, RT::ROW, kq, 32 * dt), regs_op<T>(sacc, kc * E),
+        dvacc[dt] = M::run(tile_op_rows<T, D>(Ds, kq, 32 * dt), regs_op<T>(sacc, kc * E),
                            dvacc[dt]);
-        dkacc[dt] = M::run(lds_op_rows<T>(Qs, RT::ROW, kq, 32 * dt), regs_op<T>(pacc, kc * E),
+        dkacc[dt] = M::run(tile_op_rows<T, D>(Qs, kq, 32 * dt), regs_op<T>(pacc, kc * E),
                            dkacc[dt]);
       }
     }
@@ -633,8 +627,7 @@ constexpr int kLdsBytes = 160 * 1024;
 
 template <typename T, int D, int NW>
 constexpr int dq_static_lds() {
-  return (int)sizeof(T) * 4 * kBlock * (D + (sizeof(T) == 2 ? 16 : 4)) +
-         (NW + 3) * kMaxBudget * 4 + 64;
+  return (int)sizeof(T) * 4 * kBlock * D + (NW + 3) * kMaxBudget * 4 + 64;
 }
 
 template <typename T, int D, int NW>

@@ -39,14 +39,13 @@ template <typename T, typename TO, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   using M = Mfma<T>;
   constexpr int NT = NW * kWave;
-  constexpr int PAD = sizeof(T) == 2 ? 16 : 4;
-  using RT = RowTile<T, D, NT, PAD>;
+  using RT = RowTile<T, D, NT>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS;          // k-steps over head_dim
   constexpr int NDT = D / 32;          // 32-row d tiles of O^T
   constexpr int NKC = kBlock / KS;     // k-steps over a 64-key tile
   constexpr int SPT = 32 / KS;         // k-steps per 32-key half tile
-  constexpr int TILE = kBlock * RT::ROW;
+  constexpr int TILE = RT::ELEMS;
 
   __shared__ __attribute__((aligned(16))) T tiles[2 * 2 * TILE];  // [buf][K | V]
   __shared__ int s_j[kMaxBudget];
@@ -127,12 +126,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     const int j = s_j[it];
     const long tok = seq_start + (long)j * kBlock;
     const int nv = min(kBlock, seq_len - j * kBlock);
-    rowtile_load<T, T, D, NT, PAD>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);
-    rowtile_load<T, T, D, NT, PAD>(vst, vv + (tok * p.hkv + g) * D, kstride, nv);
+    rowtile_load<T, T, D, NT>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);
+    rowtile_load<T, T, D, NT>(vst, vv + (tok * p.hkv + g) * D, kstride, nv);
   };
   auto store_tile = [&](int b) {
-    rowtile_store<T, D, NT, PAD>(kst, tiles + (2 * b + 0) * TILE);
-    rowtile_store<T, D, NT, PAD>(vst, tiles + (2 * b + 1) * TILE);
+    rowtile_store<T, D, NT>(kst, tiles + (2 * b + 0) * TILE);
+    rowtile_store<T, D, NT>(vst, tiles + (2 * b + 1) * TILE);
   };
   if (ntiles > 0) {
     load_tile(0);
@@ -155,12 +154,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     f32x16 sacc[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const T *arow = Ks + (32 * mt + chain_key_of_row<T>(l32)) * RT::ROW + hf * E;
+      const int krow = 32 * mt + chain_key_of_row<T>(l32);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const typename M::Op a = lds_op<T>(arow + ks * KS);
+        const typename M::Op a = tile_op<T, D>(Ks, krow, hf * E + ks * KS);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = M::run(a, qreg[nt][ks], sacc[mt][nt]);
       }
@@ -213,7 +212,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        const typename M::Op a = lds_op_rows<T>(Vs, RT::ROW, kc * KS, 32 * dt);
+        const typename M::Op a = tile_op_rows<T, D>(Vs, kc * KS, 32 * dt);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = M::run(a, pop[nt][kc], oacc[dt][nt]);
       }

@@ -1,138 +1,127 @@
 // Staging of one 64-row x D tile: global -> registers -> LDS.
 //
-// A thread owns chunks of 4 consecutive rows x VEC consecutive columns
-// (VEC = 16 bytes of the LDS element type T).  Loads are 16-byte (or 32-byte
-// when an fp32 source is narrowed to bf16) and coalesced along the row; the
-// chunk can then be written row-major (one 16-byte store per row) and/or
-// transposed (VEC stores of 4 consecutive rows), which gives the
-// column-contiguous operands the MFMA needs when a product contracts over
-// the tile's rows.
+// A thread owns 16-byte chunks (VEC elements of the LDS element type T);
+// consecutive threads take consecutive chunks of a row, so the global loads
+// are coalesced 16-byte (or 32-byte when an fp32 source is narrowed to bf16)
+// accesses.  The chunks live in registers as native 4 x u32 vectors.
 #pragma once
 #include "sas_device.h"
 
 namespace sas {
 
-template <typename T, int D, int NT>
-struct Tile4 {
-  static constexpr int VEC = 16 / sizeof(T);
-  static constexpr int DC = D / VEC;                 // column chunks per row group
-  static constexpr int TOT = (kBlock / 4) * DC;      // chunks per tile
-  static constexpr int CH = (TOT + NT - 1) / NT;     // chunks per thread
-  static constexpr int ROW = D + VEC;                // row-major stride (elements)
-  static constexpr int TROW = kBlock + VEC;          // transposed stride (elements)
-  T v[CH][4][VEC];
+// Row-major tiles in LDS, 64 rows x D columns, no padding, with the 16-byte
+// chunks of each row permuted by an XOR swizzle so that both access
+// patterns the kernels use are free of bank conflicts:
+//   - 16-byte operand reads where 16 lanes read the same column chunk of 16
+//     different rows (rows differ in their low 4 bits), and
+//   - transposed reads (ds_read_b64_tr_b16) where a 16-lane group reads
+//     8 bytes x 4 lanes of two adjacent chunks in 4 consecutive rows.
+// With 16 chunks per row the chunk c of row r is stored at
+// c ^ ((r & 7) << 1 | (r >> 3) & 1): 16 consecutive rows see 16 distinct
+// values, and rows 4a..4a+3 see 4 distinct even/odd pairs, so the 8 chunks
+// of a transposed read never share a bank.
+template <typename T, int D>
+struct Swz {
+  static constexpr int VEC = 16 / sizeof(T);  // elements per chunk
+  static constexpr int CPR = D / VEC;         // chunks per row
+  __device__ static inline int f(int r) {
+    if constexpr (CPR >= 16)
+      return ((r & 7) << 1) | ((r >> 3) & 1);
+    else
+      return (r >> 1) & (CPR - 1);
+  }
+  // element offset of (row, col) inside a tile
+  __device__ static inline int off(int r, int col) {
+    return r * D + (((col / VEC) ^ f(r)) * VEC) + (col % VEC);
+  }
 };
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes of T from TS elements at src (TS == T: one load; fp32 -> bf16:
+// two 16-byte loads, rounded to nearest even).
 template <typename TS, typename T>
-__device__ inline void load_vec(T *dst, const TS *src, int n_elem) {
+__device__ inline u32x4 load_chunk(const TS *src) {
   if constexpr (sizeof(TS) == sizeof(T)) {
-    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
-  } else {  // fp32 source narrowed to bf16
+    return *reinterpret_cast<const u32x4 *>(src);
+  } else {
     const float4 a = reinterpret_cast<const float4 *>(src)[0];
     const float4 b = reinterpret_cast<const float4 *>(src)[1];
-    dst[0] = (T)a.x; dst[1] = (T)a.y; dst[2] = (T)a.z; dst[3] = (T)a.w;
-    dst[4] = (T)b.x; dst[5] = (T)b.y; dst[6] = (T)b.z; dst[7] = (T)b.w;
-  }
-  (void)n_elem;
-}
-
-// rows >= nvalid are zero.  Row r of the tile starts at base + r * stride.
-template <typename TS, typename T, int D, int NT>
-__device__ inline void tile4_load(Tile4<T, D, NT> &st, const TS *base, long stride, int nvalid) {
-  using F = Tile4<T, D, NT>;
-#pragma unroll
-  for (int it = 0; it < F::CH; ++it) {
-    const int c = threadIdx.x + it * NT;
-    const int kg = c / F::DC, dc = c % F::DC;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int row = 4 * kg + x;
-      if ((F::TOT % NT == 0 || c < F::TOT) && row < nvalid) {
-        load_vec<TS, T>(st.v[it][x], base + row * stride + dc * F::VEC, F::VEC);
-      } else {
-#pragma unroll
-        for (int e = 0; e < F::VEC; ++e) st.v[it][x][e] = T(0.f);
-      }
-    }
+    const bf16x8 w = {(__bf16)a.x, (__bf16)a.y, (__bf16)a.z, (__bf16)a.w,
+                      (__bf16)b.x, (__bf16)b.y, (__bf16)b.z, (__bf16)b.w};
+    return __builtin_bit_cast(u32x4, w);
   }
 }
 
+// Register staging of one tile.
 template <typename T, int D, int NT>
-__device__ inline void tile4_store_rm(const Tile4<T, D, NT> &st, T *lds) {
-  using F = Tile4<T, D, NT>;
-#pragma unroll
-  for (int it = 0; it < F::CH; ++it) {
-    const int c = threadIdx.x + it * NT;
-    if (F::TOT % NT != 0 && c >= F::TOT) continue;
-    const int kg = c / F::DC, dc = c % F::DC;
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      *reinterpret_cast<uint4 *>(lds + (4 * kg + x) * F::ROW + dc * F::VEC) =
-          *reinterpret_cast<const uint4 *>(st.v[it][x]);
-  }
-}
-
-template <typename T, int D, int NT>
-__device__ inline void tile4_store_tr(const Tile4<T, D, NT> &st, T *lds) {
-  using F = Tile4<T, D, NT>;
-#pragma unroll
-  for (int it = 0; it < F::CH; ++it) {
-    const int c = threadIdx.x + it * NT;
-    if (F::TOT % NT != 0 && c >= F::TOT) continue;
-    const int kg = c / F::DC, dc = c % F::DC;
-#pragma unroll
-    for (int e = 0; e < F::VEC; ++e) {
-      T *dst = lds + (dc * F::VEC + e) * F::TROW + 4 * kg;
-      if constexpr (sizeof(T) == 2) {
-        bf16x4 w = {st.v[it][0][e], st.v[it][1][e], st.v[it][2][e], st.v[it][3][e]};
-        *reinterpret_cast<bf16x4 *>(dst) = w;
-      } else {
-        *reinterpret_cast<float4 *>(dst) =
-            make_float4(st.v[it][0][e], st.v[it][1][e], st.v[it][2][e], st.v[it][3][e]);
-      }
-    }
-  }
-}
-
-// Row-major staging only: 16-byte chunks (VEC elements of T), a row of D
-// elements is D / VEC chunks, consecutive threads take consecutive chunks.
-template <typename T, int D, int NT, int PAD>
 struct RowTile {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int DC = D / VEC;
   static constexpr int TOT = kBlock * DC;
   static constexpr int CH = (TOT + NT - 1) / NT;
-  static constexpr int ROW = D + PAD;  // LDS row stride (elements)
-  T v[CH][VEC];
+  static constexpr int ELEMS = kBlock * D;  // LDS elements per tile
+  u32x4 v[CH];
 };
 
-template <typename TS, typename T, int D, int NT, int PAD>
-__device__ inline void rowtile_load(RowTile<T, D, NT, PAD> &st, const TS *base, long stride,
+// Rows >= nvalid are loaded from row nvalid - 1 (finite values; the kernels
+// mask those rows out of every product that could see them).
+template <typename TS, typename T, int D, int NT>
+__device__ inline void rowtile_load(RowTile<T, D, NT> &st, const TS *base, long stride,
                                     int nvalid) {
-  using F = RowTile<T, D, NT, PAD>;
+  using F = RowTile<T, D, NT>;
 #pragma unroll
   for (int it = 0; it < F::CH; ++it) {
     const int c = threadIdx.x + it * NT;
     const int row = c / F::DC, dc = c % F::DC;
-    if ((F::TOT % NT == 0 || c < F::TOT) && row < nvalid) {
-      load_vec<TS, T>(st.v[it], base + row * stride + dc * F::VEC, F::VEC);
-    } else {
-#pragma unroll
-      for (int e = 0; e < F::VEC; ++e) st.v[it][e] = T(0.f);
+    if (F::TOT % NT == 0 || c < F::TOT) {
+      const int r = row < nvalid ? row : nvalid - 1;
+      st.v[it] = load_chunk<TS, T>(base + r * stride + dc * F::VEC);
     }
   }
 }
 
-template <typename T, int D, int NT, int PAD>
-__device__ inline void rowtile_store(const RowTile<T, D, NT, PAD> &st, T *lds) {
-  using F = RowTile<T, D, NT, PAD>;
+template <typename T, int D, int NT>
+__device__ inline void rowtile_store(const RowTile<T, D, NT> &st, T *lds) {
+  using F = RowTile<T, D, NT>;
 #pragma unroll
   for (int it = 0; it < F::CH; ++it) {
     const int c = threadIdx.x + it * NT;
     if (F::TOT % NT != 0 && c >= F::TOT) continue;
     const int row = c / F::DC, dc = c % F::DC;
-    *reinterpret_cast<uint4 *>(lds + row * F::ROW + dc * F::VEC) =
-        *reinterpret_cast<const uint4 *>(st.v[it]);
+    *reinterpret_cast<u32x4 *>(lds + Swz<T, D>::off(row, dc * F::VEC)) = st.v[it];
+  }
+}
+
+// MFMA operand from a swizzled tile, k-contiguous along a row:
+// lane gets X[row][col .. col + E - 1].
+template <typename T, int D>
+__device__ inline typename Mfma<T>::Op tile_op(const T *X, int row, int col) {
+  const T *p = X + Swz<T, D>::off(row, col);
+  if constexpr (sizeof(T) == 2)
+    return *reinterpret_cast<const bf16x8 *>(p);
+  else
+    return *p;
+}
+
+// MFMA operand contracting over the tile's ROWS (see lds_op_rows in
+// sas_device.h for the lane mapping): lane l receives
+// X[kb + h*E + e][mb + l % 32], e = 0..E-1.
+template <typename T, int D>
+__device__ inline typename Mfma<T>::Op tile_op_rows(const T *X, int kb, int mb) {
+  const int lane = threadIdx.x % kWave;
+  if constexpr (sizeof(T) == 2) {
+    const int g = lane / 16, s = lane % 16;
+    const int row = kb + 8 * (g / 2) + s / 4;
+    const int col = mb + 16 * (g % 2) + 4 * (s % 4);
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(const lds_short *)(X + Swz<T, D>::off(row, col)));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(const lds_short *)(X + Swz<T, D>::off(row + 4, col)));
+    const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+  } else {
+    return X[Swz<T, D>::off(kb + lane / 32, mb + lane % 32)];
   }
 }
 

@@ -14,7 +14,12 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsas.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sas_api.cpp", "gate.hip", "fwd.hip", "bwd.hip", "decode.hip"]
+SOURCES = ["sas_api.cpp", "gate.hip", "fwd.hip", "bwd.hip", "bwd_dkdv.hip", "decode.hip"]
+
+# Kernels whose accumulators and MFMA results are better placed by asking for
+# the VGPR form of MFMA (fewer accumulator moves between AGPRs and VGPRs in the
+# inner loop; measured faster for these two, slower for the dq kernel).
+MFMA_VGPR_FORM = {"fwd.hip", "bwd_dkdv.hip"}
 
 # Packed fp32 VALU ops are kept off: hipcc would otherwise form them from
 # ordinary float code.
@@ -29,6 +34,8 @@ def _compile(src: str, verbose: bool) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
     cmd = [HIPCC, *COMMON, "-c"]
+    if src in MFMA_VGPR_FORM:
+        cmd += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += [path, "-o", obj]

@@ -118,6 +118,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
+  // the register operands are complete before any tile load is issued, so
+  // the wait counter tracking never makes a tile wait for its own prefetch
+  wait_vmem_all();
   __syncthreads();
   const int ntiles = s_n;
   const long kstride = (long)p.hkv * D;

@@ -98,6 +98,12 @@ __device__ inline typename Mfma<T>::Op lds_op_rows(const T *X, int ld, int kb, i
   }
 }
 
+// Wait until every vector-memory load this wave issued has returned
+// (s_waitcnt vmcnt(0); the expcnt and lgkmcnt fields are left at their
+// maxima, i.e. not waited on).  Resets the compiler's pending-load tracking
+// at a point where that is cheap.
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------------------
 // Conversions
 // ---------------------------------------------------------------------------

@@ -93,6 +93,59 @@ __device__ inline void rowtile_store(const RowTile<T, D, NT> &st, T *lds) {
   }
 }
 
+// E consecutive values of an output-dtype tensor (dO, o) held in registers
+// with vector loads; get(e) is value e as a float, as_op<T>() the values as
+// one MFMA operand of type T (rounded to nearest even when TO is wider).
+template <typename TO, int E>
+struct OutChunk;
+
+template <>
+struct OutChunk<__bf16, 8> {
+  u32x4 w;
+  __device__ void load(const __bf16 *p) { w = *reinterpret_cast<const u32x4 *>(p); }
+  __device__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ float get(int e) const {
+    const unsigned x = w[e / 2];
+    return __uint_as_float((e % 2) ? (x & 0xffff0000u) : (x << 16));
+  }
+  template <typename T>
+  __device__ bf16x8 as_op() const { return __builtin_bit_cast(bf16x8, w); }
+};
+
+template <>
+struct OutChunk<float, 8> {
+  float4 a, b;
+  __device__ void load(const float *p) {
+    a = reinterpret_cast<const float4 *>(p)[0];
+    b = reinterpret_cast<const float4 *>(p)[1];
+  }
+  __device__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ float get(int e) const {
+    const float4 &c = e < 4 ? a : b;
+    switch (e % 4) {
+      case 0: return c.x;
+      case 1: return c.y;
+      case 2: return c.z;
+      default: return c.w;
+    }
+  }
+  template <typename T>
+  __device__ bf16x8 as_op() const {
+    return bf16x8{(__bf16)a.x, (__bf16)a.y, (__bf16)a.z, (__bf16)a.w,
+                  (__bf16)b.x, (__bf16)b.y, (__bf16)b.z, (__bf16)b.w};
+  }
+};
+
+template <>
+struct OutChunk<float, 1> {
+  float v;
+  __device__ void load(const float *p) { v = *p; }
+  __device__ void zero() { v = 0.f; }
+  __device__ float get(int) const { return v; }
+  template <typename T>
+  __device__ float as_op() const { return v; }
+};
+
 // MFMA operand from a swizzled tile, k-contiguous along a row:
 // lane gets X[row][col .. col + E - 1].
 template <typename T, int D>

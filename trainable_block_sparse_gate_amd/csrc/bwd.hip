@@ -190,6 +190,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
       for (int e = 0; e < E; ++e) dacc += dch[ks].get(e) * och[ks].get(e);
       doreg[nt][ks] = dch[ks].template as_op<T>();
     }
+    // a wider dO is handed to the dk/dv phase rounded to the input dtype
+    if constexpr (sizeof(TO) != sizeof(T)) {
+      if (ql < nq && head_ok) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          *reinterpret_cast<typename M::Op *>(p.dO16 + base + ks * KS) = doreg[nt][ks];
+      }
+    }
     dacc += __shfl_xor(dacc, 32);
     Dv[nt] = dacc;
     lse2[nt] = INFINITY;  // padding rows: P = 0
@@ -295,13 +303,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   }
 
   // Exact D per query row, then dlg of each tile = sum P dP - sum_t D_t G_t.
+  // Both row statistics are stored for all 64 rows of the block (rows past
+  // its end: lse +inf, D 0) so the dk/dv phase can fetch them as a whole.
   float Ex[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     Ex[nt] = Eacc[nt] + __shfl_xor(Eacc[nt], 32);
     const int ql = 32 * nt + l32;
-    if (ql < nq && hf == 0 && head_ok)
-      p.Dbuf[(long)h * p.T + seq_start + (long)i * kBlock + ql] = Ex[nt];
+    if (hf == 0 && head_ok) {
+      const long at = ((long)h * p.QB + Q) * kBlock + ql;
+      p.Dbuf[at] = ql < nq ? Ex[nt] : 0.f;
+      p.Lbuf[at] = lse2[nt];
+    }
   }
   for (int it = 0; it < ntiles; ++it) {
     float c = 0.f;

@@ -10,6 +10,8 @@
 // each writes a partial sum and the last one to finish adds all of them in
 // segment order, so the result does not depend on which workgroup finishes
 // last.
+#include <type_traits>
+
 #include "sas_device.h"
 #include "sas_launch.h"
 #include "tile_stage.h"
@@ -18,28 +20,43 @@ namespace sas {
 // ------------------------------------------------------------------ dk/dv
 // Workgroup of 4 waves: wave = (query half qh, key half kh).  Each wave
 // owns 32 keys (K, V as B operands in registers) and, per step, 32 of the
-// 64 query rows of one head of one keeping row.  Q and dO tiles are double
-// buffered in LDS (row-major only) with the step after next in flight from
-// memory; the products that contract over query rows read their operands
+// 64 query rows of one head of one keeping row.  The Q and dO tiles of a
+// step, and the row statistics (lse * log2 e and D, written per 64-row
+// block by the dq phase), go from global memory straight into LDS with
+// global_load_lds (no register staging).  bf16 tiles use three LDS buffers
+// and are requested two steps ahead; fp32 tiles use two, one step ahead.
+// The products that contract over query rows read their operands
 // transposed straight from the row-major tiles.
 constexpr int kSegMax = 64;  // entries per segment the kernel can hold
 
-template <typename T, typename TO, int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   using M = Mfma<T>;
-  constexpr int NT = 256;
-  using RT = RowTile<T, D, NT>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
-  constexpr int TILE = RT::ELEMS;                 // elements per tile
-  constexpr int LDS_T = 2 * 2 * TILE;             // {Q, dO} x 2 buffers
-  constexpr int LDS_RED = 2 * 2 * NDT * 16 * kWave;  // floats: 2 waves x (dk, dv)
-  constexpr int LDS_BYTES =
-      (LDS_T * (int)sizeof(T) > LDS_RED * 4) ? LDS_T * (int)sizeof(T) : LDS_RED * 4;
+  constexpr int NBUF = sizeof(T) == 2 ? 3 : 2;    // LDS buffers per tile kind
+  constexpr int TILE = kBlock * D;                // elements per tile
+  constexpr int VEC = 16 / (int)sizeof(T);        // elements per 16-byte chunk
+  constexpr int CPR = D / VEC;                    // chunks per row
+  constexpr int RPS = kWave / CPR;                // rows per 1 KB request
+  constexpr int SPW = kBlock / RPS / 4;           // 1 KB requests per wave per tile
+  constexpr int PER_STEP = 2 * SPW + 1;           // requests per wave per step
+  static_assert(kBlock % (4 * RPS) == 0, "tile rows must split evenly over the waves");
+  static_assert(2 * NDT * 16 * kWave * 4 <= 2 * TILE * (int)sizeof(T),
+                "a buffer holds one half of the final reduction");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
-  __shared__ __attribute__((aligned(16))) float s_lse[2][kBlock];
-  __shared__ __attribute__((aligned(16))) float s_D[2][kBlock];
+  // Each buffer is its own LDS variable, so the compiler can tell that the
+  // requests in flight into one buffer never alias reads of another and
+  // inserts no wait for them; the loop below is unrolled over the buffers.
+  __shared__ __attribute__((aligned(16))) T buf0[2 * TILE];  // [Q | dO][64][D]
+  __shared__ __attribute__((aligned(16))) T buf1[2 * TILE];
+  __shared__ __attribute__((aligned(16))) T buf2[NBUF == 3 ? 2 * TILE : 8];
+  // row statistics: [wave][256] per buffer; waves 0 / 1 bring lse * log2 e /
+  // D in their first 64 entries (the rest, and waves 2 and 3, are filler
+  // that keeps every wave's request count the same)
+  __shared__ __attribute__((aligned(16))) float stat0[4][4 * kBlock];
+  __shared__ __attribute__((aligned(16))) float stat1[4][4 * kBlock];
+  __shared__ __attribute__((aligned(16))) float stat2[NBUF == 3 ? 4 : 1][4 * kBlock];
   __shared__ int s_ent[kSegMax];
   __shared__ float s_lg[kSegMax];
   __shared__ int s_last;
@@ -81,8 +98,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const T *q = static_cast<const T *>(p.q);
   const T *kk = static_cast<const T *>(p.k);
   const T *vv = static_cast<const T *>(p.v);
-  const TO *dO = static_cast<const TO *>(p.dO);
-  T *tiles = reinterpret_cast<T *>(smem);  // [buf][Q | dO][64][ROW]
+  const T *dO = static_cast<const T *>(p.dO_t);
 
   typename M::Op kreg[NKS], vreg[NKS];
   {
@@ -97,8 +113,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         vreg[ks] = typename M::Op{};
       }
     }
-    // K and V are complete before any step's loads are issued; the wait
-    // counter tracking then never makes a step wait for its own prefetch
+    // K and V are complete before the first tile request, so the explicit
+    // counts below only ever see tile requests
     wait_vmem_all();
   }
   f32x16 dkacc[NDT], dvacc[NDT];
@@ -107,59 +123,78 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 
   const int G = p.G;
   const int nsteps = nent * G;
-  const long qstride = (long)p.hq * D;
-  RT qst, dst;
-  // lse and D of the staged step, raw: nothing consumes them before the
-  // step is stored, so the loads stay in flight for a whole step
-  float st_lse = 0.f, st_D = 0.f;
-  bool st_ok = false;
   __syncthreads();  // s_ent / s_lg visible
 
-  auto load_step = [&](int st) {
+  auto tiles_of = [&](auto B) -> T * {
+    if constexpr (decltype(B)::value == 0) return buf0;
+    else if constexpr (decltype(B)::value == 1) return buf1;
+    else return buf2;
+  };
+  auto stats_of = [&](auto B) -> float(*)[4 * kBlock] {
+    if constexpr (decltype(B)::value == 0) return stat0;
+    else if constexpr (decltype(B)::value == 1) return stat1;
+    else return stat2;
+  };
+
+  // Requests of step st into buffer B: every wave first fetches one piece
+  // of row statistics (wave 0: lse, wave 1: D, 16 lanes' worth repeated
+  // over the wave), then SPW 1 KB pieces (RPS rows) of the Q tile and of
+  // the dO tile.  Lane l of a request lands at byte 16 l of the piece, i.e.
+  // at physical chunk l % CPR of its row; it fetches the logical chunk that
+  // the swizzle puts there.  Rows past the block's end repeat its last row
+  // (masked later).  Every wave issues exactly PER_STEP requests per step,
+  // unconditionally (steps past the end re-fetch the last step into a
+  // buffer that is not read again), so fixed wait counts are exact and the
+  // compiler's own tracking of the requests stays precise.
+  auto issue_step = [&](auto B, int st_req) {
+    const int st = min(st_req, nsteps - 1);
+    T *tl = tiles_of(B);
+    float(*stat)[4 * kBlock] = stats_of(B);
     const int ent = s_ent[st / G];
-    const int i = (ent >> 8) - q0;
+    const int qb = ent >> 8;  // packed query-block index
+    const int i = qb - q0;
     const int h = g * G + st % G;
     const long t0 = seq_start + (long)i * kBlock;
     const int nq = min(kBlock, seq_len - i * kBlock);
-    rowtile_load<T, T, D, NT>(qst, q + (t0 * p.hq + h) * D, qstride, nq);
-    rowtile_load<TO, T, D, NT>(dst, dO + (t0 * p.hq + h) * D, qstride, nq);
-    if (threadIdx.x < kBlock) {
-      st_ok = threadIdx.x < nq;
-      const int r = st_ok ? threadIdx.x : nq - 1;
-      st_lse = p.lse[(long)h * p.T + t0 + r];
-      st_D = p.Dbuf[(long)h * p.T + t0 + r];
+    {
+      const float *src =
+          ((wave & 1) ? p.Dbuf : p.Lbuf) + ((long)h * p.QB + qb) * kBlock + 4 * (lane % 16);
+      load_lds16(src, &stat[wave][0]);
+    }
+    const int r_in = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk) {
+      const T *src = tk == 0 ? q : dO;
+#pragma unroll
+      for (int sg = 0; sg < SPW; ++sg) {
+        const int piece = wave * SPW + sg;
+        const int r = piece * RPS + r_in;
+        const int rr = r < nq ? r : nq - 1;
+        const int c = pc ^ Swz<T, D>::f(r);
+        load_lds16(src + ((t0 + rr) * p.hq + h) * D + c * VEC, tl + tk * TILE + piece * RPS * D);
+      }
     }
   };
-  auto store_step = [&](int b) {
-    rowtile_store<T, D, NT>(qst, tiles + (2 * b + 0) * TILE);
-    rowtile_store<T, D, NT>(dst, tiles + (2 * b + 1) * TILE);
-    if (threadIdx.x < kBlock) {
-      s_lse[b][threadIdx.x] = st_ok ? st_lse * kLog2e : INFINITY;
-      s_D[b][threadIdx.x] = st_ok ? st_D : 0.f;
-    }
-  };
-  if (nsteps > 0) {
-    load_step(0);
-    store_step(0);
-    if (nsteps > 1) load_step(1);
-  }
-  __syncthreads();
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
-  // Per step: compute from one buffer, then store the next step's tile
-  // (loaded one step earlier) into the other buffer, issue the loads of the
-  // step after that, and barrier.  No LDS write of a wave is in flight while
-  // its transposed reads (ds_read_b64_tr_b16) issue: with writes pending,
-  // those reads returned wrong data on gfx950.
-  for (int st = 0; st < nsteps; ++st) {
-    const int b = st & 1;
+  // One step from buffer B: request the step NBUF - 1 ahead into the buffer
+  // the previous step read, compute, wait until this wave's requests of the
+  // next step have landed (those further ahead may still be in flight),
+  // barrier (every wave's requests visible, buffer B free for reuse).
+  auto step = [&](auto B, int st) {
+    constexpr int b = decltype(B)::value;
+    issue_step(std::integral_constant<int, (b + NBUF - 1) % NBUF>{}, st + NBUF - 1);
 
     const int e = st / G;
     const int i = (s_ent[e] >> 8) - q0;
     const int nq = min(kBlock, seq_len - i * kBlock);
     const float lg2 = s_lg[e];
     const bool diag = (i == j);
-    const T *Qs = tiles + (2 * b + 0) * TILE;
-    const T *Ds = tiles + (2 * b + 1) * TILE;
+    const T *Qs = tiles_of(B);
+    const T *Ds = Qs + TILE;
+    const float(*stat)[4 * kBlock] = stats_of(B);
 
     // S[query][key] and dP[query][key] for 32 queries x this wave's 32 keys;
     // query rows loaded in chain order so P and dS feed the next products.
@@ -178,16 +213,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int r0 = 0; r0 < 16; r0 += 4) {
         const int q4 = 32 * qh + chain_slot<T>(r0, hf);
-        const float4 a = *reinterpret_cast<const float4 *>(&s_lse[b][q4]);
-        const float4 c = *reinterpret_cast<const float4 *>(&s_D[b][q4]);
+        const float4 a = *reinterpret_cast<const float4 *>(&stat[0][q4]);
+        const float4 c = *reinterpret_cast<const float4 *>(&stat[1][q4]);
         lse_r[r0] = a.x; lse_r[r0 + 1] = a.y; lse_r[r0 + 2] = a.z; lse_r[r0 + 3] = a.w;
         D_r[r0] = c.x; D_r[r0 + 1] = c.y; D_r[r0 + 2] = c.z; D_r[r0 + 3] = c.w;
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        lse_r[r] = s_lse[b][32 * qh + chain_slot<T>(r, hf)];
-        D_r[r] = s_D[b][32 * qh + chain_slot<T>(r, hf)];
+        lse_r[r] = stat[0][32 * qh + chain_slot<T>(r, hf)];
+        D_r[r] = stat[1][32 * qh + chain_slot<T>(r, hf)];
       }
     }
     // full tiles (the common case) need no mask; the test is uniform
@@ -222,20 +257,40 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
                            dkacc[dt]);
       }
     }
-    if (st + 1 < nsteps) store_step(b ^ 1);
-    if (st + 2 < nsteps) load_step(st + 2);
-    __syncthreads();
+    wait_vmem<NBUF == 3 ? PER_STEP : 0>();
+    barrier_keep_requests();
+  };
+
+  // Prologue: the first NBUF - 1 steps.  Waiting for all of them (not just
+  // step 0) leaves no request in flight at the loop entry, which keeps the
+  // compiler's tracking of which buffer a request targets exact in the loop.
+  if (nsteps > 0) {
+    issue_step(I0{}, 0);
+    if constexpr (NBUF == 3) issue_step(I1{}, 1);
+    wait_vmem<0>();
+    barrier_keep_requests();
+    for (int st = 0; st < nsteps; st += NBUF) {
+      step(I0{}, st);
+      if (st + 1 < nsteps) step(I1{}, st + 1);
+      if constexpr (NBUF == 3)
+        if (st + 2 < nsteps) step(I2{}, st + 2);
+    }
+    // the last requests (re-fetches past the end) land before the buffers
+    // are reused below
+    wait_vmem<0>();
   }
 
-  // Add the two query halves: waves qh = 1 hand their sums to qh = 0.
-  float *red = reinterpret_cast<float *>(smem);
+  // Add the two query halves: waves qh = 1 hand their sums to qh = 0
+  // (dK through buffer 0, dV through buffer 1; every request has landed).
+  float *redk = reinterpret_cast<float *>(buf0);
+  float *redv = reinterpret_cast<float *>(buf1);
   if (qh == 1) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        red[((kh * 2 + 0) * NDT * 16 + dt * 16 + r) * kWave + lane] = dkacc[dt][r];
-        red[((kh * 2 + 1) * NDT * 16 + dt * 16 + r) * kWave + lane] = dvacc[dt][r];
+        redk[(kh * NDT * 16 + dt * 16 + r) * kWave + lane] = dkacc[dt][r];
+        redv[(kh * NDT * 16 + dt * 16 + r) * kWave + lane] = dvacc[dt][r];
       }
   }
   __syncthreads();
@@ -244,8 +299,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        dkacc[dt][r] += red[((kh * 2 + 0) * NDT * 16 + dt * 16 + r) * kWave + lane];
-        dvacc[dt][r] += red[((kh * 2 + 1) * NDT * 16 + dt * 16 + r) * kWave + lane];
+        dkacc[dt][r] += redk[(kh * NDT * 16 + dt * 16 + r) * kWave + lane];
+        dvacc[dt][r] += redv[(kh * NDT * 16 + dt * 16 + r) * kWave + lane];
       }
     // lane holds key `key`, 4 consecutive d per register group
     float *dk_out, *dv_out;
@@ -299,23 +354,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <typename T, typename TO, int D>
+template <typename T, int D>
 static hipError_t launch_dkdv_t(const BwdParams &p, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, TO, D>), dim3(p.U), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(p.U), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(const BwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
                            hipStream_t stream) {
-  if (dtype_bf16) {
-    if (out_bf16)
-      return head_dim == 128 ? launch_dkdv_t<__bf16, __bf16, 128>(p, stream)
-                             : launch_dkdv_t<__bf16, __bf16, 64>(p, stream);
-    return head_dim == 128 ? launch_dkdv_t<__bf16, float, 128>(p, stream)
-                           : launch_dkdv_t<__bf16, float, 64>(p, stream);
-  }
-  return head_dim == 128 ? launch_dkdv_t<float, float, 128>(p, stream)
-                         : launch_dkdv_t<float, float, 64>(p, stream);
+  (void)out_bf16;  // dO reaches this kernel in the input dtype (p.dO_t)
+  if (dtype_bf16)
+    return head_dim == 128 ? launch_dkdv_t<__bf16, 128>(p, stream)
+                           : launch_dkdv_t<__bf16, 64>(p, stream);
+  return head_dim == 128 ? launch_dkdv_t<float, 128>(p, stream)
+                         : launch_dkdv_t<float, 64>(p, stream);
 }
 
 }  // namespace sas

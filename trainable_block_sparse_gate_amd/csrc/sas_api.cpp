@@ -204,7 +204,8 @@ namespace {
 constexpr int kSeg = 32;  // keeping rows per dk/dv segment (at most 64)
 
 struct BwdLayout {
-  size_t off_D, off_list, off_count, off_segoff, off_done, off_dlgpart, off_partial, total;
+  size_t off_L, off_D, off_dO16, off_list, off_count, off_segoff, off_done, off_dlgpart,
+      off_partial, total;
   int U, nhc, max_nb;
 };
 
@@ -220,7 +221,12 @@ BwdLayout bwd_layout(const sas_problem *p, int max_nb) {
   // segments: sum over key blocks of max(1, ceil(count / kSeg)), count <= kept entries
   L.U = (int)((nx * p->budget_blocks + kSeg - 1) / kSeg + nx);
   size_t off = 0;
-  L.off_D = off;        off = align256(off + sizeof(float) * (size_t)p->hq * p->total_tokens);
+  const size_t rows = (size_t)p->hq * p->total_qblocks * 64;  // per-block padded rows
+  L.off_L = off;        off = align256(off + sizeof(float) * rows);
+  L.off_D = off;        off = align256(off + sizeof(float) * rows);
+  L.off_dO16 = off;     // bf16 copy of an fp32 dO for the dk/dv phase
+  if (p->dtype == SAS_BF16 && p->out_dtype == SAS_F32)
+    off = align256(off + 2 * (size_t)p->total_tokens * p->hq * p->head_dim);
   L.off_list = off;     off = align256(off + sizeof(int32_t) * nx * L.max_nb);
   L.off_count = off;    off = align256(off + sizeof(int32_t) * nx);
   L.off_segoff = off;   off = align256(off + sizeof(int32_t) * (nx + 1));
@@ -259,7 +265,10 @@ sas_status bwd_setup(const sas_problem *p, void *workspace, size_t workspace_byt
   b->max_nb = L.max_nb;
   b->scale = p->scale;
   b->scale_log2 = p->scale * 1.4426950408889634f;
+  b->Lbuf = reinterpret_cast<float *>(ws + L.off_L);
   b->Dbuf = reinterpret_cast<float *>(ws + L.off_D);
+  b->dO16 = (p->dtype == SAS_BF16 && p->out_dtype == SAS_F32)
+                ? reinterpret_cast<__bf16 *>(ws + L.off_dO16) : nullptr;
   b->list = reinterpret_cast<int32_t *>(ws + L.off_list);
   b->count = reinterpret_cast<int32_t *>(ws + L.off_count);
   b->seg_off = reinterpret_cast<int32_t *>(ws + L.off_segoff);
@@ -337,6 +346,7 @@ sas_status sas_bwd_dkdv(const sas_problem *p, const void *q, const void *k, cons
   b.k = k;
   b.v = v;
   b.dO = dO;
+  b.dO_t = b.dO16 ? static_cast<const void *>(b.dO16) : dO;
   b.lse = lse;
   b.sel_lg = sel_loggate;
   b.dk = dk;

@@ -104,6 +104,32 @@ __device__ inline typename Mfma<T>::Op lds_op_rows(const T *X, int ld, int kb, i
 // at a point where that is cheap.
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N) alone (N < 64; vmcnt sits in bits 3:0 and 15:14).
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the workgroup-scope fence that __syncthreads()
+// adds (that fence also waits for every global->LDS request in flight):
+// this wave's LDS accesses are complete, the compiler moves no memory
+// access across it, and outstanding global->LDS requests stay in flight.
+__device__ inline void barrier_keep_requests() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt at their maxima
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// One 16-byte-per-lane global -> LDS request (global_load_lds_dwordx4):
+// lane l's 16 bytes from gsrc land at lds_base + 16 l; lds_base must be the
+// same for every lane of the wave.  Completion is counted by vmcnt.
+__device__ inline void load_lds16(const void *gsrc, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds_base,
+                                   16, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Conversions
 // ---------------------------------------------------------------------------

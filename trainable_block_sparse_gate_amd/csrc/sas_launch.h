@@ -61,8 +61,11 @@ struct BwdParams {
   const int32_t *cu_seqlens, *cu_qblocks;
   int num_seqs, T, QB, hq, hkv, G, Kb, max_nb;
   float scale, scale_log2;
+  const void *dO_t;  // dO in the input dtype: dO itself, or dO16 when dO is wider
   // workspace carve-up
-  float *Dbuf;       // [hq][T]      rowsum(dO * o)
+  float *Lbuf;       // [hq][QB][64] lse * log2(e) per query row; +inf past a block's end
+  float *Dbuf;       // [hq][QB][64] exact D = sum_u P dP per query row; 0 past the end
+  __bf16 *dO16;      // [T][hq][D] dO rounded to bf16 (bf16 inputs, fp32 dO), else NULL
   int32_t *list;     // [hkv*QB][max_nb]  (query block << 8 | slot) per key block
   int32_t *count;    // [hkv*QB]
   int32_t *seg_off;  // [hkv*QB + 1] prefix sum of segments per key block

@@ -12,14 +12,17 @@
 //            on values the oracle reproduces bit for bit.  Summaries are
 //            channel-major, so lanes (blocks) read consecutive addresses.
 //   attend:  split-K over the kept blocks of every (sequence, kv head):
-//            each workgroup streams a few 64-token K/V blocks (16-byte
-//            coalesced loads, next block prefetched into registers), keeps
-//            an fp32 online softmax per query head with the block's log
-//            gate added, and writes an unnormalised partial; a second
-//            kernel merges the partials with a log-sum-exp combine in a
-//            fixed order.
+//            each wave of a workgroup streams its own share of 64-token
+//            K/V blocks (16-byte coalesced loads, several passes in flight
+//            in registers), keeps an fp32 online softmax per query head
+//            with the block's log gate added; the waves merge into an
+//            unnormalised partial per split, and a second kernel merges
+//            the partials with a log-sum-exp combine in a fixed order.
+#include <type_traits>
+
 #include "sas_device.h"
 #include "sas_launch.h"
+#include "tile_stage.h"
 
 namespace sas {
 
@@ -72,156 +75,271 @@ __global__ __launch_bounds__(256) void pooled_scores_kernel(DecodeParams p) {
 }
 
 // ------------------------------------------------------------------ attend
-// Thread layout per 64-token block: thread = (key group kr, channel chunk
-// dc); a chunk is 8 channels (16 bytes), KR = 256 / (D / 8) key groups,
-// each thread owns keys kr, kr + KR, ... (KPT of them).  Running max and
-// sum of every query head live in LDS; one wave per head updates them.
+// A workgroup takes one split of the kept blocks of one (sequence, kv head)
+// row; each of its 4 waves streams every 4th of those blocks on its own
+// (own online softmax, no barrier until the end).  Per 64-token block a
+// wave runs both products on 16x16x32 bf16 MFMAs with the G query heads as
+// the 16 columns (unused columns see zero queries):
+//   S^T[key][head] = K Q^T  -- K rows read from the tile in the key order
+//                              that makes each lane's S^T registers the 8
+//                              consecutive keys the next product contracts
+//                              over;
+//   O^T[d][head]  += V^T P^T -- V read transposed from its tile.
+// K and V pass through wave-private swizzled LDS tiles.  The next block's
+// K and V are requested into staging registers (1 KB contiguous per load,
+// 32-bit offsets from a uniform base) before the current block is
+// computed, and written to the tiles once the current block's reads are
+// done.  All requests land in registers, so the compiler's wait counts
+// stay exact.  The running max
+// per head moves only when a score passes it by more than kDecRescale
+// (log2 units).  At the end the waves are merged through LDS into the
+// split's unnormalised partial.
+constexpr float kDecRescale = 8.f;
+constexpr int kDecStepKeys = 32;  // keys per step: 32 or 64
+
 template <int D, int G>
-__global__ __launch_bounds__(256) void decode_attend_kernel(DecodeParams p) {
-  constexpr int DC = D / 8;
-  constexpr int KR = 256 / DC;
-  constexpr int KPT = kBlock / KR;
-  __shared__ float part[kBlock][G][DC + 1];  // per-chunk partial dot products
-  __shared__ float prob[G][kBlock];
-  __shared__ float s_m[G], s_l[G], s_alpha[G];
-  __shared__ float obuf[KR][G][D];
+__global__ __launch_bounds__(256, kDecodeWgPerCu) void decode_attend_kernel(DecodeParams p) {
+  static_assert(G <= 16, "query heads of a group are the 16 MFMA columns");
+  constexpr int SK = kDecStepKeys;         // keys per step (a block is 64 / SK steps)
+  constexpr int SPB = kBlock / SK;         // steps per block
+  constexpr int NSL = SK / 32;             // 32-key slices per step
+  constexpr int NKS = D / 32;              // contraction slices of S^T
+  constexpr int NDT = D / 16;              // 16-row tiles of O^T
+  constexpr int TILE = SK * D;             // tile elements
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int RPS = kWave / CPR;         // rows per 1 KB request
+  constexpr int NREQ = SK / RPS;           // requests per tile
+  static_assert(kMaxBudget / 4 <= kWave, "a wave's blocks fit one per lane");
+  __shared__ __attribute__((aligned(16))) __bf16 ktile[4][TILE];  // one per wave
+  __shared__ __attribute__((aligned(16))) __bf16 vtile[4][TILE];
+  __shared__ float s_m[4][G], s_l[4][G];
+  static_assert(G * D * 4 <= TILE * 2, "a wave's merged output fits in its K tile");
 
   const int row = blockIdx.y;  // b * hkv + g
   const int split = blockIdx.x;
   const int b = row / p.hkv, g = row % p.hkv;
   const int L = p.seqlens[b];
   const int cur = (L - 1) / kBlock;
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int kr = tid / DC, dc = tid % DC;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int q16 = lane / 16, c16 = lane % 16;
   const int32_t *sel = p.sel_idx + (long)row * p.Kb;
   const float *slg = p.sel_lg ? p.sel_lg + (long)row * p.Kb : nullptr;
-  const int s0 = split * p.per_split, s1 = min(p.Kb, s0 + p.per_split);
+  const int s0 = split * p.per_split + wave, s1 = min(p.Kb, split * p.per_split + p.per_split);
+  const int nb = s0 < s1 ? (s1 - s0 + 3) / 4 : 0;  // this wave's blocks: s0, s0 + 4, ...
   const __bf16 *kc = static_cast<const __bf16 *>(p.k);
   const __bf16 *vc = static_cast<const __bf16 *>(p.v);
   const __bf16 *q = static_cast<const __bf16 *>(p.q);
 
-  // this thread's 8 channels of every query head of the group, pre-scaled
-  float qv[G][8];
+  // Q^T as B operands: column c16 = query head c16 of the group (zero past G)
+  bf16x8 qreg[NKS];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const uint4 raw =
-        *reinterpret_cast<const uint4 *>(q + ((long)b * p.hq + g * G + hh) * D + dc * 8);
-    const __bf16 *qq = reinterpret_cast<const __bf16 *>(&raw);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[hh][e] = (float)qq[e] * p.scale_log2;
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (c16 < G)
+      qreg[ks] = *reinterpret_cast<const bf16x8 *>(q + ((long)b * p.hq + g * G + c16) * D +
+                                                   32 * ks + 8 * q16);
+    else
+      qreg[ks] = bf16x8{};
   }
-  float acc[G][8];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-  if (tid < G) {
-    s_m[tid] = -INFINITY;
-    s_l[tid] = 0.f;
+  // Blocks of this wave, looked up once: lane k holds block k's first-row
+  // offset (K and V alike), valid keys and log gate, read back with
+  // readlane (a memory lookup inside the loop would wait for every request
+  // in flight).  A slot that keeps no block (index -1 or past the current
+  // block) reads the current block with every key masked.
+  long b_off = 0;
+  int b_nv = 0;
+  float b_lg2 = 0.f;
+  if (lane < nb) {
+    const int c = s0 + 4 * lane;
+    const int j = sel[c];
+    const bool ok = j >= 0 && j <= cur;
+    const int jj = ok ? j : cur;
+    b_nv = !ok ? 0 : (jj == cur ? L - cur * kBlock : kBlock);
+    b_off = kv_row(p, kc, b, g, jj * kBlock) - kc;  // a block never crosses a page
+    b_lg2 = slg ? slg[c] * kLog2e : 0.f;
   }
+  wait_vmem_all();
 
-  auto valid_block = [&](int sl, int &j, int &nv) {
-    j = sel[sl];
-    if (j < 0 || j > cur) return false;
-    nv = (j == cur) ? L - cur * kBlock : kBlock;
-    return true;
+  // Staging, two register sets: lane l takes 16-byte chunk l % CPR of rows
+  // i * RPS + l / CPR of the step (each load is RPS whole rows,
+  // contiguous), K and V alike.
+  u32x4 kst[2][NREQ], vst[2][NREQ];
+  const int r_in = lane / CPR, pc = lane % CPR;
+  // Addresses: a uniform base (the step's first row) plus a 32-bit byte
+  // offset per lane, so the loads take the scalar-base form and need no
+  // 64-bit address registers.
+  auto issue_step = [&](auto SET, int st) {
+    constexpr int x = decltype(SET)::value;
+    const int k = st / SPB, ko = (st % SPB) * SK;
+    const long off = lane_value(b_off, k);
+    const int last = max(lane_value(b_nv, k), 1) - 1;  // rows past the end are never read
+    const char *kb = reinterpret_cast<const char *>(kc + off);
+    const char *vb = reinterpret_cast<const char *>(vc + off);
+#pragma unroll
+    for (int i = 0; i < NREQ; ++i) {
+      const unsigned ob = (unsigned)(min(ko + i * RPS + r_in, last) * (D * 2) + pc * 16);
+      kst[x][i] = *reinterpret_cast<const u32x4 *>(kb + ob);
+      vst[x][i] = *reinterpret_cast<const u32x4 *>(vb + ob);
+    }
   };
-  uint4 kst[KPT], vst[KPT];
-  auto load_block = [&](int j, int nv) {
+  // staged K, V -> the wave's tiles, chunks permuted by the swizzle
+  auto store_step = [&](auto SET) {
+    constexpr int x = decltype(SET)::value;
 #pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-      const int key = kr + m * KR;
-      if (key < nv) {
-        kst[m] = *reinterpret_cast<const uint4 *>(kv_row(p, kc, b, g, j * kBlock + key) + dc * 8);
-        vst[m] = *reinterpret_cast<const uint4 *>(kv_row(p, vc, b, g, j * kBlock + key) + dc * 8);
-      } else {
-        kst[m] = make_uint4(0, 0, 0, 0);
-        vst[m] = make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < NREQ; ++i) {
+      const int o = Swz<__bf16, D>::off(i * RPS + r_in, pc * 8);
+      *reinterpret_cast<u32x4 *>(ktile[wave] + o) = kst[x][i];
+      *reinterpret_cast<u32x4 *>(vtile[wave] + o) = vst[x][i];
     }
   };
-  int sl = s0, j = 0, nv = 0;
-  while (sl < s1 && !valid_block(sl, j, nv)) ++sl;
-  if (sl < s1) load_block(j, nv);
+  using X0 = std::integral_constant<int, 0>;
+  using X1 = std::integral_constant<int, 1>;
+  // key (within the step) of row r (0..15) of S^T tile t of 32-key slice
+  // sl: output register i of lane group q16 then holds key 32 sl + 8 q16 +
+  // 4 t + i, the order the next product contracts over
+  const int krow = 8 * (c16 / 4) + (c16 % 4);
 
-  while (sl < s1) {
-    const int nvc = nv;
-    const float lg2 = slg ? slg[sl] * kLog2e : 0.f;
-    float vf[KPT][8];
+  f32x4 oacc[NDT];
 #pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-      const __bf16 *kk = reinterpret_cast<const __bf16 *>(&kst[m]);
-      const __bf16 *vv = reinterpret_cast<const __bf16 *>(&vst[m]);
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{};
+  float m = -INFINITY, l = 0.f;  // per column (head c16); l is this lane's share
+
+  auto compute_step = [&](int st) {
+    const int k = st / SPB, ko = (st % SPB) * SK;
+    const int nv = lane_value(b_nv, k) - ko;  // valid keys of this step (may be <= 0)
+    const float lg2 = lane_value(b_lg2, k);
+    const __bf16 *kt = ktile[wave], *vt = vtile[wave];
+    f32x4 sacc[NSL][2];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float d_ = 0.f;
+    for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d_ = fmaf(qv[hh][e], (float)kk[e], d_);
-        part[kr + m * KR][hh][dc] = d_;
+      for (int t = 0; t < 2; ++t) {
+        sacc[sl][t] = f32x4{};
+        const int key = 32 * sl + 4 * t + krow;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          sacc[sl][t] = mfma16(tile_op<__bf16, D>(kt, key, 32 * ks + 8 * q16), qreg[ks],
+                               sacc[sl][t]);
       }
+    float z[NSL][2][4];
+    bool need = false;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vf[m][e] = (float)vv[e];
-    }
-    // prefetch the next valid block of this split
-    int sn = sl + 1, jn = 0, nvn = 0;
-    while (sn < s1 && !valid_block(sn, jn, nvn)) ++sn;
-    if (sn < s1) load_block(jn, nvn);
-    __syncthreads();
-    // one wave per head: finish the dot products, gate, mask, update stats
-    for (int hh = wave; hh < G; hh += 4) {
-      float z = 0.f;
+    for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
-      for (int c = 0; c < DC; ++c) z += part[lane][hh][c];
-      z = lane < nvc ? z + lg2 : -INFINITY;
-      const float m_old = s_m[hh];
-      const float m_new = fmaxf(m_old, wave_max(z));
-      const float pz = (m_new == -INFINITY) ? 0.f : fast_exp2(z - m_new);
-      const float sum = wave_sum(pz);
-      prob[hh][lane] = pz;
-      if (lane == 0) {
-        const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
-        s_alpha[hh] = alpha;
-        s_l[hh] = s_l[hh] * alpha + sum;
-        s_m[hh] = m_new;
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 32 * sl + 8 * q16 + 4 * t + i;
+          z[sl][t][i] = key < nv ? sacc[sl][t][i] * p.scale_log2 + lg2 : -INFINITY;
+          need |= z[sl][t][i] > m + kDecRescale;
+        }
+    if (__any(need)) {  // rare: move the running max of each column, rescale
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[sl][t][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      if (mn > m) {
+        const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        m = mn;
       }
     }
-    __syncthreads();
+    // P^T as B operands (8 consecutive keys per lane), then O^T += V^T P^T
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float alpha = s_alpha[hh];
+    for (int sl = 0; sl < NSL; ++sl) {
+      bf16x8 pb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int m = 0; m < KPT; ++m) {
-        const float pr = prob[hh][kr + m * KR];
+        for (int i = 0; i < 4; ++i) {
+          const float pr = z[sl][t][i] == -INFINITY ? 0.f : fast_exp2(z[sl][t][i] - m);
+          l += pr;
+          pb[4 * t + i] = (__bf16)pr;
+        }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr, vf[m][e], acc[hh][e]);
-      }
+      for (int dt = 0; dt < NDT; ++dt)
+        oacc[dt] = mfma16(tile_op_rows16<D>(vt, 32 * sl, 16 * dt), pb, oacc[dt]);
     }
-    __syncthreads();
-    sl = sn;
-    j = jn;
-    nv = nvn;
+  };
+
+  // Step st + 2 is requested (into the register set step st freed) before
+  // step st is computed; step st + 1, requested one step earlier, is then
+  // written to the tiles.  Past the end the last step is re-requested
+  // (cache hits), so the count of requests in flight is the same on every
+  // path.  The tiles are rewritten only after this wave's reads of them
+  // have completed, and read again only after the writes completed
+  // (transposed reads issued while the wave's own LDS writes are pending
+  // have returned wrong data on gfx950).
+  constexpr int PER_STEP = 2 * NREQ;  // requests per step
+  const int nst = nb * SPB;
+  auto step = [&](auto CUR, auto NXT, int st) {
+    issue_step(CUR, min(st + 2, nst - 1));  // set CUR held step st, now stored
+    compute_step(st);
+    wait_lds_all();
+    wait_vmem<PER_STEP>();  // step st + 1 (set NXT) has landed
+    store_step(NXT);
+    wait_lds_all();
+  };
+  if (nst > 0) {
+    issue_step(X0{}, 0);
+    issue_step(X1{}, min(1, nst - 1));
+    wait_vmem<PER_STEP>();
+    store_step(X0{});
+    wait_vmem_all();  // nothing in flight at the loop entry
+    wait_lds_all();
+    for (int st = 0; st < nst; st += 2) {
+      step(X0{}, X1{}, st);
+      if (st + 1 >= nst) break;
+      step(X1{}, X0{}, st + 1);
+    }
+    wait_vmem<0>();
   }
 
-  // sum the key groups, then write this split's unnormalised partial
+  // Merge the 4 lane groups of each column, then the 4 waves, into this
+  // split's unnormalised partial.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  // each wave's output goes to its own K tile, which it no longer reads
+  auto obuf = [&](int w, int hh, int d) -> float & {
+    return reinterpret_cast<float *>(ktile[w])[hh * D + d];
+  };
+  wait_lds_all();
+  if (c16 < G) {
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) obuf[kr][hh][dc * 8 + e] = acc[hh][e];
+      for (int i = 0; i < 4; ++i) obuf(wave, c16, 16 * dt + 4 * q16 + i) = oacc[dt][i];
+    if (q16 == 0) {
+      s_m[wave][c16] = m;
+      s_l[wave][c16] = l;
+    }
+  }
   __syncthreads();
   float *out = p.partial + ((long)row * p.nsplit + split) * G * (D + 2);
-  for (int x = tid; x < G * D; x += 256) {
-    const int hh = x / D, d = x % D;
-    float o = 0.f;
+  for (int x = threadIdx.x; x < G * (D + 1); x += 256) {
+    const int hh = x / (D + 1), d = x % (D + 1);
+    float M = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < KR; ++r) o += obuf[r][hh][d];
-    out[hh * (D + 2) + d] = o;
-  }
-  if (tid < G) {
-    out[tid * (D + 2) + D] = s_m[tid];
-    out[tid * (D + 2) + D + 1] = s_l[tid];
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][hh]);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = s_m[w][hh] == -INFINITY ? 0.f : fast_exp2(s_m[w][hh] - M);
+      sum += sc * (d < D ? obuf(w, hh, d) : s_l[w][hh]);
+    }
+    if (d < D) {
+      out[hh * (D + 2) + d] = sum;
+    } else {
+      out[hh * (D + 2) + D] = M;
+      out[hh * (D + 2) + D + 1] = sum;
+    }
   }
 }
 

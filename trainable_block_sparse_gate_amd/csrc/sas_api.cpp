@@ -441,10 +441,15 @@ sas::DecodeParams decode_params(const sas_decode_problem *p) {
   d.sqrt_d = sqrtf((float)p->head_dim);
   d.scale_log2 = p->scale * 1.4426950408889634f;
   d.out_bf16 = p->out_dtype == SAS_BF16;
-  // split-K: enough workgroups to cover the chip several times over
+  // split-K: a workgroup's 4 waves each stream every 4th block of its
+  // split; as many workgroups as the chip holds at once (256 compute units
+  // x the attend kernel's residency) keep it streaming in a single round,
+  // and a split holds at least one block per wave.
   const int rows = p->batch * p->hkv;
-  int nsplit = (2048 + rows - 1) / rows;
-  if (nsplit > p->budget_blocks) nsplit = p->budget_blocks;
+  const int max_split = (p->budget_blocks + 3) / 4;
+  const int target = 256 * sas::kDecodeWgPerCu;
+  int nsplit = (target + rows - 1) / rows;
+  if (nsplit > max_split) nsplit = max_split;
   if (nsplit < 1) nsplit = 1;
   d.per_split = (p->budget_blocks + nsplit - 1) / nsplit;
   d.nsplit = (p->budget_blocks + d.per_split - 1) / d.per_split;

@@ -48,6 +48,12 @@ struct Mfma<float> {
   }
 };
 
+// 16x16x32 bf16 MFMA: lane l holds A[l % 16][8 (l / 16) + e] and
+// B[8 (l / 16) + e][l % 16], e = 0..7; D register r is D[4 (l / 16) + r][l % 16].
+__device__ inline f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Row of the D tile held by register r of a lane in half h.
 __device__ __host__ constexpr inline int d_row(int r, int h) { return 8 * (r / 4) + 4 * h + (r % 4); }
 
@@ -105,10 +111,14 @@ __device__ inline typename Mfma<T>::Op lds_op_rows(const T *X, int ld, int kb, i
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // s_waitcnt vmcnt(N) alone (N < 64; vmcnt sits in bits 3:0 and 15:14).
+// The scheduler moves no instruction across it, so whatever follows in the
+// source really runs after the wait.
 template <int N>
 __device__ inline void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Workgroup barrier without the workgroup-scope fence that __syncthreads()
@@ -120,6 +130,25 @@ __device__ inline void barrier_keep_requests() {
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
+}
+
+// Value of x in lane k (k uniform across the wave), without touching memory.
+__device__ inline int lane_value(int x, int k) { return __builtin_amdgcn_readlane(x, k); }
+__device__ inline float lane_value(float x, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
+}
+__device__ inline long lane_value(long x, int k) {
+  const unsigned lo = __builtin_amdgcn_readlane((int)(unsigned)((unsigned long)x), k);
+  const unsigned hi = __builtin_amdgcn_readlane((int)(unsigned)((unsigned long)x >> 32), k);
+  return (long)(((unsigned long)hi << 32) | lo);
+}
+
+// Wait until this wave's LDS reads and writes have completed (lgkmcnt(0));
+// the scheduler moves no instruction across it.
+__device__ inline void wait_lds_all() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // One 16-byte-per-lane global -> LDS request (global_load_lds_dwordx4):

@@ -178,6 +178,26 @@ __device__ inline typename Mfma<T>::Op tile_op_rows(const T *X, int kb, int mb) 
   }
 }
 
+// Operand of a 16x16x32 bf16 MFMA that contracts over the ROWS of a
+// swizzled tile: lane l (group q = l / 16, s = l % 16) receives
+// X[kb + 8 q + e][mb + s], e = 0..7 (two ds_read_b64_tr_b16 of 4 rows each;
+// within a 16-lane group output lane j, element e comes from source lane
+// 4 e + j / 4, element j % 4, so source lane s points at row kb + 8 q + s / 4,
+// columns mb + 4 (s % 4) .. + 3).
+template <int D>
+__device__ inline bf16x8 tile_op_rows16(const __bf16 *X, int kb, int mb) {
+  const int lane = threadIdx.x % kWave;
+  const int q = lane / 16, s = lane % 16;
+  const int row = kb + 8 * q + s / 4;
+  const int col = mb + 4 * (s % 4);
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16 *)(const lds_short *)(X + Swz<__bf16, D>::off(row, col)));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16 *)(const lds_short *)(X + Swz<__bf16, D>::off(row + 4, col)));
+  const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
 template <typename T>
 __device__ inline typename Mfma<T>::Op lds_op(const T *p) {
   if constexpr (sizeof(T) == 2)

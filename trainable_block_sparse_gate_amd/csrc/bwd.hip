@@ -263,20 +263,40 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
           pacc[nt] = M::run(bb, doreg[nt][ks], pacc[nt]);
         }
       }
-      // dS^T = P^T (dP^T - D), P^T recomputed from the saved lse
+      // dS^T = P^T (dP^T - D), P^T recomputed from the saved lse.  The sums
+      // of P dP and of P over the 16 values of a lane are pairwise trees
+      // (short dependency chains); the causal mask is only evaluated on the
+      // diagonal tile.
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int ql = 32 * nt + l32;
+        const float c = lg2 - lse2[nt];
+        float pd[16], pp[16];
+        if (!diag) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pp[r] = fast_exp2(fmaf(sacc[nt][r], p.scale_log2, c));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(fmaf(sacc[nt][r], p.scale_log2, c));
+            pp[r] = 32 * mt + chain_slot<T>(r, hf) > ql ? 0.f : e;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(sacc[nt][r] * p.scale_log2 + lg2 - lse2[nt]);
-          if (diag && 32 * mt + chain_slot<T>(r, hf) > ql) pr = 0.f;
-          const float pdp = pr * pacc[nt][r];
-          tile_F += pdp;
-          Eacc[nt] += pdp;
-          Gp[nt] += pr;
-          sacc[nt][r] = pdp - pr * Dv[nt];
+          pd[r] = pp[r] * pacc[nt][r];
+          sacc[nt][r] = fmaf(-pp[r], Dv[nt], pd[r]);
         }
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+          for (int r = 0; r < w; ++r) {
+            pd[r] += pd[r + w];
+            pp[r] += pp[r + w];
+          }
+        tile_F += pd[0];
+        Eacc[nt] += pd[0];
+        Gp[nt] += pp[0];
       }
       // dQ^T[d][query] += K^T[d][key] dS^T[key][query] over this 32-key half
 #pragma unroll

@@ -170,33 +170,46 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 
     // Online softmax per query column (log2 domain, gate folded in).
     typename M::Op pop[2][NKC];  // probabilities as B operands of O^T += V^T P^T
+    // The max is taken over the raw scores (the scale is positive and the
+    // gate term is the same for the whole tile); the causal mask is only
+    // evaluated on the diagonal tile; the row sum is a pairwise tree.
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int ql = 32 * nt + l32;
+      if (diag) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * mt + chain_slot<T>(r, hf) > ql) sacc[mt][nt][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float z = sacc[mt][nt][r] * p.scale_log2 + lg2;
-          if (diag && 32 * mt + chain_slot<T>(r, hf) > ql) z = -INFINITY;
-          sacc[mt][nt][r] = z;
-          mx = fmaxf(mx, z);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float zmax = mx * p.scale_log2 + lg2;
       // move the reference only on a large increase (first tile: from -inf)
-      const bool move = mx > m_run[nt] + kRescale;
-      const float m_new = move ? mx : m_run[nt];
+      const bool move = zmax > m_run[nt] + kRescale;
+      const float m_new = move ? zmax : m_run[nt];
       const float alpha = move ? fast_exp2(m_run[nt] - m_new) : 1.f;
-      float sum = 0.f;
+      // a tile whose gate is zero adds nothing (and no 0 * inf)
+      const float c = lg2 == -INFINITY ? -INFINITY : lg2 - m_new;
+      float ps[16];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(sacc[mt][nt][r] - m_new);
+          const float pr = fast_exp2(fmaf(sacc[mt][nt][r], p.scale_log2, c));
           sacc[mt][nt][r] = pr;
-          sum += pr;
+          ps[r] = mt == 0 ? pr : ps[r] + pr;
         }
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int r = 0; r < w; ++r) ps[r] += ps[r + w];
+      float sum = ps[0];
       sum += __shfl_xor(sum, 32);
       l_run[nt] = l_run[nt] * alpha + sum;
       m_run[nt] = m_new;

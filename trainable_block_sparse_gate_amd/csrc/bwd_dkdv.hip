@@ -279,9 +279,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     // are reused below
     wait_vmem<0>();
   }
+  // every wave's requests have landed (each waited for its own above)
+  // before any wave writes into the buffers
+  __syncthreads();
 
   // Add the two query halves: waves qh = 1 hand their sums to qh = 0
-  // (dK through buffer 0, dV through buffer 1; every request has landed).
+  // (dK through buffer 0, dV through buffer 1).
   float *redk = reinterpret_cast<float *>(buf0);
   float *redv = reinterpret_cast<float *>(buf1);
   if (qh == 1) {

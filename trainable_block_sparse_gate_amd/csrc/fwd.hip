@@ -35,10 +35,17 @@ namespace sas {
 // and well inside bf16 range.
 constexpr float kRescale = 8.f;
 
+// Query tiles (of 32 rows) per wave: 1 = two waves per head, 32 query rows
+// each, which keeps a wave within 256 registers so two waves share a SIMD
+// (one's softmax overlaps the other's MFMAs).
+constexpr int kFwdQT = 1;
+
 template <typename T, typename TO, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p) {
   using M = Mfma<T>;
-  constexpr int NT = NW * kWave;
+  constexpr int QT = kFwdQT;           // 32-query tiles per wave
+  constexpr int WPH = 2 / QT;          // waves per head
+  constexpr int NT = NW * WPH * kWave;
   using RT = RowTile<T, D, NT>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS;          // k-steps over head_dim
@@ -61,7 +68,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int g = blockIdx.y / nhc, hc = blockIdx.y % nhc;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int hf = lane / 32, l32 = lane % 32;
-  const int hh = hc * NW + wave;
+  const int hh = hc * NW + wave / WPH;
+  const int nt0 = (wave % WPH) * QT;  // this wave's first 32-query tile
   const bool head_ok = hh < p.G;
   const int h = g * p.G + (head_ok ? hh : 0);
 
@@ -95,28 +103,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     s_n = n;
   }
 
-  // Q as the B operand of S^T = K Q^T: lane -> query column, 2 tiles of 32.
-  typename M::Op qreg[2][NKS];
+  // Q as the B operand of S^T = K Q^T: lane -> query column.
+  typename M::Op qreg[QT][NKS];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int ql = 32 * nt + l32;
+  for (int t = 0; t < QT; ++t) {
+    const int ql = 32 * (nt0 + t) + l32;
     const T *qp = q + ((long)(seq_start + i * kBlock + ql) * p.hq + h) * D + hf * E;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if (ql < nq)
-        qreg[nt][ks] = lds_op<T>(qp + ks * KS);
+        qreg[t][ks] = lds_op<T>(qp + ks * KS);
       else
-        qreg[nt][ks] = typename M::Op{};
+        qreg[t][ks] = typename M::Op{};
     }
   }
 
-  f32x16 oacc[NDT][2];
+  f32x16 oacc[NDT][QT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x16{};
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+    for (int t = 0; t < QT; ++t) oacc[dt][t] = f32x16{};
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+  }
 
   // the register operands are complete before any tile load is issued, so
   // the wait counter tracking never makes a tile wait for its own prefetch
@@ -153,47 +165,47 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     const T *Ks = tiles + (2 * b + 0) * TILE;
     const T *Vs = tiles + (2 * b + 1) * TILE;
 
-    // S^T[key][query] for two 32-key halves x two 32-query tiles.
-    f32x16 sacc[2][2];
+    // S^T[key][query] for two 32-key halves x this wave's 32-query tiles.
+    f32x16 sacc[2][QT];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int krow = 32 * mt + chain_key_of_row<T>(l32);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x16{};
+      for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const typename M::Op a = tile_op<T, D>(Ks, krow, hf * E + ks * KS);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = M::run(a, qreg[nt][ks], sacc[mt][nt]);
+        for (int t = 0; t < QT; ++t) sacc[mt][t] = M::run(a, qreg[t][ks], sacc[mt][t]);
       }
     }
 
-    // Online softmax per query column (log2 domain, gate folded in).
-    typename M::Op pop[2][NKC];  // probabilities as B operands of O^T += V^T P^T
-    // The max is taken over the raw scores (the scale is positive and the
-    // gate term is the same for the whole tile); the causal mask is only
+    // Online softmax per query column (log2 domain, gate folded in).  The
+    // max is taken over the raw scores (the scale is positive and the gate
+    // term is the same for the whole tile); the causal mask is only
     // evaluated on the diagonal tile; the row sum is a pairwise tree.
+    typename M::Op pop[QT][NKC];  // probabilities as B operands of O^T += V^T P^T
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int ql = 32 * nt + l32;
+    for (int t = 0; t < QT; ++t) {
+      const int ql = 32 * (nt0 + t) + l32;
       if (diag) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * mt + chain_slot<T>(r, hf) > ql) sacc[mt][nt][r] = -INFINITY;
+            if (32 * mt + chain_slot<T>(r, hf) > ql) sacc[mt][t][r] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][t][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float zmax = mx * p.scale_log2 + lg2;
       // move the reference only on a large increase (first tile: from -inf)
-      const bool move = zmax > m_run[nt] + kRescale;
-      const float m_new = move ? zmax : m_run[nt];
-      const float alpha = move ? fast_exp2(m_run[nt] - m_new) : 1.f;
+      const bool move = zmax > m_run[t] + kRescale;
+      const float m_new = move ? zmax : m_run[t];
+      const float alpha = move ? fast_exp2(m_run[t] - m_new) : 1.f;
       // a tile whose gate is zero adds nothing (and no 0 * inf)
       const float c = lg2 == -INFINITY ? -INFINITY : lg2 - m_new;
       float ps[16];
@@ -201,8 +213,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(fmaf(sacc[mt][nt][r], p.scale_log2, c));
-          sacc[mt][nt][r] = pr;
+          const float pr = fast_exp2(fmaf(sacc[mt][t][r], p.scale_log2, c));
+          sacc[mt][t][r] = pr;
           ps[r] = mt == 0 ? pr : ps[r] + pr;
         }
 #pragma unroll
@@ -211,16 +223,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
         for (int r = 0; r < w; ++r) ps[r] += ps[r + w];
       float sum = ps[0];
       sum += __shfl_xor(sum, 32);
-      l_run[nt] = l_run[nt] * alpha + sum;
-      m_run[nt] = m_new;
+      l_run[t] = l_run[t] * alpha + sum;
+      m_run[t] = m_new;
       if (__builtin_amdgcn_read_exec() & __ballot(move)) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[dt][t][r] *= alpha;
       }
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) pop[nt][kc] = regs_op<T>(sacc[kc / SPT][nt], (kc % SPT) * E);
+      for (int kc = 0; kc < NKC; ++kc) pop[t][kc] = regs_op<T>(sacc[kc / SPT][t], (kc % SPT) * E);
     }
 
     // O^T[d][query] += V^T[d][key] P^T[key][query], V read transposed
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
       for (int kc = 0; kc < NKC; ++kc) {
         const typename M::Op a = tile_op_rows<T, D>(Vs, kc * KS, 32 * dt);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = M::run(a, pop[nt][kc], oacc[dt][nt]);
+        for (int t = 0; t < QT; ++t) oacc[dt][t] = M::run(a, pop[t][kc], oacc[dt][t]);
       }
     }
     if (it + 1 < ntiles) store_tile(b ^ 1);
@@ -241,12 +253,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   if (!head_ok) return;
   TO *o = static_cast<TO *>(p.o);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int ql = 32 * nt + l32;
+  for (int t = 0; t < QT; ++t) {
+    const int ql = 32 * (nt0 + t) + l32;
     if (ql >= nq) continue;
-    const long t = seq_start + i * kBlock + ql;
-    const float inv = 1.f / l_run[nt];
-    TO *op = o + (t * p.hq + h) * D;
+    const long tq = seq_start + i * kBlock + ql;
+    const float inv = 1.f / l_run[t];
+    TO *op = o + (tq * p.hq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -255,22 +267,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
         if constexpr (sizeof(TO) == 2) {
           bf16x4 w;
 #pragma unroll
-          for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[dt][nt][4 * rg + x] * inv);
+          for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[dt][t][4 * rg + x] * inv);
           *reinterpret_cast<bf16x4 *>(op + d0) = w;
         } else {
-          float4 w = make_float4(oacc[dt][nt][4 * rg] * inv, oacc[dt][nt][4 * rg + 1] * inv,
-                                 oacc[dt][nt][4 * rg + 2] * inv, oacc[dt][nt][4 * rg + 3] * inv);
+          float4 w = make_float4(oacc[dt][t][4 * rg] * inv, oacc[dt][t][4 * rg + 1] * inv,
+                                 oacc[dt][t][4 * rg + 2] * inv, oacc[dt][t][4 * rg + 3] * inv);
           *reinterpret_cast<float4 *>(op + d0) = w;
         }
       }
-    if (hf == 0) p.lse[(long)h * p.T + t] = (m_run[nt] + fast_log2(l_run[nt])) * kLn2;
+    if (hf == 0) p.lse[(long)h * p.T + tq] = (m_run[t] + fast_log2(l_run[t])) * kLn2;
   }
 }
 
 template <typename T, typename TO, int D, int NW>
 static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t stream) {
   dim3 grid(p.QB, p.hkv * ((p.G + NW - 1) / NW));
-  hipLaunchKernelGGL((fwd_kernel<T, TO, D, NW>), grid, dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<T, TO, D, NW>), grid, dim3(NW * (2 / kFwdQT) * 64), 0, stream,
+                     p);
   return hipGetLastError();
 }
 

@@ -15,10 +15,23 @@ timing.  Per-kernel durations come from HIP events recorded on the stream
 the library launches on.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Profile summaries (no GPU needed; they read rocprofv3 csv output):
+    python bench.py --summarize-trace DIR --cmd "..." --out profiles/X.md
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --cmd "..." --out profiles/Y.md
+The second also writes profiles/traffic.json: HBM bytes per dispatch of the
+library's kernels, from FETCH_SIZE / WRITE_SIZE scaled by what the same
+counters read for the 1 GiB device copy this script runs untimed, tagged
+with a hash of the kernel sources; a bench run reports that traffic only
+while the hash still matches.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,7 +51,161 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--cmd", default="", help="command line recorded in a summary")
+    ap.add_argument("--out", help="markdown file a summary is written to")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+CALIBRATION_BYTES = 1 << 30
+
+
+def source_hash():
+    """Hash of everything the library is built from (kernels, headers, build)."""
+    pkg = os.path.join(ROOT, "trainable_block_sparse_gate_amd")
+    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*")) +
+                   [os.path.join(pkg, "build.py"), os.path.join(ROOT, "include", "sas.h")])
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_kernel(name):
+    if "rocclr_copyBuffer" in name:
+        return "copyBuffer"
+    m = re.search(r"([a-z_]+_kernel)", name)
+    if m and ("sas" in name):
+        return m.group(1)
+    return None
+
+
+def read_counter_csv(d):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, cmd, out):
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for r in read_counter_csv(d):
+            if r["Counter_Name"] != counter:
+                continue
+            k = short_kernel(r["Kernel_Name"])
+            if k is None:
+                continue
+            per.setdefault(k, {}).setdefault(counter, []).append(float(r["Counter_Value"]))
+    # the calibration copies are the largest copyBuffer dispatches (1 GiB)
+    cp = per.get("copyBuffer", {})
+    fetch_cp = sorted(cp.get("FETCH_SIZE", []))[-3:]
+    write_cp = sorted(cp.get("WRITE_SIZE", []))[-3:]
+    if not fetch_cp or not write_cp:
+        sys.exit("no calibration copy dispatches found in the counter output")
+    f_fetch = CALIBRATION_BYTES / (sum(fetch_cp) / len(fetch_cp) * 1024)
+    f_write = CALIBRATION_BYTES / (sum(write_cp) / len(write_cp) * 1024)
+    kernels = {}
+    for k, c in sorted(per.items()):
+        if k == "copyBuffer" or "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        fk = sum(c["FETCH_SIZE"]) / len(c["FETCH_SIZE"])
+        wk = sum(c["WRITE_SIZE"]) / len(c["WRITE_SIZE"])
+        kernels[k] = {"dispatches": len(c["FETCH_SIZE"]), "fetch_kib": round(fk, 1),
+                      "write_kib": round(wk, 1),
+                      "bytes_per_launch": int(fk * 1024 * f_fetch + wk * 1024 * f_write)}
+    rec = {"source_hash": source_hash(), "command": cmd,
+           "calibration": {"copy_bytes": CALIBRATION_BYTES, "fetch_kib": round(fetch_cp[-1], 1),
+                           "write_kib": round(write_cp[-1], 1), "fetch_factor": round(f_fetch, 4),
+                           "write_factor": round(f_write, 4)},
+           "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    lines = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Two counter passes over the same bench run, then this summary:", "", "```",
+             cmd, "```", "",
+             f"Calibration: the untimed 1 GiB device copy reads {fetch_cp[-1]:.0f} KiB "
+             f"(FETCH_SIZE) and writes {write_cp[-1]:.0f} KiB (WRITE_SIZE) per dispatch, so "
+             f"the counters are scaled by {f_fetch:.4f} (fetch) and {f_write:.4f} (write).",
+             f"Source hash {rec['source_hash']}.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch |",
+             "|---|---|---|---|---|"]
+    for k, v in kernels.items():
+        lines.append(f"| `{k}` | {v['dispatches']} | {v['fetch_kib']:.0f} | {v['write_kib']:.0f} | "
+                     f"{v['bytes_per_launch']:,} |")
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as fh:
+            fh.write(text)
+    print(text)
+
+
+def summarize_trace(d, cmd, out):
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats:
+        sys.exit(f"no kernel_stats.csv under {d}")
+    with open(stats[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    info = {}
+    if trace:
+        with open(trace[0]) as fh:
+            for r in csv.DictReader(fh):
+                info.setdefault(r["Kernel_Name"], r)
+
+    def name(n):
+        if n.startswith("_Z"):
+            try:
+                import subprocess
+                n = subprocess.run(["c++filt", n], capture_output=True, text=True,
+                                   check=True).stdout.strip()
+            except (OSError, subprocess.CalledProcessError):
+                pass
+        if short_kernel(n):
+            return re.sub(r"^void ", "", re.sub(r"\(sas::\w+\)$", "", n))
+        m = re.search(r"at::native::[A-Za-z_:]*", n)
+        return (m.group(0) if m else n[:48]) + " (torch)"
+
+    lines = ["# Kernel trace summary (rocprofv3 --kernel-trace --stats)", "", "```", cmd, "```",
+             "", "| kernel | calls | avg us | total us | % | WGs | WG size | LDS B | VGPR | AGPR |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        n = r["Name"]
+        t = info.get(n, {})
+        wg = int(t.get("Workgroup_Size_X", 0) or 0)
+        grid = int(t.get("Grid_Size_X", 0) or 0) * int(t.get("Grid_Size_Y", 1) or 1) * \
+            int(t.get("Grid_Size_Z", 1) or 1)
+        nwg = grid // wg if wg else 0
+        lines.append(f"| `{name(n)}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} | "
+                     f"{nwg} | {wg} | {t.get('LDS_Block_Size', '')} | {t.get('VGPR_Count', '')} | "
+                     f"{t.get('Accum_VGPR_Count', '')} |")
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as fh:
+            fh.write(text)
+    print(text)
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json, or None
+    when there is none or the kernels have changed since it was taken."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return k["bytes_per_launch"] if k else None
 
 
 class Marks:
@@ -123,7 +290,8 @@ def train_bench(args, torch, sas, wl, metrics, case):
     achieved = kern[dom][1] / (phases[dom] * 1e-3) / 1e12
     roof = {"kernel": kern[dom][0], "bound": "mfma", "achieved": round(achieved, 2),
             "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / metrics.PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(achieved / metrics.PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for(kern[dom][0]),
             "ms_per_launch": round(phases[dom], 4)}
     per_kernel = {n: {"ms": round(phases[n], 4),
                       "tflops": round(kern[n][1] / (phases[n] * 1e-3) / 1e12, 2)}
@@ -175,7 +343,7 @@ def decode_bench(args, torch, sas, wl, metrics):
                         f"budget {spec.budget_blocks} blocks",
             "kv_bytes": kv, "us": round(t_dec / n * 1e3, 2), "value": round(gbs, 1),
             "unit": "GB/s", "frac": round(gbs / metrics.PEAK_HBM_GBS, 4),
-            "peak": metrics.PEAK_HBM_GBS,
+            "peak": metrics.PEAK_HBM_GBS, "traffic": traffic_for("decode_attend_kernel"),
             "selection": {"us": round(t_sel / n * 1e3, 2), "summary_bytes": scan,
                           "GB/s": round(scan_gbs, 1)}}
 
@@ -229,6 +397,12 @@ def cpu_baseline(case, metrics):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.cmd, args.out)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.cmd, args.out)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path shards without exchange over kv heads and sequences; see DESIGN.md)",

@@ -161,13 +161,11 @@ def summarize_trace(d, cmd, out):
                 info.setdefault(r["Kernel_Name"], r)
 
     def name(n):
-        if n.startswith("_Z"):
-            try:
-                import subprocess
-                n = subprocess.run(["c++filt", n], capture_output=True, text=True,
-                                   check=True).stdout.strip()
-            except (OSError, subprocess.CalledProcessError):
-                pass
+        m = re.match(r"_ZN3sas\d+(\w+?_kernel)I(\w+?)EEvNS_", n)
+        if m:  # template arguments: DF16b = bf16, f = float, Li<n>E = n
+            args = re.findall(r"DF16b|f|Li\d+E", m.group(2))
+            args = [{"DF16b": "bf16", "f": "float"}.get(a, a[2:-1]) for a in args]
+            return f"{m.group(1)}<{', '.join(args)}>"
         if short_kernel(n):
             return re.sub(r"^void ", "", re.sub(r"\(sas::\w+\)$", "", n))
         m = re.search(r"at::native::[A-Za-z_:]*", n)

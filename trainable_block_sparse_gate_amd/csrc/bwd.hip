@@ -99,29 +99,34 @@ __global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p)
 }
 
 // ------------------------------------------------------------------ dq
-// The forward's geometry: waves are the query heads of one kv head, 64 rows
-// each, Q and dO held in registers as B operands.  K and V tiles of the kept
+// The forward's geometry: WPH waves per query head of one kv head, QT 32-row
+// query tiles per wave, Q and dO held in registers as B operands.  K and V tiles of the kept
 // blocks are double buffered in LDS (row-major); dQ^T = K^T dS^T reads K
 // transposed with ds_read_b64_tr_b16.  Per tile: compute from one buffer,
 // then store the next tile into the other, issue the loads of the one after,
 // and barrier (no LDS write of a wave in flight while its transposed reads
 // issue).
+constexpr int kDqQT = 1;  // 32-query tiles per wave (1: two waves per head)
+
 template <typename T, typename TO, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams p) {
   using M = Mfma<T>;
-  constexpr int NT = NW * kWave;
+  constexpr int QT = kDqQT;
+  constexpr int WPH = 2 / QT;  // waves per head
+  constexpr int NWV = NW * WPH;
+  constexpr int NT = NWV * kWave;
   using RT = RowTile<T, D, NT>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
   constexpr int TILE = RT::ELEMS;
 
   __shared__ __attribute__((aligned(16))) T tiles[2 * 2 * TILE];  // [buf][K | V]
-  __shared__ float s_F[NW][kMaxBudget];  // per tile: sum of P dP over the wave's rows
+  __shared__ float s_F[NWV][kMaxBudget];  // per tile: sum of P dP over the wave's rows
   __shared__ int s_slot[kMaxBudget];     // tiles in processing order
   __shared__ int s_j[kMaxBudget];
   __shared__ float s_lg[kMaxBudget];     // log gate * log2(e)
   __shared__ int s_n;
-  extern __shared__ float s_G[];         // [NW][Kb][64]: per tile, sum of P per query row
+  extern __shared__ float s_G[];         // [NWV][Kb][32 QT]: per tile, sum of P per query row
 
   const T *q = static_cast<const T *>(p.q);
   const T *kk = static_cast<const T *>(p.k);
@@ -134,7 +139,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   const int g = blockIdx.y / nhc, hc = blockIdx.y % nhc;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int hf = lane / 32, l32 = lane % 32;
-  const int hh = hc * NW + wave;
+  const int hh = hc * NW + wave / WPH;
+  const int nt0 = (wave % WPH) * QT;  // this wave's first 32-query tile
   const bool head_ok = hh < p.G;
   const int h = g * p.G + (head_ok ? hh : 0);
   const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, Q);
@@ -163,11 +169,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   // Q and dO as B operands (lane -> query column), D and lse per column.
   // Per query tile every load is issued before any is used, so the tile
   // costs one memory latency rather than one per chunk.
-  typename M::Op qreg[2][NKS], doreg[2][NKS];
-  float Dv[2], lse2[2];
+  typename M::Op qreg[QT][NKS], doreg[QT][NKS];
+  float Dv[QT], lse2[QT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int ql = 32 * nt + l32;
+  for (int nt = 0; nt < QT; ++nt) {
+    const int ql = 32 * (nt0 + nt) + l32;
     const long t = seq_start + (long)i * kBlock + ql;
     const long base = (t * p.hq + h) * D + hf * E;
     OutChunk<TO, E> dch[NKS], och[NKS];
@@ -203,13 +209,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
     lse2[nt] = INFINITY;  // padding rows: P = 0
     if (ql < nq) lse2[nt] = p.lse[(long)h * p.T + t] * kLog2e;
   }
-  float Eacc[2] = {0.f, 0.f};  // exact D: sum_u P dP (lane-partial)
-
-  f32x16 dqacc[NDT][2];
+  float Eacc[QT];  // exact D: sum_u P dP (lane-partial)
+  f32x16 dqacc[NDT][QT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int nt = 0; nt < QT; ++nt) {
+    Eacc[nt] = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) dqacc[dt][nt] = f32x16{};
+    for (int dt = 0; dt < NDT; ++dt) dqacc[dt][nt] = f32x16{};
+  }
 
   // the register operands are complete before any tile load is issued, so
   // the wait counter tracking never makes a tile wait for its own prefetch
@@ -244,21 +251,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
     const T *Vs = tiles + (2 * b + 1) * TILE;
 
     float tile_F = 0.f;
-    float Gp[2] = {0.f, 0.f};
+    float Gp[QT];
+#pragma unroll
+    for (int nt = 0; nt < QT; ++nt) Gp[nt] = 0.f;
     // one 32-key half at a time (not unrolled: keeps both halves' live
     // ranges from overlapping)
 #pragma unroll 1
     for (int mt = 0; mt < 2; ++mt) {
-      f32x16 sacc[2], pacc[2];
+      f32x16 sacc[QT], pacc[QT];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sacc[nt] = pacc[nt] = f32x16{};
+      for (int nt = 0; nt < QT; ++nt) sacc[nt] = pacc[nt] = f32x16{};
       const int krow = 32 * mt + chain_key_of_row<T>(l32);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const typename M::Op a = tile_op<T, D>(Ks, krow, hf * E + ks * KS);
         const typename M::Op bb = tile_op<T, D>(Vs, krow, hf * E + ks * KS);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < QT; ++nt) {
           sacc[nt] = M::run(a, qreg[nt][ks], sacc[nt]);
           pacc[nt] = M::run(bb, doreg[nt][ks], pacc[nt]);
         }
@@ -268,8 +277,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
       // (short dependency chains); the causal mask is only evaluated on the
       // diagonal tile.
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int ql = 32 * nt + l32;
+      for (int nt = 0; nt < QT; ++nt) {
+        const int ql = 32 * (nt0 + nt) + l32;
         const float c = lg2 - lse2[nt];
         float pd[16], pp[16];
         if (!diag) {
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
         for (int kc = 0; kc < SPT; ++kc) {
           const typename M::Op a = tile_op_rows<T, D>(Ks, 32 * mt + kc * KS, 32 * dt);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < QT; ++nt)
             dqacc[dt][nt] = M::run(a, regs_op<T>(sacc[nt], kc * E), dqacc[dt][nt]);
         }
       }
@@ -313,9 +322,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
     tile_F = wave_sum(tile_F);
     if (lane == 0) s_F[wave][it] = head_ok ? tile_F : 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < QT; ++nt) {
       const float gsum = Gp[nt] + __shfl_xor(Gp[nt], 32);
-      if (hf == 0) s_G[(wave * p.Kb + it) * kBlock + 32 * nt + l32] = gsum;
+      if (hf == 0) s_G[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = gsum;
     }
     if (it + 1 < ntiles) store_tile(b ^ 1);
     if (it + 2 < ntiles) load_tile(it + 2);
@@ -325,11 +334,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   // Exact D per query row, then dlg of each tile = sum P dP - sum_t D_t G_t.
   // Both row statistics are stored for all 64 rows of the block (rows past
   // its end: lse +inf, D 0) so the dk/dv phase can fetch them as a whole.
-  float Ex[2];
+  float Ex[QT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < QT; ++nt) {
     Ex[nt] = Eacc[nt] + __shfl_xor(Eacc[nt], 32);
-    const int ql = 32 * nt + l32;
+    const int ql = 32 * (nt0 + nt) + l32;
     if (hf == 0 && head_ok) {
       const long at = ((long)h * p.QB + Q) * kBlock + ql;
       p.Dbuf[at] = ql < nq ? Ex[nt] : 0.f;
@@ -340,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
     float c = 0.f;
     if (hf == 0) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) c += Ex[nt] * s_G[(wave * p.Kb + it) * kBlock + 32 * nt + l32];
+      for (int nt = 0; nt < QT; ++nt) c += Ex[nt] * s_G[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32];
     }
     c = wave_sum(c);
     if (lane == 0) s_F[wave][it] = head_ok ? s_F[wave][it] - c : 0.f;
@@ -348,8 +357,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
 
   if (head_ok) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int ql = 32 * nt + l32;
+    for (int nt = 0; nt < QT; ++nt) {
+      const int ql = 32 * (nt0 + nt) + l32;
       if (ql >= nq) continue;
       const long t = seq_start + (long)i * kBlock + ql;
       float *dqp = p.dq + (t * p.hq + h) * D;
@@ -373,7 +382,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
     for (int it = 0; it < ntiles; ++it)
       if (s_slot[it] == sl) {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) val += s_F[w][it];
+        for (int w = 0; w < NWV; ++w) val += s_F[w][it];
       }
     dst[sl] = val;
   }
@@ -394,19 +403,20 @@ constexpr int kLdsBytes = 160 * 1024;
 
 template <typename T, int D, int NW>
 constexpr int dq_static_lds() {
-  return (int)sizeof(T) * 4 * kBlock * D + (NW + 3) * kMaxBudget * 4 + 64;
+  return (int)sizeof(T) * 4 * kBlock * D + (NW * (2 / kDqQT) + 3) * kMaxBudget * 4 + 64;
 }
 
 template <typename T, int D, int NW>
 static size_t dq_dynamic_lds(const BwdParams &p) {
-  return sizeof(float) * NW * p.Kb * kBlock;
+  return sizeof(float) * NW * p.Kb * kBlock;  // NW (2/QT) waves x 32 QT rows
 }
 
 template <typename T, typename TO, int D, int NW>
 static hipError_t launch_dq_t(const BwdParams &p, hipStream_t stream) {
   const int nhc = (p.G + NW - 1) / NW;
   const size_t dyn = dq_dynamic_lds<T, D, NW>(p);
-  hipLaunchKernelGGL((bwd_dq_kernel<T, TO, D, NW>), dim3(p.QB, p.hkv * nhc), dim3(NW * 64), dyn,
+  hipLaunchKernelGGL((bwd_dq_kernel<T, TO, D, NW>), dim3(p.QB, p.hkv * nhc),
+                     dim3(NW * (2 / kDqQT) * 64), dyn,
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nhc == 1) return e;

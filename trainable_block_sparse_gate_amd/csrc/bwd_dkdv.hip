@@ -271,9 +271,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     barrier_keep_requests();
     for (int st = 0; st < nsteps; st += NBUF) {
       step(I0{}, st);
-      if (st + 1 < nsteps) step(I1{}, st + 1);
-      if constexpr (NBUF == 3)
-        if (st + 2 < nsteps) step(I2{}, st + 2);
+      if (st + 1 < nsteps) {
+        step(I1{}, st + 1);
+        // nested, so that no path reaches this step while the requests of
+        // the skipped one (into the buffer it reads) are still counted
+        if constexpr (NBUF == 3)
+          if (st + 2 < nsteps) step(I2{}, st + 2);
+      }
     }
     // the last requests (re-fetches past the end) land before the buffers
     // are reused below

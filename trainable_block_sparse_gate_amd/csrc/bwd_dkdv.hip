@@ -161,17 +161,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
           ((wave & 1) ? p.Dbuf : p.Lbuf) + ((long)h * p.QB + qb) * kBlock + 4 * (lane % 16);
       load_lds16(src, &stat[wave][0]);
     }
+    // uniform base of the block's rows for head h; per lane a 32-bit byte
+    // offset (row, swizzled chunk), so the request takes a scalar base
+    const long head0 = (t0 * p.hq + h) * D;
+    const char *qbase = reinterpret_cast<const char *>(q + head0);
+    const char *dbase = reinterpret_cast<const char *>(dO + head0);
+    const unsigned rstride = (unsigned)(p.hq * D * (int)sizeof(T));
     const int r_in = lane / CPR, pc = lane % CPR;
 #pragma unroll
     for (int tk = 0; tk < 2; ++tk) {
-      const T *src = tk == 0 ? q : dO;
+      const char *src = tk == 0 ? qbase : dbase;
 #pragma unroll
       for (int sg = 0; sg < SPW; ++sg) {
         const int piece = wave * SPW + sg;
         const int r = piece * RPS + r_in;
         const int rr = r < nq ? r : nq - 1;
         const int c = pc ^ Swz<T, D>::f(r);
-        load_lds16(src + ((t0 + rr) * p.hq + h) * D + c * VEC, tl + tk * TILE + piece * RPS * D);
+        const unsigned off = (unsigned)rr * rstride + (unsigned)(c * 16);
+        load_lds16(src + off, tl + tk * TILE + piece * RPS * D);
       }
     }
   };
@@ -200,10 +207,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     // query rows loaded in chain order so P and dS feed the next products.
     f32x16 sacc = f32x16{}, pacc = f32x16{};
     const int qrow = 32 * qh + chain_key_of_row<T>(l32);
+    // operands are read ahead of the products that use them (order fixed
+    // by the scheduling groups below), so the reads' latency overlaps them
+    typename M::Op qa[NKS], da[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      sacc = M::run(tile_op<T, D>(Qs, qrow, hf * E + ks * KS), kreg[ks], sacc);
-      pacc = M::run(tile_op<T, D>(Ds, qrow, hf * E + ks * KS), vreg[ks], pacc);
+      qa[ks] = tile_op<T, D>(Qs, qrow, hf * E + ks * KS);
+      da[ks] = tile_op<T, D>(Ds, qrow, hf * E + ks * KS);
     }
     // this lane's 16 query rows, in register order, come in four runs of 4
     // consecutive rows: fetch their lse and D as float4s
@@ -224,6 +234,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         lse_r[r] = stat[0][32 * qh + chain_slot<T>(r, hf)];
         D_r[r] = stat[1][32 * qh + chain_slot<T>(r, hf)];
       }
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      sacc = M::run(qa[ks], kreg[ks], sacc);
+      pacc = M::run(da[ks], vreg[ks], pacc);
+    }
+    if constexpr (E == 8) {
+      // the first 16 LDS reads are issued before the first product, the rest
+      // one per product
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * NKS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // full tiles (the common case) need no mask; the test is uniform
     if (!diag && nq == kBlock && nvalid == kBlock) {
@@ -246,16 +272,36 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       }
     }
     // dV^T[d][key] += dO^T[d][query] P[query][key];  dK^T += Q^T dS
+    // (the transposed reads of one d tile are issued a tile ahead)
+    typename M::Op ta[2][2 * SPT];
+#pragma unroll
+    for (int kc = 0; kc < SPT; ++kc) {
+      ta[0][2 * kc] = tile_op_rows<T, D>(Ds, 32 * qh + kc * KS, 0);
+      ta[0][2 * kc + 1] = tile_op_rows<T, D>(Qs, 32 * qh + kc * KS, 0);
+    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
+      if (dt + 1 < NDT) {
+#pragma unroll
+        for (int kc = 0; kc < SPT; ++kc) {
+          ta[(dt + 1) & 1][2 * kc] = tile_op_rows<T, D>(Ds, 32 * qh + kc * KS, 32 * (dt + 1));
+          ta[(dt + 1) & 1][2 * kc + 1] = tile_op_rows<T, D>(Qs, 32 * qh + kc * KS, 32 * (dt + 1));
+        }
+      }
 #pragma unroll
       for (int kc = 0; kc < SPT; ++kc) {
-        const int kq = 32 * qh + kc * KS;
-        dvacc[dt] = M::run(tile_op_rows<T, D>(Ds, kq, 32 * dt), regs_op<T>(sacc, kc * E),
-                           dvacc[dt]);
-        dkacc[dt] = M::run(tile_op_rows<T, D>(Qs, kq, 32 * dt), regs_op<T>(pacc, kc * E),
-                           dkacc[dt]);
+        dvacc[dt] = M::run(ta[dt & 1][2 * kc], regs_op<T>(sacc, kc * E), dvacc[dt]);
+        dkacc[dt] = M::run(ta[dt & 1][2 * kc + 1], regs_op<T>(pacc, kc * E), dkacc[dt]);
       }
+    }
+    if constexpr (E == 8) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+      for (int k = 0; k < 2 * NDT * SPT - 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     }
     wait_vmem<NBUF == 3 ? PER_STEP : 0>();
     barrier_keep_requests();

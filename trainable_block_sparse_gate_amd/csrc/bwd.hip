@@ -34,13 +34,15 @@
 namespace sas {
 
 // ------------------------------------------------------------------ csr
-// One wave per x = g * QB + kb.  Rows that can keep key block j of sequence
-// s are its query blocks i >= j.
+// One wave per x = kb * hkv + g (key-block major: the segments of early key
+// blocks, which the most rows keep, come first in the dk/dv grid, so the
+// longest workgroups start first and the short ones fill the tail).  Rows
+// that can keep key block j of sequence s are its query blocks i >= j.
 __global__ __launch_bounds__(256) void bwd_csr_kernel(BwdParams p) {
   const int x = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (x >= p.hkv * p.QB) return;
-  const int g = x / p.QB, kb = x % p.QB;
+  const int kb = x / p.hkv, g = x % p.hkv;
   const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, kb);
   const int q0 = p.cu_qblocks[s], nb = p.cu_qblocks[s + 1] - q0;
   const int j = kb - q0;

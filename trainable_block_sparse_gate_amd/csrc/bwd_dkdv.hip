@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     if (p.seg_off[mid] <= w) lo = mid; else hi = mid - 1;
   }
   const int x = lo;
-  const int g = x / p.QB, kb = x % p.QB;
+  const int kb = x / p.hkv, g = x % p.hkv;  // key-block major order
   const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, kb);
   const int q0 = p.cu_qblocks[s];
   const int j = kb - q0;

@@ -67,12 +67,13 @@ struct BwdParams {
   float *Lbuf;       // [hq][QB][64] lse * log2(e) per query row; +inf past a block's end
   float *Dbuf;       // [hq][QB][64] exact D = sum_u P dP per query row; 0 past the end
   __bf16 *dO16;      // [T][hq][D] dO rounded to bf16 (bf16 inputs, fp32 dO), else NULL
-  int32_t *list;     // [hkv*QB][max_nb]  (query block << 8 | slot) per key block
-  int32_t *count;    // [hkv*QB]
-  int32_t *seg_off;  // [hkv*QB + 1] prefix sum of segments per key block
+  // key blocks are indexed x = kb * hkv + g (key-block major)
+  int32_t *list;     // [QB*hkv][max_nb]  (query block << 8 | slot) per key block
+  int32_t *count;    // [QB*hkv]
+  int32_t *seg_off;  // [QB*hkv + 1] prefix sum of segments per key block
   float *dlg_part;   // [nhc][hkv*QB][Kb] when a row's heads span workgroups
   float *partial;    // [U][2][64][D] partial dK / dV of split key blocks
-  int32_t *done;     // [hkv*QB] finished segments per key block
+  int32_t *done;     // [QB*hkv] finished segments per key block
   int seg;           // keeping rows per segment
   int U;             // upper bound on the number of segments (dk/dv grid)
 };

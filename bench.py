@@ -313,11 +313,14 @@ def decode_bench(args, torch, sas, wl, metrics):
     sel, lg, glse, scores = sas.decode_select(prob, t["q"], ksum)
     ws = torch.empty(max(1, sas.decode_workspace_bytes(prob)), dtype=torch.uint8, device="cuda")
     o, lse = sas.decode(prob, t["q"], t["k"], t["v"], sel, lg, workspace=ws)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # > Infinity Cache
+    # Between iterations the caches are refilled by READING a 1 GiB buffer
+    # (more than L2 + Infinity Cache), so no kept K/V block is cached when a
+    # decode starts and no dirty line of the flush is written back during it.
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     t_sel = t_dec = 0.0
     for it in range(args.decode_steps + 3):
-        flush.zero_()
+        flush.sum()
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record()
         sas.decode_select(prob, t["q"], ksum, out=(sel, lg, glse, scores))

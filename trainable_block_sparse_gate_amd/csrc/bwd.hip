@@ -139,7 +139,7 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
   const int Q = blockIdx.x;
   const int nhc = (p.G + NW - 1) / NW;
   const int g = blockIdx.y / nhc, hc = blockIdx.y % nhc;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = wave_id(), lane = threadIdx.x % kWave;
   const int hf = lane / 32, l32 = lane % 32;
   const int hh = hc * NW + wave / WPH;
   const int nt0 = (wave % WPH) * QT;  // this wave's first 32-query tile

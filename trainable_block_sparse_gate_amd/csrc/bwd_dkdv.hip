@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int e0 = seg * p.seg, e1 = min(cnt, e0 + p.seg);
   const int nent = max(0, e1 - e0);
 
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = wave_id(), lane = threadIdx.x % kWave;
   const int hf = lane / 32, l32 = lane % 32;
   const int kh = wave % 2, qh = wave / 2;
   const int key = 32 * kh + l32;  // this lane's key (column of S)

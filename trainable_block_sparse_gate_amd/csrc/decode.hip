@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256, kDecodeWgPerCu) void decode_attend_kernel(Deco
   const int b = row / p.hkv, g = row % p.hkv;
   const int L = p.seqlens[b];
   const int cur = (L - 1) / kBlock;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = wave_id(), lane = threadIdx.x % kWave;
   const int q16 = lane / 16, c16 = lane % 16;
   const int32_t *sel = p.sel_idx + (long)row * p.Kb;
   const float *slg = p.sel_lg ? p.sel_lg + (long)row * p.Kb : nullptr;
@@ -294,10 +294,20 @@ __global__ __launch_bounds__(256, kDecodeWgPerCu) void decode_attend_kernel(Deco
     store_step(X0{});
     wait_vmem_all();  // nothing in flight at the loop entry
     wait_lds_all();
-    for (int st = 0; st < nst; st += 2) {
-      step(X0{}, X1{}, st);
-      if (st + 1 >= nst) break;
-      step(X1{}, X0{}, st + 1);
+    if constexpr (SPB % 2 == 0) {
+      // an even number of steps: no path leaves the loop between the two
+      // halves, so the requests of the first half are never counted as
+      // pending when the next iteration reuses its registers
+      for (int st = 0; st < nst; st += 2) {
+        step(X0{}, X1{}, st);
+        step(X1{}, X0{}, st + 1);
+      }
+    } else {
+      for (int st = 0; st < nst; st += 2) {
+        step(X0{}, X1{}, st);
+        if (st + 1 >= nst) break;
+        step(X1{}, X0{}, st + 1);
+      }
     }
     wait_vmem<0>();
   }
@@ -322,6 +332,47 @@ __global__ __launch_bounds__(256, kDecodeWgPerCu) void decode_attend_kernel(Deco
     }
   }
   __syncthreads();
+  if (p.nsplit == 1) {
+    // the workgroup holds the whole row: normalise and write o and lse here
+    // (the same arithmetic as the combine over one split)
+    __shared__ float s_M[G], s_L[G];
+    if (threadIdx.x < G) {
+      const int hh = threadIdx.x;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][hh]);
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sc = s_m[w][hh] == -INFINITY ? 0.f : fast_exp2(s_m[w][hh] - M);
+        sum += sc * s_l[w][hh];
+      }
+      const float wgt = M == -INFINITY ? 0.f : 1.f;  // exp2(M - M) of the one split
+      s_M[hh] = M;
+      s_L[hh] = sum * wgt;
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < G * D; x += 256) {
+      const int hh = x / D, d = x % D;
+      const float M = s_M[hh];
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sc = s_m[w][hh] == -INFINITY ? 0.f : fast_exp2(s_m[w][hh] - M);
+        sum += sc * obuf(w, hh, d);
+      }
+      const float acc = sum * (M == -INFINITY ? 0.f : 1.f);
+      const long at = ((long)b * p.hq + g * G + hh) * D + d;
+      const float val = acc / s_L[hh];
+      if (p.out_bf16)
+        static_cast<__bf16 *>(p.o)[at] = from_f32<__bf16>(val);
+      else
+        static_cast<float *>(p.o)[at] = val;
+      if (d == 0 && p.lse)
+        p.lse[(long)b * p.hq + g * G + hh] = (M + fast_log2(s_L[hh])) * kLn2;
+    }
+    return;
+  }
   float *out = p.partial + ((long)row * p.nsplit + split) * G * (D + 2);
   for (int x = threadIdx.x; x < G * (D + 1); x += 256) {
     const int hh = x / (D + 1), d = x % (D + 1);
@@ -386,7 +437,7 @@ static hipError_t launch_attend_t(const DecodeParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_attend_kernel<D, G>), dim3(p.nsplit, rows), dim3(256), 0, stream,
                      p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.nsplit == 1) return e;  // one split: already final
   if (p.out_bf16)
     hipLaunchKernelGGL((decode_combine_kernel<D, G, __bf16>), dim3(rows), dim3(256), 0, stream,
                        p);

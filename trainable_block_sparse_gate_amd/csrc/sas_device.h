@@ -132,6 +132,13 @@ __device__ inline void barrier_keep_requests() {
   __asm__ volatile("" ::: "memory");
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform value:
+// threadIdx.x / 64 is the same in every lane, but only readfirstlane lets
+// the compiler know, so that what depends on it (head indices, loop
+// bounds, addresses) stays in scalar registers and loops over it stay
+// uniform branches rather than exec-masked ones.  Call with all lanes active.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
 // Value of x in lane k (k uniform across the wave), without touching memory.
 __device__ inline int lane_value(int x, int k) { return __builtin_amdgcn_readlane(x, k); }
 __device__ inline float lane_value(float x, int k) {

@@ -7,7 +7,7 @@
 namespace sas {
 
 constexpr int kMaxBudget = 256;  // largest budget_blocks a row may hold
-constexpr int kDecodeWgPerCu = 2;  // decode workgroups resident per compute unit
+constexpr int kDecodeWgPerCu = 1;  // decode workgroups resident per compute unit
 
 struct GateParams {
   // Row layout: training rows (decode == 0) are r = g * QB + Q with the

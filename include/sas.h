@@ -108,7 +108,9 @@ typedef struct sas_decode_problem {
   int32_t max_seqlen;      /* contiguous: cache capacity per (batch, kv head) */
   int32_t max_pages;       /* paged: row stride of page_table */
   int32_t num_pages;       /* paged: physical pages in the cache */
-  int32_t nblk_stride;     /* summaries: row stride (>= largest history count) */
+  int32_t nblk_stride;     /* summaries: row stride (>= largest history count);
+                              a multiple of 4 lets the pooled scores read the
+                              summaries 16 bytes at a time */
   float scale;
   const int32_t *seqlens;       /* device [batch]: cache length L, query token included */
   const int32_t *seqlens_host;  /* host copy */

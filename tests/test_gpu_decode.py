@@ -106,3 +106,30 @@ def test_paged_equals_contiguous_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(sel, sel_p) and torch.equal(lg, lg_p)
     assert torch.equal(o, o_p) and torch.equal(lse, lse_p)
+
+
+def test_unaligned_summary_stride_bitwise():
+    """A summary stride that is not a multiple of 4 takes the one-block
+    scoring kernel; summaries, scores, selection and output are the same
+    bits as with the padded stride."""
+    import torch
+    seqlens, hq, hkv, d, Kb = CASES["g8_d128_bigK"]
+    host = wl.draw_decode_host_small(seqlens, hq, hkv, d, Kb, True, seed=11)
+    res = []
+    for stride in (None, 41):  # padded default (40), and 41: 40 history blocks
+        prob = sas.Decode(seqlens, hq, hkv, d, Kb, True, max(seqlens),
+                          page_table=host["page_table"], num_pages=host["k"].shape[0],
+                          nblk_stride=stride)
+        say(f"[decode stride {prob.nblk_stride}]")
+        q = dev_tensor(host["q"], host["q_bits"], "bf16")
+        kc = dev_tensor(host["k"], host["k_bits"], "bf16")
+        vc = dev_tensor(host["v"], host["v_bits"], "bf16")
+        ksum = sas.pool_keys(prob, kc)
+        sel, lg, glse, scores = sas.decode_select(prob, q, ksum)
+        o, lse = sas.decode(prob, q, kc, vc, sel, lg)
+        torch.cuda.synchronize()
+        nh = (max(seqlens) - 1) // 64
+        res.append((ksum[..., :nh].cpu(), scores[..., :nh].cpu(), sel.cpu(), lg.cpu(), o.cpu(),
+                    lse.cpu()))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)

@@ -74,6 +74,52 @@ __global__ __launch_bounds__(256) void pooled_scores_kernel(DecodeParams p) {
   p.scores[((long)b * p.hkv + g) * p.nblk_stride + j] = acc / p.sqrt_d;
 }
 
+// Four consecutive blocks per thread (16-byte loads, four independent chains
+// each in channel order, so every score is bit-identical to the one-block
+// form), channels in batches of 16 loads in flight.  For summary strides
+// that are multiples of 4.
+template <int D>
+__global__ __launch_bounds__(256) void pooled_scores4_kernel(DecodeParams p) {
+#pragma clang fp contract(off)
+  __shared__ float qbar[D];
+  const int bg = blockIdx.y;
+  const int b = bg / p.hkv, g = bg % p.hkv;
+  const int G = p.hq / p.hkv;
+  const __bf16 *q = static_cast<const __bf16 *>(p.q);
+  for (int e = threadIdx.x; e < D; e += blockDim.x) {
+    float acc = 0.f;
+    for (int hh = 0; hh < G; ++hh) acc = acc + (float)q[((long)b * p.hq + g * G + hh) * D + e];
+    qbar[e] = acc / (float)G;
+  }
+  __syncthreads();
+  const int nhist = (p.seqlens[b] - 1) / kBlock;
+  const int j0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  if (j0 >= nhist) return;
+  const float *ks = p.ksum + ((long)b * p.hkv + g) * D * p.nblk_stride + j0;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  constexpr int BATCH = 16;
+#pragma unroll 1
+  for (int e0 = 0; e0 < D; e0 += BATCH) {
+    float4 v[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+      v[u] = *reinterpret_cast<const float4 *>(ks + (long)(e0 + u) * p.nblk_stride);
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const float w = qbar[e0 + u];
+      a0 = fmaf(w, v[u].x, a0);
+      a1 = fmaf(w, v[u].y, a1);
+      a2 = fmaf(w, v[u].z, a2);
+      a3 = fmaf(w, v[u].w, a3);
+    }
+  }
+  float *out = p.scores + ((long)b * p.hkv + g) * p.nblk_stride + j0;
+  out[0] = a0 / p.sqrt_d;
+  if (j0 + 1 < nhist) out[1] = a1 / p.sqrt_d;
+  if (j0 + 2 < nhist) out[2] = a2 / p.sqrt_d;
+  if (j0 + 3 < nhist) out[3] = a3 / p.sqrt_d;
+}
+
 // ------------------------------------------------------------------ attend
 // A workgroup takes one split of the kept blocks of one (sequence, kv head)
 // row; each of its 4 waves streams every 4th of those blocks on its own
@@ -426,6 +472,14 @@ hipError_t launch_pool_keys(const DecodeParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_pooled_scores(const DecodeParams &p, hipStream_t stream) {
+  if (p.nblk_stride % 4 == 0 && (p.D == 128 || p.D == 64)) {
+    const dim3 grid((p.nblk_stride / 4 + 255) / 256, p.batch * p.hkv);
+    if (p.D == 128)
+      hipLaunchKernelGGL(pooled_scores4_kernel<128>, grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(pooled_scores4_kernel<64>, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(pooled_scores_kernel, dim3((p.nblk_stride + 255) / 256, p.batch * p.hkv),
                      dim3(256), 0, stream, p);
   return hipGetLastError();

@@ -238,7 +238,8 @@ class Decode:
     the ctypes struct."""
 
     def __init__(self, seqlens, hq, hkv, head_dim, budget_blocks, paged, max_seqlen,
-                 page_table=None, num_pages=0, out_dtype="bf16", scale=None, device="cuda"):
+                 page_table=None, num_pages=0, out_dtype="bf16", scale=None, device="cuda",
+                 nblk_stride=None):
         import torch
         self.seqlens = [int(x) for x in seqlens]
         self.sl_host = np.array(self.seqlens, np.int32)
@@ -246,7 +247,11 @@ class Decode:
         self.hq, self.hkv, self.d, self.Kb = hq, hkv, head_dim, budget_blocks
         self.batch = len(self.seqlens)
         self.paged = paged
-        self.nblk_stride = max(1, max((n - 1) // BLOCK for n in self.seqlens))
+        # summary row stride: history blocks of the longest sequence, rounded
+        # up to a multiple of 4 (the library then reads summaries as float4)
+        self.nblk_stride = -(-max(1, max((n - 1) // BLOCK for n in self.seqlens)) // 4) * 4
+        if nblk_stride is not None:
+            self.nblk_stride = int(nblk_stride)
         self.pt_dev = None
         max_pages = 0
         if paged:

@@ -179,6 +179,22 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
         for (int t = 0; t < QT; ++t) sacc[mt][t] = M::run(a, qreg[t][ks], sacc[mt][t]);
       }
     }
+    if constexpr (E == 8) {
+      // K reads run ahead of the products that use them
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * NKS * QT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the first d tile's V operands are requested before the softmax, whose
+    // arithmetic then covers their latency
+    typename M::Op vop[2][NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) vop[0][kc] = tile_op_rows<T, D>(Vs, kc * KS, 0);
+    if constexpr (E == 8) __builtin_amdgcn_sched_barrier(0);
 
     // Online softmax per query column (log2 domain, gate folded in).  The
     // max is taken over the raw scores (the scale is positive and the gate
@@ -235,15 +251,29 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
       for (int kc = 0; kc < NKC; ++kc) pop[t][kc] = regs_op<T>(sacc[kc / SPT][t], (kc % SPT) * E);
     }
 
-    // O^T[d][query] += V^T[d][key] P^T[key][query], V read transposed
+    // O^T[d][query] += V^T[d][key] P^T[key][query], V read transposed (the
+    // operands of the next d tile are requested a tile ahead)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
+      if (dt + 1 < NDT) {
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+          vop[(dt + 1) & 1][kc] = tile_op_rows<T, D>(Vs, kc * KS, 32 * (dt + 1));
+      }
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        const typename M::Op a = tile_op_rows<T, D>(Vs, kc * KS, 32 * dt);
 #pragma unroll
-        for (int t = 0; t < QT; ++t) oacc[dt][t] = M::run(a, pop[t][kc], oacc[dt][t]);
+        for (int t = 0; t < QT; ++t) oacc[dt][t] = M::run(vop[dt & 1][kc], pop[t][kc], oacc[dt][t]);
       }
+    }
+    if constexpr (E == 8) {
+#pragma unroll
+      for (int k = 0; k < NDT * NKC * QT - NKC * QT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NKC * QT, 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (it + 1 < ntiles) store_tile(b ^ 1);
     if (it + 2 < ntiles) load_tile(it + 2);

@@ -25,8 +25,8 @@
 //   4. dkdv:   (bwd_dkdv.hip) one workgroup per segment of a key block:
 //              K and V stay in registers, Q/dO tiles of the keeping rows
 //              stream through LDS, dK^T and dV^T accumulate in registers;
-//              split key blocks are summed in segment order by the last
-//              segment to finish.
+//              the partials of split key blocks are summed in segment order
+//              by a second, small kernel.
 #include "sas_device.h"
 #include "sas_launch.h"
 #include "tile_stage.h"
@@ -82,7 +82,6 @@ __global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p)
   int local = 0;
   for (int x = b0; x < b1; ++x) {
     local += max(1, (p.count[x] + p.seg - 1) / p.seg);
-    p.done[x] = 0;
   }
   part[threadIdx.x] = local;
   __syncthreads();

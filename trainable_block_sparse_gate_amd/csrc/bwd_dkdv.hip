@@ -7,9 +7,8 @@
 // the preparation kernels build: K and V stay in registers, Q/dO tiles of
 // the keeping rows stream through LDS, dK^T and dV^T accumulate in
 // registers.  Key blocks kept by many rows are split over several segments;
-// each writes a partial sum and the last one to finish adds all of them in
-// segment order, so the result does not depend on which workgroup finishes
-// last.
+// each writes a partial sum and a second, small kernel adds them in segment
+// order, so the result does not depend on the order the workgroups finish.
 #include <type_traits>
 
 #include "sas_device.h"
@@ -59,7 +58,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float stat2[NBUF == 3 ? 4 : 1][4 * kBlock];
   __shared__ int s_ent[kSegMax];
   __shared__ float s_lg[kSegMax];
-  __shared__ int s_last;
 
   const int w = blockIdx.x;
   const int nx = p.hkv * p.QB;
@@ -382,15 +380,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         }
     }
   }
-  if (nseg == 1) return;
+}
 
-  // Split key block: the last segment to finish adds the partials in order.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&p.done[x], 1) == nseg - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+// Split key blocks: add the partials of their segments in segment order
+// (a separate launch, so the partials are visible without device-scope
+// fences inside the dK/dV kernel; one workgroup per key block, blocks that
+// were not split return at once).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdParams p) {
+  const int x = blockIdx.x;
+  const int nseg = p.seg_off[x + 1] - p.seg_off[x];
+  if (nseg == 1) return;
+  const int kb = x / p.hkv, g = x % p.hkv;  // key-block major order
+  const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, kb);
+  const int j = kb - p.cu_qblocks[s];
+  const int seq_start = p.cu_seqlens[s];
+  const int nvalid = min(kBlock, p.cu_seqlens[s + 1] - seq_start - j * kBlock);
+  const long ktok0 = seq_start + (long)j * kBlock;
   const int n = kBlock * D;
   const float *part0 = p.partial + (long)p.seg_off[x] * 2 * n;
   for (int e = threadIdx.x * 4; e < 2 * n; e += 256 * 4) {
@@ -410,6 +416,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 template <typename T, int D>
 static hipError_t launch_dkdv_t(const BwdParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(p.U), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3(p.hkv * p.QB), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

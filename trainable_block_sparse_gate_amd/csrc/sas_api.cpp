@@ -201,10 +201,10 @@ sas_status sas_gate_bwd(const sas_problem *p, const float *logits, int64_t ld,
 
 namespace {
 
-constexpr int kSeg = 32;  // keeping rows per dk/dv segment (at most 64)
+constexpr int kSeg = 64;  // keeping rows per dk/dv segment (at most 64)
 
 struct BwdLayout {
-  size_t off_L, off_D, off_dO16, off_list, off_count, off_segoff, off_done, off_dlgpart,
+  size_t off_L, off_D, off_dO16, off_list, off_count, off_segoff, off_dlgpart,
       off_partial, total;
   int U, nhc, max_nb;
 };
@@ -230,7 +230,6 @@ BwdLayout bwd_layout(const sas_problem *p, int max_nb) {
   L.off_list = off;     off = align256(off + sizeof(int32_t) * nx * L.max_nb);
   L.off_count = off;    off = align256(off + sizeof(int32_t) * nx);
   L.off_segoff = off;   off = align256(off + sizeof(int32_t) * (nx + 1));
-  L.off_done = off;     off = align256(off + sizeof(int32_t) * nx);
   L.off_dlgpart = off;
   if (L.nhc > 1) off = align256(off + sizeof(float) * L.nhc * nx * p->budget_blocks);
   L.off_partial = off;  off = align256(off + sizeof(float) * (size_t)L.U * 2 * 64 * p->head_dim);
@@ -272,7 +271,6 @@ sas_status bwd_setup(const sas_problem *p, void *workspace, size_t workspace_byt
   b->list = reinterpret_cast<int32_t *>(ws + L.off_list);
   b->count = reinterpret_cast<int32_t *>(ws + L.off_count);
   b->seg_off = reinterpret_cast<int32_t *>(ws + L.off_segoff);
-  b->done = reinterpret_cast<int32_t *>(ws + L.off_done);
   b->dlg_part = reinterpret_cast<float *>(ws + L.off_dlgpart);
   b->partial = reinterpret_cast<float *>(ws + L.off_partial);
   b->seg = kSeg;

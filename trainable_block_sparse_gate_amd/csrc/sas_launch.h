@@ -73,7 +73,6 @@ struct BwdParams {
   int32_t *seg_off;  // [QB*hkv + 1] prefix sum of segments per key block
   float *dlg_part;   // [nhc][hkv*QB][Kb] when a row's heads span workgroups
   float *partial;    // [U][2][64][D] partial dK / dV of split key blocks
-  int32_t *done;     // [QB*hkv] finished segments per key block
   int seg;           // keeping rows per segment
   int U;             // upper bound on the number of segments (dk/dv grid)
 };

@@ -39,10 +39,13 @@ namespace sas {
 // longest workgroups start first and the short ones fill the tail).  Rows
 // that can keep key block j of sequence s are its query blocks i >= j.
 __global__ __launch_bounds__(256) void bwd_csr_kernel(BwdParams p) {
-  const int x = blockIdx.x * 4 + threadIdx.x / kWave;
+  // waves walk the key blocks head by head (neighbouring waves read the same
+  // selection rows); results are stored at the key-block-major index x
+  const int wv = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  if (x >= p.hkv * p.QB) return;
-  const int kb = x / p.hkv, g = x % p.hkv;
+  if (wv >= p.hkv * p.QB) return;
+  const int g = wv / p.QB, kb = wv % p.QB;
+  const int x = kb * p.hkv + g;
   const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, kb);
   const int q0 = p.cu_qblocks[s], nb = p.cu_qblocks[s + 1] - q0;
   const int j = kb - q0;

@@ -125,12 +125,15 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
   constexpr int TILE = RT::ELEMS;
 
   __shared__ __attribute__((aligned(16))) T tiles[2 * 2 * TILE];  // [buf][K | V]
-  __shared__ float s_F[NWV][kMaxBudget];  // per tile: sum of P dP over the wave's rows
+  __shared__ float s_F[NWV][kMaxBudget];  // per tile: the wave's share of dlg
   __shared__ int s_slot[kMaxBudget];     // tiles in processing order
   __shared__ int s_j[kMaxBudget];
   __shared__ float s_lg[kMaxBudget];     // log gate * log2(e)
   __shared__ int s_n;
-  extern __shared__ float s_G[];         // [NWV][Kb][32 QT]: per tile, sum of P per query row
+  // [2][NWV][Kb][32 QT]: per tile and query row, the sums over the tile's
+  // keys of P (s_G) and of P dP (s_Fq)
+  extern __shared__ float s_G[];
+  float *s_Fq = s_G + NWV * p.Kb * 32 * QT;
 
   const T *q = static_cast<const T *>(p.q);
   const T *kk = static_cast<const T *>(p.k);
@@ -254,10 +257,9 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
     const T *Ks = tiles + (2 * b + 0) * TILE;
     const T *Vs = tiles + (2 * b + 1) * TILE;
 
-    float tile_F = 0.f;
-    float Gp[QT];
+    float Fp[QT], Gp[QT];  // lane partials: sum of P dP, of P
 #pragma unroll
-    for (int nt = 0; nt < QT; ++nt) Gp[nt] = 0.f;
+    for (int nt = 0; nt < QT; ++nt) Fp[nt] = Gp[nt] = 0.f;
     // one 32-key half at a time (not unrolled: keeps both halves' live
     // ranges from overlapping)
 #pragma unroll 1
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
             pd[r] += pd[r + w];
             pp[r] += pp[r + w];
           }
-        tile_F += pd[0];
+        Fp[nt] += pd[0];
         Eacc[nt] += pd[0];
         Gp[nt] += pp[0];
       }
@@ -323,12 +325,16 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
         }
       }
     }
-    tile_F = wave_sum(tile_F);
-    if (lane == 0) s_F[wave][it] = head_ok ? tile_F : 0.f;
+    // per query row (the two lane halves added); the sums over rows wait
+    // until after the loop, off the tile pipeline
 #pragma unroll
     for (int nt = 0; nt < QT; ++nt) {
+      const float fsum = Fp[nt] + __shfl_xor(Fp[nt], 32);
       const float gsum = Gp[nt] + __shfl_xor(Gp[nt], 32);
-      if (hf == 0) s_G[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = gsum;
+      if (hf == 0) {
+        s_Fq[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = fsum;
+        s_G[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = gsum;
+      }
     }
     if (it + 1 < ntiles) store_tile(b ^ 1);
     if (it + 2 < ntiles) load_tile(it + 2);
@@ -349,14 +355,22 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
       p.Lbuf[at] = lse2[nt];
     }
   }
-  for (int it = 0; it < ntiles; ++it) {
-    float c = 0.f;
-    if (hf == 0) {
+  // this wave's share of dlg per tile, one tile per lane, rows in order:
+  // sum over the wave's rows of (sum P dP - D_t sum P); D_t of row q comes
+  // from lane q (read across lanes, no memory)
+  for (int t0 = 0; t0 < ntiles; t0 += kWave) {
+    const int t = t0 + lane;
+    float val = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < QT; ++nt) c += Ex[nt] * s_G[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32];
-    }
-    c = wave_sum(c);
-    if (lane == 0) s_F[wave][it] = head_ok ? s_F[wave][it] - c : 0.f;
+    for (int nt = 0; nt < QT; ++nt)
+      for (int q = 0; q < 32; ++q) {
+        const float e = lane_value(Ex[nt], q);
+        if (t < ntiles) {
+          const int at = (wave * p.Kb + t) * (32 * QT) + 32 * nt + q;
+          val += s_Fq[at] - e * s_G[at];
+        }
+      }
+    if (t < ntiles) s_F[wave][t] = head_ok ? val : 0.f;
   }
 
   if (head_ok) {
@@ -412,7 +426,7 @@ constexpr int dq_static_lds() {
 
 template <typename T, int D, int NW>
 static size_t dq_dynamic_lds(const BwdParams &p) {
-  return sizeof(float) * NW * p.Kb * kBlock;  // NW (2/QT) waves x 32 QT rows
+  return 2 * sizeof(float) * NW * p.Kb * kBlock;  // s_G, s_Fq: NW (2/QT) waves x 32 QT rows
 }
 
 template <typename T, typename TO, int D, int NW>

@@ -137,7 +137,7 @@ def test_bwd_hot_key_blocks_split_over_segments():
     """A long sequence with a few columns boosted so that most rows keep the
     same key blocks: those blocks are split over many segments."""
     import torch
-    lengths, hq, hkv, d, Kb = [4096 + 37], 8, 2, 128, 8
+    lengths, hq, hkv, d, Kb = [8192 + 37], 8, 2, 128, 8
     case = wl.make_varlen("hot", lengths, hq, hkv, d, Kb, dtype="bf16", logit_sigma=1.0,
                           workload_id=71, boost_frac=0.05, boost=6.0)
     prob = sas.Varlen(lengths, hq, hkv, d, Kb)
@@ -147,9 +147,9 @@ def test_bwd_hot_key_blocks_split_over_segments():
     torch.cuda.synchronize()
     ridx, rlg, rlse = oracle.gate_topk(case.cu_seqlens, case.logits, hkv, Kb)
     assert np.array_equal(sel.cpu().numpy(), ridx)
-    counts = np.bincount(ridx[0][ridx[0] >= 0].ravel(), minlength=65)
+    counts = np.bincount(ridx[0][ridx[0] >= 0].ravel())
     say(f"  most-kept block count: {counts.max()}")
-    assert counts.max() > 32  # at least two segments of 32
+    assert counts.max() > 64  # at least two segments of 64 rows
     ro, rl = oracle.fwd(case.cu_seqlens, case.q, case.k, case.v, ridx, rlg, Kb, case.scale)
     assert_close("o", o.float().cpu().numpy(), ro, TOL["bf16"])
     check_bwd(case, prob, dv, (sel, lg, glse, o, lse), (ridx, rlg, rlse, ro, rl))

@@ -79,7 +79,7 @@ def source_hash():
 def short_kernel(name):
     if "rocclr_copyBuffer" in name:
         return "copyBuffer"
-    m = re.search(r"([a-z_]+_kernel)", name)
+    m = re.search(r"([a-z0-9_]+_kernel)", name)
     if m and ("sas" in name):
         return m.group(1)
     return None

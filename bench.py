@@ -79,10 +79,12 @@ def source_hash():
 def short_kernel(name):
     if "rocclr_copyBuffer" in name:
         return "copyBuffer"
-    m = re.search(r"([a-z0-9_]+_kernel)", name)
-    if m and ("sas" in name):
-        return m.group(1)
-    return None
+    if "sas" not in name:
+        return None
+    m = re.search(r"_ZN3sas\d+([a-z][a-z0-9_]*?_kernel)", name)  # mangled
+    if not m:
+        m = re.search(r"([a-z][a-z0-9_]*_kernel)", name)
+    return m.group(1) if m else None
 
 
 def read_counter_csv(d):

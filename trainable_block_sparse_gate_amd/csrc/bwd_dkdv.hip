@@ -382,15 +382,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-// Split key blocks: add the partials of their segments in segment order
-// (a separate launch, so the partials are visible without device-scope
-// fences inside the dK/dV kernel; one workgroup per key block, blocks that
-// were not split return at once).
+// Sum, in segment order, the nseg partials of split key block x into dk, dv.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdParams p) {
-  const int x = blockIdx.x;
-  const int nseg = p.seg_off[x + 1] - p.seg_off[x];
-  if (nseg == 1) return;
+__device__ void reduce_key_block(const BwdParams &p, int x, int nseg) {
   const int kb = x / p.hkv, g = x % p.hkv;  // key-block major order
   const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, kb);
   const int j = kb - p.cu_qblocks[s];
@@ -412,13 +406,28 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdParams p) {
   }
 }
 
+// Split key blocks: add the partials of their segments in segment order
+// (a separate launch, so the partials are visible without device-scope
+// fences inside the dK/dV kernel).  Each workgroup walks a strided share of
+// the key blocks and skips those that were not split.
+constexpr int kReduceWgs = 256;
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdParams p) {
+  for (int x = blockIdx.x; x < p.hkv * p.QB; x += gridDim.x) {
+    const int nseg = p.seg_off[x + 1] - p.seg_off[x];
+    if (nseg > 1) reduce_key_block<D>(p, x, nseg);
+  }
+}
+
 // ------------------------------------------------------------------ launch
 template <typename T, int D>
 static hipError_t launch_dkdv_t(const BwdParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(p.U), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3(p.hkv * p.QB), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3(min(kReduceWgs, p.hkv * p.QB)), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

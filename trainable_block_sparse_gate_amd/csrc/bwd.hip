@@ -373,23 +373,41 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
     if (t < ntiles) s_F[wave][t] = head_ok ? val : 0.f;
   }
 
+  // dQ goes out through the (now idle) tile buffers, one half of the
+  // columns at a time: each wave puts its rows' half into a private
+  // swizzled region, then stores whole 16-byte chunks, 16 lanes per half
+  // row, so rows are written in full lines.
   if (head_ok) {
+    using SW = Swz<float, D / 2>;
+    constexpr int ROWS = 32 * QT, HC = D / 8;  // rows, 16-byte chunks per half row
+    static_assert(NWV * ROWS * (D / 2) * 4 <= 2 * 2 * TILE * (int)sizeof(T),
+                  "all waves' half rows fit the tiles");
+    float *ob = reinterpret_cast<float *>(tiles) + wave * (ROWS * (D / 2));
 #pragma unroll
-    for (int nt = 0; nt < QT; ++nt) {
-      const int ql = 32 * (nt0 + nt) + l32;
-      if (ql >= nq) continue;
-      const long t = seq_start + (long)i * kBlock + ql;
-      float *dqp = p.dq + (t * p.hq + h) * D;
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int nt = 0; nt < QT; ++nt)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int d0 = 32 * dt + d_row(4 * rg, hf);
-          *reinterpret_cast<float4 *>(dqp + d0) =
-              make_float4(dqacc[dt][nt][4 * rg] * p.scale, dqacc[dt][nt][4 * rg + 1] * p.scale,
-                          dqacc[dt][nt][4 * rg + 2] * p.scale,
-                          dqacc[dt][nt][4 * rg + 3] * p.scale);
+        for (int dt = half * NDT / 2; dt < (half + 1) * NDT / 2; ++dt)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int d0 = 32 * dt + d_row(4 * rg, hf) - half * (D / 2);
+            *reinterpret_cast<float4 *>(ob + SW::off(32 * nt + l32, d0)) = make_float4(
+                dqacc[dt][nt][4 * rg] * p.scale, dqacc[dt][nt][4 * rg + 1] * p.scale,
+                dqacc[dt][nt][4 * rg + 2] * p.scale, dqacc[dt][nt][4 * rg + 3] * p.scale);
+          }
+      wait_lds_all();
+#pragma unroll
+      for (int c0 = 0; c0 < ROWS * HC; c0 += kWave) {
+        const int c = c0 + lane, r = c / HC, cc = c % HC;
+        const int ql = 32 * nt0 + r;
+        if (ql < nq) {
+          const long t = seq_start + (long)i * kBlock + ql;
+          *reinterpret_cast<float4 *>(p.dq + (t * p.hq + h) * D + half * (D / 2) + 4 * cc) =
+              *reinterpret_cast<const float4 *>(ob + SW::off(r, 4 * cc));
         }
+      }
+      wait_lds_all();  // the region is rewritten by the next half
     }
   }
   __syncthreads();

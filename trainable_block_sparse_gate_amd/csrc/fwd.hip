@@ -282,6 +282,47 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
 
   if (!head_ok) return;
   TO *o = static_cast<TO *>(p.o);
+  if constexpr (sizeof(TO) == 2 && sizeof(T) == 2) {
+    // bf16 output goes through the (now idle) tile buffers: each wave puts
+    // its 32 QT rows into a private swizzled region, then stores whole
+    // 16-byte chunks, 16 lanes per row, so every row is written in full
+    // lines rather than in 8-byte pieces spread over many instructions.
+    using SW = Swz<__bf16, D>;
+    constexpr int ROWS = 32 * QT, CPR = D / 8;
+    static_assert((NT / kWave) * ROWS * D <= 2 * 2 * TILE, "all waves' rows fit the tiles");
+    __bf16 *ob = reinterpret_cast<__bf16 *>(tiles) + wave * (ROWS * D);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const float inv = 1.f / l_run[t];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = 32 * dt + d_row(4 * rg, hf);
+          bf16x4 w;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[dt][t][4 * rg + x] * inv);
+          *reinterpret_cast<bf16x4 *>(ob + SW::off(32 * t + l32, d0)) = w;
+        }
+      const int ql = 32 * (nt0 + t) + l32;
+      if (hf == 0 && ql < nq) {
+        const long tq = seq_start + i * kBlock + ql;
+        p.lse[(long)h * p.T + tq] = (m_run[t] + fast_log2(l_run[t])) * kLn2;
+      }
+    }
+    wait_lds_all();
+#pragma unroll
+    for (int c0 = 0; c0 < ROWS * CPR; c0 += kWave) {
+      const int c = c0 + lane, r = c / CPR, cc = c % CPR;
+      const int ql = 32 * nt0 + r;
+      if (ql < nq) {
+        const long tq = seq_start + i * kBlock + ql;
+        *reinterpret_cast<u32x4 *>(o + (tq * p.hq + h) * D + 8 * cc) =
+            *reinterpret_cast<const u32x4 *>(ob + SW::off(r, 8 * cc));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int ql = 32 * (nt0 + t) + l32;

@@ -182,19 +182,16 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
   for (int nt = 0; nt < QT; ++nt) {
     const int ql = 32 * (nt0 + nt) + l32;
     const long t = seq_start + (long)i * kBlock + ql;
-    const long base = (t * p.hq + h) * D + hf * E;
+    // rows past the block's end read its last row: their P is zero (lse
+    // +inf), so neither their values nor their D reach any result, and the
+    // loads need no branch and issue back to back
+    const long base = ((t - max(0, ql - (nq - 1))) * p.hq + h) * D + hf * E;
     OutChunk<TO, E> dch[NKS], och[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      if (ql < nq) {
-        qreg[nt][ks] = lds_op<T>(q + base + ks * KS);
-        dch[ks].load(dO + base + ks * KS);
-        och[ks].load(oo + base + ks * KS);
-      } else {
-        qreg[nt][ks] = typename M::Op{};
-        dch[ks].zero();
-        och[ks].zero();
-      }
+      qreg[nt][ks] = lds_op<T>(q + base + ks * KS);
+      dch[ks].load(dO + base + ks * KS);
+      och[ks].load(oo + base + ks * KS);
     }
     float dacc = 0.f;
 #pragma unroll

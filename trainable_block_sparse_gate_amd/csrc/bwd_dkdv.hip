@@ -87,10 +87,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int kh = wave % 2, qh = wave / 2;
   const int key = 32 * kh + l32;  // this lane's key (column of S)
 
+  // The segment's entries (query block << 8 | slot, and the slot's log
+  // gate), then K and V: all requested before anything waits, so the K/V
+  // latency overlaps the first tile requests below.
+  int my_ent = 0;
+  float my_lg = 0.f;
   if (threadIdx.x < nent) {
-    const int ent = p.list[(long)x * p.max_nb + e0 + threadIdx.x];
-    s_ent[threadIdx.x] = ent;
-    s_lg[threadIdx.x] = p.sel_lg[((long)g * p.QB + (ent >> 8)) * p.Kb + (ent & 255)] * kLog2e;
+    my_ent = p.list[(long)x * p.max_nb + e0 + threadIdx.x];
+    my_lg = p.sel_lg[((long)g * p.QB + (my_ent >> 8)) * p.Kb + (my_ent & 255)];
   }
 
   const T *q = static_cast<const T *>(p.q);
@@ -98,22 +102,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const T *vv = static_cast<const T *>(p.v);
   const T *dO = static_cast<const T *>(p.dO_t);
 
+  // keys past the block's end read its last row (finite values; their
+  // probabilities are masked to zero and their sums never written), so the
+  // loads need no branch and all issue back to back
   typename M::Op kreg[NKS], vreg[NKS];
   {
-    const long base = ((ktok0 + key) * p.hkv + g) * D + hf * E;
+    const long base = ((ktok0 + min(key, nvalid - 1)) * p.hkv + g) * D + hf * E;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      if (key < nvalid) {
-        kreg[ks] = lds_op<T>(kk + base + ks * KS);
-        vreg[ks] = lds_op<T>(vv + base + ks * KS);
-      } else {
-        kreg[ks] = typename M::Op{};
-        vreg[ks] = typename M::Op{};
-      }
+      kreg[ks] = lds_op<T>(kk + base + ks * KS);
+      vreg[ks] = lds_op<T>(vv + base + ks * KS);
     }
-    // K and V are complete before the first tile request, so the explicit
-    // counts below only ever see tile requests
-    wait_vmem_all();
+  }
+  if (threadIdx.x < nent) {
+    s_ent[threadIdx.x] = my_ent;
+    s_lg[threadIdx.x] = my_lg * kLog2e;
   }
   f32x16 dkacc[NDT], dvacc[NDT];
 #pragma unroll
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 
   const int G = p.G;
   const int nsteps = nent * G;
-  __syncthreads();  // s_ent / s_lg visible
+  barrier_keep_requests();  // s_ent / s_lg visible; K and V may still be in flight
 
   auto tiles_of = [&](auto B) -> T * {
     if constexpr (decltype(B)::value == 0) return buf0;
@@ -306,8 +309,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   };
 
   // Prologue: the first NBUF - 1 steps.  Waiting for all of them (not just
-  // step 0) leaves no request in flight at the loop entry, which keeps the
-  // compiler's tracking of which buffer a request targets exact in the loop.
+  // step 0) -- and for K and V -- leaves no request in flight at the loop
+  // entry, which keeps the compiler's tracking of which buffer a request
+  // targets exact in the loop.
   if (nsteps > 0) {
     issue_step(I0{}, 0);
     if constexpr (NBUF == 3) issue_step(I1{}, 1);

@@ -107,15 +107,12 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
   typename M::Op qreg[QT][NKS];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    const int ql = 32 * (nt0 + t) + l32;
+    // rows past the block's end read its last row (their outputs are never
+    // written), so the loads need no branch and issue back to back
+    const int ql = min(32 * (nt0 + t) + l32, nq - 1);
     const T *qp = q + ((long)(seq_start + i * kBlock + ql) * p.hq + h) * D + hf * E;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (ql < nq)
-        qreg[t][ks] = lds_op<T>(qp + ks * KS);
-      else
-        qreg[t][ks] = typename M::Op{};
-    }
+    for (int ks = 0; ks < NKS; ++ks) qreg[t][ks] = lds_op<T>(qp + ks * KS);
   }
 
   f32x16 oacc[NDT][QT];

@@ -177,14 +177,17 @@ __global__ __launch_bounds__(256, kDecodeWgPerCu) void decode_attend_kernel(Deco
   const __bf16 *q = static_cast<const __bf16 *>(p.q);
 
   // Q^T as B operands: column c16 = query head c16 of the group (zero past G)
+  // (columns past G load head 0 and are zeroed afterwards: no branch, the
+  // loads issue back to back)
   bf16x8 qreg[NKS];
+  {
+    const __bf16 *qp = q + ((long)b * p.hq + g * G + (c16 < G ? c16 : 0)) * D + 8 * q16;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    if (c16 < G)
-      qreg[ks] = *reinterpret_cast<const bf16x8 *>(q + ((long)b * p.hq + g * G + c16) * D +
-                                                   32 * ks + 8 * q16);
-    else
-      qreg[ks] = bf16x8{};
+    for (int ks = 0; ks < NKS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8 *>(qp + 32 * ks);
+    if (G < 16) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qreg[ks] = c16 < G ? qreg[ks] : bf16x8{};
+    }
   }
   // Blocks of this wave, looked up once: lane k holds block k's first-row
   // offset (K and V alike), valid keys and log gate, read back with

@@ -199,12 +199,16 @@ __global__ __launch_bounds__(256, kDecodeWgPerCu) void decode_attend_kernel(Deco
   float b_lg2 = 0.f;
   if (lane < nb) {
     const int c = s0 + 4 * lane;
+    // the log gate is requested with the index (an ungated call reads the
+    // index array in its place and discards it), so only the page lookup
+    // waits for the index
+    const float lgv = *(slg ? slg + c : reinterpret_cast<const float *>(sel + c));
     const int j = sel[c];
     const bool ok = j >= 0 && j <= cur;
     const int jj = ok ? j : cur;
     b_nv = !ok ? 0 : (jj == cur ? L - cur * kBlock : kBlock);
     b_off = kv_row(p, kc, b, g, jj * kBlock) - kc;  // a block never crosses a page
-    b_lg2 = slg ? slg[c] * kLog2e : 0.f;
+    b_lg2 = slg ? lgv * kLog2e : 0.f;
   }
   wait_vmem_all();
 

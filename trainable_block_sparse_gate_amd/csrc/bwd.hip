@@ -157,20 +157,11 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
   const int nq = min(kBlock, seq_len - i * kBlock);
   const long row = (long)g * p.QB + Q;
 
-  if (threadIdx.x == 0) {
-    const int32_t *sel = p.sel_idx + row * p.Kb;
-    const float *slg = p.sel_lg + row * p.Kb;
-    int n = 0;
-    for (int sl = 0; sl < p.Kb; ++sl) {
-      const int j = sel[sl];
-      if (j >= 0 && j <= i) {
-        s_slot[n] = sl;
-        s_j[n] = j;
-        s_lg[n] = slg[sl] * kLog2e;
-        ++n;
-      }
-    }
-    s_n = n;
+  // the kept blocks in slot order (wave 0, all slots read at once)
+  if (wave == 0) {
+    const int n = wave_kept_blocks(p.sel_idx + row * p.Kb, p.sel_lg + row * p.Kb, p.Kb, i, false,
+                                   s_j, s_slot, s_lg);
+    if (lane == 0) s_n = n;
   }
 
   // Q and dO as B operands (lane -> query column), D and lse per column.

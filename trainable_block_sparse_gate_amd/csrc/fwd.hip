@@ -82,25 +82,11 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
 
   // tile order: the current (diagonal) block first, so the running max is
   // finite before any gated history tile, then the kept history blocks
-  if (threadIdx.x == 0) {
-    const int32_t *sel = p.sel_idx + row * p.Kb;
-    const float *slg = p.sel_lg + row * p.Kb;
-    int n = 0;
-    for (int sl = 0; sl < p.Kb; ++sl)
-      if (sel[sl] == i) {
-        s_j[n] = i;
-        s_lg[n] = slg[sl] * kLog2e;
-        ++n;
-      }
-    for (int sl = 0; sl < p.Kb; ++sl) {
-      const int j = sel[sl];
-      if (j >= 0 && j < i) {
-        s_j[n] = j;
-        s_lg[n] = slg[sl] * kLog2e;
-        ++n;
-      }
-    }
-    s_n = n;
+  // the kept blocks, current block first (wave 0, all slots read at once)
+  if (wave == 0) {
+    const int n = wave_kept_blocks(p.sel_idx + row * p.Kb, p.sel_lg + row * p.Kb, p.Kb, i, true,
+                                   s_j, nullptr, s_lg);
+    if (lane == 0) s_n = n;
   }
 
   // Q as the B operand of S^T = K Q^T: lane -> query column.

@@ -139,6 +139,57 @@ __device__ inline void barrier_keep_requests() {
 // uniform branches rather than exec-masked ones.  Call with all lanes active.
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 
+// The kept blocks of one selection row as seen by query block i, built by
+// one whole wave: the slots' block indices j (-1 = empty) with j <= i, in
+// slot order -- with the current block i moved to the front when
+// current_first -- are written to out_j (and their slots to out_slot when it
+// is given, their log gates times log2 e to out_lg2).  All of the row's
+// slots are read at once (one per lane, Kb <= 4 * 64).  Returns the count.
+__device__ inline int wave_kept_blocks(const int32_t *sel, const float *slg, int Kb, int i,
+                                       bool current_first, int *out_j, int *out_slot,
+                                       float *out_lg2) {
+  const int lane = threadIdx.x % kWave;
+  int jv[4];
+  float lgv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int sl = 64 * c + lane;
+    jv[c] = -1;
+    lgv[c] = 0.f;
+    if (sl < Kb) {
+      jv[c] = sel[sl];
+      lgv[c] = slg[sl];
+    }
+  }
+  int nd = 0;  // the current block (at most once), when it goes first
+  if (current_first) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool cur = jv[c] == i;
+      if (cur) {
+        out_j[0] = i;
+        if (out_slot) out_slot[0] = 64 * c + lane;
+        out_lg2[0] = lgv[c] * kLog2e;
+      }
+      nd += __popcll(__ballot(cur));
+    }
+  }
+  int n = nd;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bool ok = jv[c] >= 0 && (current_first ? jv[c] < i : jv[c] <= i);
+    const uint64_t m = __ballot(ok);
+    if (ok) {
+      const int pos = n + __popcll(m & ((1ull << lane) - 1ull));
+      out_j[pos] = jv[c];
+      if (out_slot) out_slot[pos] = 64 * c + lane;
+      out_lg2[pos] = lgv[c] * kLog2e;
+    }
+    n += __popcll(m);
+  }
+  return n;
+}
+
 // Value of x in lane k (k uniform across the wave), without touching memory.
 __device__ inline int lane_value(int x, int k) { return __builtin_amdgcn_readlane(x, k); }
 __device__ inline float lane_value(float x, int k) {

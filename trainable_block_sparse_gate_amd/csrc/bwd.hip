@@ -165,10 +165,12 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
   }
 
   // Q and dO as B operands (lane -> query column), D and lse per column.
-  // Per query tile every load is issued before any is used, so the tile
-  // costs one memory latency rather than one per chunk.
+  // Every load is issued before any is used, and the first K/V tile is
+  // requested before the Q/dO/O data is consumed, so the prologue costs one
+  // memory latency.
   typename M::Op qreg[QT][NKS], doreg[QT][NKS];
   float Dv[QT], lse2[QT];
+  OutChunk<TO, E> dch[QT][NKS], och[QT][NKS];
 #pragma unroll
   for (int nt = 0; nt < QT; ++nt) {
     const int ql = 32 * (nt0 + nt) + l32;
@@ -177,30 +179,12 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
     // +inf), so neither their values nor their D reach any result, and the
     // loads need no branch and issue back to back
     const long base = ((t - max(0, ql - (nq - 1))) * p.hq + h) * D + hf * E;
-    OutChunk<TO, E> dch[NKS], och[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       qreg[nt][ks] = lds_op<T>(q + base + ks * KS);
-      dch[ks].load(dO + base + ks * KS);
-      och[ks].load(oo + base + ks * KS);
+      dch[nt][ks].load(dO + base + ks * KS);
+      och[nt][ks].load(oo + base + ks * KS);
     }
-    float dacc = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) dacc += dch[ks].get(e) * och[ks].get(e);
-      doreg[nt][ks] = dch[ks].template as_op<T>();
-    }
-    // a wider dO is handed to the dk/dv phase rounded to the input dtype
-    if constexpr (sizeof(TO) != sizeof(T)) {
-      if (ql < nq && head_ok) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          *reinterpret_cast<typename M::Op *>(p.dO16 + base + ks * KS) = doreg[nt][ks];
-      }
-    }
-    dacc += __shfl_xor(dacc, 32);
-    Dv[nt] = dacc;
     lse2[nt] = INFINITY;  // padding rows: P = 0
     if (ql < nq) lse2[nt] = p.lse[(long)h * p.T + t] * kLog2e;
   }
@@ -213,10 +197,7 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
     for (int dt = 0; dt < NDT; ++dt) dqacc[dt][nt] = f32x16{};
   }
 
-  // the register operands are complete before any tile load is issued, so
-  // the wait counter tracking never makes a tile wait for its own prefetch
-  wait_vmem_all();
-  __syncthreads();
+  barrier_keep_requests();  // the tile list is visible; the loads above may be in flight
   const int ntiles = s_n;
   const long kstride = (long)p.hkv * D;
   RT kst, vst;
@@ -231,8 +212,32 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
     rowtile_store<T, D, NT>(kst, tiles + (2 * b + 0) * TILE);
     rowtile_store<T, D, NT>(vst, tiles + (2 * b + 1) * TILE);
   };
+  if (ntiles > 0) load_tile(0);
+
+#pragma unroll
+  for (int nt = 0; nt < QT; ++nt) {
+    const int ql = 32 * (nt0 + nt) + l32;
+    const long base = ((seq_start + (long)i * kBlock + ql) * p.hq + h) * D + hf * E;
+    float dacc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) dacc += dch[nt][ks].get(e) * och[nt][ks].get(e);
+      doreg[nt][ks] = dch[nt][ks].template as_op<T>();
+    }
+    // a wider dO is handed to the dk/dv phase rounded to the input dtype
+    if constexpr (sizeof(TO) != sizeof(T)) {
+      if (ql < nq && head_ok) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          *reinterpret_cast<typename M::Op *>(p.dO16 + base + ks * KS) = doreg[nt][ks];
+      }
+    }
+    dacc += __shfl_xor(dacc, 32);
+    Dv[nt] = dacc;
+  }
+
   if (ntiles > 0) {
-    load_tile(0);
     store_tile(0);
     if (ntiles > 1) load_tile(1);
   }

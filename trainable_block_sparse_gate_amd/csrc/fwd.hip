@@ -82,7 +82,7 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
 
   // tile order: the current (diagonal) block first, so the running max is
   // finite before any gated history tile, then the kept history blocks
-  // the kept blocks, current block first (wave 0, all slots read at once)
+  // (built by wave 0, all slots read at once)
   if (wave == 0) {
     const int n = wave_kept_blocks(p.sel_idx + row * p.Kb, p.sel_lg + row * p.Kb, p.Kb, i, true,
                                    s_j, nullptr, s_lg);
@@ -113,10 +113,9 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
     l_run[t] = 0.f;
   }
 
-  // the register operands are complete before any tile load is issued, so
-  // the wait counter tracking never makes a tile wait for its own prefetch
-  wait_vmem_all();
-  __syncthreads();
+  // the tile list is visible; Q may still be in flight, so its latency
+  // overlaps the first tile's (storing that tile waits for both)
+  barrier_keep_requests();
   const int ntiles = s_n;
   const long kstride = (long)p.hkv * D;
   RT kst, vst;

@@ -336,7 +336,8 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
 
   // Exact D per query row, then dlg of each tile = sum P dP - sum_t D_t G_t.
   // Both row statistics are stored for all 64 rows of the block (rows past
-  // its end: lse +inf, D 0) so the dk/dv phase can fetch them as a whole.
+  // its end: lse +inf, D 0) so the dk/dv phase can fetch them as a whole,
+  // in the form that phase seeds its products with: -lse / scale and -D.
   float Ex[QT];
 #pragma unroll
   for (int nt = 0; nt < QT; ++nt) {
@@ -344,8 +345,8 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
     const int ql = 32 * (nt0 + nt) + l32;
     if (hf == 0 && head_ok) {
       const long at = ((long)h * p.QB + Q) * kBlock + ql;
-      p.Dbuf[at] = ql < nq ? Ex[nt] : 0.f;
-      p.Lbuf[at] = lse2[nt];
+      p.Dbuf[at] = ql < nq ? -Ex[nt] : 0.f;
+      p.Lbuf[at] = -lse2[nt] / p.scale_log2;
     }
   }
   // this wave's share of dlg per tile, one tile per lane, rows in order:

@@ -19,7 +19,13 @@ namespace sas {
 // ------------------------------------------------------------------ dk/dv
 // Workgroup of 4 waves: wave = (query half qh, key half kh).  Each wave
 // owns 32 keys (K, V as B operands in registers) and, per step, 32 of the
-// 64 query rows of one head of one keeping row.  The Q and dO tiles of a
+// 64 query rows of one head of one keeping row for S, dP, P and dS.  For
+// bf16 the dV / dK products then split d instead of the query rows: wave
+// (kh, qh) accumulates d tiles [qh NDT/2, (qh + 1) NDT/2) of its keys over
+// all 64 rows, taking P and dS of the other query half from the wave that
+// formed them (same keys) through LDS, so every wave holds half of the
+// accumulators and no final reduction is needed.  fp32 keeps all d tiles
+// per wave and adds the two query halves at the end.  The Q and dO tiles of a
 // step, and the row statistics (lse * log2 e and D, written per 64-row
 // block by the dq phase), go from global memory straight into LDS with
 // global_load_lds (no register staging).  bf16 tiles use three LDS buffers
@@ -40,6 +46,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int RPS = kWave / CPR;                // rows per 1 KB request
   constexpr int SPW = kBlock / RPS / 4;           // 1 KB requests per wave per tile
   constexpr int PER_STEP = 2 * SPW + 1;           // requests per wave per step
+  constexpr bool kSplitD = (E == 8);              // dV / dK split over d (bf16)
+  constexpr int NACC = kSplitD ? NDT / 2 : NDT;   // d tiles accumulated per wave
   static_assert(kBlock % (4 * RPS) == 0, "tile rows must split evenly over the waves");
   static_assert(2 * NDT * 16 * kWave * 4 <= 2 * TILE * (int)sizeof(T),
                 "a buffer holds one half of the final reduction");
@@ -50,14 +58,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) T buf0[2 * TILE];  // [Q | dO][64][D]
   __shared__ __attribute__((aligned(16))) T buf1[2 * TILE];
   __shared__ __attribute__((aligned(16))) T buf2[NBUF == 3 ? 2 * TILE : 8];
-  // row statistics: [wave][256] per buffer; waves 0 / 1 bring lse * log2 e /
-  // D in their first 64 entries (the rest, and waves 2 and 3, are filler
+  // row statistics: [wave][256] per buffer; waves 0 / 1 bring -lse / scale
+  // and -D in their first 64 entries (the rest, and waves 2 and 3, are filler
   // that keeps every wave's request count the same)
   __shared__ __attribute__((aligned(16))) float stat0[4][4 * kBlock];
   __shared__ __attribute__((aligned(16))) float stat1[4][4 * kBlock];
   __shared__ __attribute__((aligned(16))) float stat2[NBUF == 3 ? 4 : 1][4 * kBlock];
-  __shared__ int s_ent[kSegMax];
-  __shared__ float s_lg[kSegMax];
+  // P and dS of each wave as bf16 B operands, lane-linear: [wave][P kc | dS kc][lane]
+  __shared__ bf16x8 xch[kSplitD ? 4 : 1][kSplitD ? 2 * SPT : 1][kWave];
 
   const int w = blockIdx.x;
   const int nx = p.hkv * p.QB;
@@ -87,15 +95,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int kh = wave % 2, qh = wave / 2;
   const int key = 32 * kh + l32;  // this lane's key (column of S)
 
-  // The segment's entries (query block << 8 | slot, and the slot's log
-  // gate), then K and V: all requested before anything waits, so the K/V
-  // latency overlaps the first tile requests below.
+  // The segment's entries (query block << 8 | slot) and the slots' log
+  // gates, entry l in lane l of every wave (a segment holds at most 64; a
+  // step reads its entry with readlane, no memory round trip), then K and
+  // V: all requested before anything waits.
   int my_ent = 0;
   float my_lg = 0.f;
-  if (threadIdx.x < nent) {
-    my_ent = p.list[(long)x * p.max_nb + e0 + threadIdx.x];
-    my_lg = p.sel_lg[((long)g * p.QB + (my_ent >> 8)) * p.Kb + (my_ent & 255)];
-  }
+  if (lane < nent) my_ent = p.list[(long)x * p.max_nb + e0 + lane];
 
   const T *q = static_cast<const T *>(p.q);
   const T *kk = static_cast<const T *>(p.k);
@@ -114,17 +120,28 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       vreg[ks] = lds_op<T>(vv + base + ks * KS);
     }
   }
-  if (threadIdx.x < nent) {
-    s_ent[threadIdx.x] = my_ent;
-    s_lg[threadIdx.x] = my_lg * kLog2e;
-  }
-  f32x16 dkacc[NDT], dvacc[NDT];
+  if (lane < nent) my_lg = p.sel_lg[((long)g * p.QB + (my_ent >> 8)) * p.Kb + (my_ent & 255)];
+  f32x16 dkacc[NACC], dvacc[NACC];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
+  for (int dt = 0; dt < NACC; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
+
+  // bf16 operand offsets (bytes) inside a tile, for this lane: the row
+  // operand of chunk ks is at oq ^ 32 ks, the transposed operand of d tile
+  // dt and 16-row chunk c at (ot0 ^ 64 dt) + 32 D c and (ot1 ^ 64 dt) + 32 D c
+  // (the swizzle's XOR acts on bits the row offset leaves free, and it does
+  // not depend on the row's multiple of 16)
+  const int qrow = 32 * qh + chain_key_of_row<T>(l32);
+  unsigned oq = 0, ot0 = 0, ot1 = 0;
+  if constexpr (E == 8) {
+    const int g4 = lane / 16, s16 = lane % 16;
+    const int trow = 8 * (g4 / 2) + s16 / 4, tcol = 16 * (g4 % 2) + 4 * (s16 % 4);
+    oq = 2u * Swz<T, D>::off(qrow, hf * E);
+    ot0 = 2u * Swz<T, D>::off(trow, tcol);
+    ot1 = 2u * Swz<T, D>::off(trow + 4, tcol);
+  }
 
   const int G = p.G;
   const int nsteps = nent * G;
-  barrier_keep_requests();  // s_ent / s_lg visible; K and V may still be in flight
 
   auto tiles_of = [&](auto B) -> T * {
     if constexpr (decltype(B)::value == 0) return buf0;
@@ -138,7 +155,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   };
 
   // Requests of step st into buffer B: every wave first fetches one piece
-  // of row statistics (wave 0: lse, wave 1: D, 16 lanes' worth repeated
+  // of row statistics (wave 0: -lse / scale, wave 1: -D, 16 lanes' worth repeated
   // over the wave), then SPW 1 KB pieces (RPS rows) of the Q tile and of
   // the dO tile.  Lane l of a request lands at byte 16 l of the piece, i.e.
   // at physical chunk l % CPR of its row; it fetches the logical chunk that
@@ -146,42 +163,48 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   // (masked later).  Every wave issues exactly PER_STEP requests per step,
   // unconditionally (steps past the end re-fetch the last step into a
   // buffer that is not read again), so fixed wait counts are exact and the
-  // compiler's own tracking of the requests stays precise.
-  auto issue_step = [&](auto B, int st_req) {
+  // compiler's own tracking of the requests stays precise.  step_req forms
+  // the scalar part (row block and head of the step, clamped to the last
+  // one, and the uniform bases of its rows).
+  struct Req {
+    const char *qbase, *dbase;
+    const float *sbase;
+    int nq;
+  };
+  auto step_req = [&](int st_req) -> Req {
     const int st = min(st_req, nsteps - 1);
-    T *tl = tiles_of(B);
-    float(*stat)[4 * kBlock] = stats_of(B);
-    const int ent = s_ent[st / G];
+    const int ent = __builtin_amdgcn_readlane(my_ent, st / G);
     const int qb = ent >> 8;  // packed query-block index
     const int i = qb - q0;
     const int h = g * G + st % G;
     const long t0 = seq_start + (long)i * kBlock;
-    const int nq = min(kBlock, seq_len - i * kBlock);
-    {
-      const float *src =
-          ((wave & 1) ? p.Dbuf : p.Lbuf) + ((long)h * p.QB + qb) * kBlock + 4 * (lane % 16);
-      load_lds16(src, &stat[wave][0]);
-    }
-    // uniform base of the block's rows for head h; per lane a 32-bit byte
-    // offset (row, swizzled chunk), so the request takes a scalar base
     const long head0 = (t0 * p.hq + h) * D;
-    const char *qbase = reinterpret_cast<const char *>(q + head0);
-    const char *dbase = reinterpret_cast<const char *>(dO + head0);
-    const unsigned rstride = (unsigned)(p.hq * D * (int)sizeof(T));
-    const int r_in = lane / CPR, pc = lane % CPR;
-#pragma unroll
-    for (int tk = 0; tk < 2; ++tk) {
-      const char *src = tk == 0 ? qbase : dbase;
-#pragma unroll
-      for (int sg = 0; sg < SPW; ++sg) {
-        const int piece = wave * SPW + sg;
-        const int r = piece * RPS + r_in;
-        const int rr = r < nq ? r : nq - 1;
-        const int c = pc ^ Swz<T, D>::f(r);
-        const unsigned off = (unsigned)rr * rstride + (unsigned)(c * 16);
-        load_lds16(src + off, tl + tk * TILE + piece * RPS * D);
-      }
+    return Req{reinterpret_cast<const char *>(q + head0), reinterpret_cast<const char *>(dO + head0),
+               ((wave & 1) ? p.Dbuf : p.Lbuf) + ((long)h * p.QB + qb) * kBlock,
+               min(kBlock, seq_len - i * kBlock)};
+  };
+  // Request k of a step into buffer B (k = 0: this wave's piece of row
+  // statistics, then SPW pieces of Q and SPW of dO); per lane a 32-bit byte
+  // offset (row, swizzled chunk) from the uniform base, so the request takes
+  // a scalar base.
+  auto issue_piece = [&](auto B, const Req &r, int k) {
+    if (k == 0) {
+      load_lds16(r.sbase + 4 * (lane % 16), &stats_of(B)[wave][0]);
+      return;
     }
+    const int tk = (k - 1) / SPW, sg = (k - 1) % SPW;
+    const unsigned rstride = (unsigned)(p.hq * D * (int)sizeof(T));
+    const int piece = wave * SPW + sg;
+    const int rw = piece * RPS + lane / CPR;
+    const int rr = rw < r.nq ? rw : r.nq - 1;
+    const int c = (lane % CPR) ^ Swz<T, D>::f(rw);
+    const unsigned off = (unsigned)rr * rstride + (unsigned)(c * 16);
+    load_lds16((tk == 0 ? r.qbase : r.dbase) + off, tiles_of(B) + tk * TILE + piece * RPS * D);
+  };
+  auto issue_step = [&](auto B, int st_req) {
+    const Req r = step_req(st_req);
+#pragma unroll
+    for (int k = 0; k < PER_STEP; ++k) issue_piece(B, r, k);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -193,12 +216,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   // barrier (every wave's requests visible, buffer B free for reuse).
   auto step = [&](auto B, int st) {
     constexpr int b = decltype(B)::value;
-    issue_step(std::integral_constant<int, (b + NBUF - 1) % NBUF>{}, st + NBUF - 1);
+    // The offsets are opaque to the compiler from here on, so the per-chunk
+    // offsets are formed in each step (one XOR each) rather than all held in
+    // registers across the loop.
+    unsigned aq = oq, a0 = ot0, a1 = ot1;
+    asm volatile("" : "+v"(aq), "+v"(a0), "+v"(a1));
+    // the requests of step st + NBUF - 1 go out one per product pair below:
+    // issued back to back they would hold up this wave's products while the
+    // address unit works through every wave's requests
+    using BN = std::integral_constant<int, (b + NBUF - 1) % NBUF>;
+    const Req rq = step_req(st + NBUF - 1);
 
     const int e = st / G;
-    const int i = (s_ent[e] >> 8) - q0;
+    const int i = (__builtin_amdgcn_readlane(my_ent, e) >> 8) - q0;
     const int nq = min(kBlock, seq_len - i * kBlock);
-    const float lg2 = s_lg[e];
+    const float lg2 = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_lg), e)) * kLog2e;
     const bool diag = (i == j);
     const T *Qs = tiles_of(B);
     const T *Ds = Qs + TILE;
@@ -206,103 +239,175 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 
     // S[query][key] and dP[query][key] for 32 queries x this wave's 32 keys;
     // query rows loaded in chain order so P and dS feed the next products.
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-    const int qrow = 32 * qh + chain_key_of_row<T>(l32);
-    // operands are read ahead of the products that use them (order fixed
-    // by the scheduling groups below), so the reads' latency overlaps them
-    typename M::Op qa[NKS], da[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      qa[ks] = tile_op<T, D>(Qs, qrow, hf * E + ks * KS);
-      da[ks] = tile_op<T, D>(Ds, qrow, hf * E + ks * KS);
-    }
-    // this lane's 16 query rows, in register order, come in four runs of 4
-    // consecutive rows: fetch their lse and D as float4s
-    // (bf16 chain order; the fp32 order interleaves, so it reads one by one)
-    float lse_r[16], D_r[16];
+    // The products start from the row statistics, so that after them
+    //   sacc = S - lse / scale   and   pacc = dP - D,
+    // and P = exp2(scale_log2 * sacc + lg2), dS = P * pacc take no further
+    // per-row term.  This lane's 16 rows, in register order, come in four
+    // runs of 4 consecutive rows: their statistics are read as float4s
+    // (bf16 chain order; the fp32 order interleaves, so it reads one by one).
+    f32x16 sacc, pacc;
     if constexpr (E == 8) {
 #pragma unroll
       for (int r0 = 0; r0 < 16; r0 += 4) {
         const int q4 = 32 * qh + chain_slot<T>(r0, hf);
         const float4 a = *reinterpret_cast<const float4 *>(&stat[0][q4]);
         const float4 c = *reinterpret_cast<const float4 *>(&stat[1][q4]);
-        lse_r[r0] = a.x; lse_r[r0 + 1] = a.y; lse_r[r0 + 2] = a.z; lse_r[r0 + 3] = a.w;
-        D_r[r0] = c.x; D_r[r0 + 1] = c.y; D_r[r0 + 2] = c.z; D_r[r0 + 3] = c.w;
+        sacc[r0] = a.x; sacc[r0 + 1] = a.y; sacc[r0 + 2] = a.z; sacc[r0 + 3] = a.w;
+        pacc[r0] = c.x; pacc[r0 + 1] = c.y; pacc[r0 + 2] = c.z; pacc[r0 + 3] = c.w;
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        lse_r[r] = stat[0][32 * qh + chain_slot<T>(r, hf)];
-        D_r[r] = stat[1][32 * qh + chain_slot<T>(r, hf)];
+        sacc[r] = stat[0][32 * qh + chain_slot<T>(r, hf)];
+        pacc[r] = stat[1][32 * qh + chain_slot<T>(r, hf)];
       }
     }
+    // operands are read RA chunks ahead of the products that use them, in
+    // regions fenced by scheduling barriers, so the reads' latency overlaps
+    // the products while only a short window of them is held in registers
+    typename M::Op qa[NKS], da[NKS];
+    auto read_row_ops = [&](int ks) {
+      if constexpr (E == 8) {
+        const char *at = reinterpret_cast<const char *>(Qs) + (aq ^ (32u * ks));
+        qa[ks] = *reinterpret_cast<const bf16x8 *>(at);
+        da[ks] = *reinterpret_cast<const bf16x8 *>(at + 2 * TILE);
+      } else {
+        qa[ks] = tile_op<T, D>(Qs, qrow, hf * E + ks * KS);
+        da[ks] = tile_op<T, D>(Ds, qrow, hf * E + ks * KS);
+      }
+    };
+    constexpr int RA = NKS < 4 ? NKS : 4;
+#pragma unroll
+    for (int ks = 0; ks < RA; ++ks) read_row_ops(ks);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
+      if constexpr (E == 8) __builtin_amdgcn_sched_barrier(0);
+      if (ks < PER_STEP) issue_piece(BN{}, rq, ks);
+      if (ks + RA < NKS) read_row_ops(ks + RA);
       sacc = M::run(qa[ks], kreg[ks], sacc);
       pacc = M::run(da[ks], vreg[ks], pacc);
     }
-    if constexpr (E == 8) {
-      // the first 16 LDS reads are issued before the first product, the rest
-      // one per product
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
-      for (int k = 0; k < 2 * NKS; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // full tiles (the common case) need no mask; the test is uniform
-    if (!diag && nq == kBlock && nvalid == kBlock) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(sacc[r] * p.scale_log2 + lg2 - lse_r[r]);
-        sacc[r] = pr;
-        pacc[r] = pr * (pacc[r] - D_r[r]);
-      }
-    } else {
-      const bool key_ok = key < nvalid;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * qh + chain_slot<T>(r, hf);
-        const bool ok = key_ok && ql < nq && !(diag && key > ql);
-        const float z = ok ? sacc[r] * p.scale_log2 + lg2 - lse_r[r] : -INFINITY;
-        const float pr = fast_exp2(z);
-        sacc[r] = pr;
-        pacc[r] = pr * (pacc[r] - D_r[r]);
-      }
-    }
-    // dV^T[d][key] += dO^T[d][query] P[query][key];  dK^T += Q^T dS
-    // (the transposed reads of one d tile are issued a tile ahead)
-    typename M::Op ta[2][2 * SPT];
-#pragma unroll
-    for (int kc = 0; kc < SPT; ++kc) {
-      ta[0][2 * kc] = tile_op_rows<T, D>(Ds, 32 * qh + kc * KS, 0);
-      ta[0][2 * kc + 1] = tile_op_rows<T, D>(Qs, 32 * qh + kc * KS, 0);
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      if (dt + 1 < NDT) {
-#pragma unroll
-        for (int kc = 0; kc < SPT; ++kc) {
-          ta[(dt + 1) & 1][2 * kc] = tile_op_rows<T, D>(Ds, 32 * qh + kc * KS, 32 * (dt + 1));
-          ta[(dt + 1) & 1][2 * kc + 1] = tile_op_rows<T, D>(Qs, 32 * qh + kc * KS, 32 * (dt + 1));
+    for (int k = NKS; k < PER_STEP; ++k) issue_piece(BN{}, rq, k);
+    if constexpr (E == 8) __builtin_amdgcn_sched_barrier(0);
+    // P = exp2(scale_log2 * sacc + lg2) and dS = P * pacc, in place
+    auto probabilities = [&]() {
+      // full tiles (the common case) need no mask; the test is uniform
+      if (!diag && nq == kBlock && nvalid == kBlock) {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = fast_exp2(fmaf(sacc[r], p.scale_log2, lg2));
+          sacc[r] = pr;
+          pacc[r] = pr * pacc[r];
+        }
+      } else {
+        const bool key_ok = key < nvalid;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 32 * qh + chain_slot<T>(r, hf);
+          const bool ok = key_ok && ql < nq && !(diag && key > ql);
+          const float pr = fast_exp2(ok ? fmaf(sacc[r], p.scale_log2, lg2) : -INFINITY);
+          sacc[r] = pr;
+          pacc[r] = pr * pacc[r];
         }
       }
+    };
+    // dV^T[d][key] += dO^T[d][query] P[query][key];  dK^T += Q^T dS
+    if constexpr (kSplitD) {
+      // this wave's d tiles over all four 16-row chunks: the transposed dO
+      // and Q operands (chunk c at 32 D c bytes), requested before the
+      // probabilities are formed so that their latency overlaps that work
+      constexpr int NC = 2 * SPT;
+      auto trans_op = [&](const T *X, int c, int dt) -> bf16x8 {
+        const char *tb = reinterpret_cast<const char *>(X) + c * 32 * D;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16 *)(const lds_short *)(tb + (a0 ^ (64u * dt))));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16 *)(const lds_short *)(tb + (a1 ^ (64u * dt))));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      // [cc]: chunk (cc + SPT qh) % NC, i.e. the own query half first (its
+      // products need nothing from the partner); indices stay compile-time
+      bf16x8 tdo[NACC][NC], tq[NACC][NC];
+      auto read_trans = [&](int cc0) {
+#pragma unroll
+        for (int cc = cc0; cc < cc0 + SPT; ++cc) {
+          const int c = (cc + qh * SPT) % NC;
+#pragma unroll
+          for (int dl = 0; dl < NACC; ++dl) {
+            tdo[dl][cc] = trans_op(Ds, c, qh * NACC + dl);
+            tq[dl][cc] = trans_op(Qs, c, qh * NACC + dl);
+          }
+        }
+      };
+      read_trans(0);
+      __builtin_amdgcn_sched_barrier(0);
+      probabilities();
+      bf16x8 own[2][SPT];
 #pragma unroll
       for (int kc = 0; kc < SPT; ++kc) {
-        dvacc[dt] = M::run(ta[dt & 1][2 * kc], regs_op<T>(sacc, kc * E), dvacc[dt]);
-        dkacc[dt] = M::run(ta[dt & 1][2 * kc + 1], regs_op<T>(pacc, kc * E), dkacc[dt]);
+        own[0][kc] = regs_op<T>(sacc, kc * E);
+        own[1][kc] = regs_op<T>(pacc, kc * E);
       }
-    }
-    if constexpr (E == 8) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
-      for (int k = 0; k < 2 * NDT * SPT - 4; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      for (int dl = 0; dl < NACC; ++dl)
+#pragma unroll
+        for (int kc = 0; kc < SPT; ++kc) {
+          dvacc[dl] = M::run(tdo[dl][kc], own[0][kc], dvacc[dl]);
+          dkacc[dl] = M::run(tq[dl][kc], own[1][kc], dkacc[dl]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      read_trans(SPT);  // the other half's operands, while those products run
+      // P and dS go to the partner only after this wave's transposed reads
+      // are issued: a transposed read issued while LDS writes of the same
+      // wave are in flight has returned wrong data
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kc = 0; kc < SPT; ++kc) {
+        xch[wave][kc][lane] = own[0][kc];
+        xch[wave][SPT + kc][lane] = own[1][kc];
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+      // the partner's P and dS (same keys, other query half) are in LDS
+      __builtin_amdgcn_sched_barrier(0);
+      barrier_keep_requests();
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 oth[2][SPT];
+#pragma unroll
+      for (int kc = 0; kc < SPT; ++kc) {
+        oth[0][kc] = xch[wave ^ 2][kc][lane];
+        oth[1][kc] = xch[wave ^ 2][SPT + kc][lane];
+      }
+#pragma unroll
+      for (int dl = 0; dl < NACC; ++dl)
+#pragma unroll
+        for (int kc = 0; kc < SPT; ++kc) {
+          dvacc[dl] = M::run(tdo[dl][SPT + kc], oth[0][kc], dvacc[dl]);
+          dkacc[dl] = M::run(tq[dl][SPT + kc], oth[1][kc], dkacc[dl]);
+        }
+    } else {
+      probabilities();
+      // (the transposed reads of one d tile are issued a tile ahead)
+      typename M::Op ta[2][2 * SPT];
+#pragma unroll
+      for (int kc = 0; kc < SPT; ++kc) {
+        ta[0][2 * kc] = tile_op_rows<T, D>(Ds, 32 * qh + kc * KS, 0);
+        ta[0][2 * kc + 1] = tile_op_rows<T, D>(Qs, 32 * qh + kc * KS, 0);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        if (dt + 1 < NDT) {
+#pragma unroll
+          for (int kc = 0; kc < SPT; ++kc) {
+            ta[(dt + 1) & 1][2 * kc] = tile_op_rows<T, D>(Ds, 32 * qh + kc * KS, 32 * (dt + 1));
+            ta[(dt + 1) & 1][2 * kc + 1] = tile_op_rows<T, D>(Qs, 32 * qh + kc * KS, 32 * (dt + 1));
+          }
+        }
+#pragma unroll
+        for (int kc = 0; kc < SPT; ++kc) {
+          dvacc[dt] = M::run(ta[dt & 1][2 * kc], regs_op<T>(sacc, kc * E), dvacc[dt]);
+          dkacc[dt] = M::run(ta[dt & 1][2 * kc + 1], regs_op<T>(pacc, kc * E), dkacc[dt]);
+        }
+      }
     }
     wait_vmem<NBUF == 3 ? PER_STEP : 0>();
     barrier_keep_requests();
@@ -331,37 +436,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     // are reused below
     wait_vmem<0>();
   }
-  // every wave's requests have landed (each waited for its own above)
-  // before any wave writes into the buffers
-  __syncthreads();
-
-  // Add the two query halves: waves qh = 1 hand their sums to qh = 0
-  // (dK through buffer 0, dV through buffer 1).
-  float *redk = reinterpret_cast<float *>(buf0);
-  float *redv = reinterpret_cast<float *>(buf1);
-  if (qh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        redk[(kh * NDT * 16 + dt * 16 + r) * kWave + lane] = dkacc[dt][r];
-        redv[(kh * NDT * 16 + dt * 16 + r) * kWave + lane] = dvacc[dt][r];
-      }
-  }
-  __syncthreads();
-  if (qh == 0) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dkacc[dt][r] += redk[(kh * NDT * 16 + dt * 16 + r) * kWave + lane];
-        dvacc[dt][r] += redv[(kh * NDT * 16 + dt * 16 + r) * kWave + lane];
-      }
-    // lane holds key `key`, 4 consecutive d per register group
+  // lane holds key `key`, 4 consecutive d per register group
+  auto write_out = [&](int dt0) {
     float *dk_out, *dv_out;
-    bool write = true;
     if (nseg == 1) {
-      write = key < nvalid;
+      if (key >= nvalid) return;
       dk_out = p.dk + ((ktok0 + key) * p.hkv + g) * D;
       dv_out = p.dv + ((ktok0 + key) * p.hkv + g) * D;
     } else {
@@ -369,19 +448,48 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       dk_out = part + (long)key * D;
       dv_out = part + (long)(kBlock + key) * D;
     }
-    if (write) {
+#pragma unroll
+    for (int dl = 0; dl < NACC; ++dl)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = 32 * (dt0 + dl) + d_row(4 * rg, hf);
+        *reinterpret_cast<float4 *>(dk_out + d0) =
+            make_float4(dkacc[dl][4 * rg] * p.scale, dkacc[dl][4 * rg + 1] * p.scale,
+                        dkacc[dl][4 * rg + 2] * p.scale, dkacc[dl][4 * rg + 3] * p.scale);
+        *reinterpret_cast<float4 *>(dv_out + d0) =
+            make_float4(dvacc[dl][4 * rg], dvacc[dl][4 * rg + 1], dvacc[dl][4 * rg + 2],
+                        dvacc[dl][4 * rg + 3]);
+      }
+  };
+  if constexpr (kSplitD) {
+    write_out(qh * NACC);  // each wave owns distinct d tiles of its keys
+  } else {
+    // every wave's requests have landed (each waited for its own above)
+    // before any wave writes into the buffers
+    __syncthreads();
+    // Add the two query halves: waves qh = 1 hand their sums to qh = 0
+    // (dK through buffer 0, dV through buffer 1).
+    float *redk = reinterpret_cast<float *>(buf0);
+    float *redv = reinterpret_cast<float *>(buf1);
+    if (qh == 1) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int d0 = 32 * dt + d_row(4 * rg, hf);
-          *reinterpret_cast<float4 *>(dk_out + d0) =
-              make_float4(dkacc[dt][4 * rg] * p.scale, dkacc[dt][4 * rg + 1] * p.scale,
-                          dkacc[dt][4 * rg + 2] * p.scale, dkacc[dt][4 * rg + 3] * p.scale);
-          *reinterpret_cast<float4 *>(dv_out + d0) =
-              make_float4(dvacc[dt][4 * rg], dvacc[dt][4 * rg + 1], dvacc[dt][4 * rg + 2],
-                          dvacc[dt][4 * rg + 3]);
+        for (int r = 0; r < 16; ++r) {
+          redk[(kh * NDT * 16 + dt * 16 + r) * kWave + lane] = dkacc[dt][r];
+          redv[(kh * NDT * 16 + dt * 16 + r) * kWave + lane] = dvacc[dt][r];
         }
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dkacc[dt][r] += redk[(kh * NDT * 16 + dt * 16 + r) * kWave + lane];
+          dvacc[dt][r] += redv[(kh * NDT * 16 + dt * 16 + r) * kWave + lane];
+        }
+      write_out(0);
     }
   }
 }

@@ -64,8 +64,8 @@ struct BwdParams {
   float scale, scale_log2;
   const void *dO_t;  // dO in the input dtype: dO itself, or dO16 when dO is wider
   // workspace carve-up
-  float *Lbuf;       // [hq][QB][64] lse * log2(e) per query row; +inf past a block's end
-  float *Dbuf;       // [hq][QB][64] exact D = sum_u P dP per query row; 0 past the end
+  float *Lbuf;       // [hq][QB][64] -lse / scale per query row; -inf past a block's end
+  float *Dbuf;       // [hq][QB][64] -D, D = sum_u P dP exactly, per query row; 0 past the end
   __bf16 *dO16;      // [T][hq][D] dO rounded to bf16 (bf16 inputs, fp32 dO), else NULL
   // key blocks are indexed x = kb * hkv + g (key-block major)
   int32_t *list;     // [QB*hkv][max_nb]  (query block << 8 | slot) per key block

@@ -356,8 +356,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
           dvacc[dl] = M::run(tdo[dl][kc], own[0][kc], dvacc[dl]);
           dkacc[dl] = M::run(tq[dl][kc], own[1][kc], dkacc[dl]);
         }
-      __builtin_amdgcn_sched_barrier(0);
-      read_trans(SPT);  // the other half's operands, while those products run
+      read_trans(SPT);  // the other half's operands, between those products
+#pragma unroll
+      for (int k = 0; k < 2 * NACC * SPT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+      }
       // P and dS go to the partner only after this wave's transposed reads
       // are issued: a transposed read issued while LDS writes of the same
       // wave are in flight has returned wrong data

@@ -337,7 +337,9 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
   // Exact D per query row, then dlg of each tile = sum P dP - sum_t D_t G_t.
   // Both row statistics are stored for all 64 rows of the block (rows past
   // its end: lse +inf, D 0) so the dk/dv phase can fetch them as a whole,
-  // in the form that phase seeds its products with: -lse / scale and -D.
+  // in the form that phase seeds its products with: -lse / scale and -D,
+  // for bf16 inputs as 16-byte records [hi, mid, lo, 0 x 5] of three bf16
+  // parts that add up to the value (an MFMA A operand).
   float Ex[QT];
 #pragma unroll
   for (int nt = 0; nt < QT; ++nt) {
@@ -345,8 +347,14 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
     const int ql = 32 * (nt0 + nt) + l32;
     if (hf == 0 && head_ok) {
       const long at = ((long)h * p.QB + Q) * kBlock + ql;
-      p.Dbuf[at] = ql < nq ? -Ex[nt] : 0.f;
-      p.Lbuf[at] = -lse2[nt] / p.scale_log2;
+      const float Ln = -lse2[nt] / p.scale_log2, Dn = ql < nq ? -Ex[nt] : 0.f;
+      if constexpr (sizeof(T) == 2) {
+        reinterpret_cast<bf16x8 *>(p.Lbuf)[at] = split3_bf16(Ln);
+        reinterpret_cast<bf16x8 *>(p.Dbuf)[at] = split3_bf16(Dn);
+      } else {
+        p.Lbuf[at] = Ln;
+        p.Dbuf[at] = Dn;
+      }
     }
   }
   // this wave's share of dlg per tile, one tile per lane, rows in order:

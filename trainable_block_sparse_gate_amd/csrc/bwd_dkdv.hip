@@ -26,27 +26,35 @@ namespace sas {
 // formed them (same keys) through LDS, so every wave holds half of the
 // accumulators and no final reduction is needed.  fp32 keeps all d tiles
 // per wave and adds the two query halves at the end.  The Q and dO tiles of a
-// step, and the row statistics (lse * log2 e and D, written per 64-row
-// block by the dq phase), go from global memory straight into LDS with
-// global_load_lds (no register staging).  bf16 tiles use three LDS buffers
-// and are requested two steps ahead; fp32 tiles use two, one step ahead.
-// The products that contract over query rows read their operands
-// transposed straight from the row-major tiles.
+// step go from global memory straight into LDS with global_load_lds (no
+// register staging), into two buffers, one step ahead.  The row statistics
+// (-lse / scale and -D, written per 64-row block by the dq phase) seed the
+// S and dP products: for bf16 as one extra MFMA per product whose A operand
+// is a per-row record [hi, mid, lo, 0, ...] of the value split into three
+// bf16 parts (one 16-byte load per lane, a step ahead) and whose B operand
+// is all ones, so every key column receives hi + mid + lo; for fp32 they
+// come through LDS.  A bf16 workgroup then needs exactly 80 KB of LDS and
+// at most 256 registers per lane, so two workgroups share a compute unit
+// and one's softmax overlaps the other's products.  The products that
+// contract over query rows read their operands transposed straight from
+// the row-major tiles.
 constexpr int kSegMax = 64;  // entries per segment the kernel can hold
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(
+    BwdParams p) {
   using M = Mfma<T>;
   constexpr int KS = M::K, E = M::E;
   constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
-  constexpr int NBUF = sizeof(T) == 2 ? 3 : 2;    // LDS buffers per tile kind
+  constexpr int NBUF = 2;                         // LDS buffers per tile kind
   constexpr int TILE = kBlock * D;                // elements per tile
   constexpr int VEC = 16 / (int)sizeof(T);        // elements per 16-byte chunk
   constexpr int CPR = D / VEC;                    // chunks per row
   constexpr int RPS = kWave / CPR;                // rows per 1 KB request
   constexpr int SPW = kBlock / RPS / 4;           // 1 KB requests per wave per tile
-  constexpr int PER_STEP = 2 * SPW + 1;           // requests per wave per step
   constexpr bool kSplitD = (E == 8);              // dV / dK split over d (bf16)
+  // requests per wave per step (fp32: one more, its piece of the statistics)
+  constexpr int PER_STEP = kSplitD ? 2 * SPW : 2 * SPW + 1;
   constexpr int NACC = kSplitD ? NDT / 2 : NDT;   // d tiles accumulated per wave
   static_assert(kBlock % (4 * RPS) == 0, "tile rows must split evenly over the waves");
   static_assert(2 * NDT * 16 * kWave * 4 <= 2 * TILE * (int)sizeof(T),
@@ -57,15 +65,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   // inserts no wait for them; the loop below is unrolled over the buffers.
   __shared__ __attribute__((aligned(16))) T buf0[2 * TILE];  // [Q | dO][64][D]
   __shared__ __attribute__((aligned(16))) T buf1[2 * TILE];
-  __shared__ __attribute__((aligned(16))) T buf2[NBUF == 3 ? 2 * TILE : 8];
-  // row statistics: [wave][256] per buffer; waves 0 / 1 bring -lse / scale
-  // and -D in their first 64 entries (the rest, and waves 2 and 3, are filler
-  // that keeps every wave's request count the same)
-  __shared__ __attribute__((aligned(16))) float stat0[4][4 * kBlock];
-  __shared__ __attribute__((aligned(16))) float stat1[4][4 * kBlock];
-  __shared__ __attribute__((aligned(16))) float stat2[NBUF == 3 ? 4 : 1][4 * kBlock];
-  // P and dS of each wave as bf16 B operands, lane-linear: [wave][P kc | dS kc][lane]
-  __shared__ bf16x8 xch[kSplitD ? 4 : 1][kSplitD ? 2 * SPT : 1][kWave];
+  // bf16: P and dS of each wave as B operands, lane-linear
+  // ([wave][P kc | dS kc][lane]); fp32: the row statistics of each buffer
+  // ([buffer][wave][256]: waves 0 / 1 bring -lse / scale and -D in their
+  // first 64 entries, the rest is filler that keeps every wave's request
+  // count the same)
+  constexpr int XCH_BYTES = 4 * 2 * SPT * kWave * 16, STAT_BYTES = 4 * 4 * kBlock * 4;
+  __shared__ __attribute__((aligned(16))) char aux[kSplitD ? XCH_BYTES : NBUF * STAT_BYTES];
+  static_assert(!kSplitD || 2 * 2 * TILE * sizeof(T) + XCH_BYTES <= 80 * 1024,
+                "two bf16 workgroups fit one compute unit's LDS");
 
   const int w = blockIdx.x;
   const int nx = p.hkv * p.QB;
@@ -145,19 +153,19 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 
   auto tiles_of = [&](auto B) -> T * {
     if constexpr (decltype(B)::value == 0) return buf0;
-    else if constexpr (decltype(B)::value == 1) return buf1;
-    else return buf2;
+    else return buf1;
   };
   auto stats_of = [&](auto B) -> float(*)[4 * kBlock] {
-    if constexpr (decltype(B)::value == 0) return stat0;
-    else if constexpr (decltype(B)::value == 1) return stat1;
-    else return stat2;
+    return reinterpret_cast<float(*)[4 * kBlock]>(aux + decltype(B)::value * STAT_BYTES);
+  };
+  auto xch = [&](int wv, int slot) -> bf16x8 & {
+    return reinterpret_cast<bf16x8 *>(aux)[(wv * 2 * SPT + slot) * kWave + lane];
   };
 
-  // Requests of step st into buffer B: every wave first fetches one piece
-  // of row statistics (wave 0: -lse / scale, wave 1: -D, 16 lanes' worth repeated
-  // over the wave), then SPW 1 KB pieces (RPS rows) of the Q tile and of
-  // the dO tile.  Lane l of a request lands at byte 16 l of the piece, i.e.
+  // Requests of step st into buffer B: SPW 1 KB pieces (RPS rows) of the Q
+  // tile and of the dO tile, for fp32 preceded by one piece of row
+  // statistics (wave 0: -lse / scale, wave 1: -D, 16 lanes' worth repeated
+  // over the wave).  Lane l of a request lands at byte 16 l of the piece, i.e.
   // at physical chunk l % CPR of its row; it fetches the logical chunk that
   // the swizzle puts there.  Rows past the block's end repeat its last row
   // (masked later).  Every wave issues exactly PER_STEP requests per step,
@@ -169,6 +177,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   struct Req {
     const char *qbase, *dbase;
     const float *sbase;
+    long srow;  // first statistics row of the step's block and head
     int nq;
   };
   auto step_req = [&](int st_req) -> Req {
@@ -179,20 +188,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     const int h = g * G + st % G;
     const long t0 = seq_start + (long)i * kBlock;
     const long head0 = (t0 * p.hq + h) * D;
+    const long srow = ((long)h * p.QB + qb) * kBlock;
     return Req{reinterpret_cast<const char *>(q + head0), reinterpret_cast<const char *>(dO + head0),
-               ((wave & 1) ? p.Dbuf : p.Lbuf) + ((long)h * p.QB + qb) * kBlock,
-               min(kBlock, seq_len - i * kBlock)};
+               ((wave & 1) ? p.Dbuf : p.Lbuf) + srow, srow, min(kBlock, seq_len - i * kBlock)};
   };
-  // Request k of a step into buffer B (k = 0: this wave's piece of row
-  // statistics, then SPW pieces of Q and SPW of dO); per lane a 32-bit byte
-  // offset (row, swizzled chunk) from the uniform base, so the request takes
-  // a scalar base.
+  // Request k of a step into buffer B (SPW pieces of Q, then SPW of dO;
+  // fp32: k = 0 is this wave's piece of row statistics); per lane a 32-bit
+  // byte offset (row, swizzled chunk) from the uniform base, so the request
+  // takes a scalar base.
   auto issue_piece = [&](auto B, const Req &r, int k) {
-    if (k == 0) {
-      load_lds16(r.sbase + 4 * (lane % 16), &stats_of(B)[wave][0]);
-      return;
+    if constexpr (!kSplitD) {
+      if (k == 0) {
+        load_lds16(r.sbase + 4 * (lane % 16), &stats_of(B)[wave][0]);
+        return;
+      }
+      k -= 1;
     }
-    const int tk = (k - 1) / SPW, sg = (k - 1) % SPW;
+    const int tk = k / SPW, sg = k % SPW;
     const unsigned rstride = (unsigned)(p.hq * D * (int)sizeof(T));
     const int piece = wave * SPW + sg;
     const int rw = piece * RPS + lane / CPR;
@@ -201,14 +213,30 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     const unsigned off = (unsigned)rr * rstride + (unsigned)(c * 16);
     load_lds16((tk == 0 ? r.qbase : r.dbase) + off, tiles_of(B) + tk * TILE + piece * RPS * D);
   };
+  // bf16: the statistics of a step as MFMA A operands, from the records the
+  // dq phase writes ([hi, mid, lo, 0 x 5] in bf16 per query row, 16 bytes):
+  // this lane's query row, one load per statistic; with B all ones in the
+  // lower half-wave (zero in the upper) the product puts hi + mid + lo into
+  // every key column.
+  bf16x8 stl = {}, stdd = {};
+  const unsigned ones_w = hf == 0 ? 0x3F803F80u : 0u;  // two bf16 ones, or zeros
+  // first query row of this lane's rows (register r holds row qlb0 + an
+  // offset fixed by r)
+  const int qlb0 = 32 * qh + chain_slot<T>(0, hf);
+  auto load_stats = [&](const Req &r) {
+    if constexpr (kSplitD) {
+      stl = reinterpret_cast<const bf16x8 *>(p.Lbuf)[r.srow + qrow];
+      stdd = reinterpret_cast<const bf16x8 *>(p.Dbuf)[r.srow + qrow];
+    }
+  };
   auto issue_step = [&](auto B, int st_req) {
     const Req r = step_req(st_req);
+    load_stats(r);
 #pragma unroll
     for (int k = 0; k < PER_STEP; ++k) issue_piece(B, r, k);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
 
   // One step from buffer B: request the step NBUF - 1 ahead into the buffer
   // the previous step read, compute, wait until this wave's requests of the
@@ -219,8 +247,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     // The offsets are opaque to the compiler from here on, so the per-chunk
     // offsets are formed in each step (one XOR each) rather than all held in
     // registers across the loop.
-    unsigned aq = oq, a0 = ot0, a1 = ot1;
-    asm volatile("" : "+v"(aq), "+v"(a0), "+v"(a1));
+    unsigned aq = oq, a0 = ot0, a1 = ot1, ow = ones_w;
+    int qlb = qlb0;
+    asm volatile("" : "+v"(aq), "+v"(a0), "+v"(a1), "+v"(ow), "+v"(qlb));
     // the requests of step st + NBUF - 1 go out one per product pair below:
     // issued back to back they would hold up this wave's products while the
     // address unit works through every wave's requests
@@ -235,27 +264,25 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     const bool diag = (i == j);
     const T *Qs = tiles_of(B);
     const T *Ds = Qs + TILE;
-    const float(*stat)[4 * kBlock] = stats_of(B);
 
     // S[query][key] and dP[query][key] for 32 queries x this wave's 32 keys;
     // query rows loaded in chain order so P and dS feed the next products.
     // The products start from the row statistics, so that after them
     //   sacc = S - lse / scale   and   pacc = dP - D,
     // and P = exp2(scale_log2 * sacc + lg2), dS = P * pacc take no further
-    // per-row term.  This lane's 16 rows, in register order, come in four
-    // runs of 4 consecutive rows: their statistics are read as float4s
-    // (bf16 chain order; the fp32 order interleaves, so it reads one by one).
+    // per-row term.
     f32x16 sacc, pacc;
-    if constexpr (E == 8) {
-#pragma unroll
-      for (int r0 = 0; r0 < 16; r0 += 4) {
-        const int q4 = 32 * qh + chain_slot<T>(r0, hf);
-        const float4 a = *reinterpret_cast<const float4 *>(&stat[0][q4]);
-        const float4 c = *reinterpret_cast<const float4 *>(&stat[1][q4]);
-        sacc[r0] = a.x; sacc[r0 + 1] = a.y; sacc[r0 + 2] = a.z; sacc[r0 + 3] = a.w;
-        pacc[r0] = c.x; pacc[r0 + 1] = c.y; pacc[r0 + 2] = c.z; pacc[r0 + 3] = c.w;
-      }
+    if constexpr (kSplitD) {
+      // one product per statistic (see load_stats); the registers are then
+      // free for the next step's statistics, requested right away
+      typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4v{ow, ow, ow, ow});
+      sacc = M::run(stl, ones, f32x16{});
+      pacc = M::run(stdd, ones, f32x16{});
+      load_stats(rq);
     } else {
+      // this lane's 16 rows, in register order, read one by one
+      const float(*stat)[4 * kBlock] = stats_of(B);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sacc[r] = stat[0][32 * qh + chain_slot<T>(r, hf)];
@@ -276,7 +303,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         da[ks] = tile_op<T, D>(Ds, qrow, hf * E + ks * KS);
       }
     };
-    constexpr int RA = NKS < 4 ? NKS : 4;
+    constexpr int RA = NKS < 2 ? NKS : 2;
 #pragma unroll
     for (int ks = 0; ks < RA; ++ks) read_row_ops(ks);
 #pragma unroll
@@ -301,11 +328,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
           pacc[r] = pr * pacc[r];
         }
       } else {
+        // row of register r: qlb + o, o fixed by r
         const bool key_ok = key < nvalid;
+        const int kq = key - qlb;
   #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ql = 32 * qh + chain_slot<T>(r, hf);
-          const bool ok = key_ok && ql < nq && !(diag && key > ql);
+          const int o = chain_slot<T>(r, 0) - chain_slot<T>(0, 0);
+          const bool ok = key_ok && qlb < nq - o && !(diag && kq > o);
           const float pr = fast_exp2(ok ? fmaf(sacc[r], p.scale_log2, lg2) : -INFINITY);
           sacc[r] = pr;
           pacc[r] = pr * pacc[r];
@@ -340,9 +369,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
           }
         }
       };
-      read_trans(0);
-      __builtin_amdgcn_sched_barrier(0);
       probabilities();
+      read_trans(0);
       bf16x8 own[2][SPT];
 #pragma unroll
       for (int kc = 0; kc < SPT; ++kc) {
@@ -368,8 +396,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kc = 0; kc < SPT; ++kc) {
-        xch[wave][kc][lane] = own[0][kc];
-        xch[wave][SPT + kc][lane] = own[1][kc];
+        xch(wave, kc) = own[0][kc];
+        xch(wave, SPT + kc) = own[1][kc];
       }
       // the partner's P and dS (same keys, other query half) are in LDS
       __builtin_amdgcn_sched_barrier(0);
@@ -378,8 +406,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       bf16x8 oth[2][SPT];
 #pragma unroll
       for (int kc = 0; kc < SPT; ++kc) {
-        oth[0][kc] = xch[wave ^ 2][kc][lane];
-        oth[1][kc] = xch[wave ^ 2][SPT + kc][lane];
+        oth[0][kc] = xch(wave ^ 2, kc);
+        oth[1][kc] = xch(wave ^ 2, SPT + kc);
       }
 #pragma unroll
       for (int dl = 0; dl < NACC; ++dl)
@@ -413,28 +441,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
-    wait_vmem<NBUF == 3 ? PER_STEP : 0>();
+    wait_vmem<0>();
     barrier_keep_requests();
   };
 
-  // Prologue: the first NBUF - 1 steps.  Waiting for all of them (not just
-  // step 0) -- and for K and V -- leaves no request in flight at the loop
-  // entry, which keeps the compiler's tracking of which buffer a request
-  // targets exact in the loop.
+  // Prologue: step 0.  Waiting for it -- and for K and V -- leaves no
+  // request in flight at the loop entry, which keeps the compiler's tracking
+  // of which buffer a request targets exact in the loop.
   if (nsteps > 0) {
     issue_step(I0{}, 0);
-    if constexpr (NBUF == 3) issue_step(I1{}, 1);
     wait_vmem<0>();
     barrier_keep_requests();
     for (int st = 0; st < nsteps; st += NBUF) {
       step(I0{}, st);
-      if (st + 1 < nsteps) {
-        step(I1{}, st + 1);
-        // nested, so that no path reaches this step while the requests of
-        // the skipped one (into the buffer it reads) are still counted
-        if constexpr (NBUF == 3)
-          if (st + 2 < nsteps) step(I2{}, st + 2);
-      }
+      if (st + 1 < nsteps) step(I1{}, st + 1);
     }
     // the last requests (re-fetches past the end) land before the buffers
     // are reused below

@@ -222,8 +222,8 @@ BwdLayout bwd_layout(const sas_problem *p, int max_nb) {
   L.U = (int)((nx * p->budget_blocks + kSeg - 1) / kSeg + nx);
   size_t off = 0;
   const size_t rows = (size_t)p->hq * p->total_qblocks * 64;  // per-block padded rows
-  L.off_L = off;        off = align256(off + sizeof(float) * rows);
-  L.off_D = off;        off = align256(off + sizeof(float) * rows);
+  L.off_L = off;        off = align256(off + 16 * rows);  // 16-byte row records
+  L.off_D = off;        off = align256(off + 16 * rows);
   L.off_dO16 = off;     // bf16 copy of an fp32 dO for the dk/dv phase
   if (p->dtype == SAS_BF16 && p->out_dtype == SAS_F32)
     off = align256(off + 2 * (size_t)p->total_tokens * p->hq * p->head_dim);

@@ -132,6 +132,21 @@ __device__ inline void barrier_keep_requests() {
   __asm__ volatile("" ::: "memory");
 }
 
+// x as three bf16 parts [hi, mid, lo, 0, 0, 0, 0, 0] with hi + mid + lo = x
+// to within 2^-24 relative (each part is the rounding of what the previous
+// ones leave; the differences are exact in fp32).  Infinite x gives
+// [x, 0, ...].
+__device__ inline bf16x8 split3_bf16(float x) {
+  bf16x8 r = {};
+  const __bf16 hi = (__bf16)x;
+  const float r1 = __builtin_isfinite(x) ? x - (float)hi : 0.f;
+  const __bf16 mid = (__bf16)r1;
+  r[0] = hi;
+  r[1] = mid;
+  r[2] = (__bf16)(r1 - (float)mid);
+  return r;
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform value:
 // threadIdx.x / 64 is the same in every lane, but only readfirstlane lets
 // the compiler know, so that what depends on it (head indices, loop

@@ -64,8 +64,12 @@ struct BwdParams {
   float scale, scale_log2;
   const void *dO_t;  // dO in the input dtype: dO itself, or dO16 when dO is wider
   // workspace carve-up
-  float *Lbuf;       // [hq][QB][64] -lse / scale per query row; -inf past a block's end
-  float *Dbuf;       // [hq][QB][64] -D, D = sum_u P dP exactly, per query row; 0 past the end
+  // [hq][QB][64] per query row, 16 bytes each: -lse / scale (-inf past a
+  // block's end) and -D (D = sum_u P dP exactly; 0 past the end); fp32 inputs
+  // use the first 4 bytes as a float, bf16 inputs a [hi, mid, lo, 0 x 5]
+  // bf16 record of the value
+  float *Lbuf;
+  float *Dbuf;
   __bf16 *dO16;      // [T][hq][D] dO rounded to bf16 (bf16 inputs, fp32 dO), else NULL
   // key blocks are indexed x = kb * hkv + g (key-block major)
   int32_t *list;     // [QB*hkv][max_nb]  (query block << 8 | slot) per key block

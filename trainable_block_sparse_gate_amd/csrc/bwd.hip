@@ -55,12 +55,11 @@ __global__ __launch_bounds__(256) void bwd_csr_kernel(BwdParams p) {
     const int i = i0 + lane;
     int slot = -1;
     if (i < nb) {
+      // a block appears at most once in a row's kept list; the slots are
+      // read with no early exit, so their loads issue back to back
       const int32_t *sel = p.sel_idx + ((long)g * p.QB + q0 + i) * p.Kb;
-      for (int sl = 0; sl < p.Kb; ++sl)
-        if (sel[sl] == j) {
-          slot = sl;
-          break;
-        }
+#pragma unroll 16
+      for (int sl = 0; sl < p.Kb; ++sl) slot = sel[sl] == j ? sl : slot;
     }
     const uint64_t m = __ballot(slot >= 0);
     if (slot >= 0) {

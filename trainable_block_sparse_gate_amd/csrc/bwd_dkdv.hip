@@ -529,16 +529,29 @@ __device__ void reduce_key_block(const BwdParams &p, int x, int nseg) {
   const long ktok0 = seq_start + (long)j * kBlock;
   const int n = kBlock * D;
   const float *part0 = p.partial + (long)p.seg_off[x] * 2 * n;
-  for (int e = threadIdx.x * 4; e < 2 * n; e += 256 * 4) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sg = 0; sg < nseg; ++sg) {
-      const float4 v = *reinterpret_cast<const float4 *>(part0 + (long)sg * 2 * n + e);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  // each thread owns NV float4s of the 2 n sums; a segment's NV loads are
+  // all issued before any is added
+  constexpr int NV = 2 * kBlock * D / (256 * 4);
+  float4 acc[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sg = 0; sg < nseg; ++sg) {
+    float4 v[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      v[u] = *reinterpret_cast<const float4 *>(part0 + (long)sg * 2 * n + 4 * (threadIdx.x + 256 * u));
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      acc[u].x += v[u].x; acc[u].y += v[u].y; acc[u].z += v[u].z; acc[u].w += v[u].w;
     }
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int e = 4 * (threadIdx.x + 256 * u);
     const int which = e / n, kk2 = (e % n) / D, d = e % D;
     if (kk2 >= nvalid) continue;
     float *out = (which == 0 ? p.dk : p.dv) + ((ktok0 + kk2) * p.hkv + g) * D + d;
-    *reinterpret_cast<float4 *>(out) = acc;
+    *reinterpret_cast<float4 *>(out) = acc[u];
   }
 }
 

@@ -16,8 +16,10 @@ import numpy as np
 
 from .build import LIB, build
 
-GATE_HIST = 0  # softmax over the history blocks; current block log-gate 0
-GATE_ALL = 1   # softmax over history and current block
+GATE_HIST = 0     # softmax over the history blocks; current block log-gate 0
+GATE_ALL = 1      # softmax over history and current block
+GATE_SIGMOID = 2  # independent gates sigmoid(s); current block log-gate 0
+GATE_RAW = 3      # the raw logit as the log-gate; current block log-gate 0
 
 _lib = None
 

@@ -27,6 +27,11 @@
  *   - GATE_HIST (mode 0, the pages' reading): g = softmax over the history
  *     blocks j < i only, the current block keeps log g = 0.
  *     GATE_ALL (mode 1): softmax over j <= i, current block included.
+ *     The activation ablations of [P] section 4 / [R] 3-3, with the current
+ *     block unbiased in both: GATE_SIGMOID (mode 2): independent gates
+ *     g_j = sigmoid(s_j), log g_j = -log(1 + exp(-s_j)); GATE_RAW (mode 3):
+ *     the unnormalised logit injected as is, log g_j = s_j.  These have no
+ *     normaliser; their gate_lse output is 0.
  *   - the normaliser runs over every causal history candidate; the Top-K then
  *     keeps a subset, so kept gates sum to at most 1.
  *   - budget Kb counts the current block; k = min(Kb - 1, i) history blocks.
@@ -59,6 +64,15 @@
 
 #define ORACLE_GATE_HIST 0
 #define ORACLE_GATE_ALL 1
+#define ORACLE_GATE_SIGMOID 2
+#define ORACLE_GATE_RAW 3
+
+/* log sigmoid(x) = -log(1 + exp(-x)), written so that neither branch
+ * overflows: for x < 0 it is x - log(1 + exp(x)). */
+static double log_sigmoid(double x) {
+  if (x >= 0.0) return -log1p(exp(-x));
+  return x - log1p(exp(x));
+}
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -89,9 +103,10 @@ int sas_oracle_num_qblocks(int nseq, const int32_t *cu, int blk) {
  */
 static void gate_row(const float *s, int i, int Kb, int mode, int32_t *idx, double *lg,
                      double *lse_out, unsigned char *chosen) {
+  int independent = (mode == ORACLE_GATE_SIGMOID || mode == ORACLE_GATE_RAW);
   int nn = (mode == ORACLE_GATE_ALL) ? i + 1 : i; /* size of the normaliser set */
-  double lse = -INFINITY;
-  if (nn > 0) {
+  double lse = independent ? 0.0 : -INFINITY;
+  if (nn > 0 && !independent) {
     double m = -INFINITY;
     for (int j = 0; j < nn; ++j)
       if ((double)s[j] > m) m = (double)s[j];
@@ -119,7 +134,12 @@ static void gate_row(const float *s, int i, int Kb, int mode, int32_t *idx, doub
   for (int j = 0; j < i; ++j) {
     if (!chosen[j]) continue;
     idx[pos] = j;
-    lg[pos] = (lse == -INFINITY) ? -INFINITY : (double)s[j] - lse;
+    if (mode == ORACLE_GATE_SIGMOID)
+      lg[pos] = log_sigmoid((double)s[j]);
+    else if (mode == ORACLE_GATE_RAW)
+      lg[pos] = (double)s[j];
+    else
+      lg[pos] = (lse == -INFINITY) ? -INFINITY : (double)s[j] - lse;
     ++pos;
   }
   idx[pos] = i;
@@ -402,6 +422,17 @@ int sas_oracle_gate_bwd(int nseq, const int32_t *cu, int blk, int hkv, int Kb, i
     const float *sr = logits + r * ld;
     double *out = dlogits + r * ld;
     for (long c = 0; c < ld; ++c) out[c] = 0.0;
+    if (mode == ORACLE_GATE_SIGMOID || mode == ORACLE_GATE_RAW) {
+      /* independent gates: d s_j = d log g_j * (d log g_j / d s_j), kept
+       * history blocks only; d log sigmoid(s) / ds = sigmoid(-s) */
+      for (int sl = 0; sl < Kb; ++sl) {
+        int j = sel_idx[r * Kb + sl];
+        if (j < 0 || j >= i) continue;
+        double dl = dlg[r * Kb + sl];
+        out[j] += (mode == ORACLE_GATE_RAW) ? dl : dl / (1.0 + exp((double)sr[j]));
+      }
+      continue;
+    }
     int nn = (mode == ORACLE_GATE_ALL) ? i + 1 : i;
     if (nn == 0) continue;
     double m = -INFINITY;

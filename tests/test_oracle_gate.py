@@ -53,7 +53,8 @@ def _case(lengths, hkv, ld_extra=0, seed=0, blk=4, sigma=2.0, kind="normal"):
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "zeros_signed", "neginf"])
 @pytest.mark.parametrize("Kb", [1, 2, 3, 5, 40])
-@pytest.mark.parametrize("mode", [oracle.GATE_HIST, oracle.GATE_ALL])
+@pytest.mark.parametrize("mode", [oracle.GATE_HIST, oracle.GATE_ALL, oracle.GATE_SIGMOID,
+                                  oracle.GATE_RAW])
 def test_topk_matches_brute_force(kind, Kb, mode):
     lengths = [37, 4, 64, 1, 23]
     blk = 4
@@ -164,3 +165,35 @@ def test_workload_logits_layout_and_boost():
     for s, per_head in enumerate(case.boosted):
         for cols in per_head:
             assert len(cols) == 1
+
+
+@pytest.mark.parametrize("mode", [oracle.GATE_SIGMOID, oracle.GATE_RAW])
+def test_independent_activations_match_closed_forms(mode):
+    """The activation ablations (paper text section 4, review 3-3): kept
+    history blocks get log sigmoid(s) or s itself, the current block log-gate
+    0, padding -inf; there is no normaliser (gate_lse 0).  The expected values
+    are written here from the definitions with the math module."""
+    lengths = [37, 23]
+    blk, Kb = 4, 4
+    cu, lg, QB = _case(lengths, 2, ld_extra=2, seed=11 + mode, blk=blk)
+    lg[0, 5, 1] = -np.inf  # an infinite logit: gate 0 (log -inf) in both modes
+    idx, sl, lse = oracle.gate_topk(cu, lg, 2, Kb, mode, blk=blk)
+    assert np.all(lse == 0.0)
+    for g in range(2):
+        for Q, (s, i) in enumerate(rows_of(cu, blk)):
+            k = min(Kb - 1, i)
+            for sl_i in range(Kb):
+                j = int(idx[g, Q, sl_i])
+                if sl_i < k:
+                    x = float(lg[g, Q, j])
+                    if mode == oracle.GATE_RAW:
+                        want = x
+                    elif x == -math.inf:
+                        want = -math.inf
+                    else:
+                        want = -math.log(1.0 + math.exp(-x))
+                    assert sl[g, Q, sl_i] == pytest.approx(want, rel=1e-14, abs=1e-14)
+                elif sl_i == k:
+                    assert j == i and sl[g, Q, sl_i] == 0.0
+                else:
+                    assert j == -1 and sl[g, Q, sl_i] == -math.inf

@@ -16,7 +16,8 @@ def grid_logits(shape, seed, sigma=2.0):
     return (np.round(x / H) * H).astype(np.float32)
 
 
-@pytest.mark.parametrize("mode", [oracle.GATE_HIST, oracle.GATE_ALL])
+@pytest.mark.parametrize("mode", [oracle.GATE_HIST, oracle.GATE_ALL, oracle.GATE_SIGMOID,
+                                  oracle.GATE_RAW])
 def test_gate_bwd_matches_finite_differences(mode):
     blk, hkv, Kb = 4, 2, 3
     lengths = [30, 13]
@@ -41,6 +42,7 @@ def test_gate_bwd_matches_finite_differences(mode):
     for g in range(hkv):
         for Q, (s, i) in enumerate(rows):
             ncols = i + 1 if mode == oracle.GATE_ALL else i
+            kept = set(int(j) for j in idx[g, Q] if 0 <= j < i)
             for m in range(8):
                 xp, xm = lg.copy(), lg.copy()
                 xp[g, Q, m] += np.float32(H)
@@ -49,8 +51,11 @@ def test_gate_bwd_matches_finite_differences(mode):
                 assert abs(fd - d_logits[g, Q, m]) < 2e-6, (g, Q, m, fd, d_logits[g, Q, m])
                 if m >= ncols:
                     assert d_logits[g, Q, m] == 0.0
-    # shift invariance of the gate => the gradient of every row sums to zero
-    assert np.max(np.abs(d_logits.sum(-1))) < 1e-12
+                if mode in (oracle.GATE_SIGMOID, oracle.GATE_RAW) and m not in kept:
+                    assert d_logits[g, Q, m] == 0.0  # independent gates: kept blocks only
+    if mode in (oracle.GATE_HIST, oracle.GATE_ALL):
+        # shift invariance of the gate => the gradient of every row sums to zero
+        assert np.max(np.abs(d_logits.sum(-1))) < 1e-12
 
 
 def test_end_to_end_logit_gradient_through_attention():

@@ -70,12 +70,18 @@ typedef int32_t sas_status;
 #define SAS_BF16 0
 #define SAS_F32 1
 
-/* Gate normaliser.  SAS_GATE_HIST is the pages' reading: softmax over the
+/* Gate activation.  SAS_GATE_HIST is the pages' method: softmax over the
  * history blocks j < i, the current block keeps log gate 0 (review section
  * 2-1, g0 = 1; paper text: the normaliser is not applied to the current
- * block).  SAS_GATE_ALL normalises over j <= i, the current block included. */
+ * block).  SAS_GATE_ALL normalises over j <= i, the current block included.
+ * The activation ablations (paper text section 4; review 3-3), the current
+ * block unbiased in both: SAS_GATE_SIGMOID gives independent gates
+ * g_j = sigmoid(s_j), SAS_GATE_RAW injects the raw logit (log g_j = s_j);
+ * they have no normaliser and write gate_lse = 0. */
 #define SAS_GATE_HIST 0
 #define SAS_GATE_ALL 1
+#define SAS_GATE_SIGMOID 2
+#define SAS_GATE_RAW 3
 
 #define SAS_KV_CONTIGUOUS 0 /* cache [batch][hkv][max_seqlen][head_dim] */
 #define SAS_KV_PAGED 1      /* cache [num_pages][hkv][64][head_dim] + page table */
@@ -123,7 +129,7 @@ typedef struct sas_decode_problem {
  *   logits      [hkv][total_qblocks][ld] fp32: column j = key block j of the
  *               row's own sequence; only columns j < i (and j = i in
  *               SAS_GATE_ALL) are read.  ld >= the longest sequence's blocks.
- *   gate_mode   SAS_GATE_HIST or SAS_GATE_ALL.
+ *   gate_mode   SAS_GATE_HIST, SAS_GATE_ALL, SAS_GATE_SIGMOID or SAS_GATE_RAW.
  *   sel_idx     out [rows][Kb] int32; sel_loggate out [rows][Kb] fp32;
  *   gate_lse    out [rows] fp32: log of the gate normaliser (-inf when empty).
  * Top-K compares the stored fp32 logits: larger first, lower index on ties,
@@ -186,7 +192,10 @@ sas_status sas_bwd_dkdv(const sas_problem *p, const void *q, const void *k, cons
  * is shared by all history blocks):
  *   d s_m = [m kept] dlg_m - exp(s_m - gate_lse) * sum over kept j of dlg_j
  * for m in the normaliser set; other columns (up to ld) are written 0.
- * In SAS_GATE_HIST the current block's slot carries no gradient.
+ * In SAS_GATE_HIST the current block's slot carries no gradient.  With
+ * independent gates only kept history blocks get one:
+ *   SAS_GATE_SIGMOID  d s_m = [m kept] dlg_m * sigmoid(-s_m)
+ *   SAS_GATE_RAW      d s_m = [m kept] dlg_m   (gate_lse is not read)
  *   d_logits out [hkv][total_qblocks][ld] fp32.
  */
 sas_status sas_gate_bwd(const sas_problem *p, const float *logits, int64_t ld,

@@ -119,6 +119,21 @@ def test_bwd_all_softmax_mode():
     check_bwd(case, prob, dv, gpu, ref, mode=sas.GATE_ALL)
 
 
+@pytest.mark.parametrize("mode", [sas.GATE_SIGMOID, sas.GATE_RAW])
+@pytest.mark.parametrize("name", ["ragged_g4_d128", "g2_d64_f32"])
+def test_activation_ablations_fwd_bwd(name, mode):
+    """Independent sigmoid gates and raw-logit injection (the pages'
+    activation ablation): gate, forward, backward and gate backward."""
+    case, prob, dv, gpu, ref = run_case(name, mode=mode)
+    check_bwd(case, prob, dv, gpu, ref, mode=mode)
+
+
+def test_sigmoid_gate_neg_inf_logits():
+    case, prob, dv, gpu, ref = run_case("ragged_g4_d128", mode=sas.GATE_SIGMOID,
+                                        neg_inf_frac=0.3)
+    check_bwd(case, prob, dv, gpu, ref, mode=sas.GATE_SIGMOID)
+
+
 def test_bwd_neg_inf_logits():
     case, prob, dv, gpu, ref = run_case("ragged_g4_d128", neg_inf_frac=0.3)
     check_bwd(case, prob, dv, gpu, ref)

@@ -5,6 +5,9 @@
 //   lse      = log sum_{j in N} exp(s_j),  N = {j < i} (or {j <= i})
 //   log g_j  = s_j - lse,  the current block keeps log g = 0 in the first mode
 //   kept     = the min(Kb-1, i) largest s_j over j < i, lower j on ties.
+// The activation ablations (paper text section 4; review 3-3) replace the
+// normalised log gate of the kept history blocks by log sigmoid(s_j)
+// (mode 2) or s_j itself (mode 3); they have no normaliser.
 // The Top-K threshold is found with an exact radix select over 32-bit
 // order-preserving keys of the fp32 scores (4 passes of 8 bits, LDS
 // histograms); the kept blocks are then emitted in index order with a
@@ -12,7 +15,10 @@
 //
 // Backward (review section 2-1; paper text, ablation results, where the
 // normaliser is shared by every history block):
-//   d s_m = [m kept] dlg_m - exp(s_m - lse) * sum over kept j of dlg_j.
+//   d s_m = [m kept] dlg_m - exp(s_m - lse) * sum over kept j of dlg_j;
+// with independent gates d s_m = [m kept] dlg_m * (d log g_m / d s_m).
+
+constexpr int kGateSigmoid = 2, kGateRaw = 3;  // the activation ablations
 #include "sas_device.h"
 #include "sas_launch.h"
 
@@ -93,18 +99,22 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
   int i;
   row_geometry(p, r, i);
   const float *srow = p.scores + (long)r * p.ld;
+  const bool independent = p.mode == kGateSigmoid || p.mode == kGateRaw;
   const int nn = (p.mode == 1) ? i + 1 : i;
   const int k = min(p.Kb - 1, i);
 
-  // Normaliser.
-  float mx = -INFINITY;
-  for (int j = tid; j < nn; j += kGateThreads) mx = fmaxf(mx, srow[j]);
-  mx = block_max(mx, red);
-  float sum = 0.f;
-  if (mx != -INFINITY)
-    for (int j = tid; j < nn; j += kGateThreads) sum += expf(srow[j] - mx);
-  sum = block_sum(sum, red);
-  const float lse = (nn == 0 || mx == -INFINITY) ? -INFINITY : mx + logf(sum);
+  // Normaliser (independent gates have none; the uniform test skips it).
+  float lse = 0.f;
+  if (!independent) {
+    float mx = -INFINITY;
+    for (int j = tid; j < nn; j += kGateThreads) mx = fmaxf(mx, srow[j]);
+    mx = block_max(mx, red);
+    float sum = 0.f;
+    if (mx != -INFINITY)
+      for (int j = tid; j < nn; j += kGateThreads) sum += expf(srow[j] - mx);
+    sum = block_sum(sum, red);
+    lse = (nn == 0 || mx == -INFINITY) ? -INFINITY : mx + logf(sum);
+  }
 
   // Exact k-th largest key (radix select), unless every candidate is kept.
   const bool keep_all = (k == i);
@@ -170,7 +180,12 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
       const int pos = base + block_scan_flag(take, take_tot, cnt);
       if (take) {
         oidx[pos] = j;
-        olg[pos] = (lse == -INFINITY) ? -INFINITY : sj - lse;
+        if (p.mode == kGateSigmoid)  // log sigmoid(s) = min(s, 0) - log(1 + exp(-|s|))
+          olg[pos] = fminf(sj, 0.f) - log1pf(expf(-fabsf(sj)));
+        else if (p.mode == kGateRaw)
+          olg[pos] = sj;
+        else
+          olg[pos] = (lse == -INFINITY) ? -INFINITY : sj - lse;
       }
       base += take_tot;
       eq_base += eq_tot;
@@ -203,8 +218,9 @@ __global__ __launch_bounds__(kGateThreads) void gate_bwd_kernel(GateBwdParams p)
   const int Q = r % p.QB;
   const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, Q);
   const int i = Q - p.cu_qblocks[s];
+  const bool independent = p.mode == kGateSigmoid || p.mode == kGateRaw;
   const int nn = (p.mode == 1) ? i + 1 : i;
-  const float lse = p.gate_lse[r];
+  const float lse = independent ? 0.f : p.gate_lse[r];
   const int32_t *sel = p.sel_idx + (long)r * p.Kb;
   const float *dlg = p.dlg + (long)r * p.Kb;
   if (tid == 0) {
@@ -229,7 +245,20 @@ __global__ __launch_bounds__(kGateThreads) void gate_bwd_kernel(GateBwdParams p)
   float *out = p.dlogits + (long)r * p.ld;
   for (long c = tid; c < p.ld; c += kGateThreads) {
     float val = 0.f;
-    if (c < nn && lse != -INFINITY) {
+    if (independent) {
+      // kept history blocks only; d log sigmoid(s) / ds = sigmoid(-s)
+      if (c < i) {
+        int lo = 0, hi = n - 1;
+        while (lo <= hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_j[mid] == c) {
+            val = p.mode == kGateRaw ? s_d[mid] : s_d[mid] / (1.f + expf(srow[c]));
+            break;
+          }
+          if (s_j[mid] < c) lo = mid + 1; else hi = mid - 1;
+        }
+      }
+    } else if (c < nn && lse != -INFINITY) {
       val = -expf(srow[c] - lse) * tot;
       int lo = 0, hi = n - 1;
       while (lo <= hi) {

@@ -179,3 +179,46 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a[:4], b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_full_scope_zero_gates_is_dense_causal_attention(dtype):
+    """Full training scope (every history block kept, paper text section 4)
+    with log g = 0 is plain causal attention (review 1-1): the GPU forward
+    and backward against torch's float64 scaled-dot-product attention on the
+    CPU, and against the oracle."""
+    import torch
+    from tests.dense_reference import sdpa_sequence
+    lengths, hq, hkv, d = [300, 77], 4, 2, 64
+    Kb = 6  # more than the 5 blocks of the longest sequence: nothing is dropped
+    case = wl.make_varlen("full_scope", lengths, hq, hkv, d, Kb, dtype=dtype, logit_sigma=2.0,
+                          workload_id=70)
+    prob = sas.Varlen(lengths, hq, hkv, d, Kb, dtype=dtype, out_dtype=dtype)
+    dv = case_to_device(case)
+    say(f"[full scope zero gates {dtype}]")
+    sel, lg, _ = sas.gate_topk(prob, dv["logits"])
+    lg = torch.where(sel >= 0, torch.zeros_like(lg), lg)  # log g = 0 on every kept block
+    o, lse = sas.fwd(prob, dv["q"], dv["k"], dv["v"], sel, lg)
+    dq, dk, dvv, dlg = sas.bwd(prob, dv["q"], dv["k"], dv["v"], o, dv["dO"], lse, sel, lg)
+    torch.cuda.synchronize()
+    idx = sel.cpu().numpy()
+    for g in range(hkv):
+        for Q in range(idx.shape[1]):
+            kept = [int(j) for j in idx[g, Q] if j >= 0]
+            assert kept == list(range(len(kept))), "full scope keeps every block up to the current"
+    tol = TOL[dtype]
+    cu = case.cu_seqlens
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        L = b - a
+        M = np.where(np.triu(np.ones((L, L), bool), 1), -np.inf, 0.0)[None].repeat(hkv, 0)
+        ref = sdpa_sequence(case.q[a:b], case.k[a:b], case.v[a:b], M, case.scale,
+                            dO=case.dO[a:b])
+        assert_close(f"o[{s}]", o.float().cpu().numpy()[a:b], ref["o"], tol)
+        assert_close(f"lse[{s}]", lse.cpu().numpy()[:, a:b], ref["lse"], tol)
+        assert_close(f"dq[{s}]", dq.cpu().numpy()[a:b], ref["dq"], tol)
+        assert_close(f"dk[{s}]", dk.cpu().numpy()[a:b], ref["dk"], tol)
+        assert_close(f"dv[{s}]", dvv.cpu().numpy()[a:b], ref["dv"], tol)
+    rdq, rdk, rdv, rdlg = oracle.bwd(cu, case.q, case.k, case.v, case.dO, idx,
+                                     lg.cpu().numpy().astype(np.float64), Kb, case.scale)
+    assert_close("dlg", dlg.cpu().numpy(), rdlg, tol)

@@ -20,6 +20,7 @@ GATE_HIST = 0     # softmax over the history blocks; current block log-gate 0
 GATE_ALL = 1      # softmax over history and current block
 GATE_SIGMOID = 2  # independent gates sigmoid(s); current block log-gate 0
 GATE_RAW = 3      # the raw logit as the log-gate; current block log-gate 0
+GATE_STE = 4      # hard gate 1 forward, soft-softmax straight-through backward
 
 _lib = None
 

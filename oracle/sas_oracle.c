@@ -32,6 +32,14 @@
  *     g_j = sigmoid(s_j), log g_j = -log(1 + exp(-s_j)); GATE_RAW (mode 3):
  *     the unnormalised logit injected as is, log g_j = s_j.  These have no
  *     normaliser; their gate_lse output is 0.
+ *     GATE_STE (mode 4), the ranking-preservation ablation: a hard gate
+ *     (log g = 0, gate 1, on every kept block) in the forward, with the
+ *     straight-through gradient of the soft history softmax in the backward:
+ *     the loss gradient with respect to a kept block's gate is taken as the
+ *     gradient with respect to its soft gate g_j = exp(s_j - lse), so
+ *       d s_m = sum over kept j of dL/dg_j * g_j ([j = m] - g_m)
+ *     with dL/dg_j = d log g_j (the hard gate is 1).  gate_lse is the soft
+ *     normaliser.
  *   - the normaliser runs over every causal history candidate; the Top-K then
  *     keeps a subset, so kept gates sum to at most 1.
  *   - budget Kb counts the current block; k = min(Kb - 1, i) history blocks.
@@ -66,6 +74,7 @@
 #define ORACLE_GATE_ALL 1
 #define ORACLE_GATE_SIGMOID 2
 #define ORACLE_GATE_RAW 3
+#define ORACLE_GATE_STE 4
 
 /* log sigmoid(x) = -log(1 + exp(-x)), written so that neither branch
  * overflows: for x < 0 it is x - log(1 + exp(x)). */
@@ -138,6 +147,8 @@ static void gate_row(const float *s, int i, int Kb, int mode, int32_t *idx, doub
       lg[pos] = log_sigmoid((double)s[j]);
     else if (mode == ORACLE_GATE_RAW)
       lg[pos] = (double)s[j];
+    else if (mode == ORACLE_GATE_STE)
+      lg[pos] = 0.0; /* hard gate: every kept block weighs 1 */
     else
       lg[pos] = (lse == -INFINITY) ? -INFINITY : (double)s[j] - lse;
     ++pos;
@@ -442,6 +453,20 @@ int sas_oracle_gate_bwd(int nseq, const int32_t *cu, int blk, int hkv, int Kb, i
     double acc = 0.0;
     for (int j = 0; j < nn; ++j) acc += exp((double)sr[j] - m);
     double lse = m + log(acc);
+    if (mode == ORACLE_GATE_STE) {
+      /* straight-through: dL/dg_j (= d log g_j at g = 1) through the soft
+       * gate's Jacobian g_j ([j = m] - g_m) */
+      double tot_g = 0.0;
+      for (int sl = 0; sl < Kb; ++sl) {
+        int j = sel_idx[r * Kb + sl];
+        if (j < 0 || j >= i) continue;
+        double gj = exp((double)sr[j] - lse);
+        tot_g += gj * dlg[r * Kb + sl];
+        out[j] += gj * dlg[r * Kb + sl];
+      }
+      for (int j = 0; j < nn; ++j) out[j] -= exp((double)sr[j] - lse) * tot_g;
+      continue;
+    }
     double tot = 0.0;
     for (int sl = 0; sl < Kb; ++sl) {
       int j = sel_idx[r * Kb + sl];

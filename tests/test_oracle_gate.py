@@ -54,7 +54,7 @@ def _case(lengths, hkv, ld_extra=0, seed=0, blk=4, sigma=2.0, kind="normal"):
 @pytest.mark.parametrize("kind", ["normal", "ties", "zeros_signed", "neginf"])
 @pytest.mark.parametrize("Kb", [1, 2, 3, 5, 40])
 @pytest.mark.parametrize("mode", [oracle.GATE_HIST, oracle.GATE_ALL, oracle.GATE_SIGMOID,
-                                  oracle.GATE_RAW])
+                                  oracle.GATE_RAW, oracle.GATE_STE])
 def test_topk_matches_brute_force(kind, Kb, mode):
     lengths = [37, 4, 64, 1, 23]
     blk = 4

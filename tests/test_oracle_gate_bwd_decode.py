@@ -169,3 +169,47 @@ def test_decode_all_blocks_ungated_is_dense_single_query_attention():
         torch.tensor(q)[:, None], torch.tensor(K)[None].expand(G, L, d),
         torch.tensor(V)[None].expand(G, L, d), scale=1 / math.sqrt(d))[:, 0]
     assert np.max(np.abs(o - ref.numpy())) < 1e-12
+
+
+def test_ste_gate_matches_torch_straight_through_autograd():
+    """The ranking-preservation ablation (paper text section 4): hard Top-K
+    gates in the forward, the soft softmax gate's gradient in the backward.
+    The oracle's gate backward against torch autograd of
+    g = g_hard + g_soft - g_soft.detach() (float64), with dL/dg = the given
+    d log g on the kept history blocks (the hard gate is 1)."""
+    blk, hkv, Kb = 4, 2, 3
+    lengths = [30, 13]
+    cu = np.array([0, 30, 43], np.int32)
+    QB = 8 + 4
+    lg = grid_logits((hkv, QB, 8), 5)
+    idx, sl, glse = oracle.gate_topk(cu, lg, hkv, Kb, oracle.GATE_STE, blk=blk)
+    W = np.random.default_rng(6).normal(size=idx.shape)
+    W[idx < 0] = 0.0
+    d_logits = oracle.gate_bwd(cu, lg, idx, W, hkv, Kb, oracle.GATE_STE, blk=blk)
+    rows = []
+    for s in range(2):
+        nb = (lengths[s] + blk - 1) // blk
+        rows += [(s, i) for i in range(nb)]
+    for g in range(hkv):
+        for Q, (s, i) in enumerate(rows):
+            k = min(Kb - 1, i)
+            # forward: hard gate 1 on every kept block, the soft normaliser in gate_lse
+            assert np.all(sl[g, Q, :k + 1] == 0.0)
+            if i > 0:
+                assert glse[g, Q] == pytest.approx(
+                    float(torch.logsumexp(torch.tensor(lg[g, Q, :i], dtype=torch.float64), 0)),
+                    abs=1e-12)
+            x = torch.tensor(lg[g, Q, :8], dtype=torch.float64, requires_grad=True)
+            loss = torch.zeros((), dtype=torch.float64)
+            if i > 0:
+                soft = torch.softmax(x[:i], 0)
+                for slot in range(k):
+                    j = int(idx[g, Q, slot])
+                    gste = 1.0 + soft[j] - soft[j].detach()
+                    loss = loss + float(W[g, Q, slot]) * gste
+            if loss.requires_grad:
+                loss.backward()
+                want = x.grad.numpy()
+            else:
+                want = np.zeros(8)
+            assert np.max(np.abs(d_logits[g, Q] - want)) < 1e-12, (g, Q)

@@ -77,11 +77,15 @@ typedef int32_t sas_status;
  * The activation ablations (paper text section 4; review 3-3), the current
  * block unbiased in both: SAS_GATE_SIGMOID gives independent gates
  * g_j = sigmoid(s_j), SAS_GATE_RAW injects the raw logit (log g_j = s_j);
- * they have no normaliser and write gate_lse = 0. */
+ * they have no normaliser and write gate_lse = 0.  SAS_GATE_STE is the
+ * ranking-preservation ablation: hard gates (log g = 0 on every kept block)
+ * in the forward, the history softmax's straight-through gradient in the
+ * backward; gate_lse is the soft normaliser. */
 #define SAS_GATE_HIST 0
 #define SAS_GATE_ALL 1
 #define SAS_GATE_SIGMOID 2
 #define SAS_GATE_RAW 3
+#define SAS_GATE_STE 4
 
 #define SAS_KV_CONTIGUOUS 0 /* cache [batch][hkv][max_seqlen][head_dim] */
 #define SAS_KV_PAGED 1      /* cache [num_pages][hkv][64][head_dim] + page table */
@@ -129,7 +133,8 @@ typedef struct sas_decode_problem {
  *   logits      [hkv][total_qblocks][ld] fp32: column j = key block j of the
  *               row's own sequence; only columns j < i (and j = i in
  *               SAS_GATE_ALL) are read.  ld >= the longest sequence's blocks.
- *   gate_mode   SAS_GATE_HIST, SAS_GATE_ALL, SAS_GATE_SIGMOID or SAS_GATE_RAW.
+ *   gate_mode   SAS_GATE_HIST, SAS_GATE_ALL, SAS_GATE_SIGMOID, SAS_GATE_RAW
+ *               or SAS_GATE_STE.
  *   sel_idx     out [rows][Kb] int32; sel_loggate out [rows][Kb] fp32;
  *   gate_lse    out [rows] fp32: log of the gate normaliser (-inf when empty).
  * Top-K compares the stored fp32 logits: larger first, lower index on ties,
@@ -196,6 +201,8 @@ sas_status sas_bwd_dkdv(const sas_problem *p, const void *q, const void *k, cons
  * independent gates only kept history blocks get one:
  *   SAS_GATE_SIGMOID  d s_m = [m kept] dlg_m * sigmoid(-s_m)
  *   SAS_GATE_RAW      d s_m = [m kept] dlg_m   (gate_lse is not read)
+ * and straight-through, with g = exp(s - gate_lse) the soft history gates:
+ *   SAS_GATE_STE      d s_m = g_m ([m kept] dlg_m - sum over kept j of g_j dlg_j)
  *   d_logits out [hkv][total_qblocks][ld] fp32.
  */
 sas_status sas_gate_bwd(const sas_problem *p, const float *logits, int64_t ld,

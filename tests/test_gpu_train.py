@@ -119,11 +119,12 @@ def test_bwd_all_softmax_mode():
     check_bwd(case, prob, dv, gpu, ref, mode=sas.GATE_ALL)
 
 
-@pytest.mark.parametrize("mode", [sas.GATE_SIGMOID, sas.GATE_RAW])
+@pytest.mark.parametrize("mode", [sas.GATE_SIGMOID, sas.GATE_RAW, sas.GATE_STE])
 @pytest.mark.parametrize("name", ["ragged_g4_d128", "g2_d64_f32"])
 def test_activation_ablations_fwd_bwd(name, mode):
-    """Independent sigmoid gates and raw-logit injection (the pages'
-    activation ablation): gate, forward, backward and gate backward."""
+    """Independent sigmoid gates, raw-logit injection and the straight-
+    through hard gate (the pages' activation and ranking-preservation
+    ablations): gate, forward, backward and gate backward."""
     case, prob, dv, gpu, ref = run_case(name, mode=mode)
     check_bwd(case, prob, dv, gpu, ref, mode=mode)
 

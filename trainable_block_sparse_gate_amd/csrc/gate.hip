@@ -7,7 +7,9 @@
 //   kept     = the min(Kb-1, i) largest s_j over j < i, lower j on ties.
 // The activation ablations (paper text section 4; review 3-3) replace the
 // normalised log gate of the kept history blocks by log sigmoid(s_j)
-// (mode 2) or s_j itself (mode 3); they have no normaliser.
+// (mode 2) or s_j itself (mode 3); they have no normaliser.  The
+// ranking-preservation ablation (mode 4, straight-through) keeps the
+// history normaliser but gives every kept block the hard gate 1 (log 0).
 // The Top-K threshold is found with an exact radix select over 32-bit
 // order-preserving keys of the fp32 scores (4 passes of 8 bits, LDS
 // histograms); the kept blocks are then emitted in index order with a
@@ -16,9 +18,12 @@
 // Backward (review section 2-1; paper text, ablation results, where the
 // normaliser is shared by every history block):
 //   d s_m = [m kept] dlg_m - exp(s_m - lse) * sum over kept j of dlg_j;
-// with independent gates d s_m = [m kept] dlg_m * (d log g_m / d s_m).
+// with independent gates d s_m = [m kept] dlg_m * (d log g_m / d s_m);
+// straight-through (mode 4): dL/dg_j = dlg_j (the hard gate is 1) passed
+// through the soft gate's Jacobian: d s_m = g_m ([m kept] dlg_m - sum over
+// kept j of g_j dlg_j), g = exp(s - lse).
 
-constexpr int kGateSigmoid = 2, kGateRaw = 3;  // the activation ablations
+constexpr int kGateSigmoid = 2, kGateRaw = 3, kGateSte = 4;  // the ablations
 #include "sas_device.h"
 #include "sas_launch.h"
 
@@ -184,6 +189,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
           olg[pos] = fminf(sj, 0.f) - log1pf(expf(-fabsf(sj)));
         else if (p.mode == kGateRaw)
           olg[pos] = sj;
+        else if (p.mode == kGateSte)
+          olg[pos] = 0.f;  // hard gate
         else
           olg[pos] = (lse == -INFINITY) ? -INFINITY : sj - lse;
       }
@@ -231,8 +238,11 @@ __global__ __launch_bounds__(kGateThreads) void gate_bwd_kernel(GateBwdParams p)
       const int j = sel[sl];
       if (j < 0 || j > i || (j == i && p.mode != 1)) continue;
       s_j[n] = j;
-      s_d[n] = dlg[sl];
-      tot += dlg[sl];
+      // straight-through: the kept gradient enters weighted by the soft gate
+      const float d = p.mode == kGateSte ? expf(p.logits[(long)r * p.ld + j] - lse) * dlg[sl]
+                                         : dlg[sl];
+      s_d[n] = d;
+      tot += d;
       ++n;
     }
     s_n = n;
@@ -259,6 +269,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_bwd_kernel(GateBwdParams p)
         }
       }
     } else if (c < nn && lse != -INFINITY) {
+      // (straight-through: s_d and tot already carry the soft gates)
       val = -expf(srow[c] - lse) * tot;
       int lo = 0, hi = n - 1;
       while (lo <= hi) {

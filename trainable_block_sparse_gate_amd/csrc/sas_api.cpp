@@ -116,7 +116,7 @@ sas_status sas_gate_topk(const sas_problem *p, const float *logits, int64_t ld,
   if (st) return st;
   REQUIRE(logits && sel_idx && sel_loggate && gate_lse, SAS_ERR_NULL,
           "logits / sel_idx / sel_loggate / gate_lse is NULL");
-  REQUIRE(gate_mode >= SAS_GATE_HIST && gate_mode <= SAS_GATE_RAW, SAS_ERR_SHAPE,
+  REQUIRE(gate_mode >= SAS_GATE_HIST && gate_mode <= SAS_GATE_STE, SAS_ERR_SHAPE,
           "unknown gate_mode %d", gate_mode);
   REQUIRE(ld >= mb && ld >= 1, SAS_ERR_SHAPE, "ld (%lld) < blocks of the longest sequence (%d)",
           (long long)ld, mb);
@@ -178,7 +178,7 @@ sas_status sas_gate_bwd(const sas_problem *p, const float *logits, int64_t ld,
   if (st) return st;
   REQUIRE(logits && sel_idx && gate_lse && d_loggate && d_logits, SAS_ERR_NULL,
           "a tensor argument of sas_gate_bwd is NULL");
-  REQUIRE(gate_mode >= SAS_GATE_HIST && gate_mode <= SAS_GATE_RAW, SAS_ERR_SHAPE,
+  REQUIRE(gate_mode >= SAS_GATE_HIST && gate_mode <= SAS_GATE_STE, SAS_ERR_SHAPE,
           "unknown gate_mode %d", gate_mode);
   REQUIRE(ld >= mb && ld >= 1, SAS_ERR_SHAPE, "ld (%lld) < blocks of the longest sequence (%d)",
           (long long)ld, mb);

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsas.so")
 
 SAS_BF16, SAS_F32 = 0, 1
-GATE_HIST, GATE_ALL, GATE_SIGMOID, GATE_RAW = 0, 1, 2, 3
+GATE_HIST, GATE_ALL, GATE_SIGMOID, GATE_RAW, GATE_STE = 0, 1, 2, 3, 4
 KV_CONTIGUOUS, KV_PAGED = 0, 1
 BLOCK = 64
 

@@ -139,6 +139,44 @@ def bwd(cu_seqlens, q, k, v, dO, sel_idx, sel_lg, Kb, scale, row_mask=None,
     return dq, dk, dv, dlg
 
 
+def fwd_outer(cu_seqlens, q, k, v, sel_idx, sel_lg, Kb, scale, blk=64):
+    """Outer-gate forward (the gate-position ablation): softmax of the
+    ungated logits, each key's value scaled by its block's gate.  Returns
+    (o, lse) float64; lse is that of the ungated logits."""
+    cu = _i32(cu_seqlens)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    idx, sl = _i32(sel_idx), _f64(sel_lg)
+    o = np.full((T, hq, d), np.nan)
+    lse = np.full((hq, T), np.nan)
+    rc = _load().sas_oracle_fwd_outer(
+        len(cu) - 1, _p(cu), blk, hq, hkv, d, Kb, ctypes.c_double(scale),
+        _p(q), _p(k), _p(v), _p(idx), _p(sl), _p(o), _p(lse))
+    if rc:
+        raise ValueError(f"oracle fwd_outer failed: {rc}")
+    return o, lse
+
+
+def bwd_outer(cu_seqlens, q, k, v, dO, sel_idx, sel_lg, Kb, scale, blk=64):
+    """Gradients of the outer-gate forward: (dq, dk, dv, dlg), float64."""
+    cu = _i32(cu_seqlens)
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    idx, sl = _i32(sel_idx), _f64(sel_lg)
+    dq = np.empty((T, hq, d))
+    dk = np.empty((T, hkv, d))
+    dv = np.empty((T, hkv, d))
+    dlg = np.empty(idx.shape)
+    rc = _load().sas_oracle_bwd_outer(
+        len(cu) - 1, _p(cu), blk, hq, hkv, d, Kb, ctypes.c_double(scale),
+        _p(q), _p(k), _p(v), _p(dO), _p(idx), _p(sl), _p(dq), _p(dk), _p(dv), _p(dlg))
+    if rc:
+        raise ValueError(f"oracle bwd_outer failed: {rc}")
+    return dq, dk, dv, dlg
+
+
 def gate_bwd(cu_seqlens, logits, sel_idx, dlg, hkv, Kb, mode=GATE_HIST, blk=64):
     """d logits [hkv,QB,ld] from d log-gate through the gate softmax."""
     cu = _i32(cu_seqlens)

@@ -411,6 +411,161 @@ int sas_oracle_bwd(int nseq, const int32_t *cu, int blk, int hq, int hkv, int d,
 }
 
 /*
+ * The gate-position ablation ([R] 3-2 outer-gate equation; [P] section 4,
+ * "gate position", and the ablation results: outside the softmax the
+ * probabilities are fixed and the gate only rescales the value
+ * contribution of its block):
+ *   o_t = sum_u softmax_u(scale q_t.k_u) g_blk(u) v_u,   g = exp(log g)
+ * lse is the row log-sum-exp of the ungated logits.  Backward, by the chain
+ * rule, with P the ungated probabilities:
+ *   dP_tu = g_blk(u) (dO_t . v_u)    D_t = dO_t . o_t = sum_u P_tu dP_tu
+ *   dS_tu = P_tu (dP_tu - D_t)       dq, dk from dS as in the inner gate
+ *   dv_u  = sum_t P_tu g_blk(u) dO_t
+ *   dlg_r,slot = d L / d log g = sum over the row's tokens, heads and the
+ *                slot's keys of P_tu dP_tu   (no -D term: P does not
+ *                depend on the gate)
+ */
+int sas_oracle_fwd_outer(int nseq, const int32_t *cu, int blk, int hq, int hkv, int d, int Kb,
+                         double scale, const double *q, const double *k, const double *v,
+                         const int32_t *sel_idx, const double *sel_lg, double *o, double *lse) {
+  if (hq % hkv) return -1;
+  int G = hq / hkv;
+  int *cuqb = (int *)malloc(sizeof(int) * (nseq + 1));
+  int QB = query_block_offsets(nseq, cu, blk, cuqb);
+  int T = cu[nseq];
+  long nrows = (long)hkv * QB;
+  int maxkeys = Kb * blk;
+#pragma omp parallel
+  {
+    int *u = (int *)malloc(sizeof(int) * maxkeys);
+    int *slot = (int *)malloc(sizeof(int) * maxkeys);
+    double *z = (double *)malloc(sizeof(double) * maxkeys);
+#pragma omp for schedule(dynamic, 1)
+    for (long r = 0; r < nrows; ++r) {
+      int g = (int)(r / QB), Q = (int)(r % QB);
+      int s = seq_of_qblock(nseq, cuqb, Q);
+      int i = Q - cuqb[s];
+      int start = cu[s], len = cu[s + 1] - cu[s];
+      const int32_t *idx = sel_idx + r * Kb;
+      const double *lg = sel_lg + r * Kb;
+      for (int tl = i * blk; tl < (i + 1) * blk && tl < len; ++tl) {
+        int t = start + tl;
+        int n = attended_keys(idx, Kb, i, blk, start, len, tl, u, slot);
+        for (int hh = 0; hh < G; ++hh) {
+          int h = g * G + hh;
+          const double *qt = q + ((long)t * hq + h) * d;
+          double m = -INFINITY;
+          for (int a = 0; a < n; ++a) {
+            z[a] = scale * dot_dd(qt, k + ((long)u[a] * hkv + g) * d, d); /* no gate */
+            if (z[a] > m) m = z[a];
+          }
+          double den = 0.0;
+          for (int a = 0; a < n; ++a) den += exp(z[a] - m);
+          double *ot = o + ((long)t * hq + h) * d;
+          for (int e = 0; e < d; ++e) ot[e] = 0.0;
+          for (int a = 0; a < n; ++a) {
+            double p = exp(z[a] - m) / den;
+            double gate = exp(lg[slot[a]]);
+            const double *vu = v + ((long)u[a] * hkv + g) * d;
+            for (int e = 0; e < d; ++e) ot[e] += p * gate * vu[e];
+          }
+          lse[(long)h * T + t] = m + log(den);
+        }
+      }
+    }
+    free(u);
+    free(slot);
+    free(z);
+  }
+  free(cuqb);
+  return 0;
+}
+
+int sas_oracle_bwd_outer(int nseq, const int32_t *cu, int blk, int hq, int hkv, int d, int Kb,
+                         double scale, const double *q, const double *k, const double *v,
+                         const double *dO, const int32_t *sel_idx, const double *sel_lg,
+                         double *dq, double *dk, double *dv, double *dlg) {
+  if (hq % hkv) return -1;
+  int G = hq / hkv;
+  int *cuqb = (int *)malloc(sizeof(int) * (nseq + 1));
+  int QB = query_block_offsets(nseq, cu, blk, cuqb);
+  int T = cu[nseq];
+  memset(dq, 0, sizeof(double) * (size_t)T * hq * d);
+  memset(dk, 0, sizeof(double) * (size_t)T * hkv * d);
+  memset(dv, 0, sizeof(double) * (size_t)T * hkv * d);
+  memset(dlg, 0, sizeof(double) * (size_t)hkv * QB * Kb);
+  int maxkeys = Kb * blk;
+  long npairs = (long)hkv * nseq;
+#pragma omp parallel
+  {
+    int *u = (int *)malloc(sizeof(int) * maxkeys);
+    int *slot = (int *)malloc(sizeof(int) * maxkeys);
+    double *z = (double *)malloc(sizeof(double) * maxkeys);
+    double *P = (double *)malloc(sizeof(double) * maxkeys);
+    double *ot = (double *)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 1)
+    for (long pr = 0; pr < npairs; ++pr) {
+      int g = (int)(pr / nseq), s = (int)(pr % nseq);
+      int start = cu[s], len = cu[s + 1] - cu[s];
+      int nb = cuqb[s + 1] - cuqb[s];
+      for (int i = 0; i < nb; ++i) {
+        long r = (long)g * QB + cuqb[s] + i;
+        const int32_t *idx = sel_idx + r * Kb;
+        const double *lg = sel_lg + r * Kb;
+        for (int tl = i * blk; tl < (i + 1) * blk && tl < len; ++tl) {
+          int t = start + tl;
+          int n = attended_keys(idx, Kb, i, blk, start, len, tl, u, slot);
+          for (int hh = 0; hh < G; ++hh) {
+            int h = g * G + hh;
+            const double *qt = q + ((long)t * hq + h) * d;
+            const double *dOt = dO + ((long)t * hq + h) * d;
+            double m = -INFINITY;
+            for (int a = 0; a < n; ++a) {
+              z[a] = scale * dot_dd(qt, k + ((long)u[a] * hkv + g) * d, d);
+              if (z[a] > m) m = z[a];
+            }
+            double den = 0.0;
+            for (int a = 0; a < n; ++a) den += exp(z[a] - m);
+            for (int e = 0; e < d; ++e) ot[e] = 0.0;
+            for (int a = 0; a < n; ++a) {
+              P[a] = exp(z[a] - m) / den;
+              double gate = exp(lg[slot[a]]);
+              const double *vu = v + ((long)u[a] * hkv + g) * d;
+              for (int e = 0; e < d; ++e) ot[e] += P[a] * gate * vu[e];
+            }
+            double D = 0.0;
+            for (int e = 0; e < d; ++e) D += dOt[e] * ot[e];
+            for (int a = 0; a < n; ++a) {
+              const double *ku = k + ((long)u[a] * hkv + g) * d;
+              const double *vu = v + ((long)u[a] * hkv + g) * d;
+              double gate = exp(lg[slot[a]]);
+              double dP = gate * dot_dd(dOt, vu, d);
+              double dS = P[a] * (dP - D);
+              double *dqt = dq + ((long)t * hq + h) * d;
+              double *dku = dk + ((long)u[a] * hkv + g) * d;
+              double *dvu = dv + ((long)u[a] * hkv + g) * d;
+              for (int e = 0; e < d; ++e) {
+                dqt[e] += scale * dS * ku[e];
+                dku[e] += scale * dS * qt[e];
+                dvu[e] += P[a] * gate * dOt[e];
+              }
+              dlg[r * Kb + slot[a]] += P[a] * dP;
+            }
+          }
+        }
+      }
+    }
+    free(u);
+    free(slot);
+    free(z);
+    free(P);
+    free(ot);
+  }
+  free(cuqb);
+  return 0;
+}
+
+/*
  * Gate backward: d logits from d log g through the softmax normaliser
  * ([R] 2-1 g = phi(s); [P] ablation results: the normaliser is shared by all
  * historical blocks).  With p_m = exp(log g_m) over the normaliser set N:

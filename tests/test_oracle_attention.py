@@ -232,3 +232,96 @@ def test_golden_attention_example():
     o, lse = oracle.fwd(np.array([0, T], np.int32), q, k, v, idx, lg, Kb, 1.0, blk=blk)
     assert np.allclose(o[:, 0, 0], c["expect_o"], atol=1e-12)
     assert np.allclose(np.exp(lse[0]), c["expect_lse_exp"], atol=1e-12)
+
+
+# ----------------------------------------------------------------- outer gate
+def _outer_sdpa_reference(P, sl):
+    """Outer gate through torch SDPA (float64): per query block, the keys'
+    values scaled by the row's gates, the mask free of any gate (0 on the
+    attended keys, -inf elsewhere)."""
+    cu, blk, hkv, hq = P["cu"], P["blk"], P["hkv"], P["hq"]
+    G = hq // hkv
+    T, d = P["q"].shape[0], P["d"]
+    o = np.zeros((T, hq, d))
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        L = b - a
+        ones = np.where(P["idx"] >= 0, 0.0, -np.inf)
+        M = gate_mask(cu, P["idx"], ones, hkv, blk, s)  # attended keys only, no gate
+        qb0 = sum((int(cu[x + 1]) - int(cu[x]) + blk - 1) // blk for x in range(s))
+        for i in range((L + blk - 1) // blk):
+            t0, t1 = i * blk, min((i + 1) * blk, L)
+            r = qb0 + i
+            for g in range(hkv):
+                gate = np.zeros(L)
+                for slot in range(P["Kb"]):
+                    j = int(P["idx"][g, r, slot])
+                    if j >= 0:
+                        gate[j * blk:min((j + 1) * blk, L)] = math.exp(sl[g, r, slot])
+                vg = torch.tensor(P["v"][a:b, g] * gate[:, None])
+                kg = torch.tensor(P["k"][a:b, g])
+                for hh in range(G):
+                    h = g * G + hh
+                    qt = torch.tensor(P["q"][a + t0:a + t1, h])
+                    mask = torch.tensor(M[g, t0:t1])
+                    out = torch.nn.functional.scaled_dot_product_attention(
+                        qt[None], kg[None], vg[None], attn_mask=mask[None], scale=P["scale"])[0]
+                    o[a + t0:a + t1, h] = out.numpy()
+    return o
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_outer_gate_fwd_matches_sdpa_with_scaled_values(case):
+    """The gate-position ablation (review 3-2 outer-gate equation): softmax
+    of the ungated logits times the gate-scaled values."""
+    lengths, hq, hkv, d, Kb, blk = CASES[case]
+    P = small_problem(lengths, hq, hkv, d, Kb, blk, seed=40 + case)
+    o, lse = oracle.fwd_outer(P["cu"], P["q"], P["k"], P["v"], P["idx"], P["sl"], Kb, P["scale"],
+                              blk=blk)
+    ref = _outer_sdpa_reference(P, P["sl"])
+    assert np.max(np.abs(o - ref)) < 1e-12
+    # lse is that of the ungated logits: the inner forward with zero gates
+    zero = np.where(P["idx"] >= 0, 0.0, -np.inf)
+    _, lse0 = oracle.fwd(P["cu"], P["q"], P["k"], P["v"], P["idx"], zero, Kb, P["scale"], blk=blk)
+    assert np.max(np.abs(lse - lse0)) < 1e-12
+
+
+def test_outer_gate_with_unit_gates_equals_inner_gate():
+    lengths, hq, hkv, d, Kb, blk = [29, 8, 17], 4, 2, 8, 3, 4
+    P = small_problem(lengths, hq, hkv, d, Kb, blk, seed=51)
+    zero = np.where(P["idx"] >= 0, 0.0, -np.inf)
+    o1, l1 = oracle.fwd_outer(P["cu"], P["q"], P["k"], P["v"], P["idx"], zero, Kb, P["scale"], blk=blk)
+    o2, l2 = oracle.fwd(P["cu"], P["q"], P["k"], P["v"], P["idx"], zero, Kb, P["scale"], blk=blk)
+    assert np.max(np.abs(o1 - o2)) < 1e-13 and np.max(np.abs(l1 - l2)) < 1e-13
+
+
+def test_outer_gate_bwd_matches_central_finite_differences():
+    lengths, hq, hkv, d, Kb, blk = [21, 10], 4, 2, 4, 3, 4
+    P = small_problem(lengths, hq, hkv, d, Kb, blk, seed=13)
+    dq, dk, dv, dlg = oracle.bwd_outer(P["cu"], P["q"], P["k"], P["v"], P["dO"], P["idx"],
+                                       P["sl"], Kb, P["scale"], blk=blk)
+
+    def loss(q, k, v, sl):
+        o, _ = oracle.fwd_outer(P["cu"], q, k, v, P["idx"], sl, Kb, P["scale"], blk=blk)
+        return float(np.sum(o * P["dO"]))
+
+    h = 1e-6
+    g = np.random.default_rng(1)
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        for _ in range(12):
+            pos = tuple(int(g.integers(0, n)) for n in P[name].shape)
+            args_p = {"q": P["q"], "k": P["k"], "v": P["v"]}
+            args_m = dict(args_p)
+            xp, xm = P[name].copy(), P[name].copy()
+            xp[pos] += h
+            xm[pos] -= h
+            args_p[name], args_m[name] = xp, xm
+            fd = (loss(args_p["q"], args_p["k"], args_p["v"], P["sl"]) -
+                  loss(args_m["q"], args_m["k"], args_m["v"], P["sl"])) / (2 * h)
+            assert abs(fd - grad[pos]) < 1e-7 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+    for pos in zip(*np.nonzero(P["idx"] >= 0)):
+        sp, sm = P["sl"].copy(), P["sl"].copy()
+        sp[pos] += h
+        sm[pos] -= h
+        fd = (loss(P["q"], P["k"], P["v"], sp) - loss(P["q"], P["k"], P["v"], sm)) / (2 * h)
+        assert abs(fd - dlg[pos]) < 1e-7 * max(1.0, abs(fd)), (pos, fd, dlg[pos])

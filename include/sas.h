@@ -87,6 +87,16 @@ typedef int32_t sas_status;
 #define SAS_GATE_RAW 3
 #define SAS_GATE_STE 4
 
+/* Gate position (the gate-position ablation: review 3-2; paper text
+ * section 4 and ablation results).  SAS_GATE_INNER adds log g to the logits
+ * inside the softmax (the method).  SAS_GATE_OUTER takes the softmax of the
+ * ungated logits and scales each key's value by its block's gate:
+ *   o_t = sum_u softmax_u(scale q_t.k_u) g_blk(u) v_u,
+ * lse is then that of the ungated logits, and d_loggate of a kept block is
+ * the sum over its keys of P dP with dP_tu = g (dO_t . v_u). */
+#define SAS_GATE_INNER 0
+#define SAS_GATE_OUTER 1
+
 #define SAS_KV_CONTIGUOUS 0 /* cache [batch][hkv][max_seqlen][head_dim] */
 #define SAS_KV_PAGED 1      /* cache [num_pages][hkv][64][head_dim] + page table */
 
@@ -106,6 +116,7 @@ typedef struct sas_problem {
   const int32_t *cu_qblocks;       /* device [num_seqs + 1] */
   const int32_t *cu_seqlens_host;  /* host copies of the two arrays above */
   const int32_t *cu_qblocks_host;
+  int32_t gate_position;   /* SAS_GATE_INNER (0, the method) or SAS_GATE_OUTER */
 } sas_problem;
 
 /* A single-token decode problem over a KV cache. */

@@ -223,3 +223,38 @@ def test_full_scope_zero_gates_is_dense_causal_attention(dtype):
     rdq, rdk, rdv, rdlg = oracle.bwd(cu, case.q, case.k, case.v, case.dO, idx,
                                      lg.cpu().numpy().astype(np.float64), Kb, case.scale)
     assert_close("dlg", dlg.cpu().numpy(), rdlg, tol)
+
+
+@pytest.mark.parametrize("name", ["ragged_g4_d128", "g2_d64_f32", "g1_d64_bf16"])
+def test_outer_gate_fwd_bwd(name):
+    """The gate-position ablation (review 3-2; paper text section 4): the
+    softmax over the ungated logits, the gate scaling each block's values.
+    Forward, backward (dq, dk, dv, d log g) and the gate backward on the GPU
+    against the oracle's outer-gate restatement."""
+    import torch
+    lengths, hq, hkv, d, Kb, dtype, sigma, extra = SMALL[name]
+    say(f"[outer gate {name}]")
+    case = wl.make_varlen(name, lengths, hq, hkv, d, Kb, dtype=dtype, logit_sigma=sigma,
+                          workload_id=80 + list(SMALL).index(name), **extra)
+    prob = sas.Varlen(lengths, hq, hkv, d, Kb, dtype=dtype, out_dtype=dtype,
+                      gate_position=sas.GATE_OUTER)
+    dv = case_to_device(case)
+    sel, lg, glse = sas.gate_topk(prob, dv["logits"])
+    o, lse = sas.fwd(prob, dv["q"], dv["k"], dv["v"], sel, lg)
+    dq, dk, dvv, dlg = sas.bwd(prob, dv["q"], dv["k"], dv["v"], o, dv["dO"], lse, sel, lg)
+    dlogits = sas.gate_bwd(prob, dv["logits"], sel, glse, dlg)
+    torch.cuda.synchronize()
+    ridx, rlg, _ = oracle.gate_topk(case.cu_seqlens, case.logits, hkv, Kb)
+    assert np.array_equal(sel.cpu().numpy(), ridx)
+    tol = TOL[dtype]
+    ro, rl = oracle.fwd_outer(case.cu_seqlens, case.q, case.k, case.v, ridx, rlg, Kb, case.scale)
+    assert_close("o", o.float().cpu().numpy(), ro, tol)
+    assert_close("lse", lse.cpu().numpy(), rl, tol)
+    rdq, rdk, rdv, rdlg = oracle.bwd_outer(case.cu_seqlens, case.q, case.k, case.v, case.dO,
+                                           ridx, rlg, Kb, case.scale)
+    assert_close("dq", dq.cpu().numpy(), rdq, tol)
+    assert_close("dk", dk.cpu().numpy(), rdk, tol)
+    assert_close("dv", dvv.cpu().numpy(), rdv, tol)
+    assert_close("dlg", dlg.cpu().numpy(), rdlg, tol)
+    rdz = oracle.gate_bwd(case.cu_seqlens, case.logits, ridx, rdlg, hkv, Kb)
+    assert_close("d_logits", dlogits.cpu().numpy(), rdz, tol)

@@ -111,7 +111,10 @@ __global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p)
 // issue).
 constexpr int kDqQT = 1;  // 32-query tiles per wave (1: two waves per head)
 
-template <typename T, typename TO, int D, int NW>
+// OUTER: the gate-position ablation.  P comes from the ungated logits,
+// dP is scaled by the tile's gate, and the tile's d log g is the sum of
+// P dP alone (P does not depend on the gate).
+template <typename T, typename TO, int D, int NW, bool OUTER>
 __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams p) {
   using M = Mfma<T>;
   constexpr int QT = kDqQT;
@@ -277,7 +280,8 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
 #pragma unroll
       for (int nt = 0; nt < QT; ++nt) {
         const int ql = 32 * (nt0 + nt) + l32;
-        const float c = lg2 - lse2[nt];
+        const float c = (OUTER ? 0.f : lg2) - lse2[nt];
+        const float gate = OUTER ? fast_exp2(lg2) : 1.f;
         float pd[16], pp[16];
         if (!diag) {
 #pragma unroll
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          pd[r] = pp[r] * pacc[nt][r];
+          pd[r] = pp[r] * (OUTER ? gate * pacc[nt][r] : pacc[nt][r]);
           sacc[nt][r] = fmaf(-pp[r], Dv[nt], pd[r]);
         }
 #pragma unroll
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
           }
         Fp[nt] += pd[0];
         Eacc[nt] += pd[0];
-        Gp[nt] += pp[0];
+        if constexpr (!OUTER) Gp[nt] += pp[0];  // outer: no D term in d log g
       }
       // dQ^T[d][query] += K^T[d][key] dS^T[key][query] over this 32-key half
 #pragma unroll
@@ -452,9 +456,12 @@ template <typename T, typename TO, int D, int NW>
 static hipError_t launch_dq_t(const BwdParams &p, hipStream_t stream) {
   const int nhc = (p.G + NW - 1) / NW;
   const size_t dyn = dq_dynamic_lds<T, D, NW>(p);
-  hipLaunchKernelGGL((bwd_dq_kernel<T, TO, D, NW>), dim3(p.QB, p.hkv * nhc),
-                     dim3(NW * (2 / kDqQT) * 64), dyn,
-                     stream, p);
+  if (p.outer)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, TO, D, NW, true>), dim3(p.QB, p.hkv * nhc),
+                       dim3(NW * (2 / kDqQT) * 64), dyn, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, TO, D, NW, false>), dim3(p.QB, p.hkv * nhc),
+                       dim3(NW * (2 / kDqQT) * 64), dyn, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nhc == 1) return e;
   const long n = (long)p.hkv * p.QB * p.Kb;

@@ -40,7 +40,10 @@ namespace sas {
 // the row-major tiles.
 constexpr int kSegMax = 64;  // entries per segment the kernel can hold
 
-template <typename T, int D>
+// OUTER: the gate-position ablation: P from the ungated logits, dS =
+// P (g dP - D), dV from P g (g the step's gate); -D then needs its own
+// accumulator, since dP is scaled after the product.
+template <typename T, int D, bool OUTER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(
     BwdParams p) {
   using M = Mfma<T>;
@@ -261,6 +264,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int nq = min(kBlock, seq_len - i * kBlock);
     const float lg2 = __builtin_bit_cast(
         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_lg), e)) * kLog2e;
+    const float lz = OUTER ? 0.f : lg2;             // the gate's term in the logits
+    const float gate = OUTER ? fast_exp2(lg2) : 1.f;  // the gate on the values
     const bool diag = (i == j);
     const T *Qs = tiles_of(B);
     const T *Ds = Qs + TILE;
@@ -271,14 +276,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     //   sacc = S - lse / scale   and   pacc = dP - D,
     // and P = exp2(scale_log2 * sacc + lg2), dS = P * pacc take no further
     // per-row term.
-    f32x16 sacc, pacc;
+    f32x16 sacc, pacc, dacc;  // dacc: -D (outer gate only)
     if constexpr (kSplitD) {
       // one product per statistic (see load_stats); the registers are then
       // free for the next step's statistics, requested right away
       typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
       const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4v{ow, ow, ow, ow});
       sacc = M::run(stl, ones, f32x16{});
-      pacc = M::run(stdd, ones, f32x16{});
+      if constexpr (OUTER) {
+        dacc = M::run(stdd, ones, f32x16{});
+        pacc = f32x16{};
+      } else {
+        pacc = M::run(stdd, ones, f32x16{});
+      }
       load_stats(rq);
     } else {
       // this lane's 16 rows, in register order, read one by one
@@ -287,6 +297,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int r = 0; r < 16; ++r) {
         sacc[r] = stat[0][32 * qh + chain_slot<T>(r, hf)];
         pacc[r] = stat[1][32 * qh + chain_slot<T>(r, hf)];
+        if constexpr (OUTER) {
+          dacc[r] = pacc[r];
+          pacc[r] = 0.f;
+        }
       }
     }
     // operands are read RA chunks ahead of the products that use them, in
@@ -323,9 +337,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       if (!diag && nq == kBlock && nvalid == kBlock) {
   #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(fmaf(sacc[r], p.scale_log2, lg2));
-          sacc[r] = pr;
-          pacc[r] = pr * pacc[r];
+          const float pr = fast_exp2(fmaf(sacc[r], p.scale_log2, lz));
+          if constexpr (OUTER) {
+            pacc[r] = pr * fmaf(gate, pacc[r], dacc[r]);
+            sacc[r] = pr * gate;
+          } else {
+            sacc[r] = pr;
+            pacc[r] = pr * pacc[r];
+          }
         }
       } else {
         // row of register r: qlb + o, o fixed by r
@@ -335,9 +354,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         for (int r = 0; r < 16; ++r) {
           const int o = chain_slot<T>(r, 0) - chain_slot<T>(0, 0);
           const bool ok = key_ok && qlb < nq - o && !(diag && kq > o);
-          const float pr = fast_exp2(ok ? fmaf(sacc[r], p.scale_log2, lg2) : -INFINITY);
-          sacc[r] = pr;
-          pacc[r] = pr * pacc[r];
+          const float pr = fast_exp2(ok ? fmaf(sacc[r], p.scale_log2, lz) : -INFINITY);
+          if constexpr (OUTER) {
+            pacc[r] = pr * fmaf(gate, pacc[r], dacc[r]);
+            sacc[r] = pr * gate;
+          } else {
+            sacc[r] = pr;
+            pacc[r] = pr * pacc[r];
+          }
         }
       }
     };
@@ -572,7 +596,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdParams p) {
 // ------------------------------------------------------------------ launch
 template <typename T, int D>
 static hipError_t launch_dkdv_t(const BwdParams &p, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(p.U), dim3(256), 0, stream, p);
+  if (p.outer)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), dim3(p.U), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), dim3(p.U), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3(min(kReduceWgs, p.hkv * p.QB)), dim3(256), 0,

@@ -40,7 +40,10 @@ constexpr float kRescale = 8.f;
 // (one's softmax overlaps the other's MFMAs).
 constexpr int kFwdQT = 1;
 
-template <typename T, typename TO, int D, int NW>
+// OUTER: the gate-position ablation (review 3-2; paper text section 4):
+// the softmax runs over the ungated logits and each tile's probabilities
+// are scaled by the tile's gate only where they weight the values.
+template <typename T, typename TO, int D, int NW, bool OUTER>
 __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p) {
   using M = Mfma<T>;
   constexpr int QT = kFwdQT;           // 32-query tiles per wave
@@ -199,13 +202,14 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][t][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float zmax = mx * p.scale_log2 + lg2;
+      const float lz = OUTER ? 0.f : lg2;  // the gate's term in the logits
+      const float zmax = mx * p.scale_log2 + lz;
       // move the reference only on a large increase (first tile: from -inf)
       const bool move = zmax > m_run[t] + kRescale;
       const float m_new = move ? zmax : m_run[t];
       const float alpha = move ? fast_exp2(m_run[t] - m_new) : 1.f;
       // a tile whose gate is zero adds nothing (and no 0 * inf)
-      const float c = lg2 == -INFINITY ? -INFINITY : lg2 - m_new;
+      const float c = lz == -INFINITY ? -INFINITY : lz - m_new;
       float ps[16];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -228,6 +232,14 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[dt][t][r] *= alpha;
+      }
+      if constexpr (OUTER) {
+        // the values see the gated probabilities, the row sum the ungated
+        const float gate = fast_exp2(lg2);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[mt][t][r] *= gate;
       }
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) pop[t][kc] = regs_op<T>(sacc[kc / SPT][t], (kc % SPT) * E);
@@ -335,8 +347,12 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
 template <typename T, typename TO, int D, int NW>
 static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t stream) {
   dim3 grid(p.QB, p.hkv * ((p.G + NW - 1) / NW));
-  hipLaunchKernelGGL((fwd_kernel<T, TO, D, NW>), grid, dim3(NW * (2 / kFwdQT) * 64), 0, stream,
-                     p);
+  if (p.outer)
+    hipLaunchKernelGGL((fwd_kernel<T, TO, D, NW, true>), grid, dim3(NW * (2 / kFwdQT) * 64), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, TO, D, NW, false>), grid, dim3(NW * (2 / kFwdQT) * 64), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

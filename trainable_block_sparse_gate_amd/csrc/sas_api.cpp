@@ -61,6 +61,8 @@ sas_status check_problem(const sas_problem *p, int *max_blocks) {
   REQUIRE(!(p->dtype == SAS_F32 && p->out_dtype == SAS_BF16), SAS_ERR_UNSUPPORTED,
           "fp32 inputs need an fp32 output");
   REQUIRE(std::isfinite(p->scale), SAS_ERR_SHAPE, "scale is not finite");
+  REQUIRE(p->gate_position == SAS_GATE_INNER || p->gate_position == SAS_GATE_OUTER,
+          SAS_ERR_SHAPE, "unknown gate_position %d", p->gate_position);
   REQUIRE(p->num_seqs >= 1, SAS_ERR_SHAPE, "num_seqs must be >= 1");
   REQUIRE(p->cu_seqlens && p->cu_qblocks, SAS_ERR_NULL, "cu_seqlens / cu_qblocks is NULL");
   REQUIRE(p->cu_seqlens_host && p->cu_qblocks_host, SAS_ERR_NULL,
@@ -165,6 +167,7 @@ sas_status sas_fwd(const sas_problem *p, const void *q, const void *k, const voi
   f.G = p->hq / p->hkv;
   f.Kb = p->budget_blocks;
   f.scale_log2 = p->scale * 1.4426950408889634f;
+  f.outer = p->gate_position == SAS_GATE_OUTER;
   return from_hip(sas::launch_fwd(f, p->dtype == SAS_BF16, p->out_dtype == SAS_BF16,
                                   p->head_dim, (hipStream_t)stream),
                   "fwd launch");
@@ -264,6 +267,7 @@ sas_status bwd_setup(const sas_problem *p, void *workspace, size_t workspace_byt
   b->max_nb = L.max_nb;
   b->scale = p->scale;
   b->scale_log2 = p->scale * 1.4426950408889634f;
+  b->outer = p->gate_position == SAS_GATE_OUTER;
   b->Lbuf = reinterpret_cast<float *>(ws + L.off_L);
   b->Dbuf = reinterpret_cast<float *>(ws + L.off_D);
   b->dO16 = (p->dtype == SAS_BF16 && p->out_dtype == SAS_F32)

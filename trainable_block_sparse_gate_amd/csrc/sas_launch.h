@@ -49,6 +49,7 @@ struct FwdParams {
   const int32_t *cu_seqlens, *cu_qblocks;
   int num_seqs, T, QB, hq, hkv, G, Kb;
   float scale_log2;  // softmax scale * log2(e)
+  int outer;         // gate position: 0 inside the softmax, 1 on the values
 };
 hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int out_bf16, int head_dim,
                       hipStream_t stream);
@@ -79,6 +80,7 @@ struct BwdParams {
   float *partial;    // [U][2][64][D] partial dK / dV of split key blocks
   int seg;           // keeping rows per segment
   int U;             // upper bound on the number of segments (dk/dv grid)
+  int outer;         // gate position: 0 inside the softmax, 1 on the values
 };
 hipError_t launch_bwd_prepare(const BwdParams &p, hipStream_t stream);
 bool bwd_dq_supported(const BwdParams &p, int dtype_bf16, int head_dim);

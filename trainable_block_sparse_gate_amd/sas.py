@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libsas.so")
 
 SAS_BF16, SAS_F32 = 0, 1
 GATE_HIST, GATE_ALL, GATE_SIGMOID, GATE_RAW, GATE_STE = 0, 1, 2, 3, 4
+GATE_INNER, GATE_OUTER = 0, 1  # gate position
 KV_CONTIGUOUS, KV_PAGED = 0, 1
 BLOCK = 64
 
@@ -43,6 +44,7 @@ class Problem(ctypes.Structure):
         ("out_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
         ("cu_seqlens", ctypes.c_void_p), ("cu_qblocks", ctypes.c_void_p),
         ("cu_seqlens_host", ctypes.c_void_p), ("cu_qblocks_host", ctypes.c_void_p),
+        ("gate_position", ctypes.c_int32),
     ]
 
 
@@ -121,7 +123,7 @@ class Varlen:
     cu_seqlens / cu_qblocks and the ctypes struct that points at them."""
 
     def __init__(self, lengths, hq, hkv, head_dim, budget_blocks, dtype="bf16",
-                 out_dtype=None, scale=None, device="cuda"):
+                 out_dtype=None, scale=None, device="cuda", gate_position=0):
         import torch
         self.lengths = [int(x) for x in lengths]
         cu = np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int32)
@@ -140,7 +142,8 @@ class Varlen:
         self.s = Problem(len(self.lengths), self.T, self.QB, hq, hkv, head_dim, BLOCK,
                          budget_blocks, code[dtype], code[out_dtype], self.scale,
                          self.cu_dev.data_ptr(), self.cuq_dev.data_ptr(),
-                         cu.ctypes.data, cuq.ctypes.data)
+                         cu.ctypes.data, cuq.ctypes.data, int(gate_position))
+        self.gate_position = int(gate_position)
 
     @property
     def ref(self):

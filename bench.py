@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--decode-workload", default="paged", choices=["paged", "long"],
+                    help="paged: batch 32 paged cache (the metric); long: one sequence of "
+                         "524288 tokens in a contiguous cache (selection-dominated)")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--cmd", default="", help="command line recorded in a summary")
@@ -304,13 +307,16 @@ def train_bench(args, torch, sas, wl, metrics, case):
 
 
 def decode_bench(args, torch, sas, wl, metrics):
-    spec = wl.paged_spec()
+    spec = wl.paged_spec() if args.decode_workload == "paged" else wl.decode_spec(524288)
     log(f"[bench] decode workload {spec.name}: batch {spec.batch}, lengths "
         f"{min(spec.seqlens)}..{max(spec.seqlens)}, Kb={spec.budget_blocks}")
     t = wl.draw_decode_device(spec)
-    npages = t["k"].shape[0]
-    prob = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, True,
-                      spec.max_len, page_table=t["page_table"], num_pages=npages)
+    if spec.paged:
+        prob = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, True,
+                          spec.max_len, page_table=t["page_table"], num_pages=t["k"].shape[0])
+    else:
+        prob = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, False,
+                          spec.max_len)
     ksum = sas.pool_keys(prob, t["k"])  # cache maintenance, not timed
     sel, lg, glse, scores = sas.decode_select(prob, t["q"], ksum)
     ws = torch.empty(max(1, sas.decode_workspace_bytes(prob)), dtype=torch.uint8, device="cuda")
@@ -342,8 +348,9 @@ def decode_bench(args, torch, sas, wl, metrics):
         f"selection {t_sel / n * 1e3:.1f} us over {scan / 2**20:.1f} MiB summaries")
     del t, flush
     torch.cuda.empty_cache()
-    return {"workload": f"paged: batch {spec.batch}, lengths U[32768,131072], 32/8 heads, d128, "
-                        f"budget {spec.budget_blocks} blocks",
+    desc = (f"paged: batch {spec.batch}, lengths U[32768,131072]" if spec.paged else
+            f"contiguous: batch {spec.batch}, length {spec.seqlens[0]}")
+    return {"workload": f"{desc}, 32/8 heads, d128, budget {spec.budget_blocks} blocks",
             "kv_bytes": kv, "us": round(t_dec / n * 1e3, 2), "value": round(gbs, 1),
             "unit": "GB/s", "frac": round(gbs / metrics.PEAK_HBM_GBS, 4),
             "peak": metrics.PEAK_HBM_GBS, "traffic": traffic_for("decode_attend_kernel"),

@@ -63,6 +63,29 @@ __device__ inline float block_sum(float x, float *red) {
   return r;
 }
 
+// Exclusive prefix sum of a non-negative count over the workgroup in
+// thread order, and the total.
+__device__ inline int block_scan_int(int x, int &total, int *cnt) {
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) cnt[w] = incl;
+  __syncthreads();
+  int off = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < kGateWaves; ++k) {
+    if (k < w) off += cnt[k];
+    total += cnt[k];
+  }
+  return off + incl - x;
+}
+
 // Exclusive prefix count of `flag` over the workgroup in thread order, and
 // the total.
 __device__ inline int block_scan_flag(bool flag, int &total, int *cnt) {
@@ -93,6 +116,14 @@ __device__ inline void row_geometry(const GateParams &p, int r, int &i) {
   }
 }
 
+// R > 0: the row's scores (at most kGateThreads * R) are read once into
+// registers, thread t holding the R consecutive entries R t .. R t + R - 1;
+// every pass below then works on registers instead of re-reading the row
+// (long decode rows have thousands of candidates), and the kept blocks are
+// placed with two workgroup scans in all (entries are in index order across
+// the threads).  R = 0 reads the row in each pass and places the kept
+// blocks chunk by chunk.
+template <int R>
 __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
   __shared__ float red[kGateWaves];
   __shared__ int cnt[kGateWaves];
@@ -108,15 +139,35 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
   const int nn = (p.mode == 1) ? i + 1 : i;
   const int k = min(p.Kb - 1, i);
 
+  float sv[R > 0 ? R : 1];
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      const int j = R * tid + c;
+      sv[c] = j < nn ? srow[j] : -INFINITY;
+    }
+  }
+  // f(j, s_j) for this thread's entries j < lim, in ascending order
+  auto each = [&](int lim, auto &&f) {
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        const int j = R * tid + c;
+        if (j < lim) f(j, sv[c]);
+      }
+    } else {
+      for (int j = tid; j < lim; j += kGateThreads) f(j, srow[j]);
+    }
+  };
+
   // Normaliser (independent gates have none; the uniform test skips it).
   float lse = 0.f;
   if (!independent) {
     float mx = -INFINITY;
-    for (int j = tid; j < nn; j += kGateThreads) mx = fmaxf(mx, srow[j]);
+    each(nn, [&](int, float x) { mx = fmaxf(mx, x); });
     mx = block_max(mx, red);
     float sum = 0.f;
-    if (mx != -INFINITY)
-      for (int j = tid; j < nn; j += kGateThreads) sum += expf(srow[j] - mx);
+    if (mx != -INFINITY) each(nn, [&](int, float x) { sum += expf(x - mx); });
     sum = block_sum(sum, red);
     lse = (nn == 0 || mx == -INFINITY) ? -INFINITY : mx + logf(sum);
   }
@@ -130,10 +181,10 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
       const int shift = 24 - 8 * pass;
       hist[tid] = 0;
       __syncthreads();
-      for (int j = tid; j < i; j += kGateThreads) {
-        const uint32_t key = order_key(srow[j]);
+      each(i, [&](int, float x) {
+        const uint32_t key = order_key(x);
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-      }
+      });
       __syncthreads();
       if (tid < kWave) {
         const int lane = tid;
@@ -170,32 +221,66 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
   // first `remaining` keys equal to it.
   int32_t *oidx = p.sel_idx + (long)r * p.Kb;
   float *olg = p.sel_lg + (long)r * p.Kb;
+  auto gate_of = [&](float sj) -> float {
+    if (p.mode == kGateSigmoid)  // log sigmoid(s) = min(s, 0) - log(1 + exp(-|s|))
+      return fminf(sj, 0.f) - log1pf(expf(-fabsf(sj)));
+    if (p.mode == kGateRaw) return sj;
+    if (p.mode == kGateSte) return 0.f;  // hard gate
+    return (lse == -INFINITY) ? -INFINITY : sj - lse;
+  };
   int base = 0, eq_base = 0;
+  auto emit = [&](int j, float sj) {  // j: this thread's entry of the chunk
+    const bool valid = j < i;
+    const uint32_t key = order_key(valid ? sj : 0.f);
+    const bool eq = valid && !keep_all && key == prefix;
+    int eq_tot;
+    const int eq_rank = eq_base + block_scan_flag(eq, eq_tot, cnt);
+    const bool take = valid && (keep_all || key > prefix || (eq && eq_rank < remaining));
+    int take_tot;
+    const int pos = base + block_scan_flag(take, take_tot, cnt);
+    if (take) {
+      oidx[pos] = j;
+      olg[pos] = gate_of(sj);
+    }
+    base += take_tot;
+    eq_base += eq_tot;
+  };
   if (k > 0) {
-    for (int c0 = 0; c0 < i; c0 += kGateThreads) {
-      const int j = c0 + tid;
-      const bool valid = j < i;
-      const float sj = valid ? srow[j] : 0.f;
-      const uint32_t key = order_key(sj);
-      const bool eq = valid && !keep_all && key == prefix;
-      int eq_tot;
-      const int eq_rank = eq_base + block_scan_flag(eq, eq_tot, cnt);
-      const bool take = valid && (keep_all || key > prefix || (eq && eq_rank < remaining));
-      int take_tot;
-      const int pos = base + block_scan_flag(take, take_tot, cnt);
-      if (take) {
-        oidx[pos] = j;
-        if (p.mode == kGateSigmoid)  // log sigmoid(s) = min(s, 0) - log(1 + exp(-|s|))
-          olg[pos] = fminf(sj, 0.f) - log1pf(expf(-fabsf(sj)));
-        else if (p.mode == kGateRaw)
-          olg[pos] = sj;
-        else if (p.mode == kGateSte)
-          olg[pos] = 0.f;  // hard gate
-        else
-          olg[pos] = (lse == -INFINITY) ? -INFINITY : sj - lse;
+    if constexpr (R > 0) {
+      // this thread's keys above the threshold and equal to it (the first
+      // `remaining` equal keys in index order are kept)
+      // (bit c of a mask: this thread's entry R tid + c)
+      uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        const int j = R * tid + c;
+        const uint32_t key = order_key(sv[c]);
+        if (j < i && (keep_all || key > prefix)) gtm |= 1u << c;
+        if (j < i && !keep_all && key == prefix) eqm |= 1u << c;
       }
-      base += take_tot;
-      eq_base += eq_tot;
+      int eq_tot;
+      int eq_rank = block_scan_int(__popc(eqm), eq_tot, cnt);
+      uint32_t takem = gtm;
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+        if ((eqm >> c) & 1u) {
+          if (eq_rank < remaining) takem |= 1u << c;
+          ++eq_rank;
+        }
+      int take_tot;
+      int pos = block_scan_int(__popc(takem), take_tot, cnt);
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+        if ((takem >> c) & 1u) {
+          oidx[pos] = R * tid + c;
+          olg[pos] = gate_of(sv[c]);
+          ++pos;
+        }
+    } else {
+      for (int c0 = 0; c0 < i; c0 += kGateThreads) {
+        const int j = c0 + tid;
+        emit(j, j < i ? srow[j] : 0.f);
+      }
     }
   }
   if (tid == 0) {
@@ -211,7 +296,15 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
 
 hipError_t launch_gate_topk(const GateParams &p, hipStream_t stream) {
   if (p.nrows == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_topk_kernel, dim3(p.nrows), dim3(kGateThreads), 0, stream, p);
+  // rows hold at most ld scores (one more than the history in SAS_GATE_ALL
+  // is still within ld): registers when they fit, else re-reads
+  const int64_t per = (p.ld + kGateThreads - 1) / kGateThreads;
+  const dim3 grid(p.nrows), block(kGateThreads);
+  if (per <= 1) hipLaunchKernelGGL(gate_topk_kernel<1>, grid, block, 0, stream, p);
+  else if (per <= 4) hipLaunchKernelGGL(gate_topk_kernel<4>, grid, block, 0, stream, p);
+  else if (per <= 16) hipLaunchKernelGGL(gate_topk_kernel<16>, grid, block, 0, stream, p);
+  else if (per <= 32) hipLaunchKernelGGL(gate_topk_kernel<32>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(gate_topk_kernel<0>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ __device__ inline uint32_t order_key(float x) {
 }
 
 // Workgroup reductions / scans through a small LDS scratch.
+template <int NWV = kGateWaves>
 __device__ inline float block_max(float x, float *red) {
   x = wave_max(x);
   const int w = threadIdx.x / kWave;
@@ -47,10 +48,11 @@ __device__ inline float block_max(float x, float *red) {
   __syncthreads();
   float r = red[0];
 #pragma unroll
-  for (int k = 1; k < kGateWaves; ++k) r = fmaxf(r, red[k]);
+  for (int k = 1; k < NWV; ++k) r = fmaxf(r, red[k]);
   return r;
 }
 
+template <int NWV = kGateWaves>
 __device__ inline float block_sum(float x, float *red) {
   x = wave_sum(x);
   const int w = threadIdx.x / kWave;
@@ -59,12 +61,13 @@ __device__ inline float block_sum(float x, float *red) {
   __syncthreads();
   float r = 0.f;
 #pragma unroll
-  for (int k = 0; k < kGateWaves; ++k) r += red[k];  // fixed order: deterministic
+  for (int k = 0; k < NWV; ++k) r += red[k];  // fixed order: deterministic
   return r;
 }
 
 // Exclusive prefix sum of a non-negative count over the workgroup in
 // thread order, and the total.
+template <int NWV = kGateWaves>
 __device__ inline int block_scan_int(int x, int &total, int *cnt) {
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   int incl = x;
@@ -79,7 +82,7 @@ __device__ inline int block_scan_int(int x, int &total, int *cnt) {
   int off = 0;
   total = 0;
 #pragma unroll
-  for (int k = 0; k < kGateWaves; ++k) {
+  for (int k = 0; k < NWV; ++k) {
     if (k < w) off += cnt[k];
     total += cnt[k];
   }
@@ -88,6 +91,7 @@ __device__ inline int block_scan_int(int x, int &total, int *cnt) {
 
 // Exclusive prefix count of `flag` over the workgroup in thread order, and
 // the total.
+template <int NWV = kGateWaves>
 __device__ inline int block_scan_flag(bool flag, int &total, int *cnt) {
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const uint64_t m = __ballot(flag);
@@ -98,7 +102,7 @@ __device__ inline int block_scan_flag(bool flag, int &total, int *cnt) {
   int off = 0;
   total = 0;
 #pragma unroll
-  for (int k = 0; k < kGateWaves; ++k) {
+  for (int k = 0; k < NWV; ++k) {
     if (k < w) off += cnt[k];
     total += cnt[k];
   }
@@ -116,17 +120,18 @@ __device__ inline void row_geometry(const GateParams &p, int r, int &i) {
   }
 }
 
-// R > 0: the row's scores (at most kGateThreads * R) are read once into
-// registers, thread t holding the R consecutive entries R t .. R t + R - 1;
+// R > 0: the row's scores (at most NT * R) are read once into registers,
+// thread t holding the R consecutive entries R t .. R t + R - 1;
 // every pass below then works on registers instead of re-reading the row
 // (long decode rows have thousands of candidates), and the kept blocks are
 // placed with two workgroup scans in all (entries are in index order across
 // the threads).  R = 0 reads the row in each pass and places the kept
 // blocks chunk by chunk.
-template <int R>
-__global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
-  __shared__ float red[kGateWaves];
-  __shared__ int cnt[kGateWaves];
+template <int R, int NT>
+__global__ __launch_bounds__(NT) void gate_topk_kernel(GateParams p) {
+  constexpr int NWV = NT / kWave;
+  __shared__ float red[NWV];
+  __shared__ int cnt[NWV];
   __shared__ int hist[256];
   __shared__ int s_bin, s_rem;
 
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
         if (j < lim) f(j, sv[c]);
       }
     } else {
-      for (int j = tid; j < lim; j += kGateThreads) f(j, srow[j]);
+      for (int j = tid; j < lim; j += NT) f(j, srow[j]);
     }
   };
 
@@ -165,10 +170,10 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
   if (!independent) {
     float mx = -INFINITY;
     each(nn, [&](int, float x) { mx = fmaxf(mx, x); });
-    mx = block_max(mx, red);
+    mx = block_max<NWV>(mx, red);
     float sum = 0.f;
     if (mx != -INFINITY) each(nn, [&](int, float x) { sum += expf(x - mx); });
-    sum = block_sum(sum, red);
+    sum = block_sum<NWV>(sum, red);
     lse = (nn == 0 || mx == -INFINITY) ? -INFINITY : mx + logf(sum);
   }
 
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
   if (!keep_all && k > 0) {
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      hist[tid] = 0;
+      if (tid < 256) hist[tid] = 0;
       __syncthreads();
       each(i, [&](int, float x) {
         const uint32_t key = order_key(x);
@@ -234,10 +239,10 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
     const uint32_t key = order_key(valid ? sj : 0.f);
     const bool eq = valid && !keep_all && key == prefix;
     int eq_tot;
-    const int eq_rank = eq_base + block_scan_flag(eq, eq_tot, cnt);
+    const int eq_rank = eq_base + block_scan_flag<NWV>(eq, eq_tot, cnt);
     const bool take = valid && (keep_all || key > prefix || (eq && eq_rank < remaining));
     int take_tot;
-    const int pos = base + block_scan_flag(take, take_tot, cnt);
+    const int pos = base + block_scan_flag<NWV>(take, take_tot, cnt);
     if (take) {
       oidx[pos] = j;
       olg[pos] = gate_of(sj);
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
         if (j < i && !keep_all && key == prefix) eqm |= 1u << c;
       }
       int eq_tot;
-      int eq_rank = block_scan_int(__popc(eqm), eq_tot, cnt);
+      int eq_rank = block_scan_int<NWV>(__popc(eqm), eq_tot, cnt);
       uint32_t takem = gtm;
 #pragma unroll
       for (int c = 0; c < R; ++c)
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
           ++eq_rank;
         }
       int take_tot;
-      int pos = block_scan_int(__popc(takem), take_tot, cnt);
+      int pos = block_scan_int<NWV>(__popc(takem), take_tot, cnt);
 #pragma unroll
       for (int c = 0; c < R; ++c)
         if ((takem >> c) & 1u) {
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
           ++pos;
         }
     } else {
-      for (int c0 = 0; c0 < i; c0 += kGateThreads) {
+      for (int c0 = 0; c0 < i; c0 += NT) {
         const int j = c0 + tid;
         emit(j, j < i ? srow[j] : 0.f);
       }
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(GateParams p) {
     olg[k] = (p.mode == 1) ? ((lse == -INFINITY) ? -INFINITY : srow[i] - lse) : 0.f;
     p.gate_lse[r] = lse;
   }
-  for (int x = k + 1 + tid; x < p.Kb; x += kGateThreads) {
+  for (int x = k + 1 + tid; x < p.Kb; x += NT) {
     oidx[x] = -1;
     olg[x] = -INFINITY;
   }
@@ -298,13 +303,20 @@ hipError_t launch_gate_topk(const GateParams &p, hipStream_t stream) {
   if (p.nrows == 0) return hipSuccess;
   // rows hold at most ld scores (one more than the history in SAS_GATE_ALL
   // is still within ld): registers when they fit, else re-reads
-  const int64_t per = (p.ld + kGateThreads - 1) / kGateThreads;
-  const dim3 grid(p.nrows), block(kGateThreads);
-  if (per <= 1) hipLaunchKernelGGL(gate_topk_kernel<1>, grid, block, 0, stream, p);
-  else if (per <= 4) hipLaunchKernelGGL(gate_topk_kernel<4>, grid, block, 0, stream, p);
-  else if (per <= 16) hipLaunchKernelGGL(gate_topk_kernel<16>, grid, block, 0, stream, p);
-  else if (per <= 32) hipLaunchKernelGGL(gate_topk_kernel<32>, grid, block, 0, stream, p);
-  else hipLaunchKernelGGL(gate_topk_kernel<0>, grid, block, 0, stream, p);
+  // (long rows take 1024 threads: 4x the threads on each pass of the few
+  // rows a long-context decode has)
+  const dim3 grid(p.nrows);
+  if (p.ld <= 256) hipLaunchKernelGGL((gate_topk_kernel<1, 256>), grid, dim3(256), 0, stream, p);
+  else if (p.ld <= 1024)
+    hipLaunchKernelGGL((gate_topk_kernel<4, 256>), grid, dim3(256), 0, stream, p);
+  else if (p.ld <= 4096)
+    hipLaunchKernelGGL((gate_topk_kernel<4, 1024>), grid, dim3(1024), 0, stream, p);
+  else if (p.ld <= 8192)
+    hipLaunchKernelGGL((gate_topk_kernel<8, 1024>), grid, dim3(1024), 0, stream, p);
+  else if (p.ld <= 16384)
+    hipLaunchKernelGGL((gate_topk_kernel<16, 1024>), grid, dim3(1024), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gate_topk_kernel<0, 256>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -74,13 +74,15 @@ __global__ __launch_bounds__(256) void pooled_scores_kernel(DecodeParams p) {
   p.scores[((long)b * p.hkv + g) * p.nblk_stride + j] = acc / p.sqrt_d;
 }
 
-// Four consecutive blocks per thread (16-byte loads, four independent chains
-// each in channel order, so every score is bit-identical to the one-block
-// form), channels in batches of 16 loads in flight.  For summary strides
-// that are multiples of 4.
-template <int D>
-__global__ __launch_bounds__(256) void pooled_scores4_kernel(DecodeParams p) {
+// V consecutive blocks per thread (4: 16-byte loads; 1 for short grids, so
+// that a single long sequence still spreads over every compute unit), V
+// independent chains each in channel order, so every score is bit-identical
+// to the one-block form; channels in batches of 64 / V loads in flight.  For
+// summary strides that are multiples of 4.
+template <int D, int V>
+__global__ __launch_bounds__(256) void pooled_scores_vec_kernel(DecodeParams p) {
 #pragma clang fp contract(off)
+  using vec = float __attribute__((ext_vector_type(V)));
   __shared__ float qbar[D];
   const int bg = blockIdx.y;
   const int b = bg / p.hkv, g = bg % p.hkv;
@@ -93,31 +95,30 @@ __global__ __launch_bounds__(256) void pooled_scores4_kernel(DecodeParams p) {
   }
   __syncthreads();
   const int nhist = (p.seqlens[b] - 1) / kBlock;
-  const int j0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  const int j0 = V * (blockIdx.x * blockDim.x + threadIdx.x);
   if (j0 >= nhist) return;
   const float *ks = p.ksum + ((long)b * p.hkv + g) * D * p.nblk_stride + j0;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  constexpr int BATCH = 16;
+  float a[V];
+#pragma unroll
+  for (int c = 0; c < V; ++c) a[c] = 0.f;
+  constexpr int BATCH = 64 / V;
 #pragma unroll 1
   for (int e0 = 0; e0 < D; e0 += BATCH) {
-    float4 v[BATCH];
+    vec v[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u)
-      v[u] = *reinterpret_cast<const float4 *>(ks + (long)(e0 + u) * p.nblk_stride);
+      v[u] = *reinterpret_cast<const vec *>(ks + (long)(e0 + u) * p.nblk_stride);
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const float w = qbar[e0 + u];
-      a0 = fmaf(w, v[u].x, a0);
-      a1 = fmaf(w, v[u].y, a1);
-      a2 = fmaf(w, v[u].z, a2);
-      a3 = fmaf(w, v[u].w, a3);
+#pragma unroll
+      for (int c = 0; c < V; ++c) a[c] = fmaf(w, v[u][c], a[c]);
     }
   }
   float *out = p.scores + ((long)b * p.hkv + g) * p.nblk_stride + j0;
-  out[0] = a0 / p.sqrt_d;
-  if (j0 + 1 < nhist) out[1] = a1 / p.sqrt_d;
-  if (j0 + 2 < nhist) out[2] = a2 / p.sqrt_d;
-  if (j0 + 3 < nhist) out[3] = a3 / p.sqrt_d;
+#pragma unroll
+  for (int c = 0; c < V; ++c)
+    if (j0 + c < nhist) out[c] = a[c] / p.sqrt_d;
 }
 
 // ------------------------------------------------------------------ attend
@@ -454,16 +455,36 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const int b = row / p.hkv, g = row % p.hkv;
   const float *part = p.partial + (long)row * p.nsplit * G * (D + 2);
   TO *o = static_cast<TO *>(p.o);
+  constexpr int U = 8;  // splits whose partials are loaded together
   for (int x = threadIdx.x; x < G * D; x += 256) {
     const int hh = x / D, d = x % D;
     float M = -INFINITY;
-    for (int sp = 0; sp < p.nsplit; ++sp) M = fmaxf(M, part[(sp * G + hh) * (D + 2) + D]);
+    for (int s0 = 0; s0 < p.nsplit; s0 += U) {
+      float mv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        mv[u] = (s0 + u < p.nsplit) ? part[((s0 + u) * G + hh) * (D + 2) + D] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) M = fmaxf(M, mv[u]);
+    }
     float Lsum = 0.f, acc = 0.f;
-    for (int sp = 0; sp < p.nsplit; ++sp) {
-      const float *ps = part + (sp * G + hh) * (D + 2);
-      const float w = (ps[D] == -INFINITY) ? 0.f : fast_exp2(ps[D] - M);
-      Lsum += ps[D + 1] * w;
-      acc += ps[d] * w;
+    for (int s0 = 0; s0 < p.nsplit; s0 += U) {
+      float mv[U], lv[U], av[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float *ps = part + ((s0 + u) * G + hh) * (D + 2);
+        const bool in = s0 + u < p.nsplit;
+        mv[u] = in ? ps[D] : -INFINITY;
+        lv[u] = in ? ps[D + 1] : 0.f;
+        av[u] = in ? ps[d] : 0.f;
+      }
+      // splits in order; a split past the end adds exact zeros
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = (mv[u] == -INFINITY) ? 0.f : fast_exp2(mv[u] - M);
+        Lsum += lv[u] * w;
+        acc += av[u] * w;
+      }
     }
     const int h = g * G + hh;
     o[((long)b * p.hq + h) * D + d] = from_f32<TO>(acc / Lsum);
@@ -480,11 +501,16 @@ hipError_t launch_pool_keys(const DecodeParams &p, hipStream_t stream) {
 
 hipError_t launch_pooled_scores(const DecodeParams &p, hipStream_t stream) {
   if (p.nblk_stride % 4 == 0 && (p.D == 128 || p.D == 64)) {
-    const dim3 grid((p.nblk_stride / 4 + 255) / 256, p.batch * p.hkv);
-    if (p.D == 128)
-      hipLaunchKernelGGL(pooled_scores4_kernel<128>, grid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL(pooled_scores4_kernel<64>, grid, dim3(256), 0, stream, p);
+    const dim3 grid4((p.nblk_stride / 4 + 255) / 256, p.batch * p.hkv);
+    const dim3 grid1((p.nblk_stride + 255) / 256, p.batch * p.hkv);
+    const bool narrow = (long)grid4.x * grid4.y < 256;  // fewer workgroups than CUs
+    if (p.D == 128) {
+      if (narrow) hipLaunchKernelGGL((pooled_scores_vec_kernel<128, 1>), grid1, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((pooled_scores_vec_kernel<128, 4>), grid4, dim3(256), 0, stream, p);
+    } else {
+      if (narrow) hipLaunchKernelGGL((pooled_scores_vec_kernel<64, 1>), grid1, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((pooled_scores_vec_kernel<64, 4>), grid4, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
   }
   hipLaunchKernelGGL(pooled_scores_kernel, dim3((p.nblk_stride + 255) / 256, p.batch * p.hkv),

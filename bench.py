@@ -326,10 +326,20 @@ def decode_bench(args, torch, sas, wl, metrics):
     # decode starts and no dirty line of the flush is written back during it.
     flush = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
-    t_sel = t_dec = 0.0
+    # one step's cache maintenance: a new token per (sequence, kv head)
+    # written at position L - 1 (and a finished block summarised when L - 1
+    # opens a block); timed apart from the selection and the attention
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    k_new, v_new = (torch.randn((spec.batch, spec.hkv, spec.d), device="cuda",
+                                generator=gen).to(torch.bfloat16) for _ in range(2))
+    torch.cuda.synchronize()
+    t_sel = t_dec = t_app = 0.0
     for it in range(args.decode_steps + 3):
         flush.sum()
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        ea, e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+        ea.record()
+        sas.decode_append(prob, k_new, v_new, t["k"], t["v"], ksum)
         e0.record()
         sas.decode_select(prob, t["q"], ksum, out=(sel, lg, glse, scores))
         e1.record()
@@ -337,6 +347,7 @@ def decode_bench(args, torch, sas, wl, metrics):
         e2.record()
         torch.cuda.synchronize()
         if it >= 3:
+            t_app += ea.elapsed_time(e0)
             t_sel += e0.elapsed_time(e1)
             t_dec += e1.elapsed_time(e2)
     n = args.decode_steps
@@ -345,7 +356,8 @@ def decode_bench(args, torch, sas, wl, metrics):
     gbs = kv / (t_dec / n * 1e-3) / 1e9
     scan_gbs = scan / (t_sel / n * 1e-3) / 1e9
     log(f"[bench] decode {t_dec / n * 1e3:.1f} us for {kv / 2**20:.1f} MiB -> {gbs:.0f} GB/s; "
-        f"selection {t_sel / n * 1e3:.1f} us over {scan / 2**20:.1f} MiB summaries")
+        f"selection {t_sel / n * 1e3:.1f} us over {scan / 2**20:.1f} MiB summaries; "
+        f"append {t_app / n * 1e3:.1f} us")
     del t, flush
     torch.cuda.empty_cache()
     desc = (f"paged: batch {spec.batch}, lengths U[32768,131072]" if spec.paged else
@@ -355,7 +367,9 @@ def decode_bench(args, torch, sas, wl, metrics):
             "unit": "GB/s", "frac": round(gbs / metrics.PEAK_HBM_GBS, 4),
             "peak": metrics.PEAK_HBM_GBS, "traffic": traffic_for("decode_attend_kernel"),
             "selection": {"us": round(t_sel / n * 1e3, 2), "summary_bytes": scan,
-                          "GB/s": round(scan_gbs, 1)}}
+                          "GB/s": round(scan_gbs, 1)},
+            "append_us": round(t_app / n * 1e3, 2),
+            "step_us": round((t_app + t_sel + t_dec) / n * 1e3, 2)}
 
 
 def calibration_copy(torch, nbytes=1 << 30, reps=3):

@@ -230,6 +230,26 @@ sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, float
                          void *stream);
 
 /*
+ * sas_decode_append -- one decode step's cache maintenance (review 3-7: the
+ * block summaries follow the growing cache).  p->seqlens already count the
+ * new token (L_b), which is written at position L_b - 1 of every kv head's
+ * row; when that position opens a new block (L_b - 1 a positive multiple
+ * of 64), the block before it has become history and its summary is
+ * written, with exactly the value sas_pool_keys gives it.  Together with
+ * sas_pool_keys over a prefilled prefix (the dense-prefill handoff) this
+ * keeps ksum equal to sas_pool_keys of the whole cache after every step.
+ *   k_new, v_new  [batch][hkv][head_dim] bf16 (the new token's key, value);
+ *   k_cache, v_cache in p->layout (updated in place; paged: the page of
+ *                 position L_b - 1 must be in the page table); ksum
+ *                 [batch][hkv][head_dim][nblk_stride] fp32, updated in place.
+ * The caller owns every buffer; NULL -> SAS_ERR_NULL, bad shapes as for
+ * sas_pool_keys.  Steps are ordered on the stream; the summary read uses
+ * tokens written by earlier steps only.
+ */
+sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, const void *v_new,
+                             void *k_cache, void *v_cache, float *ksum, void *stream);
+
+/*
  * sas_decode_select -- decode-time selection (review 3-7 steps 1-2; GQA
  * groups share one selection): per (batch b, kv head g) row,
  *   qbar_e = (q_{gG} + ... + q_{gG+G-1})_e / G   (fp32, heads in order)

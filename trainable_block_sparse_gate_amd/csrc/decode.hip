@@ -51,6 +51,34 @@ __global__ __launch_bounds__(128) void pool_keys_kernel(DecodeParams p) {
   p.ksum[(((long)b * p.hkv + g) * p.D + e) * p.nblk_stride + j] = acc / (float)kBlock;
 }
 
+// ------------------------------------------------------------------ append
+// One decode step's cache maintenance (review section 3-7: summaries are
+// kept per block as the cache grows).  The new token's key and value go to
+// position L - 1 of its (sequence, kv head) row; when that token opens a new
+// block, the block before it has just become history and gets its summary,
+// summed exactly as pool_keys_kernel sums it.  One thread per channel.
+__global__ __launch_bounds__(128) void append_kernel(DecodeParams p, const __bf16 *k_new,
+                                                     const __bf16 *v_new, __bf16 *kc,
+                                                     __bf16 *vc) {
+#pragma clang fp contract(off)
+  const int bg = blockIdx.x;
+  const int b = bg / p.hkv, g = bg % p.hkv;
+  const int e = threadIdx.x;
+  if (e >= p.D) return;
+  const int tok = p.seqlens[b] - 1;
+  const long src = ((long)b * p.hkv + g) * p.D + e;
+  const long dst = (kv_row(p, kc, b, g, tok) - kc) + e;
+  kc[dst] = k_new[src];
+  vc[dst] = v_new[src];
+  if (tok > 0 && tok % kBlock == 0) {
+    const int j = tok / kBlock - 1;
+    const __bf16 *row = kv_row(p, kc, b, g, j * kBlock);
+    float acc = 0.f;
+    for (int t = 0; t < kBlock; ++t) acc = acc + (float)row[(long)t * p.D + e];
+    p.ksum[(((long)b * p.hkv + g) * p.D + e) * p.nblk_stride + j] = acc / (float)kBlock;
+  }
+}
+
 // ------------------------------------------------------------------ scores
 __global__ __launch_bounds__(256) void pooled_scores_kernel(DecodeParams p) {
 #pragma clang fp contract(off)
@@ -496,6 +524,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 hipError_t launch_pool_keys(const DecodeParams &p, hipStream_t stream) {
   hipLaunchKernelGGL(pool_keys_kernel, dim3(p.nblk_stride, p.batch * p.hkv), dim3(128), 0,
                      stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const DecodeParams &p, const void *k_new, const void *v_new,
+                               void *k_cache, void *v_cache, hipStream_t stream) {
+  hipLaunchKernelGGL(append_kernel, dim3(p.batch * p.hkv), dim3(128), 0, stream, p,
+                     static_cast<const __bf16 *>(k_new), static_cast<const __bf16 *>(v_new),
+                     static_cast<__bf16 *>(k_cache), static_cast<__bf16 *>(v_cache));
   return hipGetLastError();
 }
 

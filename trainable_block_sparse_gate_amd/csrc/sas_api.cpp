@@ -483,6 +483,19 @@ sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, float
   return from_hip(sas::launch_pool_keys(d, (hipStream_t)stream), "pool_keys launch");
 }
 
+sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, const void *v_new,
+                             void *k_cache, void *v_cache, float *ksum, void *stream) {
+  sas_status st = check_decode(p);
+  if (st) return st;
+  REQUIRE(k_new && v_new && k_cache && v_cache && ksum, SAS_ERR_NULL,
+          "a tensor argument of sas_decode_append is NULL");
+  sas::DecodeParams d = decode_params(p);
+  d.ksum = ksum;
+  return from_hip(sas::launch_decode_append(d, k_new, v_new, k_cache, v_cache,
+                                            (hipStream_t)stream),
+                  "decode_append launch");
+}
+
 sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const float *ksum,
                              float *scores, int32_t *sel_idx, float *sel_loggate,
                              float *gate_lse, void *stream) {

@@ -108,6 +108,8 @@ struct DecodeParams {
   float *partial;              // [batch*hkv][nsplit][G][D + 2]
 };
 hipError_t launch_pool_keys(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_append(const DecodeParams &p, const void *k_new, const void *v_new,
+                               void *k_cache, void *v_cache, hipStream_t stream);
 hipError_t launch_pooled_scores(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_attend(const DecodeParams &p, hipStream_t stream);
 

@@ -25,7 +25,7 @@ STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTY
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = ["sas_gate_topk", "sas_fwd", "sas_bwd_workspace_size", "sas_bwd", "sas_bwd_prepare",
            "sas_bwd_dq", "sas_bwd_dkdv", "sas_gate_bwd",
-           "sas_pool_keys", "sas_decode_select", "sas_decode_workspace_size", "sas_decode",
+           "sas_pool_keys", "sas_decode_append", "sas_decode_select", "sas_decode_workspace_size", "sas_decode",
            "sas_status_string", "sas_last_error", "sas_abi_version"]
 
 
@@ -85,6 +85,7 @@ def lib():
             "sas_bwd_dkdv": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "sas_gate_bwd": [P, vp, i64, i32, vp, vp, vp, vp, vp],
             "sas_pool_keys": [DP, vp, vp, vp],
+            "sas_decode_append": [DP, vp, vp, vp, vp, vp, vp],
             "sas_decode_select": [DP, vp, vp, vp, vp, vp, vp, vp],
             "sas_decode_workspace_size": [DP],
             "sas_decode": [DP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -281,6 +282,13 @@ def pool_keys(prob: Decode, k_cache):
                        device=k_cache.device)
     _check(lib().sas_pool_keys(prob.ref, _ptr(k_cache), _ptr(ksum), _stream()))
     return ksum
+
+
+def decode_append(prob: Decode, k_new, v_new, k_cache, v_cache, ksum):
+    """sas_decode_append: write the new token (prob.seqlens count it) into
+    the caches and, when it opens a block, the finished block's summary."""
+    _check(lib().sas_decode_append(prob.ref, _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(ksum), _stream()))
 
 
 def decode_select(prob: Decode, q, ksum, out=None):

@@ -171,6 +171,9 @@ def summarize_trace(d, cmd, out):
             args = re.findall(r"DF16b|f|Li\d+E", m.group(2))
             args = [{"DF16b": "bf16", "f": "float"}.get(a, a[2:-1]) for a in args]
             return f"{m.group(1)}<{', '.join(args)}>"
+        m = re.match(r"_ZN3sas\d+(\w+?_kernel)E", n)
+        if m:  # mangled, no template arguments
+            return f"sas::{m.group(1)}"
         if short_kernel(n):
             return re.sub(r"^void ", "", re.sub(r"\(sas::\w+\)$", "", n))
         m = re.search(r"at::native::[A-Za-z_:]*", n)

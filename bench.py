@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--summary-dtype", default="f32", choices=["f32", "bf16"],
+                    help="decode block-summary storage (bf16 halves the selector's scan)")
     ap.add_argument("--decode-workload", default="paged", choices=["paged", "long"],
                     help="paged: batch 32 paged cache (the metric); long: one sequence of "
                          "524288 tokens in a contiguous cache (selection-dominated)")
@@ -316,10 +318,11 @@ def decode_bench(args, torch, sas, wl, metrics):
     t = wl.draw_decode_device(spec)
     if spec.paged:
         prob = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, True,
-                          spec.max_len, page_table=t["page_table"], num_pages=t["k"].shape[0])
+                          spec.max_len, page_table=t["page_table"], num_pages=t["k"].shape[0],
+                          summary_dtype=args.summary_dtype)
     else:
         prob = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, False,
-                          spec.max_len)
+                          spec.max_len, summary_dtype=args.summary_dtype)
     ksum = sas.pool_keys(prob, t["k"])  # cache maintenance, not timed
     sel, lg, glse, scores = sas.decode_select(prob, t["q"], ksum)
     ws = torch.empty(max(1, sas.decode_workspace_bytes(prob)), dtype=torch.uint8, device="cuda")
@@ -355,7 +358,8 @@ def decode_bench(args, torch, sas, wl, metrics):
             t_dec += e1.elapsed_time(e2)
     n = args.decode_steps
     kv = metrics.decode_kv_bytes(spec.seqlens, spec.hkv, spec.d, spec.budget_blocks)
-    scan = metrics.decode_scan_bytes(spec.seqlens, spec.hkv, spec.d)
+    scan = metrics.decode_scan_bytes(spec.seqlens, spec.hkv, spec.d,
+                                     2 if args.summary_dtype == "bf16" else 4)
     gbs = kv / (t_dec / n * 1e-3) / 1e9
     scan_gbs = scan / (t_sel / n * 1e-3) / 1e9
     log(f"[bench] decode {t_dec / n * 1e3:.1f} us for {kv / 2**20:.1f} MiB -> {gbs:.0f} GB/s; "
@@ -370,6 +374,7 @@ def decode_bench(args, torch, sas, wl, metrics):
             "unit": "GB/s", "frac": round(gbs / metrics.PEAK_HBM_GBS, 4),
             "peak": metrics.PEAK_HBM_GBS, "traffic": traffic_for("decode_attend_kernel"),
             "selection": {"us": round(t_sel / n * 1e3, 2), "summary_bytes": scan,
+                          "summary_dtype": args.summary_dtype,
                           "GB/s": round(scan_gbs, 1)},
             "append_us": round(t_app / n * 1e3, 2),
             "step_us": round((t_app + t_sel + t_dec) / n * 1e3, 2)}

@@ -120,6 +120,13 @@ typedef struct sas_problem {
 } sas_problem;
 
 /* A single-token decode problem over a KV cache. */
+/* Block-summary storage (the pages name reduced-precision summaries as the
+ * way to cut the selector scan's bytes): SAS_SUMMARY_BF16 stores each fp32
+ * mean rounded to the nearest bf16 (ties to even), and the pooled score
+ * reads those rounded values; the score arithmetic is unchanged. */
+#define SAS_SUMMARY_F32 0
+#define SAS_SUMMARY_BF16 1
+
 typedef struct sas_decode_problem {
   int32_t batch;
   int32_t hq, hkv, head_dim, block, budget_blocks;
@@ -136,6 +143,7 @@ typedef struct sas_decode_problem {
   const int32_t *seqlens;       /* device [batch]: cache length L, query token included */
   const int32_t *seqlens_host;  /* host copy */
   const int32_t *page_table;    /* device [batch][max_pages] (paged only) */
+  int32_t summary_dtype;        /* block summaries: SAS_SUMMARY_F32 or SAS_SUMMARY_BF16 */
 } sas_decode_problem;
 
 /*
@@ -224,9 +232,10 @@ sas_status sas_gate_bwd(const sas_problem *p, const float *logits, int64_t ld,
  * sas_pool_keys -- cached block summaries for decode (review 3-7 step 1):
  * the mean key of each full history block j < (L_b - 1) / 64, summed in
  * token order in fp32 and divided by 64.
- *   k_cache in p->layout; ksum out [batch][hkv][head_dim][nblk_stride] fp32.
+ *   k_cache in p->layout; ksum out [batch][hkv][head_dim][nblk_stride] in
+ *   p->summary_dtype (fp32, or bf16 = the fp32 mean rounded to nearest even).
  */
-sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, float *ksum,
+sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, void *ksum,
                          void *stream);
 
 /*
@@ -241,13 +250,14 @@ sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, float
  *   k_new, v_new  [batch][hkv][head_dim] bf16 (the new token's key, value);
  *   k_cache, v_cache in p->layout (updated in place; paged: the page of
  *                 position L_b - 1 must be in the page table); ksum
- *                 [batch][hkv][head_dim][nblk_stride] fp32, updated in place.
+ *                 [batch][hkv][head_dim][nblk_stride] in p->summary_dtype,
+ *                 updated in place.
  * The caller owns every buffer; NULL -> SAS_ERR_NULL, bad shapes as for
  * sas_pool_keys.  Steps are ordered on the stream; the summary read uses
  * tokens written by earlier steps only.
  */
 sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, const void *v_new,
-                             void *k_cache, void *v_cache, float *ksum, void *stream);
+                             void *k_cache, void *v_cache, void *ksum, void *stream);
 
 /*
  * sas_decode_select -- decode-time selection (review 3-7 steps 1-2; GQA
@@ -259,7 +269,7 @@ sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, con
  *   sel_idx / sel_loggate out [batch*hkv][Kb]; gate_lse out [batch*hkv];
  *   scores out [batch][hkv][nblk_stride] fp32 (the pooled scores).
  */
-sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const float *ksum,
+sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const void *ksum,
                              float *scores, int32_t *sel_idx, float *sel_loggate,
                              float *gate_lse, void *stream);
 

@@ -189,14 +189,24 @@ def gate_bwd(cu_seqlens, logits, sel_idx, dlg, hkv, Kb, mode=GATE_HIST, blk=64):
     return out
 
 
-def pool_keys_row(K, blk=64):
-    """fp32 block summaries [nhist, d] of one (sequence, kv head) cache K [L, d]."""
+def round_bf16(x):
+    """Nearest bf16 value (ties to even) of every fp32 entry, as fp32."""
+    x = _f32(x)
+    out = np.empty_like(x)
+    _load().sas_oracle_round_bf16(ctypes.c_int64(x.size), _p(x), _p(out))
+    return out
+
+
+def pool_keys_row(K, blk=64, summary="f32"):
+    """Block summaries [nhist, d] of one (sequence, kv head) cache K [L, d]:
+    the fp32 means, or (summary="bf16") those rounded to bf16, as fp32."""
     K = _f32(K)
     L, d = K.shape
     nhist = (L - 1) // blk
     out = np.empty((max(nhist, 1), d), np.float32)
     _load().sas_oracle_pool_keys_row(L, blk, d, _p(K), _p(out))
-    return out[:nhist]
+    out = out[:nhist]
+    return round_bf16(out) if summary == "bf16" else out
 
 
 def decode_scores_row(q, kbar):
@@ -210,11 +220,11 @@ def decode_scores_row(q, kbar):
     return out[:nhist]
 
 
-def decode_select_row(q, K, Kb, mode=GATE_HIST, blk=64):
+def decode_select_row(q, K, Kb, mode=GATE_HIST, blk=64, summary="f32"):
     """Summaries -> pooled scores -> gate + Top-K for one decode row."""
     L = K.shape[0]
     cur = (L - 1) // blk
-    kbar = pool_keys_row(K, blk)
+    kbar = pool_keys_row(K, blk, summary)
     s = decode_scores_row(q, kbar)
     idx, sl, lse = gate_row(s, cur, Kb, mode)
     return idx, sl, lse, s

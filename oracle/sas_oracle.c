@@ -639,6 +639,29 @@ int sas_oracle_gate_bwd(int nseq, const int32_t *cu, int blk, int hkv, int Kb, i
 /* ---------------------------------------------------------------- decode */
 
 /*
+ * Reduced-precision summary storage (the pages name bf16 / fp8 summaries as
+ * the way to cut the selector scan's bytes): every fp32 value is replaced
+ * by the nearest bf16 value, ties to the even one, and returned as the fp32
+ * number that bf16 value stands for.  Written from the definition: keep the
+ * top 16 bits of the fp32 pattern after adding half a bf16 unit, minus one
+ * when the kept part is even (so exact halves go to even).  NaN stays NaN.
+ */
+int sas_oracle_round_bf16(int64_t n, const float *in, float *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t u;
+    memcpy(&u, &in[i], sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
+      out[i] = in[i];
+      continue;
+    }
+    const uint32_t keep_odd = (u >> 16) & 1u;
+    u = (u + 0x7fffu + keep_odd) & 0xffff0000u;
+    memcpy(&out[i], &u, sizeof u);
+  }
+  return 0;
+}
+
+/*
  * Block summaries of one (sequence, kv head): the mean key of every full
  * history block j < (L-1)/b, in the fixed fp32 order stated in the header
  * ([R] 3-7 step 1: the selector scores cached block summaries).

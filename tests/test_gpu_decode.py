@@ -25,7 +25,7 @@ CASES = {
 }
 
 
-def run_decode(name, paged, out_dtype="bf16", gated=True, seed=7):
+def run_decode(name, paged, out_dtype="bf16", gated=True, seed=7, summary="f32"):
     import torch
     seqlens, hq, hkv, d, Kb = CASES[name]
     say(f"[decode case {name} paged={paged} out={out_dtype} gated={gated}]")
@@ -34,7 +34,7 @@ def run_decode(name, paged, out_dtype="bf16", gated=True, seed=7):
     max_len = max(seqlens)
     npages = host["k"].shape[0] if paged else 0
     prob = sas.Decode(seqlens, hq, hkv, d, Kb, paged, max_len, page_table=host["page_table"],
-                      num_pages=npages, out_dtype=out_dtype)
+                      num_pages=npages, out_dtype=out_dtype, summary_dtype=summary)
     q = dev_tensor(host["q"], host["q_bits"], "bf16")
     kc = dev_tensor(host["k"], host["k_bits"], "bf16")
     vc = dev_tensor(host["v"], host["v_bits"], "bf16")
@@ -43,7 +43,8 @@ def run_decode(name, paged, out_dtype="bf16", gated=True, seed=7):
     o, lse = sas.decode(prob, q, kc, vc, sel, lg if gated else None)
     torch.cuda.synchronize()
     G = hq // hkv
-    ksum_h, scores_h = ksum.cpu().numpy(), scores.cpu().numpy()
+    assert ksum.dtype == (torch.bfloat16 if summary == "bf16" else torch.float32)
+    ksum_h, scores_h = ksum.float().cpu().numpy(), scores.cpu().numpy()
     sel_h, lg_h, glse_h = sel.cpu().numpy(), lg.cpu().numpy(), glse.cpu().numpy()
     o_h, lse_h = o.float().cpu().numpy(), lse.cpu().numpy()
     for b in range(B):
@@ -54,9 +55,9 @@ def run_decode(name, paged, out_dtype="bf16", gated=True, seed=7):
             K = wl.gather_row_cache(host["k"], host["page_table"], b, g, L)
             V = wl.gather_row_cache(host["v"], host["page_table"], b, g, L)
             qg = host["q"][b, g * G:(g + 1) * G]
-            kbar = oracle.pool_keys_row(K)
+            kbar = oracle.pool_keys_row(K, summary=summary)
             assert np.array_equal(ksum_h[b, g, :, :cur].T, kbar), (b, g, "summaries")
-            ridx, rlg, rlse, rs = oracle.decode_select_row(qg, K, Kb)
+            ridx, rlg, rlse, rs = oracle.decode_select_row(qg, K, Kb, summary=summary)
             assert np.array_equal(scores_h[b, g, :cur], rs), (b, g, "scores")
             assert np.array_equal(sel_h[r], ridx), (b, g, sel_h[r], ridx)
             fin = np.isfinite(rlg)
@@ -82,6 +83,15 @@ def test_decode_paged(name):
 
 def test_decode_ungated_and_fp32_output():
     run_decode("mixed_g4_d128", paged=True, out_dtype="f32", gated=False)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("name", ["mixed_g4_d128", "g2_d64"])
+def test_decode_bf16_summaries(name, paged):
+    """Summaries stored as bf16 (the fp32 means rounded to nearest even):
+    summaries, scores and selection bit-exact against the oracle's bf16
+    reading, output at the bf16 bar."""
+    run_decode(name, paged, summary="bf16")
 
 
 def test_paged_equals_contiguous_bitwise():

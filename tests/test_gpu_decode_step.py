@@ -23,15 +23,15 @@ def _bf16_dev(bits):
         torch.bfloat16).cuda()
 
 
-@pytest.mark.parametrize("paged", [False, True])
-def test_decode_step_loop(paged):
+@pytest.mark.parametrize("paged,summary", [(False, "f32"), (True, "f32"), (True, "bf16")])
+def test_decode_step_loop(paged, summary):
     import torch
     L0 = [62, 128, 300, 1, 63, 191]   # steps cross 64, 128 (first step), 192, and none
     steps, hq, hkv, d, Kb = 4, 8, 2, 128, 3
     B, G = len(L0), hq // hkv
     Lfin = [n + steps for n in L0]
     cap = max(Lfin)
-    say(f"[decode step loop paged={paged} L0={L0} steps={steps}]")
+    say(f"[decode step loop paged={paged} summary={summary} L0={L0} steps={steps}]")
     g = wl.rng(43, 1)
     kb = wl.round_bf16(wl.normal(g, (B, hkv, cap, d)))
     vb = wl.round_bf16(wl.normal(g, (B, hkv, cap, d)))
@@ -66,7 +66,8 @@ def test_decode_step_loop(paged):
 
     def problem(lens):
         return sas.Decode(lens, hq, hkv, d, Kb, paged, cap, page_table=pt,
-                          num_pages=sum(npg) if paged else 0, nblk_stride=stride)
+                          num_pages=sum(npg) if paged else 0, nblk_stride=stride,
+                          summary_dtype=summary)
 
     ksum = sas.pool_keys(problem(L0), kc)   # dense-prefill handoff
     for s in range(steps):
@@ -82,7 +83,7 @@ def test_decode_step_loop(paged):
         torch.cuda.synchronize()
         kc_d = kc.view(torch.int16).cpu().numpy().view(np.uint16)
         vc_d = vc.view(torch.int16).cpu().numpy().view(np.uint16)
-        ks_h, sel_h = ksum.cpu().numpy(), sel.cpu().numpy()
+        ks_h, sel_h = ksum.float().cpu().numpy(), sel.cpu().numpy()
         o_h = out.float().cpu().numpy()
         for b in range(B):
             L = lens[b]
@@ -97,10 +98,11 @@ def test_decode_step_loop(paged):
             cur = (L - 1) // 64
             for h in range(hkv):
                 K, V = kf[b, h, :L], vf[b, h, :L]
-                assert np.array_equal(ks_h[b, h, :, :cur].T, oracle.pool_keys_row(K)), \
+                assert np.array_equal(ks_h[b, h, :, :cur].T,
+                                      oracle.pool_keys_row(K, summary=summary)), \
                     (s, b, h, "summaries")
                 qg = qf[s, b, h * G:(h + 1) * G]
-                ridx, rlg, _, _ = oracle.decode_select_row(qg, K, Kb)
+                ridx, rlg, _, _ = oracle.decode_select_row(qg, K, Kb, summary=summary)
                 assert np.array_equal(sel_h[b * hkv + h], ridx), (s, b, h, "selection")
                 ro, _ = oracle.decode_row(qg, K, V, ridx, rlg, Kb, prob.scale)
                 err = float(np.max(np.abs(o_h[b, h * G:(h + 1) * G] - ro)))

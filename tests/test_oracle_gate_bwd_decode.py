@@ -213,3 +213,34 @@ def test_ste_gate_matches_torch_straight_through_autograd():
             else:
                 want = np.zeros(8)
             assert np.max(np.abs(d_logits[g, Q] - want)) < 1e-12, (g, Q)
+
+
+def test_bf16_summary_rounding_matches_torch_conversion():
+    """The oracle's bf16 summary storage is round-to-nearest-even: the same
+    values as torch's fp32 -> bf16 conversion, on random values, exact
+    halfway cases (which must go to the even neighbour), signed zeros,
+    infinities, overflow and subnormals."""
+    import torch
+    g = np.random.default_rng(3)
+    x = np.concatenate([
+        g.standard_normal(4096).astype(np.float32) * np.float32(3.0),
+        np.array([1 + 2**-8, 1 + 3 * 2**-8, -(1 + 2**-8), 1 + 2**-9, 0.0, -0.0, np.inf, -np.inf,
+                  3.3961e38, 1e-40, -1e-41, 2**-126], np.float32)])
+    got = oracle.round_bf16(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # the ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 and goes to 1
+    assert got[4096] == 1.0 and got[4097] == np.float32(1 + 2**-6)
+
+
+def test_bf16_summaries_are_the_rounded_fp32_means():
+    g = np.random.default_rng(4)
+    K = g.standard_normal((64 * 5 + 7, 32)).astype(np.float32)
+    f32 = oracle.pool_keys_row(K)
+    b16 = oracle.pool_keys_row(K, summary="bf16")
+    assert b16.shape == f32.shape == (5, 32)
+    assert np.array_equal(b16, oracle.round_bf16(f32))
+    assert np.max(np.abs(b16 - f32)) <= np.max(np.abs(f32)) * 2.0 ** -8
+    q = g.standard_normal((4, 32)).astype(np.float32)
+    idx, lg, lse, s = oracle.decode_select_row(q, K, 3, summary="bf16")
+    assert np.array_equal(s, oracle.decode_scores_row(q, b16))

@@ -35,6 +35,15 @@ __device__ inline const __bf16 *kv_row(const DecodeParams &p, const __bf16 *cach
   return cache + (((long)b * p.hkv + g) * p.max_seqlen + tok) * p.D;
 }
 
+// A block summary (the fp32 mean) stored as fp32, or rounded to the nearest
+// bf16 (ties to even) when summaries are bf16.
+__device__ inline void store_summary(const DecodeParams &p, long idx, float v) {
+  if (p.sum_bf16)
+    static_cast<__bf16 *>(p.ksum)[idx] = (__bf16)v;
+  else
+    static_cast<float *>(p.ksum)[idx] = v;
+}
+
 // ------------------------------------------------------------------ pool
 __global__ __launch_bounds__(128) void pool_keys_kernel(DecodeParams p) {
 #pragma clang fp contract(off)
@@ -48,7 +57,7 @@ __global__ __launch_bounds__(128) void pool_keys_kernel(DecodeParams p) {
   const __bf16 *row = kv_row(p, k, b, g, j * kBlock);  // a block never crosses a page
   float acc = 0.f;
   for (int t = 0; t < kBlock; ++t) acc = acc + (float)row[(long)t * p.D + e];
-  p.ksum[(((long)b * p.hkv + g) * p.D + e) * p.nblk_stride + j] = acc / (float)kBlock;
+  store_summary(p, (((long)b * p.hkv + g) * p.D + e) * p.nblk_stride + j, acc / (float)kBlock);
 }
 
 // ------------------------------------------------------------------ append
@@ -75,11 +84,13 @@ __global__ __launch_bounds__(128) void append_kernel(DecodeParams p, const __bf1
     const __bf16 *row = kv_row(p, kc, b, g, j * kBlock);
     float acc = 0.f;
     for (int t = 0; t < kBlock; ++t) acc = acc + (float)row[(long)t * p.D + e];
-    p.ksum[(((long)b * p.hkv + g) * p.D + e) * p.nblk_stride + j] = acc / (float)kBlock;
+    store_summary(p, (((long)b * p.hkv + g) * p.D + e) * p.nblk_stride + j,
+                  acc / (float)kBlock);
   }
 }
 
 // ------------------------------------------------------------------ scores
+template <typename TS>
 __global__ __launch_bounds__(256) void pooled_scores_kernel(DecodeParams p) {
 #pragma clang fp contract(off)
   __shared__ float qbar[256];
@@ -96,21 +107,22 @@ __global__ __launch_bounds__(256) void pooled_scores_kernel(DecodeParams p) {
   const int nhist = (p.seqlens[b] - 1) / kBlock;
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= nhist) return;
-  const float *ks = p.ksum + ((long)b * p.hkv + g) * p.D * p.nblk_stride + j;
+  const TS *ks =
+      static_cast<const TS *>(p.ksum) + ((long)b * p.hkv + g) * p.D * p.nblk_stride + j;
   float acc = 0.f;
-  for (int e = 0; e < p.D; ++e) acc = fmaf(qbar[e], ks[(long)e * p.nblk_stride], acc);
+  for (int e = 0; e < p.D; ++e) acc = fmaf(qbar[e], (float)ks[(long)e * p.nblk_stride], acc);
   p.scores[((long)b * p.hkv + g) * p.nblk_stride + j] = acc / p.sqrt_d;
 }
 
-// V consecutive blocks per thread (4: 16-byte loads; 1 for short grids, so
+// V consecutive blocks per thread (4: 16-byte fp32 / 8-byte bf16 loads; 1 for short grids, so
 // that a single long sequence still spreads over every compute unit), V
 // independent chains each in channel order, so every score is bit-identical
 // to the one-block form; channels in batches of 64 / V loads in flight.  For
 // summary strides that are multiples of 4.
-template <int D, int V>
+template <int D, int V, typename TS>
 __global__ __launch_bounds__(256) void pooled_scores_vec_kernel(DecodeParams p) {
 #pragma clang fp contract(off)
-  using vec = float __attribute__((ext_vector_type(V)));
+  using vec = TS __attribute__((ext_vector_type(V)));
   __shared__ float qbar[D];
   const int bg = blockIdx.y;
   const int b = bg / p.hkv, g = bg % p.hkv;
@@ -125,7 +137,8 @@ __global__ __launch_bounds__(256) void pooled_scores_vec_kernel(DecodeParams p) 
   const int nhist = (p.seqlens[b] - 1) / kBlock;
   const int j0 = V * (blockIdx.x * blockDim.x + threadIdx.x);
   if (j0 >= nhist) return;
-  const float *ks = p.ksum + ((long)b * p.hkv + g) * D * p.nblk_stride + j0;
+  const TS *ks =
+      static_cast<const TS *>(p.ksum) + ((long)b * p.hkv + g) * D * p.nblk_stride + j0;
   float a[V];
 #pragma unroll
   for (int c = 0; c < V; ++c) a[c] = 0.f;
@@ -140,7 +153,7 @@ __global__ __launch_bounds__(256) void pooled_scores_vec_kernel(DecodeParams p) 
     for (int u = 0; u < BATCH; ++u) {
       const float w = qbar[e0 + u];
 #pragma unroll
-      for (int c = 0; c < V; ++c) a[c] = fmaf(w, v[u][c], a[c]);
+      for (int c = 0; c < V; ++c) a[c] = fmaf(w, (float)v[u][c], a[c]);
     }
   }
   float *out = p.scores + ((long)b * p.hkv + g) * p.nblk_stride + j0;
@@ -535,23 +548,33 @@ hipError_t launch_decode_append(const DecodeParams &p, const void *k_new, const 
   return hipGetLastError();
 }
 
-hipError_t launch_pooled_scores(const DecodeParams &p, hipStream_t stream) {
+template <typename TS>
+static hipError_t launch_pooled_scores_t(const DecodeParams &p, hipStream_t stream) {
   if (p.nblk_stride % 4 == 0 && (p.D == 128 || p.D == 64)) {
     const dim3 grid4((p.nblk_stride / 4 + 255) / 256, p.batch * p.hkv);
     const dim3 grid1((p.nblk_stride + 255) / 256, p.batch * p.hkv);
     const bool narrow = (long)grid4.x * grid4.y < 256;  // fewer workgroups than CUs
     if (p.D == 128) {
-      if (narrow) hipLaunchKernelGGL((pooled_scores_vec_kernel<128, 1>), grid1, dim3(256), 0, stream, p);
-      else hipLaunchKernelGGL((pooled_scores_vec_kernel<128, 4>), grid4, dim3(256), 0, stream, p);
+      if (narrow)
+        hipLaunchKernelGGL((pooled_scores_vec_kernel<128, 1, TS>), grid1, dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((pooled_scores_vec_kernel<128, 4, TS>), grid4, dim3(256), 0, stream, p);
     } else {
-      if (narrow) hipLaunchKernelGGL((pooled_scores_vec_kernel<64, 1>), grid1, dim3(256), 0, stream, p);
-      else hipLaunchKernelGGL((pooled_scores_vec_kernel<64, 4>), grid4, dim3(256), 0, stream, p);
+      if (narrow)
+        hipLaunchKernelGGL((pooled_scores_vec_kernel<64, 1, TS>), grid1, dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((pooled_scores_vec_kernel<64, 4, TS>), grid4, dim3(256), 0, stream, p);
     }
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(pooled_scores_kernel, dim3((p.nblk_stride + 255) / 256, p.batch * p.hkv),
+  hipLaunchKernelGGL(pooled_scores_kernel<TS>, dim3((p.nblk_stride + 255) / 256, p.batch * p.hkv),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_pooled_scores(const DecodeParams &p, hipStream_t stream) {
+  return p.sum_bf16 ? launch_pooled_scores_t<__bf16>(p, stream)
+                    : launch_pooled_scores_t<float>(p, stream);
 }
 
 template <int D, int G>

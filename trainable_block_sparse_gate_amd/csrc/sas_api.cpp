@@ -404,6 +404,8 @@ sas_status check_decode(const sas_decode_problem *p) {
   REQUIRE(p->layout == SAS_KV_CONTIGUOUS || p->layout == SAS_KV_PAGED, SAS_ERR_SHAPE,
           "unknown layout %d", p->layout);
   REQUIRE(std::isfinite(p->scale), SAS_ERR_SHAPE, "scale is not finite");
+  REQUIRE(p->summary_dtype == SAS_SUMMARY_F32 || p->summary_dtype == SAS_SUMMARY_BF16,
+          SAS_ERR_DTYPE, "unknown summary_dtype %d", p->summary_dtype);
   REQUIRE(p->seqlens && p->seqlens_host, SAS_ERR_NULL, "seqlens (device and host) required");
   int maxL = 0;
   for (int b = 0; b < p->batch; ++b) {
@@ -440,6 +442,7 @@ sas::DecodeParams decode_params(const sas_decode_problem *p) {
   d.D = p->head_dim;
   d.Kb = p->budget_blocks;
   d.nblk_stride = p->nblk_stride;
+  d.sum_bf16 = p->summary_dtype == SAS_SUMMARY_BF16;
   d.sqrt_d = sqrtf((float)p->head_dim);
   d.scale_log2 = p->scale * 1.4426950408889634f;
   d.out_bf16 = p->out_dtype == SAS_BF16;
@@ -471,7 +474,7 @@ size_t sas_decode_workspace_size(const sas_decode_problem *p) {
   return decode_ws_bytes(p);
 }
 
-sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, float *ksum,
+sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, void *ksum,
                          void *stream) {
   sas_status st = check_decode(p);
   if (st) return st;
@@ -484,7 +487,7 @@ sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, float
 }
 
 sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, const void *v_new,
-                             void *k_cache, void *v_cache, float *ksum, void *stream) {
+                             void *k_cache, void *v_cache, void *ksum, void *stream) {
   sas_status st = check_decode(p);
   if (st) return st;
   REQUIRE(k_new && v_new && k_cache && v_cache && ksum, SAS_ERR_NULL,
@@ -496,7 +499,7 @@ sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, con
                   "decode_append launch");
 }
 
-sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const float *ksum,
+sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const void *ksum,
                              float *scores, int32_t *sel_idx, float *sel_loggate,
                              float *gate_lse, void *stream) {
   sas_status st = check_decode(p);
@@ -505,7 +508,7 @@ sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const f
           "a tensor argument of sas_decode_select is NULL");
   sas::DecodeParams d = decode_params(p);
   d.q = q;
-  d.ksum = const_cast<float *>(ksum);
+  d.ksum = const_cast<void *>(ksum);
   d.scores = scores;
   hipError_t e = sas::launch_pooled_scores(d, (hipStream_t)stream);
   if (e != hipSuccess) return from_hip(e, "pooled scores launch");

@@ -95,7 +95,8 @@ struct DecodeParams {
   const int32_t *page_table;   // [batch][max_pages] when paged
   int paged, max_pages, max_seqlen;
   int batch, hq, hkv, D, Kb, nblk_stride;
-  float *ksum;                 // [batch][hkv][D][nblk_stride]
+  void *ksum;                  // [batch][hkv][D][nblk_stride], fp32 or bf16
+  int sum_bf16;                // summaries stored as bf16
   float *scores;               // [batch][hkv][nblk_stride]
   float sqrt_d;                // sqrtf(D), for the pooled score
   const int32_t *sel_idx;      // [batch*hkv][Kb]

@@ -51,9 +51,10 @@ def decode_kv_bytes(seqlens, hkv, d, budget_blocks, elem_bytes=2):
     return total
 
 
-def decode_scan_bytes(seqlens, hkv, d):
-    """fp32 block-summary bytes the pooled selector scans."""
-    return sum((L - 1) // BLOCK for L in seqlens) * hkv * d * 4
+def decode_scan_bytes(seqlens, hkv, d, elem_bytes=4):
+    """Block-summary bytes the pooled selector scans (4 per value for fp32
+    summaries, 2 for bf16)."""
+    return sum((L - 1) // BLOCK for L in seqlens) * hkv * d * elem_bytes
 
 
 def decode_q_bytes(batch, hq, d):

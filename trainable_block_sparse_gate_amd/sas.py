@@ -16,6 +16,7 @@ SAS_BF16, SAS_F32 = 0, 1
 GATE_HIST, GATE_ALL, GATE_SIGMOID, GATE_RAW, GATE_STE = 0, 1, 2, 3, 4
 GATE_INNER, GATE_OUTER = 0, 1  # gate position
 KV_CONTIGUOUS, KV_PAGED = 0, 1
+SUMMARY_F32, SUMMARY_BF16 = 0, 1
 BLOCK = 64
 
 STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTYPE",
@@ -58,6 +59,7 @@ class DecodeProblem(ctypes.Structure):
         ("num_pages", ctypes.c_int32), ("nblk_stride", ctypes.c_int32),
         ("scale", ctypes.c_float), ("seqlens", ctypes.c_void_p),
         ("seqlens_host", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+        ("summary_dtype", ctypes.c_int32),
     ]
 
 
@@ -243,7 +245,7 @@ class Decode:
 
     def __init__(self, seqlens, hq, hkv, head_dim, budget_blocks, paged, max_seqlen,
                  page_table=None, num_pages=0, out_dtype="bf16", scale=None, device="cuda",
-                 nblk_stride=None):
+                 nblk_stride=None, summary_dtype="f32"):
         import torch
         self.seqlens = [int(x) for x in seqlens]
         self.sl_host = np.array(self.seqlens, np.int32)
@@ -269,7 +271,9 @@ class Decode:
             SAS_BF16 if out_dtype == "bf16" else SAS_F32,
             KV_PAGED if paged else KV_CONTIGUOUS, max_seqlen, max_pages, num_pages,
             self.nblk_stride, self.scale, self.sl_dev.data_ptr(), self.sl_host.ctypes.data,
-            self.pt_dev.data_ptr() if paged else None)
+            self.pt_dev.data_ptr() if paged else None,
+            SUMMARY_BF16 if summary_dtype == "bf16" else SUMMARY_F32)
+        self.summary_dtype = summary_dtype
 
     @property
     def ref(self):
@@ -278,7 +282,8 @@ class Decode:
 
 def pool_keys(prob: Decode, k_cache):
     import torch
-    ksum = torch.empty((prob.batch, prob.hkv, prob.d, prob.nblk_stride), dtype=torch.float32,
+    ksum = torch.empty((prob.batch, prob.hkv, prob.d, prob.nblk_stride),
+                       dtype=torch.bfloat16 if prob.summary_dtype == "bf16" else torch.float32,
                        device=k_cache.device)
     _check(lib().sas_pool_keys(prob.ref, _ptr(k_cache), _ptr(ksum), _stream()))
     return ksum

@@ -296,7 +296,7 @@ const char *sas_last_error(void);
 /* ABI version of this header: bumped on any incompatible change. */
 int32_t sas_abi_version(void);
 
-#define SAS_ABI_VERSION 1
+#define SAS_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sas_abi_version() == 1
+    assert lib.sas_abi_version() == sas.ABI_VERSION == 2
     assert lib.sas_status_string(0) == b"ok"
     assert b"unsupported" in lib.sas_status_string(-5)
 

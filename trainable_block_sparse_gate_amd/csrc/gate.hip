@@ -133,7 +133,7 @@ __global__ __launch_bounds__(NT) void gate_topk_kernel(GateParams p) {
   __shared__ float red[NWV];
   __shared__ int cnt[NWV];
   __shared__ int hist[256];
-  __shared__ int s_bin, s_rem;
+  __shared__ int s_bin, s_rem, s_cnt;
 
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -210,6 +210,7 @@ __global__ __launch_bounds__(NT) void gate_topk_kernel(GateParams p) {
           if (cum < remaining && cum + cs[x] >= remaining) {
             s_bin = 4 * lane + x;
             s_rem = remaining - cum;
+            s_cnt = cs[x];
           }
           cum += cs[x];
         }
@@ -218,7 +219,12 @@ __global__ __launch_bounds__(NT) void gate_topk_kernel(GateParams p) {
       prefix |= (uint32_t)s_bin << shift;
       pmask |= 255u << shift;
       remaining = s_rem;
+      const bool whole_bin = s_rem == s_cnt;
       __syncthreads();
+      // every key of the threshold bin is kept: the bits below it cannot
+      // change the kept set, so the select stops (keys then compare on the
+      // bits decided so far)
+      if (whole_bin) break;
     }
   }
 
@@ -236,7 +242,7 @@ __global__ __launch_bounds__(NT) void gate_topk_kernel(GateParams p) {
   int base = 0, eq_base = 0;
   auto emit = [&](int j, float sj) {  // j: this thread's entry of the chunk
     const bool valid = j < i;
-    const uint32_t key = order_key(valid ? sj : 0.f);
+    const uint32_t key = order_key(valid ? sj : 0.f) & pmask;
     const bool eq = valid && !keep_all && key == prefix;
     int eq_tot;
     const int eq_rank = eq_base + block_scan_flag<NWV>(eq, eq_tot, cnt);
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(NT) void gate_topk_kernel(GateParams p) {
 #pragma unroll
       for (int c = 0; c < R; ++c) {
         const int j = R * tid + c;
-        const uint32_t key = order_key(sv[c]);
+        const uint32_t key = order_key(sv[c]) & pmask;
         if (j < i && (keep_all || key > prefix)) gtm |= 1u << c;
         if (j < i && !keep_all && key == prefix) eqm |= 1u << c;
       }

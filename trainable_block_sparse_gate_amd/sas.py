@@ -18,6 +18,7 @@ GATE_INNER, GATE_OUTER = 0, 1  # gate position
 KV_CONTIGUOUS, KV_PAGED = 0, 1
 SUMMARY_F32, SUMMARY_BF16 = 0, 1
 BLOCK = 64
+ABI_VERSION = 2  # the header's SAS_ABI_VERSION these structs follow
 
 STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTYPE",
           -4: "SAS_ERR_ALIGN", -5: "SAS_ERR_UNSUPPORTED", -6: "SAS_ERR_WORKSPACE",
@@ -103,6 +104,9 @@ def lib():
         L.sas_decode_workspace_size.restype = sz
         L.sas_status_string.restype = ctypes.c_char_p
         L.sas_last_error.restype = ctypes.c_char_p
+        if L.sas_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.sas_abi_version()}, the binding "
+                               f"expects {ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib
 

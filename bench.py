@@ -437,7 +437,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the path shards without exchange over kv heads and sequences; see DESIGN.md)",
+              "(the path shards without exchange over kv heads and sequences)",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -6,7 +6,7 @@ import numpy as np
 
 from trainable_block_sparse_gate_amd import workloads as wl
 
-# spec tolerances: max-abs 2e-2 for bf16 paths, 1e-4 for fp32 paths
+# parity tolerances: max-abs 2e-2 for bf16 paths, 1e-4 for fp32 paths
 TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 

@@ -323,14 +323,29 @@ int sas_oracle_bwd(int nseq, const int32_t *cu, int blk, int hq, int hkv, int d,
   int *cuqb = (int *)malloc(sizeof(int) * (nseq + 1));
   int QB = query_block_offsets(nseq, cu, blk, cuqb);
   int T = cu[nseq];
+  long nrows = (long)hkv * QB;
   memset(dq, 0, sizeof(double) * (size_t)T * hq * d);
   memset(dk, 0, sizeof(double) * (size_t)T * hkv * d);
   memset(dv, 0, sizeof(double) * (size_t)T * hkv * d);
-  memset(dlg, 0, sizeof(double) * (size_t)hkv * QB * Kb);
+  memset(dlg, 0, sizeof(double) * (size_t)nrows * Kb);
+  /* Rows whose softmax statistics are needed: those asked for, and those
+   * that keep a key block whose dk / dv are asked for. */
+  unsigned char *need = (unsigned char *)calloc(nrows > 0 ? nrows : 1, 1);
+  for (long r = 0; r < nrows; ++r) {
+    int g = (int)(r / QB), Q = (int)(r % QB);
+    int s = seq_of_qblock(nseq, cuqb, Q);
+    need[r] = row_mask ? row_mask[r] : 1;
+    for (int sl = 0; sl < Kb && !need[r]; ++sl) {
+      int j = sel_idx[r * Kb + sl];
+      if (j >= 0 && (!kblk_mask || kblk_mask[(long)g * QB + cuqb[s] + j])) need[r] = 1;
+    }
+  }
+  /* per (token, head): lse_t = log sum_u exp(z_tu) and D_t = dO_t . o_t */
+  double *lse_t = (double *)malloc(sizeof(double) * ((size_t)T * hq + 1));
+  double *D_t = (double *)malloc(sizeof(double) * ((size_t)T * hq + 1));
   int maxkeys = Kb * blk;
-  long npairs = (long)hkv * nseq;
-  /* Key rows of one (kv head, sequence) are touched only by that pair's rows,
-   * so pairs are independent. */
+
+  /* Query side, one row at a time (rows write disjoint dq and dlg). */
 #pragma omp parallel
   {
     int *u = (int *)malloc(sizeof(int) * maxkeys);
@@ -339,63 +354,47 @@ int sas_oracle_bwd(int nseq, const int32_t *cu, int blk, int hq, int hkv, int d,
     double *P = (double *)malloc(sizeof(double) * maxkeys);
     double *ot = (double *)malloc(sizeof(double) * d);
 #pragma omp for schedule(dynamic, 1)
-    for (long pr = 0; pr < npairs; ++pr) {
-      int g = (int)(pr / nseq), s = (int)(pr % nseq);
+    for (long r = 0; r < nrows; ++r) {
+      if (!need[r]) continue;
+      int g = (int)(r / QB), Q = (int)(r % QB);
+      int s = seq_of_qblock(nseq, cuqb, Q);
+      int i = Q - cuqb[s];
       int start = cu[s], len = cu[s + 1] - cu[s];
-      int nb = cuqb[s + 1] - cuqb[s];
-      for (int i = 0; i < nb; ++i) {
-        long r = (long)g * QB + cuqb[s] + i;
-        const int32_t *idx = sel_idx + r * Kb;
-        const double *lg = sel_lg + r * Kb;
-        int want_row = row_mask ? row_mask[r] : 1;
-        int want_keys = 0;
-        for (int sl = 0; sl < Kb; ++sl) {
-          if (idx[sl] < 0) continue;
-          if (!kblk_mask || kblk_mask[(long)g * QB + cuqb[s] + idx[sl]]) want_keys = 1;
-        }
-        if (!want_row && !want_keys) continue;
-        for (int tl = i * blk; tl < (i + 1) * blk && tl < len; ++tl) {
-          int t = start + tl;
-          int n = attended_keys(idx, Kb, i, blk, start, len, tl, u, slot);
-          for (int hh = 0; hh < G; ++hh) {
-            int h = g * G + hh;
-            const double *qt = q + ((long)t * hq + h) * d;
-            const double *dOt = dO + ((long)t * hq + h) * d;
-            double m = -INFINITY;
-            for (int a = 0; a < n; ++a) {
-              z[a] = scale * dot_dd(qt, k + ((long)u[a] * hkv + g) * d, d) + lg[slot[a]];
-              if (z[a] > m) m = z[a];
-            }
-            double den = 0.0;
-            for (int a = 0; a < n; ++a) den += exp(z[a] - m);
-            for (int e = 0; e < d; ++e) ot[e] = 0.0;
-            for (int a = 0; a < n; ++a) {
-              P[a] = exp(z[a] - m) / den;
-              const double *vu = v + ((long)u[a] * hkv + g) * d;
-              for (int e = 0; e < d; ++e) ot[e] += P[a] * vu[e];
-            }
-            double D = 0.0;
-            for (int e = 0; e < d; ++e) D += dOt[e] * ot[e];
-            for (int a = 0; a < n; ++a) {
-              const double *ku = k + ((long)u[a] * hkv + g) * d;
-              const double *vu = v + ((long)u[a] * hkv + g) * d;
-              double dP = dot_dd(dOt, vu, d);
-              double dS = P[a] * (dP - D);
-              if (want_row) {
-                double *dqt = dq + ((long)t * hq + h) * d;
-                for (int e = 0; e < d; ++e) dqt[e] += scale * dS * ku[e];
-                dlg[r * Kb + slot[a]] += dS;
-              }
-              int kb = idx[slot[a]];
-              if (!kblk_mask || kblk_mask[(long)g * QB + cuqb[s] + kb]) {
-                double *dku = dk + ((long)u[a] * hkv + g) * d;
-                double *dvu = dv + ((long)u[a] * hkv + g) * d;
-                for (int e = 0; e < d; ++e) {
-                  dku[e] += scale * dS * qt[e];
-                  dvu[e] += P[a] * dOt[e];
-                }
-              }
-            }
+      const int32_t *idx = sel_idx + r * Kb;
+      const double *lg = sel_lg + r * Kb;
+      int want_row = row_mask ? row_mask[r] : 1;
+      for (int tl = i * blk; tl < (i + 1) * blk && tl < len; ++tl) {
+        int t = start + tl;
+        int n = attended_keys(idx, Kb, i, blk, start, len, tl, u, slot);
+        for (int hh = 0; hh < G; ++hh) {
+          int h = g * G + hh;
+          const double *qt = q + ((long)t * hq + h) * d;
+          const double *dOt = dO + ((long)t * hq + h) * d;
+          double m = -INFINITY;
+          for (int a = 0; a < n; ++a) {
+            z[a] = scale * dot_dd(qt, k + ((long)u[a] * hkv + g) * d, d) + lg[slot[a]];
+            if (z[a] > m) m = z[a];
+          }
+          double den = 0.0;
+          for (int a = 0; a < n; ++a) den += exp(z[a] - m);
+          for (int e = 0; e < d; ++e) ot[e] = 0.0;
+          for (int a = 0; a < n; ++a) {
+            P[a] = exp(z[a] - m) / den;
+            const double *vu = v + ((long)u[a] * hkv + g) * d;
+            for (int e = 0; e < d; ++e) ot[e] += P[a] * vu[e];
+          }
+          double D = 0.0;
+          for (int e = 0; e < d; ++e) D += dOt[e] * ot[e];
+          lse_t[(long)t * hq + h] = m + log(den);
+          D_t[(long)t * hq + h] = D;
+          if (!want_row) continue;
+          double *dqt = dq + ((long)t * hq + h) * d;
+          for (int a = 0; a < n; ++a) {
+            const double *ku = k + ((long)u[a] * hkv + g) * d;
+            const double *vu = v + ((long)u[a] * hkv + g) * d;
+            double dS = P[a] * (dot_dd(dOt, vu, d) - D);
+            for (int e = 0; e < d; ++e) dqt[e] += scale * dS * ku[e];
+            dlg[r * Kb + slot[a]] += dS;
           }
         }
       }
@@ -406,6 +405,55 @@ int sas_oracle_bwd(int nseq, const int32_t *cu, int blk, int hq, int hkv, int d,
     free(P);
     free(ot);
   }
+
+  /* Key side, one key block at a time (blocks write disjoint dk and dv):
+   * for key u of block j, the sum over every (row, token, head) that
+   * attends to it, in row, token, head order, of
+   *   P_tu = exp(z_tu - lse_t),  dS_tu = P_tu (dO_t . v_u - D_t). */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long x = 0; x < nrows; ++x) {
+    if (kblk_mask && !kblk_mask[x]) continue;
+    int g = (int)(x / QB), Qk = (int)(x % QB);
+    int s = seq_of_qblock(nseq, cuqb, Qk);
+    int j = Qk - cuqb[s];
+    int start = cu[s], len = cu[s + 1] - cu[s];
+    int nb = cuqb[s + 1] - cuqb[s];
+    int lo = j * blk, hi = lo + blk < len ? lo + blk : len;
+    for (int i = j; i < nb; ++i) {
+      long r = (long)g * QB + cuqb[s] + i;
+      int sl = -1;
+      for (int c = 0; c < Kb; ++c)
+        if (sel_idx[r * Kb + c] == j) sl = c;
+      if (sl < 0) continue;
+      double lg = sel_lg[r * Kb + sl];
+      for (int tl = i * blk; tl < (i + 1) * blk && tl < len; ++tl) {
+        int t = start + tl;
+        for (int pu = lo; pu < hi; ++pu) {
+          if (i == j && pu > tl) break; /* causal inside the current block */
+          long uu = start + pu;
+          const double *ku = k + (uu * hkv + g) * d;
+          const double *vu = v + (uu * hkv + g) * d;
+          double *dku = dk + (uu * hkv + g) * d;
+          double *dvu = dv + (uu * hkv + g) * d;
+          for (int hh = 0; hh < G; ++hh) {
+            int h = g * G + hh;
+            const double *qt = q + ((long)t * hq + h) * d;
+            const double *dOt = dO + ((long)t * hq + h) * d;
+            double z = scale * dot_dd(qt, ku, d) + lg;
+            double Ptu = exp(z - lse_t[(long)t * hq + h]);
+            double dS = Ptu * (dot_dd(dOt, vu, d) - D_t[(long)t * hq + h]);
+            for (int e = 0; e < d; ++e) {
+              dku[e] += scale * dS * qt[e];
+              dvu[e] += Ptu * dOt[e];
+            }
+          }
+        }
+      }
+    }
+  }
+  free(lse_t);
+  free(D_t);
+  free(need);
   free(cuqb);
   return 0;
 }

@@ -144,6 +144,17 @@ typedef struct sas_decode_problem {
   const int32_t *seqlens_host;  /* host copy */
   const int32_t *page_table;    /* device [batch][max_pages] (paged only) */
   int32_t summary_dtype;        /* block summaries: SAS_SUMMARY_F32 or SAS_SUMMARY_BF16 */
+  const int32_t *page_table_host; /* optional host copy of page_table (paged only): when
+                                     given, every entry a sequence uses (its first
+                                     ceil(L_b / 64)) is checked to lie in [0, num_pages)
+                                     before any launch (SAS_ERR_SHAPE otherwise); when
+                                     NULL the device entries are trusted */
+  int32_t num_splits;           /* sas_decode: 0 = the library picks the split of every
+                                   row's kept blocks over workgroups (enough workgroups
+                                   to fill the device's compute units); n >= 1 asks for
+                                   n splits (at most budget_blocks; fewer when n does
+                                   not divide the blocks evenly).  The split changes
+                                   only the fp32 summation order of the result. */
 } sas_decode_problem;
 
 /*
@@ -283,6 +294,8 @@ sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const v
  *   lse out [batch][hq] fp32 or NULL.
  *   workspace: at least sas_decode_workspace_size(p) bytes.
  */
+/* The workspace size depends only on the problem (for num_splits = 0 it is
+ * sized for the largest split the library may pick on any device). */
 size_t sas_decode_workspace_size(const sas_decode_problem *p);
 sas_status sas_decode(const sas_decode_problem *p, const void *q, const void *k_cache,
                       const void *v_cache, const int32_t *sel_idx, const float *sel_loggate,
@@ -296,7 +309,7 @@ const char *sas_last_error(void);
 /* ABI version of this header: bumped on any incompatible change. */
 int32_t sas_abi_version(void);
 
-#define SAS_ABI_VERSION 2
+#define SAS_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sas_abi_version() == sas.ABI_VERSION == 2
+    assert lib.sas_abi_version() == sas.ABI_VERSION == 3
     assert lib.sas_status_string(0) == b"ok"
     assert b"unsupported" in lib.sas_status_string(-5)
 
@@ -100,14 +100,17 @@ def test_bwd_workspace_checks(lib):
 
 
 def decode_problem(seqlens=(700, 129), hq=8, hkv=2, d=128, Kb=4, paged=True, max_pages=None,
-                   nblk=None, max_seqlen=None, G_override=None):
+                   nblk=None, max_seqlen=None, page_table_host=None, num_splits=0,
+                   num_pages=32):
     sl = np.array(seqlens, np.int32)
     mp = max_pages if max_pages is not None else (max(seqlens) + 63) // 64
     nb = nblk if nblk is not None else max(1, (max(seqlens) - 1) // 64)
+    pth = None if page_table_host is None else np.ascontiguousarray(page_table_host, np.int32)
     p = sas.DecodeProblem(len(seqlens), hq, hkv, d, 64, Kb, 0, 0, 1 if paged else 0,
-                          max_seqlen if max_seqlen is not None else max(seqlens), mp, 32, nb,
-                          1.0 / np.sqrt(d), FAKE, sl.ctypes.data, FAKE if paged else None)
-    p._keep = sl
+                          max_seqlen if max_seqlen is not None else max(seqlens), mp, num_pages,
+                          nb, 1.0 / np.sqrt(d), FAKE, sl.ctypes.data, FAKE if paged else None, 0,
+                          None if pth is None else pth.ctypes.data, num_splits)
+    p._keep = (sl, pth)
     return p
 
 
@@ -135,3 +138,91 @@ def test_binding_raises_on_rejected_calls(lib):
         sas._check(lib.sas_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None))
     assert e.value.status == -1
     assert "problem is NULL" in str(e.value)
+
+
+def test_decode_page_table_host_checked(lib):
+    """With a host copy of the page table, every page a sequence uses must
+    lie in [0, num_pages); unused entries (past a sequence's pages) are free."""
+    ws = [FAKE, 1 << 20]
+    seqlens = (700, 129)  # 11 and 3 pages
+    table = np.full((2, 11), -1, np.int32)
+    table[0, :11] = np.arange(11)
+    table[1, :3] = [11, 12, 13]
+    good = decode_problem(seqlens, page_table_host=table, num_pages=14)
+    assert lib.sas_decode_workspace_size(ctypes.byref(good)) > 0
+    for b, c, val in ((0, 4, 14), (1, 2, -1), (0, 10, 1 << 20)):
+        bad_table = table.copy()
+        bad_table[b, c] = val
+        p = decode_problem(seqlens, page_table_host=bad_table, num_pages=14)
+        assert lib.sas_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, *ws,
+                              None) == -2
+        assert b"page_table" in lib.sas_last_error()
+        assert lib.sas_decode_append(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+        assert lib.sas_pool_keys(ctypes.byref(p), FAKE, FAKE, None) == -2
+
+
+def test_decode_num_splits_checked_and_sized(lib):
+    """num_splits in [0, budget_blocks]; the workspace follows the split."""
+    sizes = {}
+    for n in (0, 1, 2, 4, 64):
+        p = decode_problem(Kb=64, num_splits=n)
+        sizes[n] = lib.sas_decode_workspace_size(ctypes.byref(p))
+    rows_g_d = 2 * 2 * 4 * (128 + 2) * 4  # (batch x hkv) x G x (d + 2) fp32
+    assert sizes[1] == rows_g_d and sizes[2] == 2 * rows_g_d and sizes[64] == 64 * rows_g_d
+    assert sizes[0] == 16 * rows_g_d  # automatic: at most ceil(64 / 4) splits
+    for n in (-1, 65):
+        p = decode_problem(Kb=64, num_splits=n)
+        assert lib.sas_decode_workspace_size(ctypes.byref(p)) == 0
+        assert lib.sas_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              1 << 30, None) == -2
+
+
+def test_binding_checks_tensors_before_calling():
+    """The binding checks dtype, shape and contiguity of every tensor
+    against the problem before the library sees a pointer (CPU tensors: the
+    device check comes last, so each earlier mistake is what is reported)."""
+    import torch
+    prob = sas.Varlen([200, 64], 8, 2, 128, 4, device="cpu")
+    T, QB = prob.T, prob.QB
+    bf = torch.bfloat16
+    q = torch.zeros(T, 8, 128, dtype=bf)
+    k = torch.zeros(T, 2, 128, dtype=bf)
+    sel = torch.zeros(2, QB, 4, dtype=torch.int32)
+    lg = torch.zeros(2, QB, 4)
+    cases = [
+        (lambda: sas.gate_topk(prob, torch.zeros(2, QB, 4, dtype=bf)), -3),  # bf16 logits
+        (lambda: sas.gate_topk(prob, torch.zeros(2, QB, 3)), -2),  # row shorter than 4 blocks
+        (lambda: sas.gate_topk(prob, torch.zeros(2, QB + 1, 4)), -2),
+        (lambda: sas.gate_topk(prob, torch.zeros(2, QB, 4)), -2),  # CPU tensor
+        (lambda: sas.fwd(prob, q.float(), k, k, sel, lg), -3),
+        (lambda: sas.fwd(prob, q, k[:T - 1], k, sel, lg), -2),
+        (lambda: sas.fwd(prob, q.transpose(0, 1).contiguous().transpose(0, 1), k, k, sel, lg),
+         -2),  # not contiguous
+        (lambda: sas.fwd(prob, q, k, k, sel.long(), lg), -3),
+        (lambda: sas.fwd(prob, q, k, k, sel, lg[:, :, :3]), -2),
+        (lambda: sas.fwd(prob, None, k, k, sel, lg), -1),
+    ]
+    for fn, status in cases:
+        with pytest.raises(sas.SasError) as e:
+            fn()
+        assert e.value.status == status, (str(e.value), status)
+
+
+def test_binding_checks_decode_tensors():
+    import torch
+    table = np.arange(14, dtype=np.int32).reshape(1, 14)
+    prob = sas.Decode([700], 8, 2, 128, 4, True, 896, page_table=table, num_pages=14,
+                      device="cpu")
+    bf = torch.bfloat16
+    with pytest.raises(sas.SasError) as e:
+        sas.pool_keys(prob, torch.zeros(14, 2, 32, 128, dtype=bf))  # pages of 32 rows
+    assert e.value.status == -2
+    with pytest.raises(sas.SasError) as e:
+        sas.pool_keys(prob, torch.zeros(14, 2, 64, 128))  # fp32 cache
+    assert e.value.status == -3
+    q = torch.zeros(1, 8, 128, dtype=bf)
+    cache = torch.zeros(14, 2, 64, 128, dtype=bf)
+    with pytest.raises(sas.SasError) as e:
+        sas.decode(prob, q, cache, cache, torch.zeros(2, 5, dtype=torch.int32), None,
+                   workspace=torch.zeros(16, dtype=torch.uint8))
+    assert e.value.status == -2

@@ -23,7 +23,8 @@ class GatedBlockSparseAttention(torch.autograd.Function):
     """o = gated block-sparse attention(q, k, v; Top-K of gate(logits)).
 
     q [T, hq, d], k / v [T, hkv, d] in the problem's dtype; logits fp32
-    [hkv, QB, ld] (column = key block of the row's own sequence).  Returns
+    [hkv, QB, ld] (column = key block of the row's own sequence; other
+    dtypes or shapes raise SasError before anything runs).  Returns
     (o, sel_idx, sel_loggate); only o is differentiable.  Gradients come
     back in fp32, and torch casts them to each input's dtype.
     """

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -422,11 +423,66 @@ sas_status check_decode(const sas_decode_problem *p) {
             "max_pages (%d) < pages of the longest sequence (%d)", p->max_pages,
             (maxL + 63) / 64);
     REQUIRE(p->num_pages >= 1, SAS_ERR_SHAPE, "num_pages must be >= 1");
+    if (p->page_table_host) {
+      for (int b = 0; b < p->batch; ++b) {
+        const int32_t *row = p->page_table_host + (long)b * p->max_pages;
+        const int used = (p->seqlens_host[b] + 63) / 64;
+        for (int c = 0; c < used; ++c)
+          REQUIRE(row[c] >= 0 && row[c] < p->num_pages, SAS_ERR_SHAPE,
+                  "page_table[%d][%d] = %d is outside [0, num_pages = %d)", b, c, row[c],
+                  p->num_pages);
+      }
+    }
   }
+  REQUIRE(p->num_splits >= 0 && p->num_splits <= p->budget_blocks, SAS_ERR_SHAPE,
+          "num_splits (%d) must be in [0, budget_blocks = %d]", p->num_splits,
+          p->budget_blocks);
   REQUIRE(p->nblk_stride >= 1 && p->nblk_stride >= (maxL - 1) / 64, SAS_ERR_SHAPE,
           "nblk_stride (%d) < history blocks of the longest sequence (%d)", p->nblk_stride,
           (maxL - 1) / 64);
   return SAS_OK;
+}
+
+// Compute units of the current device, queried once per device (256 when
+// there is no device to ask: the value only shapes the decode split).
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Split of every row's kept blocks over workgroups.  Automatic: a
+// workgroup's 4 waves each stream every 4th block of its split, and as many
+// workgroups as the device's compute units hold at once (the attend
+// kernel's residency per unit) keep it streaming in a single round, with at
+// least one block per wave in a split.
+void decode_split(const sas_decode_problem *p, int cu_count, int *nsplit_out,
+                  int *per_split_out) {
+  const int rows = p->batch * p->hkv;
+  int nsplit = p->num_splits;
+  if (nsplit == 0) {
+    const int max_split = (p->budget_blocks + 3) / 4;
+    const int target = cu_count * sas::kDecodeWgPerCu;
+    nsplit = (target + rows - 1) / rows;
+    if (nsplit > max_split) nsplit = max_split;
+    if (nsplit < 1) nsplit = 1;
+  }
+  const int per_split = (p->budget_blocks + nsplit - 1) / nsplit;
+  *per_split_out = per_split;
+  *nsplit_out = (p->budget_blocks + per_split - 1) / per_split;
 }
 
 sas::DecodeParams decode_params(const sas_decode_problem *p) {
@@ -446,25 +502,22 @@ sas::DecodeParams decode_params(const sas_decode_problem *p) {
   d.sqrt_d = sqrtf((float)p->head_dim);
   d.scale_log2 = p->scale * 1.4426950408889634f;
   d.out_bf16 = p->out_dtype == SAS_BF16;
-  // split-K: a workgroup's 4 waves each stream every 4th block of its
-  // split; as many workgroups as the chip holds at once (256 compute units
-  // x the attend kernel's residency) keep it streaming in a single round,
-  // and a split holds at least one block per wave.
-  const int rows = p->batch * p->hkv;
-  const int max_split = (p->budget_blocks + 3) / 4;
-  const int target = 256 * sas::kDecodeWgPerCu;
-  int nsplit = (target + rows - 1) / rows;
-  if (nsplit > max_split) nsplit = max_split;
-  if (nsplit < 1) nsplit = 1;
-  d.per_split = (p->budget_blocks + nsplit - 1) / nsplit;
-  d.nsplit = (p->budget_blocks + d.per_split - 1) / d.per_split;
+  decode_split(p, p->num_splits ? 0 : device_cu_count(), &d.nsplit, &d.per_split);
   return d;
 }
 
-size_t decode_ws_bytes(const sas_decode_problem *p) {
-  const sas::DecodeParams d = decode_params(p);
-  return sizeof(float) * (size_t)p->batch * p->hkv * d.nsplit * (p->hq / p->hkv) *
+// Partial results of split rows: [rows][nsplit][G][D + 2] fp32.
+size_t decode_partial_bytes(const sas_decode_problem *p, int nsplit) {
+  return sizeof(float) * (size_t)p->batch * p->hkv * nsplit * (p->hq / p->hkv) *
          (p->head_dim + 2);
+}
+
+// Workspace sized from the problem alone: the split asked for, or (automatic
+// split) the most splits the library picks on any device.
+size_t decode_ws_bytes(const sas_decode_problem *p) {
+  int nsplit = 0, per_split = 0;
+  decode_split(p, 1 << 30, &nsplit, &per_split);
+  return decode_partial_bytes(p, nsplit);
 }
 
 }  // namespace

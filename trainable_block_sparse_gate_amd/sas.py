@@ -3,6 +3,11 @@
 Every step of the path runs in the library's HIP kernels; this module only
 turns torch device tensors into pointers, allocates outputs with torch, and
 passes torch's current stream.  It raises if the library is not built.
+
+The library sees raw pointers, so before every call the binding checks each
+tensor against the problem: dtype, device, contiguity and shape.  A tensor
+that does not match raises SasError (SAS_ERR_NULL, _DTYPE or _SHAPE) and
+nothing is launched.
 """
 import ctypes
 import os
@@ -18,7 +23,7 @@ GATE_INNER, GATE_OUTER = 0, 1  # gate position
 KV_CONTIGUOUS, KV_PAGED = 0, 1
 SUMMARY_F32, SUMMARY_BF16 = 0, 1
 BLOCK = 64
-ABI_VERSION = 2  # the header's SAS_ABI_VERSION these structs follow
+ABI_VERSION = 3  # the header's SAS_ABI_VERSION these structs follow
 
 STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTYPE",
           -4: "SAS_ERR_ALIGN", -5: "SAS_ERR_UNSUPPORTED", -6: "SAS_ERR_WORKSPACE",
@@ -60,7 +65,8 @@ class DecodeProblem(ctypes.Structure):
         ("num_pages", ctypes.c_int32), ("nblk_stride", ctypes.c_int32),
         ("scale", ctypes.c_float), ("seqlens", ctypes.c_void_p),
         ("seqlens_host", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
-        ("summary_dtype", ctypes.c_int32),
+        ("summary_dtype", ctypes.c_int32), ("page_table_host", ctypes.c_void_p),
+        ("num_splits", ctypes.c_int32),
     ]
 
 
@@ -120,6 +126,43 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+ERR_NULL, ERR_SHAPE, ERR_DTYPE = -1, -2, -3
+
+
+def _need(t, name, dtype, shape):
+    """Check one tensor argument: a tensor of `dtype`, contiguous, of exactly
+    `shape` (an entry None accepts any size along that axis).  That it is on
+    the GPU is checked by _gpu, after every argument's dtype and shape."""
+    import torch
+    if t is None:
+        raise SasError(ERR_NULL, f"{name} is None")
+    if not isinstance(t, torch.Tensor):
+        raise SasError(ERR_SHAPE, f"{name} must be a torch tensor (got {type(t).__name__})")
+    if t.dtype != dtype:
+        raise SasError(ERR_DTYPE, f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != len(shape) or any(w is not None and int(a) != int(w)
+                                    for a, w in zip(t.shape, shape)):
+        raise SasError(ERR_SHAPE, f"{name} has shape {tuple(t.shape)}, expected "
+                       f"{tuple('*' if w is None else w for w in shape)}")
+    if not t.is_contiguous():
+        raise SasError(ERR_SHAPE, f"{name} must be contiguous")
+
+
+def _gpu(*tensors):
+    """Every tensor argument (None skipped) is on the same GPU."""
+    devs = {t.device for t in tensors if t is not None}
+    for dv in devs:
+        if dv.type != "cuda":
+            raise SasError(ERR_SHAPE, f"tensor arguments must be on a GPU (got {dv})")
+    if len(devs) > 1:
+        raise SasError(ERR_SHAPE, f"tensor arguments are on different devices: {sorted(map(str, devs))}")
+
+
+def _torch_dtype(code):
+    import torch
+    return torch.bfloat16 if code == "bf16" else torch.float32
+
+
 def _stream():
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -157,20 +200,51 @@ class Varlen:
         return ctypes.byref(self.s)
 
     def torch_dtype(self, which="in"):
+        return _torch_dtype(self.dtype if which == "in" else self.out_dtype)
+
+    # argument checks (raise SasError before anything reaches the library)
+    def check_logits(self, logits, name):
         import torch
-        d = self.dtype if which == "in" else self.out_dtype
-        return torch.bfloat16 if d == "bf16" else torch.float32
+        _need(logits, name, torch.float32, (self.hkv, self.QB, None))
+        if logits.shape[-1] < max(1, self.max_blocks):
+            raise SasError(ERR_SHAPE, f"{name}: row length {logits.shape[-1]} < blocks of the "
+                           f"longest sequence ({self.max_blocks})")
+
+    def check_selection(self, sel_idx, sel_lg):
+        import torch
+        _need(sel_idx, "sel_idx", torch.int32, (self.hkv, self.QB, self.Kb))
+        _need(sel_lg, "sel_loggate", torch.float32, (self.hkv, self.QB, self.Kb))
+
+    def check_qkv(self, q, k, v):
+        dt = self.torch_dtype("in")
+        _need(q, "q", dt, (self.T, self.hq, self.d))
+        _need(k, "k", dt, (self.T, self.hkv, self.d))
+        _need(v, "v", dt, (self.T, self.hkv, self.d))
+
+    def check_bwd_inputs(self, q, k, v, o, dO, lse, sel_idx, sel_lg, workspace):
+        import torch
+        self.check_qkv(q, k, v)
+        self.check_selection(sel_idx, sel_lg)
+        _need(o, "o", self.torch_dtype("out"), (self.T, self.hq, self.d))
+        _need(dO, "dO", self.torch_dtype("out"), (self.T, self.hq, self.d))
+        _need(lse, "lse", torch.float32, (self.hq, self.T))
+        _need(workspace, "workspace", torch.uint8, (None,))
 
 
 def gate_topk(prob: Varlen, logits, mode=GATE_HIST, out=None):
     """sas_gate_topk -> (sel_idx int32 [hkv,QB,Kb], sel_loggate f32, gate_lse f32)."""
     import torch
+    prob.check_logits(logits, "logits")
     dev = logits.device
     if out is None:
         out = (torch.empty((prob.hkv, prob.QB, prob.Kb), dtype=torch.int32, device=dev),
                torch.empty((prob.hkv, prob.QB, prob.Kb), dtype=torch.float32, device=dev),
                torch.empty((prob.hkv, prob.QB), dtype=torch.float32, device=dev))
     sel, lg, lse = out
+    prob.check_logits(logits, "logits")
+    prob.check_selection(sel, lg)
+    _need(lse, "gate_lse", torch.float32, (prob.hkv, prob.QB))
+    _gpu(logits, sel, lg, lse)
     _check(lib().sas_gate_topk(prob.ref, _ptr(logits), logits.shape[-1], mode, _ptr(sel),
                                _ptr(lg), _ptr(lse), _stream()))
     return sel, lg, lse
@@ -179,11 +253,16 @@ def gate_topk(prob: Varlen, logits, mode=GATE_HIST, out=None):
 def fwd(prob: Varlen, q, k, v, sel_idx, sel_lg, out=None):
     """sas_fwd -> (o [T,hq,d] in the output dtype, lse f32 [hq,T])."""
     import torch
+    prob.check_qkv(q, k, v)
+    prob.check_selection(sel_idx, sel_lg)
     if out is None:
         out = (torch.empty((prob.T, prob.hq, prob.d), dtype=prob.torch_dtype("out"),
                            device=q.device),
                torch.empty((prob.hq, prob.T), dtype=torch.float32, device=q.device))
     o, lse = out
+    _need(o, "o", prob.torch_dtype("out"), (prob.T, prob.hq, prob.d))
+    _need(lse, "lse", torch.float32, (prob.hq, prob.T))
+    _gpu(q, k, v, sel_idx, sel_lg, o, lse)
     _check(lib().sas_fwd(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(sel_idx), _ptr(sel_lg),
                          _ptr(o), _ptr(lse), _stream()))
     return o, lse
@@ -196,14 +275,19 @@ def bwd_workspace_bytes(prob: Varlen):
 def bwd(prob: Varlen, q, k, v, o, dO, lse, sel_idx, sel_lg, workspace=None):
     """sas_bwd -> (dq, dk, dv, d_loggate), all fp32."""
     import torch
+    if workspace is not None:
+        prob.check_bwd_inputs(q, k, v, o, dO, lse, sel_idx, sel_lg, workspace)
+    else:
+        prob.check_bwd_inputs(q, k, v, o, dO, lse, sel_idx, sel_lg,
+                              torch.empty(0, dtype=torch.uint8))
     dev = q.device
     dq = torch.empty((prob.T, prob.hq, prob.d), dtype=torch.float32, device=dev)
     dk = torch.empty((prob.T, prob.hkv, prob.d), dtype=torch.float32, device=dev)
     dv = torch.empty((prob.T, prob.hkv, prob.d), dtype=torch.float32, device=dev)
     dlg = torch.empty(sel_idx.shape, dtype=torch.float32, device=dev)
-    nbytes = bwd_workspace_bytes(prob)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(bwd_workspace_bytes(prob), 1), dtype=torch.uint8, device=dev)
+    _gpu(q, k, v, o, dO, lse, sel_idx, sel_lg, dq, dk, dv, dlg, workspace)
     _check(lib().sas_bwd(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
                          _ptr(sel_idx), _ptr(sel_lg), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlg),
                          _ptr(workspace), workspace.numel(), _stream()))
@@ -217,6 +301,13 @@ def bwd_phases(prob: Varlen, q, k, v, o, dO, lse, sel_idx, sel_lg, out, workspac
     phase name before each phase and with "end" after the last (used to
     record timing events between phases)."""
     dq, dk, dv, dlg = out
+    import torch
+    prob.check_bwd_inputs(q, k, v, o, dO, lse, sel_idx, sel_lg, workspace)
+    _need(dq, "dq", torch.float32, (prob.T, prob.hq, prob.d))
+    _need(dk, "dk", torch.float32, (prob.T, prob.hkv, prob.d))
+    _need(dv, "dv", torch.float32, (prob.T, prob.hkv, prob.d))
+    _need(dlg, "d_loggate", torch.float32, (prob.hkv, prob.QB, prob.Kb))
+    _gpu(q, k, v, o, dO, lse, sel_idx, sel_lg, dq, dk, dv, dlg, workspace)
     L, st, ws, n = lib(), _stream(), _ptr(workspace), workspace.numel()
     if marks:
         marks("prepare")
@@ -236,8 +327,14 @@ def bwd_phases(prob: Varlen, q, k, v, o, dO, lse, sel_idx, sel_lg, out, workspac
 def gate_bwd(prob: Varlen, logits, sel_idx, gate_lse, dlg, mode=GATE_HIST, out=None):
     """sas_gate_bwd -> d_logits f32, shaped like logits."""
     import torch
+    prob.check_logits(logits, "logits")
+    _need(sel_idx, "sel_idx", torch.int32, (prob.hkv, prob.QB, prob.Kb))
+    _need(gate_lse, "gate_lse", torch.float32, (prob.hkv, prob.QB))
+    _need(dlg, "d_loggate", torch.float32, (prob.hkv, prob.QB, prob.Kb))
     if out is None:
         out = torch.empty(logits.shape, dtype=torch.float32, device=logits.device)
+    _need(out, "d_logits", torch.float32, tuple(logits.shape))
+    _gpu(logits, sel_idx, gate_lse, dlg, out)
     _check(lib().sas_gate_bwd(prob.ref, _ptr(logits), logits.shape[-1], mode, _ptr(sel_idx),
                               _ptr(gate_lse), _ptr(dlg), _ptr(out), _stream()))
     return out
@@ -249,7 +346,7 @@ class Decode:
 
     def __init__(self, seqlens, hq, hkv, head_dim, budget_blocks, paged, max_seqlen,
                  page_table=None, num_pages=0, out_dtype="bf16", scale=None, device="cuda",
-                 nblk_stride=None, summary_dtype="f32"):
+                 nblk_stride=None, summary_dtype="f32", num_splits=0):
         import torch
         self.seqlens = [int(x) for x in seqlens]
         self.sl_host = np.array(self.seqlens, np.int32)
@@ -263,11 +360,14 @@ class Decode:
         if nblk_stride is not None:
             self.nblk_stride = int(nblk_stride)
         self.pt_dev = None
+        self.pt_host = None
         max_pages = 0
         if paged:
             pt = np.ascontiguousarray(page_table, np.int32)
+            self.pt_host = pt
             self.pt_dev = torch.tensor(pt, device=device)
             max_pages = pt.shape[1]
+        self.max_seqlen, self.num_pages = int(max_seqlen), int(num_pages)
         self.out_dtype = out_dtype
         self.scale = float(scale if scale is not None else 1.0 / np.sqrt(head_dim))
         self.s = DecodeProblem(
@@ -276,8 +376,32 @@ class Decode:
             KV_PAGED if paged else KV_CONTIGUOUS, max_seqlen, max_pages, num_pages,
             self.nblk_stride, self.scale, self.sl_dev.data_ptr(), self.sl_host.ctypes.data,
             self.pt_dev.data_ptr() if paged else None,
-            SUMMARY_BF16 if summary_dtype == "bf16" else SUMMARY_F32)
+            SUMMARY_BF16 if summary_dtype == "bf16" else SUMMARY_F32,
+            self.pt_host.ctypes.data if paged else None, int(num_splits))
         self.summary_dtype = summary_dtype
+
+    # argument checks (raise SasError before anything reaches the library)
+    def check_q(self, q):
+        import torch
+        _need(q, "q", torch.bfloat16, (self.batch, self.hq, self.d))
+
+    def check_cache(self, cache, name):
+        import torch
+        if self.paged:
+            _need(cache, name, torch.bfloat16, (self.num_pages, self.hkv, BLOCK, self.d))
+        else:
+            _need(cache, name, torch.bfloat16, (self.batch, self.hkv, self.max_seqlen, self.d))
+
+    def check_summaries(self, ksum):
+        _need(ksum, "ksum", _torch_dtype(self.summary_dtype),
+              (self.batch, self.hkv, self.d, self.nblk_stride))
+
+    def check_selection(self, sel_idx, sel_lg, lg_optional=False):
+        import torch
+        rows = self.batch * self.hkv
+        _need(sel_idx, "sel_idx", torch.int32, (rows, self.Kb))
+        if sel_lg is not None or not lg_optional:
+            _need(sel_lg, "sel_loggate", torch.float32, (rows, self.Kb))
 
     @property
     def ref(self):
@@ -286,9 +410,11 @@ class Decode:
 
 def pool_keys(prob: Decode, k_cache):
     import torch
+    prob.check_cache(k_cache, "k_cache")
     ksum = torch.empty((prob.batch, prob.hkv, prob.d, prob.nblk_stride),
                        dtype=torch.bfloat16 if prob.summary_dtype == "bf16" else torch.float32,
                        device=k_cache.device)
+    _gpu(k_cache, ksum)
     _check(lib().sas_pool_keys(prob.ref, _ptr(k_cache), _ptr(ksum), _stream()))
     return ksum
 
@@ -296,6 +422,13 @@ def pool_keys(prob: Decode, k_cache):
 def decode_append(prob: Decode, k_new, v_new, k_cache, v_cache, ksum):
     """sas_decode_append: write the new token (prob.seqlens count it) into
     the caches and, when it opens a block, the finished block's summary."""
+    import torch
+    _need(k_new, "k_new", torch.bfloat16, (prob.batch, prob.hkv, prob.d))
+    _need(v_new, "v_new", torch.bfloat16, (prob.batch, prob.hkv, prob.d))
+    prob.check_cache(k_cache, "k_cache")
+    prob.check_cache(v_cache, "v_cache")
+    prob.check_summaries(ksum)
+    _gpu(k_new, v_new, k_cache, v_cache, ksum)
     _check(lib().sas_decode_append(prob.ref, _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                    _ptr(v_cache), _ptr(ksum), _stream()))
 
@@ -303,6 +436,8 @@ def decode_append(prob: Decode, k_new, v_new, k_cache, v_cache, ksum):
 def decode_select(prob: Decode, q, ksum, out=None):
     """sas_decode_select -> (sel_idx, sel_loggate, gate_lse, scores)."""
     import torch
+    prob.check_q(q)
+    prob.check_summaries(ksum)
     dev = q.device
     rows = prob.batch * prob.hkv
     if out is None:
@@ -312,6 +447,10 @@ def decode_select(prob: Decode, q, ksum, out=None):
                torch.empty((prob.batch, prob.hkv, prob.nblk_stride), dtype=torch.float32,
                            device=dev))
     sel, lg, lse, scores = out
+    prob.check_selection(sel, lg)
+    _need(lse, "gate_lse", torch.float32, (rows,))
+    _need(scores, "scores", torch.float32, (prob.batch, prob.hkv, prob.nblk_stride))
+    _gpu(q, ksum, sel, lg, lse, scores)
     _check(lib().sas_decode_select(prob.ref, _ptr(q), _ptr(ksum), _ptr(scores), _ptr(sel),
                                    _ptr(lg), _ptr(lse), _stream()))
     return sel, lg, lse, scores
@@ -324,6 +463,10 @@ def decode_workspace_bytes(prob: Decode):
 def decode(prob: Decode, q, k_cache, v_cache, sel_idx, sel_lg, workspace=None, out=None):
     """sas_decode -> (o [B,hq,d], lse f32 [B,hq])."""
     import torch
+    prob.check_q(q)
+    prob.check_cache(k_cache, "k_cache")
+    prob.check_cache(v_cache, "v_cache")
+    prob.check_selection(sel_idx, sel_lg, lg_optional=True)
     dev = q.device
     if out is None:
         out = (torch.empty((prob.batch, prob.hq, prob.d),
@@ -331,9 +474,14 @@ def decode(prob: Decode, q, k_cache, v_cache, sel_idx, sel_lg, workspace=None, o
                            device=dev),
                torch.empty((prob.batch, prob.hq), dtype=torch.float32, device=dev))
     o, lse = out
-    nbytes = decode_workspace_bytes(prob)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(decode_workspace_bytes(prob), 1), dtype=torch.uint8,
+                                device=dev)
+    _need(o, "o", _torch_dtype(prob.out_dtype), (prob.batch, prob.hq, prob.d))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (prob.batch, prob.hq))
+    _need(workspace, "workspace", torch.uint8, (None,))
+    _gpu(q, k_cache, v_cache, sel_idx, sel_lg, o, lse, workspace)
     _check(lib().sas_decode(prob.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sel_idx),
                             _ptr(sel_lg), _ptr(o), _ptr(lse), _ptr(workspace),
                             workspace.numel(), _stream()))

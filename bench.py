@@ -1,29 +1,39 @@
 """Throughput of the SAS gated block-sparse attention hot path on one MI355X.
 
-One step = the training pass of the hot path over one batch of the
-Qwen3-4B-shaped layer workload (1 x 16384 tokens, 32 query / 8 KV heads,
-head dim 128, 64-token blocks, budget 1024 tokens = 15 history blocks +
-current, bf16): gate + Top-K -> gated forward -> backward (prepare, dQ and
-log-gate gradient, dK/dV) -> gate backward.  `value` is the step's
-algorithmic fwd+bwd TFLOP/s over the attended (selected-block) pairs.
+One step = the training pass of the hot path over one batch of the packed
+varlen workload (4 sequences of 32768 / 24576 / 16384 / 8192 tokens in one
+buffer, 32 query / 8 KV heads, head dim 128, 64-token blocks, budget 2048
+tokens = 31 history blocks + current, bf16, selector logits N(0,3) with 5 %
+of the key-block columns boosted by +4): gate + Top-K -> gated forward ->
+backward (prepare, dQ and log-gate gradient, dK/dV) -> gate backward.
+`value` is the step's algorithmic fwd+bwd TFLOP/s over the attended
+(selected-block) pairs: 4 d FLOPs per pair and head forward, 10 d backward.
 
-The decode half of the metric is measured in the same run on the batched
-paged workload (batch 32, lengths ~ U[32768, 131072], budget 4096 tokens):
-pooled selection, then split-K decode; its KV GB/s is reported under
-"decode".  Inputs are seeded synthetic tensors, resident in HBM before
-timing.  Per-kernel durations come from HIP events recorded on the stream
-the library launches on.
+Reported in the same JSON line:
+  roofline      the longest-running kernel of the step, credited with its
+                algorithmic FLOPs (metrics.py), over its average duration
+                from HIP events on the stream the library launches on,
+                against the 2.5 PFLOP/s dense bf16 MFMA peak;
+  layer16k      the same step on the 16K-token single-layer workload;
+  decode        paged batch-32 decode (budget 4096 tokens): append, pooled
+                selection, split-K attention; KV GB/s against 8 TB/s;
+  decode_long   one sequence at 131072 and at 524288 tokens (budget 2048);
+  measured_peaks  a bf16 MFMA loop and a streaming read on this device;
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
+Inputs are seeded synthetic tensors, resident in HBM before timing.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload varlen|layer16k]
+                    [--no-cpu-baseline] [--no-decode] [--no-extra]
 
 Profile summaries (no GPU needed; they read rocprofv3 csv output):
-    python bench.py --summarize-trace DIR --cmd "..." --out profiles/X.md
+    python bench.py --summarize-trace DIR --cmd "..." --out profiles/X.md [--skip W]
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --cmd "..." --out profiles/Y.md
+    python bench.py --summarize-counters DIR --cmd "..." --out profiles/Z.md
 The second also writes profiles/traffic.json: HBM bytes per dispatch of the
 library's kernels, from FETCH_SIZE / WRITE_SIZE scaled by what the same
 counters read for the 1 GiB device copy this script runs untimed, tagged
-with a hash of the kernel sources; a bench run reports that traffic only
-while the hash still matches.
+with a hash of the kernel sources and the workload; a bench run reports that
+traffic only while both still match.
 """
 import argparse
 import csv
@@ -47,17 +57,19 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="layer16k", choices=["layer16k", "varlen"])
+    ap.add_argument("--workload", default="varlen", choices=["varlen", "layer16k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the second training workload, the long decode and the peaks")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--summary-dtype", default="f32", choices=["f32", "bf16"],
                     help="decode block-summary storage (bf16 halves the selector's scan)")
-    ap.add_argument("--decode-workload", default="paged", choices=["paged", "long"],
-                    help="paged: batch 32 paged cache (the metric); long: one sequence of "
-                         "524288 tokens in a contiguous cache (selection-dominated)")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--skip", type=int, default=0,
+                    help="summaries: leave out each kernel's first N dispatches (warm-up)")
     ap.add_argument("--cmd", default="", help="command line recorded in a summary")
     ap.add_argument("--out", help="markdown file a summary is written to")
     return ap.parse_args()
@@ -92,18 +104,19 @@ def short_kernel(name):
     return m.group(1) if m else None
 
 
-def read_counter_csv(d):
+def read_csvs(d, suffix):
     rows = []
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
     return rows
 
 
-def summarize_pmc(fetch_dir, write_dir, cmd, out):
+# ------------------------------------------------------------ summaries
+def summarize_pmc(fetch_dir, write_dir, cmd, out, workload):
     per = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        for r in read_counter_csv(d):
+        for r in read_csvs(d, "counter_collection.csv"):
             if r["Counter_Name"] != counter:
                 continue
             k = short_kernel(r["Kernel_Name"])
@@ -127,7 +140,7 @@ def summarize_pmc(fetch_dir, write_dir, cmd, out):
         kernels[k] = {"dispatches": len(c["FETCH_SIZE"]), "fetch_kib": round(fk, 1),
                       "write_kib": round(wk, 1),
                       "bytes_per_launch": int(fk * 1024 * f_fetch + wk * 1024 * f_write)}
-    rec = {"source_hash": source_hash(), "command": cmd,
+    rec = {"source_hash": source_hash(), "workloads": [workload, "paged"], "command": cmd,
            "calibration": {"copy_bytes": CALIBRATION_BYTES, "fetch_kib": round(fetch_cp[-1], 1),
                            "write_kib": round(write_cp[-1], 1), "fetch_factor": round(f_fetch, 4),
                            "write_factor": round(f_write, 4)},
@@ -140,9 +153,11 @@ def summarize_pmc(fetch_dir, write_dir, cmd, out):
              cmd, "```", "",
              f"Calibration: the untimed 1 GiB device copy reads {fetch_cp[-1]:.0f} KiB "
              f"(FETCH_SIZE) and writes {write_cp[-1]:.0f} KiB (WRITE_SIZE) per dispatch, so "
-             f"the counters are scaled by {f_fetch:.4f} (fetch) and {f_write:.4f} (write).",
-             f"Source hash {rec['source_hash']}.", "",
-             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch |",
+             f"the counters are scaled by {f_fetch:.4f} (fetch) and {f_write:.4f} (write).  "
+             "FETCH_SIZE counts every L2 miss, including those the Infinity Cache serves.",
+             f"Source hash {rec['source_hash']}; training kernels on the {workload} workload, "
+             "decode kernels on the paged batch-32 workload (the command runs no other).", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes / launch |",
              "|---|---|---|---|---|"]
     for k, v in kernels.items():
         lines.append(f"| `{k}` | {v['dispatches']} | {v['fetch_kib']:.0f} | {v['write_kib']:.0f} | "
@@ -154,68 +169,110 @@ def summarize_pmc(fetch_dir, write_dir, cmd, out):
     print(text)
 
 
-def summarize_trace(d, cmd, out):
-    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    trace = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
-    if not stats:
-        sys.exit(f"no kernel_stats.csv under {d}")
-    with open(stats[0]) as fh:
-        rows = list(csv.DictReader(fh))
-    info = {}
-    if trace:
-        with open(trace[0]) as fh:
-            for r in csv.DictReader(fh):
-                info.setdefault(r["Kernel_Name"], r)
+def kernel_label(n):
+    m = re.match(r"_ZN3sas\d+(\w+?_kernel)I(\w+?)EEvNS_", n)
+    if m:  # template arguments: DF16b = bf16, f = float, Li<n>E = n, Lb0E / Lb1E = bool
+        args = re.findall(r"DF16b|f|Li\d+E|Lb[01]E", m.group(2))
+        args = [{"DF16b": "bf16", "f": "float", "Lb0E": "false", "Lb1E": "true"}.get(a, a[2:-1])
+                for a in args]
+        return f"{m.group(1)}<{', '.join(args)}>"
+    m = re.match(r"_ZN3sas\d+(\w+?_kernel)E", n)
+    if m:  # mangled, no template arguments
+        return f"sas::{m.group(1)}"
+    if short_kernel(n):
+        return re.sub(r"^void ", "", re.sub(r"\(sas::\w+\)$", "", n))
+    m = re.search(r"at::native::[A-Za-z_:]*", n)
+    return (m.group(0) if m else n[:48]) + " (torch)"
 
-    def name(n):
-        m = re.match(r"_ZN3sas\d+(\w+?_kernel)I(\w+?)EEvNS_", n)
-        if m:  # template arguments: DF16b = bf16, f = float, Li<n>E = n
-            args = re.findall(r"DF16b|f|Li\d+E", m.group(2))
-            args = [{"DF16b": "bf16", "f": "float"}.get(a, a[2:-1]) for a in args]
-            return f"{m.group(1)}<{', '.join(args)}>"
-        m = re.match(r"_ZN3sas\d+(\w+?_kernel)E", n)
-        if m:  # mangled, no template arguments
-            return f"sas::{m.group(1)}"
-        if short_kernel(n):
-            return re.sub(r"^void ", "", re.sub(r"\(sas::\w+\)$", "", n))
-        m = re.search(r"at::native::[A-Za-z_:]*", n)
-        return (m.group(0) if m else n[:48]) + " (torch)"
 
-    lines = ["# Kernel trace summary (rocprofv3 --kernel-trace --stats)", "", "```", cmd, "```",
-             "", "| kernel | calls | avg us | total us | % | WGs | WG size | LDS B | VGPR | AGPR |",
-             "|---|---|---|---|---|---|---|---|---|---|"]
+def summarize_trace(d, cmd, out, skip):
+    """Per-kernel durations from a kernel trace: every dispatch, and the
+    steady state without each kernel's first `skip` dispatches (warm-up)."""
+    rows = read_csvs(d, "kernel_trace.csv")
+    if not rows:
+        sys.exit(f"no kernel_trace.csv under {d}")
+    per = {}
     for r in rows:
-        n = r["Name"]
-        t = info.get(n, {})
-        wg = int(t.get("Workgroup_Size_X", 0) or 0)
+        per.setdefault(r["Kernel_Name"], []).append(r)
+    total = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows)
+    lines = ["# Kernel trace summary (rocprofv3 --kernel-trace --stats)", "", "```", cmd, "```",
+             "", f"Durations in us.  Steady state = every dispatch after each kernel's first "
+             f"{skip} (the warm-up steps of the command).", "",
+             "| kernel | calls | avg (all) | avg (steady) | min | max | % of GPU time | WGs | "
+             "WG size | LDS B | VGPR | AGPR |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    summary = {}
+    for n, rs in sorted(per.items(), key=lambda kv: -sum(int(r["End_Timestamp"]) -
+                                                         int(r["Start_Timestamp"])
+                                                         for r in kv[1])):
+        rs.sort(key=lambda r: int(r["Start_Timestamp"]))
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+        steady = dur[skip:] if len(dur) > skip else dur
+        t = rs[0]
+        wg = int(t.get("Workgroup_Size_X", 0) or 0) * int(t.get("Workgroup_Size_Y", 1) or 1)
         grid = int(t.get("Grid_Size_X", 0) or 0) * int(t.get("Grid_Size_Y", 1) or 1) * \
             int(t.get("Grid_Size_Z", 1) or 1)
         nwg = grid // wg if wg else 0
-        lines.append(f"| `{name(n)}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} | "
-                     f"{nwg} | {wg} | {t.get('LDS_Block_Size', '')} | {t.get('VGPR_Count', '')} | "
+        lab = kernel_label(n)
+        summary[lab] = {"calls": len(dur), "avg_us": sum(dur) / len(dur),
+                        "steady_avg_us": sum(steady) / len(steady)}
+        lines.append(f"| `{lab}` | {len(dur)} | {sum(dur) / len(dur):.1f} | "
+                     f"{sum(steady) / len(steady):.1f} | {min(dur):.1f} | {max(dur):.1f} | "
+                     f"{100.0 * sum(dur) * 1e3 / total:.1f} | {nwg} | {wg} | "
+                     f"{t.get('LDS_Block_Size', '')} | {t.get('VGPR_Count', '')} | "
                      f"{t.get('Accum_VGPR_Count', '')} |")
     text = "\n".join(lines) + "\n"
     if out:
         with open(out, "w") as fh:
             fh.write(text)
+        with open(os.path.splitext(out)[0] + ".json", "w") as fh:
+            json.dump({"command": cmd, "skip": skip, "kernels": summary}, fh, indent=1)
     print(text)
 
 
-def traffic_for(kernel):
+def summarize_counters(d, cmd, out):
+    """Average of every counter per kernel (one --pmc pass)."""
+    per = {}
+    for r in read_csvs(d, "counter_collection.csv"):
+        k = kernel_label(r["Kernel_Name"])
+        per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for v in per.values() for c in v})
+    lines = ["# Hardware counters per dispatch (rocprofv3 --pmc)", "", "```", cmd, "```", "",
+             "Averages over the dispatches of each kernel.", "",
+             "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    rec = {}
+    for k, c in sorted(per.items()):
+        if not short_kernel(k) and "sas" not in k:
+            continue
+        vals = {n: (sum(c[n]) / len(c[n]) if n in c else None) for n in names}
+        rec[k] = vals
+        lines.append(f"| `{k}` | " + " | ".join("" if vals[n] is None else f"{vals[n]:.4g}"
+                                                 for n in names) + " |")
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as fh:
+            fh.write(text)
+        with open(os.path.splitext(out)[0] + ".json", "w") as fh:
+            json.dump({"command": cmd, "kernels": rec}, fh, indent=1)
+    print(text)
+
+
+def traffic_for(kernel, workload):
     """HBM bytes per launch of `kernel` from profiles/traffic.json, or None
-    when there is none or the kernels have changed since it was taken."""
+    when there is none, it was taken on another workload, or the kernels
+    have changed since it was taken."""
     try:
         with open(TRAFFIC_JSON) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash() or workload not in rec.get("workloads", []):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return k["bytes_per_launch"] if k else None
 
 
+# ------------------------------------------------------------ timing
 class Marks:
     """HIP events between the phases of a step, summed over steps."""
 
@@ -240,7 +297,15 @@ class Marks:
         self.events = []
 
 
-def train_bench(args, torch, sas, wl, metrics, case):
+# phase -> the kernels it launches (the first is the one the phase is named for)
+PHASE_KERNELS = {"gate_topk": ["gate_topk_kernel"], "fwd": ["fwd_kernel"],
+                 "bwd_prepare": ["bwd_csr_kernel", "bwd_seg_scan_kernel"],
+                 "bwd_dq": ["bwd_dq_kernel"],
+                 "bwd_dkdv": ["bwd_dkdv_kernel", "bwd_dkdv_reduce_kernel"],
+                 "gate_bwd": ["gate_bwd_kernel"]}
+
+
+def train_bench(args, torch, sas, metrics, case, steps, warmup):
     log(f"[bench] workload {case.name}: T={case.T} hq={case.hq} hkv={case.hkv} d={case.d} "
         f"Kb={case.budget_blocks}")
     prob = sas.Varlen(case.lengths, case.hq, case.hkv, case.d, case.budget_blocks)
@@ -275,44 +340,60 @@ def train_bench(args, torch, sas, wl, metrics, case):
         marks("end")
 
     nop = lambda n: None  # noqa: E731
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step(nop)
     torch.cuda.synchronize()
     marks = Marks(torch)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step(marks)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     marks.collect()
-    ms_step = wall * 1e3 / args.steps
-    phases = {n: marks.total[n] / args.steps for n in marks.order}
+    ms_step = wall * 1e3 / steps
+    phases = {n: marks.total[n] / steps for n in marks.order}
     fl = metrics.train_flops(case.lengths, case.hq, case.d, case.budget_blocks)
     tflops = (fl["fwd"] + fl["bwd"]) / (ms_step * 1e-3) / 1e12
     log(f"[bench] step {ms_step:.3f} ms  ->  {tflops:.1f} TFLOP/s  phases(ms): " +
         ", ".join(f"{n}={t:.3f}" for n, t in phases.items()))
-    # dominant kernel: the largest single-kernel phase
-    kern = {"fwd": ("fwd_kernel", fl["fwd"]), "bwd_dq": ("bwd_dq_kernel", fl["dq_kernel"]),
-            "bwd_dkdv": ("bwd_dkdv_kernel", fl["dkdv_kernel"])}
-    dom = max(kern, key=lambda n: phases.get(n, 0.0))
-    achieved = kern[dom][1] / (phases[dom] * 1e-3) / 1e12
-    roof = {"kernel": kern[dom][0], "bound": "mfma", "achieved": round(achieved, 2),
-            "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+    # algorithmic FLOPs credited to each kernel (metrics.py)
+    credit = {"fwd": fl["fwd"], "bwd_dq": fl["dq_kernel"], "bwd_dkdv": fl["dkdv_kernel"]}
+    executed = {"fwd": fl["fwd"], "bwd_dq": fl["dq_kernel_executed"],
+                "bwd_dkdv": fl["dkdv_kernel_executed"]}
+    per_kernel = {}
+    for n in credit:
+        tf = credit[n] / (phases[n] * 1e-3) / 1e12
+        per_kernel[n] = {"kernels": PHASE_KERNELS[n], "ms": round(phases[n], 4),
+                         "algorithmic_tflops": round(tf, 2),
+                         "frac": round(tf / metrics.PEAK_BF16_TFLOPS, 4),
+                         "executed_tflops": round(executed[n] / (phases[n] * 1e-3) / 1e12, 2)}
+    dom = max(credit, key=lambda n: phases.get(n, 0.0))
+    achieved = credit[dom] / (phases[dom] * 1e-3) / 1e12
+    kname = PHASE_KERNELS[dom][0]
+    roof = {"kernel": " + ".join(PHASE_KERNELS[dom]), "bound": "mfma",
+            "achieved": round(achieved, 2), "peak": metrics.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / metrics.PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_for(kern[dom][0]),
-            "ms_per_launch": round(phases[dom], 4)}
-    per_kernel = {n: {"ms": round(phases[n], 4),
-                      "tflops": round(kern[n][1] / (phases[n] * 1e-3) / 1e12, 2)}
-                  for n in kern}
+            "traffic": traffic_for(kname, case.name),
+            "ms_per_launch": round(phases[dom], 4),
+            "algorithmic_flops_per_launch": credit[dom],
+            "flops_credit": {"fwd": "4d", "bwd_dq": "4d", "bwd_dkdv": "6d"}[dom] +
+                            " per attended pair and head"}
+    bwd_ms = phases["bwd_prepare"] + phases["bwd_dq"] + phases["bwd_dkdv"]
+    step_kernels_ms = sum(phases.values())
     out = {"ms_per_step": ms_step, "tflops": tflops, "phases_ms": phases, "flops": fl,
-           "roofline": roof, "kernels": per_kernel}
+           "roofline": roof, "kernels": per_kernel,
+           "backward": {"ms": round(bwd_ms, 4),
+                        "tflops": round(fl["bwd"] / (bwd_ms * 1e-3) / 1e12, 2),
+                        "frac": round(fl["bwd"] / (bwd_ms * 1e-3) / 1e12 /
+                                      metrics.PEAK_BF16_TFLOPS, 4)},
+           "step_frac": round(tflops / metrics.PEAK_BF16_TFLOPS, 4),
+           "step_kernels_ms": round(step_kernels_ms, 4)}
     del q, k, v, dO, o, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return out
 
 
-def decode_bench(args, torch, sas, wl, metrics):
-    spec = wl.paged_spec() if args.decode_workload == "paged" else wl.decode_spec(524288)
+def decode_bench(args, torch, sas, wl, metrics, spec):
     log(f"[bench] decode workload {spec.name}: batch {spec.batch}, lengths "
         f"{min(spec.seqlens)}..{max(spec.seqlens)}, Kb={spec.budget_blocks}")
     t = wl.draw_decode_device(spec)
@@ -372,12 +453,67 @@ def decode_bench(args, torch, sas, wl, metrics):
     return {"workload": f"{desc}, 32/8 heads, d128, budget {spec.budget_blocks} blocks",
             "kv_bytes": kv, "us": round(t_dec / n * 1e3, 2), "value": round(gbs, 1),
             "unit": "GB/s", "frac": round(gbs / metrics.PEAK_HBM_GBS, 4),
-            "peak": metrics.PEAK_HBM_GBS, "traffic": traffic_for("decode_attend_kernel"),
+            "peak": metrics.PEAK_HBM_GBS,
+            "traffic": traffic_for("decode_attend_kernel", spec.name),
             "selection": {"us": round(t_sel / n * 1e3, 2), "summary_bytes": scan,
                           "summary_dtype": args.summary_dtype,
                           "GB/s": round(scan_gbs, 1)},
             "append_us": round(t_app / n * 1e3, 2),
             "step_us": round((t_app + t_sel + t_dec) / n * 1e3, 2)}
+
+
+def measured_peaks(torch, metrics):
+    """A bf16 MFMA loop and a streaming read on this device (libsas_peaks.so)."""
+    import ctypes
+    from trainable_block_sparse_gate_amd import build
+    if not os.path.exists(build.PEAKS_LIB):
+        return None
+    L = ctypes.CDLL(build.PEAKS_LIB)
+    L.sas_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.sas_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_void_p]
+    chains = L.sas_peak_mfma_chains()
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.empty(cus * 8 * 256, dtype=torch.float32, device="cuda")
+    wgs, iters = cus * 8, 4096
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    ms = timed(lambda: L.sas_peak_mfma_bf16(wgs, iters, ctypes.c_void_p(sink.data_ptr()), st))
+    flops = wgs * 4 * iters * chains * 32 * 32 * 16 * 2
+    mfma_tf = flops / (ms * 1e-3) / 1e12
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    rsink = torch.empty(cus * 16 * 256, dtype=torch.int32, device="cuda")
+    ms_r = timed(lambda: L.sas_peak_read(ctypes.c_void_p(buf.data_ptr()), nbytes, cus * 16,
+                                         ctypes.c_void_p(rsink.data_ptr()), st))
+    read_gbs = nbytes / (ms_r * 1e-3) / 1e9
+    del buf, rsink, sink
+    torch.cuda.empty_cache()
+    log(f"[bench] measured peaks: bf16 MFMA {mfma_tf:.0f} TFLOP/s, streaming read "
+        f"{read_gbs:.0f} GB/s ({cus} compute units)")
+    return {"bf16_mfma_tflops": round(mfma_tf, 1),
+            "bf16_mfma_frac_of_spec": round(mfma_tf / metrics.PEAK_BF16_TFLOPS, 4),
+            "stream_read_gbs": round(read_gbs, 1),
+            "stream_read_frac_of_spec": round(read_gbs / metrics.PEAK_HBM_GBS, 4),
+            "compute_units": cus,
+            "how": (f"MFMA: {wgs} workgroups x 4 waves, each {iters} x {chains} independent "
+                    "32x32x16 bf16 MFMAs on registers; read: 4 GiB grid-stride 16-byte loads; "
+                    "best of 5 launches (HIP events)")}
 
 
 def calibration_copy(torch, nbytes=1 << 30, reps=3):
@@ -392,6 +528,17 @@ def calibration_copy(torch, nbytes=1 << 30, reps=3):
     del src, dst
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, metrics):
     """The oracle as it stands, on a bounded sample of the same workload: the
     last NS query blocks of every kv head (steady state: every row keeps the
@@ -401,7 +548,7 @@ def cpu_baseline(case, metrics):
     nb = case.qblocks[-1]
     QB = case.total_qblocks
     rm = np.zeros((case.hkv, QB), np.uint8)
-    NS = min(128, nb - case.budget_blocks)
+    NS = min(64, nb - case.budget_blocks)
     rm[:, QB - NS:QB] = 1  # last NS query blocks of the last sequence
     t0 = time.perf_counter()
     idx, sl, _ = oracle.gate_topk(case.cu_seqlens, case.logits, case.hkv, case.budget_blocks)
@@ -419,36 +566,59 @@ def cpu_baseline(case, metrics):
     secs = t3 - t1
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": (f"fwd+bwd of the last {NS} query blocks of all {case.hkv} kv heads "
                        f"({NS * case.hkv} rows, {pairs} attended pairs) of the same workload, "
-                       f"fp64; fwd {t2 - t1:.1f} s, bwd {t3 - t2:.1f} s (bwd parallel over "
-                       f"kv heads); gate+Top-K of all rows {t1 - t0:.2f} s not counted"),
+                       f"fp64, algorithmic 14d FLOPs per pair and head; fwd {t2 - t1:.1f} s, "
+                       f"bwd {t3 - t2:.1f} s; gate+Top-K of all rows {t1 - t0:.2f} s not "
+                       "counted"),
             "seconds": round(secs, 2)}
 
 
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.cmd, args.out)
+        summarize_trace(args.summarize_trace, args.cmd, args.out, args.skip)
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.cmd, args.out)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.cmd, args.out,
+                      args.workload)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.cmd, args.out)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the path shards without exchange over kv heads and sequences)",
-              file=sys.stderr)
+              "(the path shards without exchange over kv heads and sequences; this run "
+              "uses one GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     from trainable_block_sparse_gate_amd import metrics, sas
     from trainable_block_sparse_gate_amd import workloads as wl
     sas.lib()  # fail loudly when the library is missing
     t0 = time.perf_counter()
-    case = wl.layer16k() if args.workload == "layer16k" else wl.varlen()
+    case = wl.varlen() if args.workload == "varlen" else wl.layer16k()
     log(f"[bench] inputs drawn in {time.perf_counter() - t0:.1f} s")
-    tr = train_bench(args, torch, sas, wl, metrics, case)
-    dec = None if args.no_decode else decode_bench(args, torch, sas, wl, metrics)
+    tr = train_bench(args, torch, sas, metrics, case, args.steps, args.warmup)
+    extra_train = None
+    if not args.no_extra:
+        other = wl.layer16k() if args.workload == "varlen" else wl.varlen()
+        r = train_bench(args, torch, sas, metrics, other, args.steps, args.warmup)
+        extra_train = {"workload": other.name, "tokens": other.T,
+                       "budget_blocks": other.budget_blocks,
+                       "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["tflops"], 2),
+                       "step_frac": r["step_frac"], "phases_ms":
+                       {k: round(v, 4) for k, v in r["phases_ms"].items()},
+                       "kernels": r["kernels"], "backward": r["backward"],
+                       "roofline": r["roofline"]}
+        del other
+    dec = None if args.no_decode else decode_bench(args, torch, sas, wl, metrics,
+                                                   wl.paged_spec())
+    dec_long = None
+    if not args.no_decode and not args.no_extra:
+        dec_long = {str(c): decode_bench(args, torch, sas, wl, metrics, wl.decode_spec(c))
+                    for c in (131072, 524288)}
+    peaks = None if args.no_extra else measured_peaks(torch, metrics)
     calibration_copy(torch)
     cpu = None
     if not args.no_cpu_baseline:
@@ -466,18 +636,26 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded normal q/k/v/dO, selector logits N(0,2))",
-        "config": {"workload": (f"{case.name}: {len(case.lengths)} x {case.T} tokens, "
+        "data": ("synthetic (seeded normal q/k/v/dO; selector logits N(0,3) with 5% of key-block "
+                 "columns +4)" if case.name == "varlen" else
+                 "synthetic (seeded normal q/k/v/dO, selector logits N(0,2))"),
+        "config": {"workload": (f"{case.name}: {len(case.lengths)} packed sequences "
+                                f"{'/'.join(map(str, case.lengths))} ({case.T} tokens), "
                                 f"{case.hq}/{case.hkv} heads, head_dim {case.d}, block 64, "
                                 f"budget {case.budget_blocks} blocks (incl. current), "
                                 "gate+topk+fwd+bwd+gate_bwd"),
                    "tokens": case.T, "budget_blocks": case.budget_blocks,
                    "attended_pairs": tr["flops"]["pairs"],
                    "fwd_flops": tr["flops"]["fwd"], "bwd_flops": tr["flops"]["bwd"]},
+        "step_frac": tr["step_frac"],
         "phases_ms": {k: round(v, 4) for k, v in tr["phases_ms"].items()},
         "kernels": tr["kernels"],
+        "backward": tr["backward"],
         "roofline": tr["roofline"],
+        extra_train["workload"] if extra_train else "extra_train": extra_train,
         "decode": dec,
+        "decode_long": dec_long,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -1,7 +1,10 @@
 """Build ``libsas.so`` (the HIP kernels + C ABI) for gfx950 with hipcc.
 
 Objects go to ``_build/`` at the repository root; the shared library is
-written next to this file so the binding finds it in-tree.
+written next to this file so the binding finds it in-tree.  The same call
+builds ``libsas_peaks.so`` (``csrc/peaks.hip``), the MFMA-loop and
+streaming-read kernels the benchmark measures the device's peaks with; the
+SAS library does not contain or load it.
 """
 import concurrent.futures as cf
 import os
@@ -12,9 +15,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsas.so")
+PEAKS_LIB = os.path.join(HERE, "libsas_peaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["sas_api.cpp", "gate.hip", "fwd.hip", "bwd.hip", "bwd_dkdv.hip", "decode.hip"]
+PEAKS_SOURCES = ["peaks.hip"]
 
 # Kernels whose accumulators and MFMA results are better placed by asking for
 # the VGPR form of MFMA (fewer accumulator moves between AGPRs and VGPRs in the
@@ -50,16 +55,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+def _link(objs, out, verbose):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = [s for s in SOURCES + PEAKS_SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES if s in objs], LIB, verbose)
+    _link([objs[s] for s in PEAKS_SOURCES if s in objs], PEAKS_LIB, verbose)
     return LIB
 
 

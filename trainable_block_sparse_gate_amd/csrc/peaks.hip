@@ -1,0 +1,82 @@
+// Measured peaks of the device, for the roofline figures the benchmark
+// reports beside the datasheet peaks.  Not part of the SAS library: this
+// builds into its own small shared library that only the benchmark loads.
+//
+//   sas_peak_mfma_bf16   every wave of a full grid issues back-to-back
+//                        32x32x16 bf16 MFMAs on register operands, with
+//                        eight independent accumulators so the matrix core
+//                        never waits on a result;
+//   sas_peak_read        a grid-stride streaming read of a device buffer
+//                        (16-byte loads, four in flight per thread), folded
+//                        into one word per thread so no load is dropped.
+// Each returns the hipError_t of its launch; the caller times the stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kChains = 8;
+
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float *sink) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(1e-3f * (float)((threadIdx.x + e) & 7));
+    b[e] = (__bf16)(1e-3f * (float)((threadIdx.x * 3 + e) & 7));
+  }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  if (s == 12345.f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;  // never true; keeps the work
+}
+
+__global__ __launch_bounds__(256) void read_kernel(const uint4 *src, long n16, unsigned *sink) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
+           d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink[(long)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+extern "C" {
+
+// flops = grid_wgs * 4 waves * iters * kChains * 32*32*16*2.
+int sas_peak_mfma_bf16(int grid_wgs, int iters, float *sink, void *stream) {
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid_wgs), dim3(256), 0, (hipStream_t)stream, iters,
+                     sink);
+  return (int)hipGetLastError();
+}
+
+int sas_peak_mfma_chains(void) { return kChains; }
+
+// Reads n_bytes (a multiple of 16) from src; sink holds grid_wgs * 256 words.
+int sas_peak_read(const void *src, long n_bytes, int grid_wgs, unsigned *sink, void *stream) {
+  hipLaunchKernelGGL(read_kernel, dim3(grid_wgs), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint4 *>(src), n_bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

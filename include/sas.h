@@ -302,6 +302,26 @@ sas_status sas_decode(const sas_decode_problem *p, const void *q, const void *k_
                       void *o, float *lse, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/*
+ * sas_decode_noalloc -- sas_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments and results as sas_decode, without
+ * the workspace: the split partials go to a fixed scratch array inside the
+ * library, SAS_DECODE_SCRATCH_BYTES per device, held by each device that
+ * runs the library until the process ends.  It allocates nothing (no
+ * hipMalloc / hipFree, no allocating library routine).
+ *   A problem whose partials, batch * hkv * splits * G * (head_dim + 2)
+ *   floats, exceed the scratch returns SAS_ERR_WORKSPACE before any launch
+ *   (rows split once need no scratch).
+ *   Every call on one device shares that device's scratch: calls on one
+ *   stream are ordered, calls that overlap in time on one device (other
+ *   streams, other threads) race and must not be issued.
+ */
+#define SAS_DECODE_SCRATCH_BYTES (4u << 20)
+sas_status sas_decode_noalloc(const sas_decode_problem *p, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *sel_idx,
+                              const float *sel_loggate, void *o, float *lse, void *stream);
+
 /* Static description of a status code. */
 const char *sas_status_string(sas_status s);
 /* Detail of the last failed call on this thread ("" if none). */

@@ -18,6 +18,7 @@
 //            with the block's log gate added; the waves merge into an
 //            unnormalised partial per split, and a second kernel merges
 //            the partials with a log-sum-exp combine in a fixed order.
+#include <mutex>
 #include <type_traits>
 
 #include "sas_device.h"
@@ -606,6 +607,35 @@ static hipError_t launch_attend_d(const DecodeParams &p, hipStream_t stream) {
 
 hipError_t launch_decode_attend(const DecodeParams &p, hipStream_t stream) {
   return p.D == 128 ? launch_attend_d<128>(p, stream) : launch_attend_d<64>(p, stream);
+}
+
+// ------------------------------------------------------------------ scratch
+// Split partials of sas_decode_noalloc: a fixed array in device memory, one
+// copy per device (each device that runs the library holds it until the
+// process ends).  In host code `decode_scratch` names a host-side stand-in,
+// not the device array: its device address is asked for once per device
+// (with that device current) and kept; kernels get that address.  Calls on
+// one device share the array and find the previous call's contents in it;
+// the partials of a call are all written before its combine reads them.
+static __device__ __align__(256) float decode_scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch_address(float **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float *per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void *addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(decode_scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = static_cast<float *>(addr);
+  }
+  *out = per_device[dev];
+  return hipSuccess;
 }
 
 }  // namespace sas

@@ -1,5 +1,5 @@
 // C ABI of the SAS library: argument checks on the host, then launches.
-// Every check runs before any HIP call, so a rejected call touches nothing.
+// Every check runs before any launch, so a rejected call touches nothing.
 #include "sas.h"
 
 #include <hip/hip_runtime.h>
@@ -603,6 +603,35 @@ sas_status sas_decode(const sas_decode_problem *p, const void *q, const void *k_
   d.o = o;
   d.lse = lse;
   d.partial = static_cast<float *>(workspace);
+  return from_hip(sas::launch_decode_attend(d, (hipStream_t)stream), "decode launch");
+}
+
+sas_status sas_decode_noalloc(const sas_decode_problem *p, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *sel_idx,
+                              const float *sel_loggate, void *o, float *lse, void *stream) {
+  sas_status st = check_decode(p);
+  if (st) return st;
+  REQUIRE(q && k_cache && v_cache && sel_idx && o, SAS_ERR_NULL,
+          "q, k_cache, v_cache, sel_idx and o are required");
+  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(o),
+          SAS_ERR_ALIGN, "q, caches and o must be 16-byte aligned");
+  sas::DecodeParams d = decode_params(p);
+  d.partial = nullptr;
+  if (d.nsplit > 1) {  // one split per row writes o and lse directly
+    const size_t need = decode_partial_bytes(p, d.nsplit);
+    REQUIRE(need <= sas::kDecodeScratchBytes, SAS_ERR_WORKSPACE,
+            "split partials need %zu bytes, the fixed scratch holds %zu (use sas_decode "
+            "with a workspace, or fewer splits)", need, sas::kDecodeScratchBytes);
+    hipError_t e = sas::decode_scratch_address(&d.partial);
+    if (e != hipSuccess) return from_hip(e, "decode scratch address");
+  }
+  d.q = q;
+  d.k = k_cache;
+  d.v = v_cache;
+  d.sel_idx = sel_idx;
+  d.sel_lg = sel_loggate;
+  d.o = o;
+  d.lse = lse;
   return from_hip(sas::launch_decode_attend(d, (hipStream_t)stream), "decode launch");
 }
 

@@ -113,5 +113,9 @@ hipError_t launch_decode_append(const DecodeParams &p, const void *k_new, const 
                                void *k_cache, void *v_cache, hipStream_t stream);
 hipError_t launch_pooled_scores(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_attend(const DecodeParams &p, hipStream_t stream);
+// The fixed device scratch sas_decode_noalloc puts split partials in: its
+// address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(4) << 20;
+hipError_t decode_scratch_address(float **out);
 
 }  // namespace sas

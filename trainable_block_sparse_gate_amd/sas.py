@@ -32,7 +32,8 @@ STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTY
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = ["sas_gate_topk", "sas_fwd", "sas_bwd_workspace_size", "sas_bwd", "sas_bwd_prepare",
            "sas_bwd_dq", "sas_bwd_dkdv", "sas_gate_bwd",
-           "sas_pool_keys", "sas_decode_append", "sas_decode_select", "sas_decode_workspace_size", "sas_decode",
+           "sas_pool_keys", "sas_decode_append", "sas_decode_select", "sas_decode_workspace_size",
+           "sas_decode", "sas_decode_noalloc",
            "sas_status_string", "sas_last_error", "sas_abi_version"]
 
 
@@ -98,6 +99,7 @@ def lib():
             "sas_decode_select": [DP, vp, vp, vp, vp, vp, vp, vp],
             "sas_decode_workspace_size": [DP],
             "sas_decode": [DP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "sas_decode_noalloc": [DP, vp, vp, vp, vp, vp, vp, vp, vp],
             "sas_status_string": [i32],
             "sas_last_error": [],
             "sas_abi_version": [],
@@ -485,4 +487,26 @@ def decode(prob: Decode, q, k_cache, v_cache, sel_idx, sel_lg, workspace=None, o
     _check(lib().sas_decode(prob.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sel_idx),
                             _ptr(sel_lg), _ptr(o), _ptr(lse), _ptr(workspace),
                             workspace.numel(), _stream()))
+    return o, lse
+
+
+DECODE_SCRATCH_BYTES = 4 << 20  # the header's SAS_DECODE_SCRATCH_BYTES
+
+
+def decode_noalloc(prob: Decode, q, k_cache, v_cache, sel_idx, sel_lg, out):
+    """sas_decode_noalloc into the caller's out = (o, lse): the library
+    allocates nothing and takes no workspace (split partials go to its
+    fixed per-device scratch)."""
+    import torch
+    prob.check_q(q)
+    prob.check_cache(k_cache, "k_cache")
+    prob.check_cache(v_cache, "v_cache")
+    prob.check_selection(sel_idx, sel_lg, lg_optional=True)
+    o, lse = out
+    _need(o, "o", _torch_dtype(prob.out_dtype), (prob.batch, prob.hq, prob.d))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (prob.batch, prob.hq))
+    _gpu(q, k_cache, v_cache, sel_idx, sel_lg, o, lse)
+    _check(lib().sas_decode_noalloc(prob.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(sel_idx), _ptr(sel_lg), _ptr(o), _ptr(lse), _stream()))
     return o, lse

@@ -234,6 +234,8 @@ def summarize_counters(d, cmd, out):
     """Average of every counter per kernel (one --pmc pass)."""
     per = {}
     for r in read_csvs(d, "counter_collection.csv"):
+        if short_kernel(r["Kernel_Name"]) in (None, "copyBuffer"):
+            continue
         k = kernel_label(r["Kernel_Name"])
         per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     names = sorted({c for v in per.values() for c in v})
@@ -242,8 +244,6 @@ def summarize_counters(d, cmd, out):
              "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
     rec = {}
     for k, c in sorted(per.items()):
-        if not short_kernel(k) and "sas" not in k:
-            continue
         vals = {n: (sum(c[n]) / len(c[n]) if n in c else None) for n in names}
         rec[k] = vals
         lines.append(f"| `{k}` | " + " | ".join("" if vals[n] is None else f"{vals[n]:.4g}"
@@ -471,13 +471,13 @@ def measured_peaks(torch, metrics):
     L = ctypes.CDLL(build.PEAKS_LIB)
     L.sas_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.sas_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p,
-                                ctypes.c_void_p]
+                                ctypes.c_void_p, ctypes.c_int]
     chains = L.sas_peak_mfma_chains()
     props = torch.cuda.get_device_properties(0)
     cus = props.multi_processor_count
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     sink = torch.empty(cus * 8 * 256, dtype=torch.float32, device="cuda")
-    wgs, iters = cus * 8, 4096
+    iters = 4096
 
     def timed(fn, reps=5):
         fn()
@@ -493,27 +493,43 @@ def measured_peaks(torch, metrics):
             best = ms if best is None else min(best, ms)
         return best
 
-    ms = timed(lambda: L.sas_peak_mfma_bf16(wgs, iters, ctypes.c_void_p(sink.data_ptr()), st))
-    flops = wgs * 4 * iters * chains * 32 * 32 * 16 * 2
+    ms = timed(lambda: L.sas_peak_mfma_bf16(cus * 8, iters, ctypes.c_void_p(sink.data_ptr()), st))
+    flops = cus * 8 * 4 * iters * chains * 32 * 32 * 16 * 2
     mfma_tf = flops / (ms * 1e-3) / 1e12
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
-    rsink = torch.empty(cus * 16 * 256, dtype=torch.int32, device="cuda")
-    ms_r = timed(lambda: L.sas_peak_read(ctypes.c_void_p(buf.data_ptr()), nbytes, cus * 16,
-                                         ctypes.c_void_p(rsink.data_ptr()), st))
-    read_gbs = nbytes / (ms_r * 1e-3) / 1e9
+    rsink = torch.empty(cus * 32 * 256, dtype=torch.int32, device="cuda")
+    reads = {}
+    for mode in (0, 1, 2):
+        for wgs in (cus * 4, cus * 16, cus * 32):
+            ms_r = timed(lambda: L.sas_peak_read(ctypes.c_void_p(buf.data_ptr()), nbytes, wgs,
+                                                 ctypes.c_void_p(rsink.data_ptr()), st, mode))
+            reads[f"mode{mode}_wgs{wgs}"] = round(nbytes / (ms_r * 1e-3) / 1e9, 1)
+    best = max(reads, key=reads.get)
+    read_gbs = reads[best]
+    # a 64 MiB buffer read over and over: more than the 32 MB of L2, so the
+    # repeats are served by the 256 MB Infinity Cache
+    small = 64 << 20
+    mall = timed(lambda: L.sas_peak_read(ctypes.c_void_p(buf.data_ptr()), small, cus * 4,
+                                         ctypes.c_void_p(rsink.data_ptr()), st, 1), reps=10)
+    mall_gbs = small / (mall * 1e-3) / 1e9
     del buf, rsink, sink
     torch.cuda.empty_cache()
     log(f"[bench] measured peaks: bf16 MFMA {mfma_tf:.0f} TFLOP/s, streaming read "
-        f"{read_gbs:.0f} GB/s ({cus} compute units)")
+        f"{read_gbs:.0f} GB/s ({best}; {reads}), 64 MiB re-read {mall_gbs:.0f} GB/s "
+        f"({cus} compute units)")
     return {"bf16_mfma_tflops": round(mfma_tf, 1),
             "bf16_mfma_frac_of_spec": round(mfma_tf / metrics.PEAK_BF16_TFLOPS, 4),
             "stream_read_gbs": round(read_gbs, 1),
             "stream_read_frac_of_spec": round(read_gbs / metrics.PEAK_HBM_GBS, 4),
+            "stream_read_variants_gbs": reads,
+            "cache_resident_read_gbs": round(mall_gbs, 1),
             "compute_units": cus,
-            "how": (f"MFMA: {wgs} workgroups x 4 waves, each {iters} x {chains} independent "
-                    "32x32x16 bf16 MFMAs on registers; read: 4 GiB grid-stride 16-byte loads; "
-                    "best of 5 launches (HIP events)")}
+            "how": (f"MFMA: {cus * 8} workgroups x 4 waves, each {iters} x {chains} "
+                    "independent 32x32x16 bf16 MFMAs on registers; read: 4 GiB, 16-byte loads, "
+                    "grid-stride (mode0) or one contiguous chunk per workgroup with 8 / 16 "
+                    "nontemporal loads in flight (mode1 / mode2), best of 5 launches each; "
+                    "cache-resident: a 64 MiB buffer re-read (Infinity Cache), best of 10")}
 
 
 def calibration_copy(torch, nbytes=1 << 30, reps=3):

@@ -3,12 +3,18 @@
  * attention ("SAS: Simple Attention Sparsification via End-to-End
  * Optimization of Context Ranking", arXiv 2609.13141).
  *
+ * Pages cited, by title: "review" is the page titled "SAS: Simple Attention
+ * Sparsification via End-to-End Optimization of Context Ranking Review"
+ * (sections as numbered there); "paper text" is the page titled "SAS: Simple
+ * Attention Sparsification via End-to-End Optimization of Context Ranking"
+ * that holds the paper's own text (sections 3 and 4, ablation setup and
+ * results).
+ *
  * The method (as the pages on it describe it):
  *   - a selector scores every history block of 64 tokens; the scores are
  *     turned into gates by a softmax over the history blocks while the
- *     always-kept current block keeps gate 1 (dimensionstp.github.io review,
- *     section 2-1 "g = phi(s), g0 = 1" and 3-3; paperslantern paper text,
- *     section 4);
+ *     always-kept current block keeps gate 1 (review, section 2-1:
+ *     g = phi(s) with g0 = 1, and 3-3; paper text, section 4);
  *   - a hard Top-K keeps the budgeted history blocks (review section 1-2);
  *   - attention runs on the kept blocks only, with log(gate) added to every
  *     logit of the block: o = softmax(q K_S^T + log g_S) V_S (review

@@ -8,13 +8,15 @@
  * table or constant with the HIP library.
  *
  * Sources (the pages on "SAS: Simple Attention Sparsification via End-to-End
- * Optimization of Context Ranking", arXiv 2609.13141):
- *   [R]  dimensionstp.github.io review: 1-1 (dense and block-sparse attention
+ * Optimization of Context Ranking", arXiv 2609.13141), cited by title:
+ *   [R]  the page titled "SAS: Simple Attention Sparsification via End-to-End
+ *        Optimization of Context Ranking Review", sections: 1-1 (dense and block-sparse attention
  *        equations), 1-2 (hard Top-K equation), 2-1 (g = phi(s), g0 = 1,
  *        broadcast), 2-2 (inner log-gate equation and the softmax/log identity),
  *        3-3 (softmax gate activation), 3-5 (sparse scope), 3-6 (fused kernel,
  *        backward keeps the selector gradient), 3-7 (decode path steps 1-4).
- *   [P]  papers.paperslantern.ai paper text: section 3 (standard attention,
+ *   [P]  the page titled "SAS: Simple Attention Sparsification via End-to-End
+ *        Optimization of Context Ranking" holding the paper's own text: section 3 (standard attention,
  *        scaling factor omitted, block partition, Top-K selected index set),
  *        section 4 (current block singled out and unbiased, gate broadcast,
  *        gate-position/activation/scope design elements), ablation results

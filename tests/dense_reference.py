@@ -2,7 +2,7 @@
 attention in float64 with an additive mask that carries the log gates.
 
 The additive mask is what the gated formulation adds to the logits
-(dimensionstp.github.io review, section 2-2: softmax(q K_S^T + log g_S) V_S):
+(the page titled "SAS: Simple Attention Sparsification via End-to-End Optimization of Context Ranking Review", section 2-2: softmax(q K_S^T + log g_S) V_S):
 log g of the key's block where the block is attended (causal inside the
 current block), -inf elsewhere.  Building it is pure indexing; the attention
 arithmetic is torch's.

@@ -117,7 +117,7 @@ def test_kept_gates_match_scipy_softmax(mode):
 @pytest.mark.parametrize("mode", [oracle.GATE_HIST, oracle.GATE_ALL])
 def test_shift_invariance(mode):
     """The normalised gate is invariant to adding one constant to all of a
-    row's scores (paperslantern paper text, ablation results)."""
+    row's scores (paper text, ablation results: the page titled "SAS: Simple Attention Sparsification via End-to-End Optimization of Context Ranking")."""
     lengths = [100, 30]
     blk = 4
     cu, lg, QB = _case(lengths, 2, seed=5, blk=blk)

@@ -2,8 +2,8 @@
 //
 // Gradients of o_t = sum_u P_tu v_u, P_t = softmax_u(scale q_t.k_u + log g),
 // which the pages say the fused kernel keeps through to the selector
-// (dimensionstp.github.io review, section 3-6; paperslantern paper text,
-// ablation results: the inner gate's gradient carries P_gated (dP - D)):
+// (review, section 3-6; paper text, ablation results: the inner gate's
+// gradient carries P_gated (dP - D)):
 //   D_t   = sum_e dO_te o_te            dP_tu = dO_t . v_u
 //   dS_tu = P_tu (dP_tu - D_t)          dq_t  = scale sum_u dS_tu k_u
 //   dk_u  = scale sum_t dS_tu q_t       dv_u  = sum_t P_tu dO_t
@@ -27,6 +27,10 @@
 //              stream through LDS, dK^T and dV^T accumulate in registers;
 //              the partials of split key blocks are summed in segment order
 //              by a second, small kernel.
+// Pages cited by title: "review" is the page "SAS: Simple Attention
+// Sparsification via End-to-End Optimization of Context Ranking Review";
+// "paper text" is the page "SAS: Simple Attention Sparsification via
+// End-to-End Optimization of Context Ranking" that holds the paper's text.
 #include "sas_device.h"
 #include "sas_launch.h"
 #include "tile_stage.h"

@@ -1,14 +1,17 @@
 // Gated block-sparse attention backward for gfx950: dK and dV.
 //
 // dk_u = scale sum_t dS_tu q_t and dv_u = sum_t P_tu dO_t over the query
-// rows whose selection keeps u's block (dimensionstp.github.io review,
-// sections 3-6: gradients pass through the gated probabilities).  One
-// workgroup per segment of a key block, from the per-key-block lists that
-// the preparation kernels build: K and V stay in registers, Q/dO tiles of
+// rows whose selection keeps u's block (review, section 3-6: gradients pass
+// through the gated probabilities).  One workgroup per segment of a key
+// block, from the per-key-block lists that the preparation kernels build: K and V stay in registers, Q/dO tiles of
 // the keeping rows stream through LDS, dK^T and dV^T accumulate in
 // registers.  Key blocks kept by many rows are split over several segments;
 // each writes a partial sum and a second, small kernel adds them in segment
 // order, so the result does not depend on the order the workgroups finish.
+// Pages cited by title: "review" is the page "SAS: Simple Attention
+// Sparsification via End-to-End Optimization of Context Ranking Review";
+// "paper text" is the page "SAS: Simple Attention Sparsification via
+// End-to-End Optimization of Context Ranking" that holds the paper's text.
 #include <type_traits>
 
 #include "sas_device.h"

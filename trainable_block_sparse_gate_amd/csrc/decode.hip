@@ -1,7 +1,7 @@
-// Decode path for gfx950 (dimensionstp.github.io review, section 3-7:
-// score cached block summaries, keep the Top-K per query group, read the
-// kept blocks of the paged KV cache, run the block-sparse decode kernel;
-// GQA groups share one selection).
+// Decode path for gfx950 (review, section 3-7: score cached block
+// summaries, keep the Top-K per query group, read the kept blocks of the
+// paged KV cache, run the block-sparse decode kernel; GQA groups share one
+// selection).
 //
 //   pool:    summary of block j = mean of its 64 keys, summed in token order
 //            in fp32 (one thread per (block, channel), reads coalesced
@@ -18,6 +18,10 @@
 //            with the block's log gate added; the waves merge into an
 //            unnormalised partial per split, and a second kernel merges
 //            the partials with a log-sum-exp combine in a fixed order.
+// Pages cited by title: "review" is the page "SAS: Simple Attention
+// Sparsification via End-to-End Optimization of Context Ranking Review";
+// "paper text" is the page "SAS: Simple Attention Sparsification via
+// End-to-End Optimization of Context Ranking" that holds the paper's text.
 #include <mutex>
 #include <type_traits>
 
@@ -273,8 +277,9 @@ __global__ __launch_bounds__(256, kDecodeWgPerCu) void decode_attend_kernel(Deco
 #pragma unroll
     for (int i = 0; i < NREQ; ++i) {
       const unsigned ob = (unsigned)(min(ko + i * RPS + r_in, last) * (D * 2) + pc * 16);
-      kst[x][i] = *reinterpret_cast<const u32x4 *>(kb + ob);
-      vst[x][i] = *reinterpret_cast<const u32x4 *>(vb + ob);
+      // streaming, non-temporal: a kept block is read once per decode
+      kst[x][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + ob));
+      vst[x][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vb + ob));
     }
   };
   // staged K, V -> the wave's tiles, chunks permuted by the swizzle

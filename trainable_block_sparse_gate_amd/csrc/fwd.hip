@@ -1,7 +1,7 @@
 // Gated block-sparse attention forward for gfx950.
 //
-// What it computes (dimensionstp.github.io review, section 2-2, and the
-// fused-kernel description in section 3-6): for each query token t of block
+// What it computes (review, section 2-2, and the fused-kernel description
+// in section 3-6): for each query token t of block
 // i and head h, o_t = softmax_u(scale * q_t.k_u + log g(blk(u))) v_u over the
 // keys of the kept history blocks and the keys u <= t of block i, plus the
 // row log-sum-exp.  The gate is added to every logit of its block inside
@@ -23,6 +23,10 @@
 //     finite before any gated history tile; the output is rescaled only when
 //     a tile's max jumps well above the running reference;
 //   - two tiles ahead are in flight: one in LDS, one in registers.
+// Pages cited by title: "review" is the page "SAS: Simple Attention
+// Sparsification via End-to-End Optimization of Context Ranking Review";
+// "paper text" is the page "SAS: Simple Attention Sparsification via
+// End-to-End Optimization of Context Ranking" that holds the paper's text.
 #include "sas_device.h"
 #include "sas_launch.h"
 #include "tile_stage.h"

@@ -1,7 +1,7 @@
 // Gate + hard Top-K (forward) and the gate backward, one workgroup per row.
 //
-// Forward (dimensionstp.github.io review, sections 1-2, 2-1 and 3-3;
-// paperslantern paper text, section 4): per row with current block i,
+// Forward (review, sections 1-2, 2-1 and 3-3; paper text, section 4): per
+// row with current block i,
 //   lse      = log sum_{j in N} exp(s_j),  N = {j < i} (or {j <= i})
 //   log g_j  = s_j - lse,  the current block keeps log g = 0 in the first mode
 //   kept     = the min(Kb-1, i) largest s_j over j < i, lower j on ties.
@@ -22,6 +22,10 @@
 // straight-through (mode 4): dL/dg_j = dlg_j (the hard gate is 1) passed
 // through the soft gate's Jacobian: d s_m = g_m ([m kept] dlg_m - sum over
 // kept j of g_j dlg_j), g = exp(s - lse).
+// Pages cited by title: "review" is the page "SAS: Simple Attention
+// Sparsification via End-to-End Optimization of Context Ranking Review";
+// "paper text" is the page "SAS: Simple Attention Sparsification via
+// End-to-End Optimization of Context Ranking" that holds the paper's text.
 
 constexpr int kGateSigmoid = 2, kGateRaw = 3, kGateSte = 4;  // the ablations
 #include "sas_device.h"

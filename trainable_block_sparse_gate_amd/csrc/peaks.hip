@@ -6,9 +6,10 @@
 //                        32x32x16 bf16 MFMAs on register operands, with
 //                        eight independent accumulators so the matrix core
 //                        never waits on a result;
-//   sas_peak_read        a grid-stride streaming read of a device buffer
-//                        (16-byte loads, four in flight per thread), folded
-//                        into one word per thread so no load is dropped.
+//   sas_peak_read        a streaming read of a device buffer (16-byte loads,
+//                        grid-stride or one contiguous chunk per workgroup,
+//                        4 to 16 loads in flight per thread), folded into
+//                        one word per thread so no load is dropped.
 // Each returns the hipError_t of its launch; the caller times the stream.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -17,6 +18,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChains = 8;
 
@@ -41,6 +43,31 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float *sink) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += acc[c][r];
   if (s == 12345.f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;  // never true; keeps the work
+}
+
+// Each workgroup streams its own contiguous chunk of the buffer, U 16-byte
+// loads in flight per thread (consecutive threads on consecutive 16 bytes).
+template <int U>
+__global__ __launch_bounds__(256) void read_chunk_kernel(const uint4 *src, long n16,
+                                                         unsigned *sink) {
+  const long per_wg = (n16 + gridDim.x - 1) / gridDim.x;
+  const long lo = (long)blockIdx.x * per_wg;
+  const long hi = lo + per_wg < n16 ? lo + per_wg : n16;
+  unsigned acc = 0;
+  long i = lo + threadIdx.x;
+  const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
+  for (; i + (U - 1) * 256 < hi; i += U * 256) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(s4 + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < hi; i += 256) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink[(long)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
 __global__ __launch_bounds__(256) void read_kernel(const uint4 *src, long n16, unsigned *sink) {
@@ -73,9 +100,20 @@ int sas_peak_mfma_bf16(int grid_wgs, int iters, float *sink, void *stream) {
 int sas_peak_mfma_chains(void) { return kChains; }
 
 // Reads n_bytes (a multiple of 16) from src; sink holds grid_wgs * 256 words.
-int sas_peak_read(const void *src, long n_bytes, int grid_wgs, unsigned *sink, void *stream) {
-  hipLaunchKernelGGL(read_kernel, dim3(grid_wgs), dim3(256), 0, (hipStream_t)stream,
-                     static_cast<const uint4 *>(src), n_bytes / 16, sink);
+// mode 0: grid-stride, four loads in flight per thread; mode 1 / 2: one
+// contiguous chunk per workgroup, 8 / 16 nontemporal loads in flight.
+int sas_peak_read(const void *src, long n_bytes, int grid_wgs, unsigned *sink, void *stream,
+                  int mode) {
+  const uint4 *s = static_cast<const uint4 *>(src);
+  if (mode == 1)
+    hipLaunchKernelGGL(read_chunk_kernel<8>, dim3(grid_wgs), dim3(256), 0, (hipStream_t)stream,
+                       s, n_bytes / 16, sink);
+  else if (mode == 2)
+    hipLaunchKernelGGL(read_chunk_kernel<16>, dim3(grid_wgs), dim3(256), 0, (hipStream_t)stream,
+                       s, n_bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(read_kernel, dim3(grid_wgs), dim3(256), 0, (hipStream_t)stream, s,
+                       n_bytes / 16, sink);
   return (int)hipGetLastError();
 }
 

@@ -197,16 +197,30 @@ def round_bf16(x):
     return out
 
 
+def round_e4m3(x):
+    """Nearest fp8 e4m3 value (ties to even; 480 and beyond, infinities and
+    NaN give NaN) of every fp32 entry, as fp32."""
+    x = _f32(x)
+    out = np.empty_like(x)
+    _load().sas_oracle_round_e4m3(ctypes.c_int64(x.size), _p(x), _p(out))
+    return out
+
+
 def pool_keys_row(K, blk=64, summary="f32"):
     """Block summaries [nhist, d] of one (sequence, kv head) cache K [L, d]:
-    the fp32 means, or (summary="bf16") those rounded to bf16, as fp32."""
+    the fp32 means, or those rounded to bf16 (summary="bf16") or to fp8 e4m3
+    (summary="fp8"), as fp32."""
     K = _f32(K)
     L, d = K.shape
     nhist = (L - 1) // blk
     out = np.empty((max(nhist, 1), d), np.float32)
     _load().sas_oracle_pool_keys_row(L, blk, d, _p(K), _p(out))
     out = out[:nhist]
-    return round_bf16(out) if summary == "bf16" else out
+    if summary == "bf16":
+        return round_bf16(out)
+    if summary == "fp8":
+        return round_e4m3(out)
+    return out
 
 
 def decode_scores_row(q, kbar):

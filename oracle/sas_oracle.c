@@ -712,6 +712,38 @@ int sas_oracle_round_bf16(int64_t n, const float *in, float *out) {
 }
 
 /*
+ * fp8 summary storage (e4m3: 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits; no infinities, exponent and mantissa all ones = NaN): every
+ * fp32 value is replaced by the nearest e4m3 value, ties to the even one,
+ * and returned as the fp32 number it stands for.  Written from the
+ * definition: below 2^-6 the spacing of the format is 2^-9 (subnormals),
+ * in [2^e, 2^(e+1)) with e >= -6 it is 2^(e-3); the value divided by its
+ * spacing is rounded to the nearest integer, ties to even (rint in the
+ * default rounding mode), and multiplied back (all exact in double).  The
+ * largest finite value is 448; a result of 480 or more (the next step of
+ * the spacing) has no encoding and becomes NaN, as do infinities and NaN.
+ */
+int sas_oracle_round_e4m3(int64_t n, const float *in, float *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double x = in[i];
+    if (isnan(x) || isinf(x)) {
+      out[i] = NAN;
+      continue;
+    }
+    const double a = fabs(x);
+    double spacing = ldexp(1.0, -9);
+    if (a >= ldexp(1.0, -6)) {
+      int e;
+      frexp(a, &e); /* a = f 2^e, f in [0.5, 1): a in [2^(e-1), 2^e) */
+      spacing = ldexp(1.0, e - 1 - 3);
+    }
+    const double r = rint(a / spacing) * spacing;
+    out[i] = r >= 480.0 ? NAN : (float)copysign(r, x);
+  }
+  return 0;
+}
+
+/*
  * Block summaries of one (sequence, kv head): the mean key of every full
  * history block j < (L-1)/b, in the fixed fp32 order stated in the header
  * ([R] 3-7 step 1: the selector scores cached block summaries).

@@ -244,3 +244,60 @@ def test_bf16_summaries_are_the_rounded_fp32_means():
     q = g.standard_normal((4, 32)).astype(np.float32)
     idx, lg, lse, s = oracle.decode_select_row(q, K, 3, summary="bf16")
     assert np.array_equal(s, oracle.decode_scores_row(q, b16))
+
+
+def _e4m3_values():
+    """Every finite fp8 e4m3 value, from its bit fields (sign, 4-bit
+    exponent with bias 7, 3-bit mantissa; 0x7f / 0xff are NaN)."""
+    vals = []
+    for code in range(256):
+        sgn, ef, m = code >> 7, (code >> 3) & 15, code & 7
+        if ef == 15 and m == 7:
+            continue
+        v = m * 2.0 ** -9 if ef == 0 else (8 + m) * 2.0 ** (ef - 10)
+        vals.append(-v if sgn else v)
+    return np.array(sorted(set(vals)), np.float64)
+
+
+def test_e4m3_summary_rounding_matches_torch_conversion():
+    """The oracle's fp8 summary storage rounds to nearest, ties to even, with
+    no saturation: the same values as torch's fp32 -> float8_e4m3fn
+    conversion, on random values over the whole range, every e4m3 value,
+    every midpoint between neighbours (ties), the overflow boundary,
+    subnormals, signed zeros, infinities and NaN."""
+    import torch
+    g = np.random.default_rng(11)
+    v = _e4m3_values()
+    mids = ((v[1:] + v[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([
+        g.standard_normal(8192).astype(np.float32) * np.float32(0.125),
+        (g.standard_normal(4096) * 100).astype(np.float32),
+        v.astype(np.float32), mids, np.nextafter(mids, np.float32(np.inf)),
+        np.nextafter(mids, np.float32(-np.inf)),
+        np.array([448, 464, 472, 479.9, 480, 1e4, -464, -480, 2**-9, 2**-10, 3 * 2**-11, 2**-11,
+                  0.0, -0.0, np.inf, -np.inf, np.nan], np.float32)])
+    got = oracle.round_e4m3(x)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float32).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    # e4m3 values are fixed points; 464 (halfway to the NaN pattern) goes to
+    # 448; the half-spacing subnormal 2^-10 goes to 0 (even)
+    assert np.array_equal(oracle.round_e4m3(v.astype(np.float32)), v.astype(np.float32))
+    r = oracle.round_e4m3(np.array([464, 480, 2**-10, 3 * 2**-10], np.float32))
+    assert r[0] == 448 and np.isnan(r[1]) and r[2] == 0.0 and r[3] == 2**-8
+
+
+def test_fp8_summaries_are_the_rounded_fp32_means():
+    g = np.random.default_rng(12)
+    K = g.standard_normal((64 * 5 + 7, 32)).astype(np.float32)
+    f32 = oracle.pool_keys_row(K)
+    f8 = oracle.pool_keys_row(K, summary="fp8")
+    assert f8.shape == f32.shape == (5, 32)
+    assert np.array_equal(f8, oracle.round_e4m3(f32))
+    # relative error of e4m3 is at most 2^-4 for normal values, and the
+    # absolute error at most 2^-10 in the subnormal range
+    assert np.all(np.abs(f8 - f32) <= np.maximum(np.abs(f32) * 2.0 ** -4, 2.0 ** -10))
+    q = g.standard_normal((4, 32)).astype(np.float32)
+    idx, lg, lse, s = oracle.decode_select_row(q, K, 3, summary="fp8")
+    assert np.array_equal(s, oracle.decode_scores_row(q, f8))

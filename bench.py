@@ -63,8 +63,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the second training workload, the long decode and the peaks")
     ap.add_argument("--decode-steps", type=int, default=20)
-    ap.add_argument("--summary-dtype", default="f32", choices=["f32", "bf16"],
-                    help="decode block-summary storage (bf16 halves the selector's scan)")
+    ap.add_argument("--summary-dtype", default="f32", choices=["f32", "bf16", "fp8"],
+                    help="decode block-summary storage (bf16 / fp8 shrink the selector's scan)")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-counters", metavar="DIR")
@@ -76,6 +76,7 @@ def parse():
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+SUMMARY_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CALIBRATION_BYTES = 1 << 30
 
@@ -405,7 +406,9 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
         prob = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, False,
                           spec.max_len, summary_dtype=args.summary_dtype)
     ksum = sas.pool_keys(prob, t["k"])  # cache maintenance, not timed
-    sel, lg, glse, scores = sas.decode_select(prob, t["q"], ksum)
+    sws = torch.empty(max(1, sas.decode_select_workspace_bytes(prob)), dtype=torch.uint8,
+                      device="cuda")
+    sel, lg, glse, scores = sas.decode_select(prob, t["q"], ksum, workspace=sws)
     ws = torch.empty(max(1, sas.decode_workspace_bytes(prob)), dtype=torch.uint8, device="cuda")
     o, lse = sas.decode(prob, t["q"], t["k"], t["v"], sel, lg, workspace=ws)
     # Between iterations the caches are refilled by READING a 1 GiB buffer
@@ -428,7 +431,7 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
         ea.record()
         sas.decode_append(prob, k_new, v_new, t["k"], t["v"], ksum)
         e0.record()
-        sas.decode_select(prob, t["q"], ksum, out=(sel, lg, glse, scores))
+        sas.decode_select(prob, t["q"], ksum, out=(sel, lg, glse, scores), workspace=sws)
         e1.record()
         sas.decode(prob, t["q"], t["k"], t["v"], sel, lg, workspace=ws, out=(o, lse))
         e2.record()
@@ -438,9 +441,35 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
             t_sel += e0.elapsed_time(e1)
             t_dec += e1.elapsed_time(e2)
     n = args.decode_steps
+    # the selection with the other summary storages (same cache, same query)
+    by_summary = {}
+    for sd in ("f32", "bf16", "fp8"):
+        if sd == args.summary_dtype:
+            continue
+        p2 = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, spec.paged,
+                        spec.max_len, page_table=t["page_table"],
+                        num_pages=t["k"].shape[0] if spec.paged else 0, summary_dtype=sd)
+        ks2 = sas.pool_keys(p2, t["k"])
+        ws2 = torch.empty(max(1, sas.decode_select_workspace_bytes(p2)), dtype=torch.uint8,
+                          device="cuda")
+        out2 = sas.decode_select(p2, t["q"], ks2, workspace=ws2)
+        tt = 0.0
+        for it in range(n + 3):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            sas.decode_select(p2, t["q"], ks2, out=out2, workspace=ws2)
+            e1.record()
+            torch.cuda.synchronize()
+            if it >= 3:
+                tt += e0.elapsed_time(e1)
+        b2 = metrics.decode_scan_bytes(spec.seqlens, spec.hkv, spec.d, SUMMARY_BYTES[sd])
+        by_summary[sd] = {"us": round(tt / n * 1e3, 2), "summary_bytes": b2,
+                          "GB/s": round(b2 / (tt / n * 1e-3) / 1e9, 1)}
+        del ks2, ws2, out2
     kv = metrics.decode_kv_bytes(spec.seqlens, spec.hkv, spec.d, spec.budget_blocks)
     scan = metrics.decode_scan_bytes(spec.seqlens, spec.hkv, spec.d,
-                                     2 if args.summary_dtype == "bf16" else 4)
+                                     SUMMARY_BYTES[args.summary_dtype])
     gbs = kv / (t_dec / n * 1e-3) / 1e9
     scan_gbs = scan / (t_sel / n * 1e-3) / 1e9
     log(f"[bench] decode {t_dec / n * 1e3:.1f} us for {kv / 2**20:.1f} MiB -> {gbs:.0f} GB/s; "
@@ -457,7 +486,7 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
             "traffic": traffic_for("decode_attend_kernel", spec.name),
             "selection": {"us": round(t_sel / n * 1e3, 2), "summary_bytes": scan,
                           "summary_dtype": args.summary_dtype,
-                          "GB/s": round(scan_gbs, 1)},
+                          "GB/s": round(scan_gbs, 1), "other_summary_dtypes": by_summary},
             "append_us": round(t_app / n * 1e3, 2),
             "step_us": round((t_app + t_sel + t_dec) / n * 1e3, 2)}
 

@@ -132,6 +132,11 @@ typedef struct sas_problem {
  * reads those rounded values; the score arithmetic is unchanged. */
 #define SAS_SUMMARY_F32 0
 #define SAS_SUMMARY_BF16 1
+/* fp8 e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities; the two codes with exponent and mantissa all ones are NaN):
+ * each fp32 mean rounded to the nearest e4m3 value, ties to even; values
+ * of 480 or more become NaN.  One byte per value, a quarter of fp32. */
+#define SAS_SUMMARY_FP8 2
 
 typedef struct sas_decode_problem {
   int32_t batch;
@@ -149,7 +154,7 @@ typedef struct sas_decode_problem {
   const int32_t *seqlens;       /* device [batch]: cache length L, query token included */
   const int32_t *seqlens_host;  /* host copy */
   const int32_t *page_table;    /* device [batch][max_pages] (paged only) */
-  int32_t summary_dtype;        /* block summaries: SAS_SUMMARY_F32 or SAS_SUMMARY_BF16 */
+  int32_t summary_dtype;        /* block summaries: SAS_SUMMARY_F32, _BF16 or _FP8 */
   const int32_t *page_table_host; /* optional host copy of page_table (paged only): when
                                      given, every entry a sequence uses (its first
                                      ceil(L_b / 64)) is checked to lie in [0, num_pages)
@@ -278,17 +283,29 @@ sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, con
 
 /*
  * sas_decode_select -- decode-time selection (review 3-7 steps 1-2; GQA
- * groups share one selection): per (batch b, kv head g) row,
+ * groups share one selection; review 4-4 and 6: the scan over every cached
+ * block is what limits long contexts): per (batch b, kv head g) row,
  *   qbar_e = (q_{gG} + ... + q_{gG+G-1})_e / G   (fp32, heads in order)
  *   s_j    = (fmaf chain over e of qbar_e * ksum_je) / sqrtf(head_dim)
  * then the gate + Top-K of sas_gate_topk with i = (L_b - 1) / 64 and
- * SAS_GATE_HIST.  q [batch][hq][d] bf16.
+ * SAS_GATE_HIST.  q [batch][hq][d] bf16; ksum in p->summary_dtype, 16-byte
+ * aligned.
  *   sel_idx / sel_loggate out [batch*hkv][Kb]; gate_lse out [batch*hkv];
  *   scores out [batch][hkv][nblk_stride] fp32 (the pooled scores).
+ * Each row's history is split into chunks taken by separate workgroups
+ * (scores and an exact Top-K per chunk), merged per row by a second kernel;
+ * the result is the whole row's Top-K.
+ *   workspace: at least sas_decode_select_workspace_size(p) bytes.
+ * A row's history is split into chunks of 256 to 2048 blocks; more than
+ * 4096 candidates in the merge (chunks x (Kb - 1)) returns
+ * SAS_ERR_UNSUPPORTED (at Kb = 32: histories beyond 270,336 blocks, 17M
+ * tokens).
  */
+size_t sas_decode_select_workspace_size(const sas_decode_problem *p);
 sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const void *ksum,
                              float *scores, int32_t *sel_idx, float *sel_loggate,
-                             float *gate_lse, void *stream);
+                             float *gate_lse, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * sas_decode -- block-sparse decode attention (review 3-7 steps 3-4) for
@@ -335,7 +352,7 @@ const char *sas_last_error(void);
 /* ABI version of this header: bumped on any incompatible change. */
 int32_t sas_abi_version(void);
 
-#define SAS_ABI_VERSION 3
+#define SAS_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

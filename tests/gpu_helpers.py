@@ -49,3 +49,13 @@ def assert_close(name, got, want, tol):
     say(f"  {name}: max_abs={err:.3e} (max|ref|={scale:.3e}, tol={tol:g})")
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     assert err <= tol, f"{name}: max_abs {err} > {tol}"
+
+
+def summaries_f32(ksum):
+    """Block summaries as the fp32 values they stand for (fp8 summaries are
+    stored as e4m3 codes in uint8; torch's float8_e4m3fn decodes them
+    exactly)."""
+    import torch
+    if ksum.dtype == torch.uint8:
+        return ksum.view(torch.float8_e4m3fn).float().cpu().numpy()
+    return ksum.float().cpu().numpy()

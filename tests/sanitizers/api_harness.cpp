@@ -42,7 +42,7 @@ hipError_t launch_decode_append(const DecodeParams &, const void *, const void *
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_pooled_scores(const DecodeParams &, hipStream_t) {
+hipError_t launch_decode_select(const DecodeParams &, const SelectParams &, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
@@ -174,7 +174,11 @@ int main() {
   if (dws == 0) { std::printf("FAIL decode workspace size 0\n"); ++g_failures; }
   expect("pool ok", sas_pool_keys(&d, D, D, nullptr), SAS_OK);
   expect("append ok", sas_decode_append(&d, D, D, D, D, D, nullptr), SAS_OK);
-  expect("select ok", sas_decode_select(&d, D, D, DF, DI, DF, DF, nullptr), SAS_OK);
+  const size_t sws = sas_decode_select_workspace_size(&d);
+  if (sws == 0) { std::printf("FAIL select workspace size 0\n"); ++g_failures; }
+  expect("select ok", sas_decode_select(&d, D, D, DF, DI, DF, DF, D, sws, nullptr), SAS_OK);
+  expect("select ws", sas_decode_select(&d, D, D, DF, DI, DF, DF, D, sws - 1, nullptr),
+         SAS_ERR_WORKSPACE);
   expect("decode ok", sas_decode(&d, D, D, D, DI, DF, D, DF, D, dws, nullptr), SAS_OK);
   expect("decode noalloc ok", sas_decode_noalloc(&d, D, D, D, DI, DF, D, DF, nullptr), SAS_OK);
   expect("decode ws", sas_decode(&d, D, D, D, DI, DF, D, DF, D, dws - 1, nullptr),
@@ -196,7 +200,14 @@ int main() {
          SAS_ERR_UNSUPPORTED);  // groups of 3 heads
   e = d;
   e.nblk_stride = 3;
-  expect("stride", sas_decode_select(&e, D, D, DF, DI, DF, DF, nullptr), SAS_ERR_SHAPE);
+  expect("stride", sas_decode_select(&e, D, D, DF, DI, DF, DF, D, sws, nullptr), SAS_ERR_SHAPE);
+  e = d;
+  e.summary_dtype = SAS_SUMMARY_FP8;
+  expect("fp8 select", sas_decode_select(&e, D, D, DF, DI, DF, DF, D,
+                                         sas_decode_select_workspace_size(&e), nullptr),
+         SAS_OK);
+  e.summary_dtype = 7;
+  expect("summary dtype", sas_pool_keys(&e, D, D, nullptr), SAS_ERR_DTYPE);
   e = d;
   e.layout = SAS_KV_CONTIGUOUS;
   e.page_table = nullptr;

@@ -39,7 +39,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sas_abi_version() == sas.ABI_VERSION == 3
+    assert lib.sas_abi_version() == sas.ABI_VERSION == 4
     assert lib.sas_status_string(0) == b"ok"
     assert b"unsupported" in lib.sas_status_string(-5)
 
@@ -226,3 +226,24 @@ def test_binding_checks_decode_tensors():
         sas.decode(prob, q, cache, cache, torch.zeros(2, 5, dtype=torch.int32), None,
                    workspace=torch.zeros(16, dtype=torch.uint8))
     assert e.value.status == -2
+
+
+def test_decode_select_workspace_and_limits(lib):
+    """The selection's workspace follows its chunking: more chunks for few
+    long rows than for many short ones; too many candidates is unsupported;
+    a short workspace is rejected before any launch."""
+    ws = lib.sas_decode_select_workspace_size
+    one_long = decode_problem(seqlens=(524288,), hq=32, hkv=8, Kb=32, paged=False)
+    many = decode_problem(seqlens=(131072,) * 32, hq=32, hkv=8, Kb=64, paged=False)
+    n_long = ws(ctypes.byref(one_long))
+    n_many = ws(ctypes.byref(many))
+    # one row of 8191 blocks over 8 kv heads: 32 chunks of 256 blocks, 31 candidates each
+    assert n_long >= 8 * 32 * 31 * 8 + 8 * 32 * 8
+    assert n_many >= 256 * 63 * 8  # at least one chunk per row
+    assert lib.sas_decode_select(ctypes.byref(one_long), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 n_long - 1, None) == -6
+    assert lib.sas_decode_select(ctypes.byref(one_long), FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, n_long, None) == -4  # summaries not 16-byte aligned
+    huge = decode_problem(seqlens=(64 * 70000,), hq=8, hkv=2, Kb=256, paged=False)
+    assert lib.sas_decode_select(ctypes.byref(huge), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 40, None) == -5

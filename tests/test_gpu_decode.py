@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_helpers import TOL, assert_close, dev_tensor, say
+from tests.gpu_helpers import TOL, assert_close, dev_tensor, say, summaries_f32
 from trainable_block_sparse_gate_amd import sas
 from trainable_block_sparse_gate_amd import workloads as wl
 
@@ -43,8 +43,8 @@ def run_decode(name, paged, out_dtype="bf16", gated=True, seed=7, summary="f32")
     o, lse = sas.decode(prob, q, kc, vc, sel, lg if gated else None)
     torch.cuda.synchronize()
     G = hq // hkv
-    assert ksum.dtype == (torch.bfloat16 if summary == "bf16" else torch.float32)
-    ksum_h, scores_h = ksum.float().cpu().numpy(), scores.cpu().numpy()
+    assert ksum.dtype == {"bf16": torch.bfloat16, "fp8": torch.uint8, "f32": torch.float32}[summary]
+    ksum_h, scores_h = summaries_f32(ksum), scores.cpu().numpy()
     sel_h, lg_h, glse_h = sel.cpu().numpy(), lg.cpu().numpy(), glse.cpu().numpy()
     o_h, lse_h = o.float().cpu().numpy(), lse.cpu().numpy()
     for b in range(B):
@@ -87,11 +87,54 @@ def test_decode_ungated_and_fp32_output():
 
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("name", ["mixed_g4_d128", "g2_d64"])
-def test_decode_bf16_summaries(name, paged):
-    """Summaries stored as bf16 (the fp32 means rounded to nearest even):
-    summaries, scores and selection bit-exact against the oracle's bf16
-    reading, output at the bf16 bar."""
-    run_decode(name, paged, summary="bf16")
+@pytest.mark.parametrize("summary", ["bf16", "fp8"])
+def test_decode_reduced_precision_summaries(name, paged, summary):
+    """Summaries stored as bf16 or fp8 e4m3 (the fp32 means rounded to
+    nearest, ties to even): summaries, scores and selection bit-exact
+    against the oracle's reading, output at the bf16 bar."""
+    run_decode(name, paged, summary=summary)
+
+
+def test_fp8_summary_codes_for_every_rounding_case():
+    """The stored e4m3 codes of summaries whose fp32 means land on chosen
+    values: exact e4m3 values, midpoints between neighbours (ties go to the
+    even code), the subnormal range, signed zeros, and means past the
+    largest finite value (448) that round to it or overflow to NaN.  Keys
+    of a block are all equal to the wanted mean, so the token-order sum is
+    exact and the mean is that value (bf16 keys: the wanted means are the
+    ones bf16 holds exactly)."""
+    import torch
+    g = np.random.default_rng(13)
+    codes = [c for c in range(256) if (c & 0x7f) != 0x7f]
+    vals = torch.tensor(codes, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    order = np.argsort(vals, kind="stable")
+    v = vals[order]
+    mids = ((v[1:] + v[:-1]) / 2)[np.diff(v) > 0]
+    # bf16 keys: keep wanted means that bf16 represents exactly
+    want = np.concatenate([v, mids, [464.0, 472.0, 480.0, 1000.0, -464.0, 2.0**-10,
+                                     0.0]]).astype(np.float32)
+    want = want[torch.from_numpy(want).to(torch.bfloat16).float().numpy() == want]
+    # keys of -0 sum to +0 (the sum starts from +0), so -0 is no mean here
+    want = want[~((want == 0) & np.signbit(want))]
+    nblk = len(want)
+    L = 64 * nblk + 1
+    hq, hkv, d, Kb = 2, 1, 64, 4
+    k = np.repeat(want[:, None], 64, axis=0)  # block j: 64 keys equal to want[j]
+    kc = np.zeros((1, hkv, L, d), np.float32)
+    kc[0, 0, :64 * nblk] = np.repeat(k, d, axis=1)[:, :d]
+    prob = sas.Decode([L], hq, hkv, d, Kb, False, L, summary_dtype="fp8")
+    kct = torch.from_numpy(kc).to(torch.bfloat16).cuda()
+    ksum = sas.pool_keys(prob, kct)
+    torch.cuda.synchronize()
+    got = ksum[0, 0, 0, :nblk].cpu()
+    ref = torch.from_numpy(want).to(torch.float8_e4m3fn).view(torch.uint8)
+    # NaN has two codes (0x7f, 0xff) and torch writes 0x7f for either sign
+    nan = (ref & 0x7f) == 0x7f
+    assert torch.equal((got & 0x7f)[nan], ref[nan] & 0x7f)
+    assert torch.equal(got[~nan], ref[~nan]), (want[~nan.numpy()][(got != ref)[~nan].numpy()])
+    assert np.array_equal(summaries_f32(ksum)[0, 0, 0, :nblk][~nan.numpy()],
+                          oracle.round_e4m3(want)[~nan.numpy()])
+    say(f"  {nblk} summaries: codes equal torch's conversion")
 
 
 def test_paged_equals_contiguous_bitwise():

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_helpers import TOL, say
+from tests.gpu_helpers import TOL, say, summaries_f32
 from trainable_block_sparse_gate_amd import sas
 from trainable_block_sparse_gate_amd import workloads as wl
 
@@ -23,7 +23,8 @@ def _bf16_dev(bits):
         torch.bfloat16).cuda()
 
 
-@pytest.mark.parametrize("paged,summary", [(False, "f32"), (True, "f32"), (True, "bf16")])
+@pytest.mark.parametrize("paged,summary", [(False, "f32"), (True, "f32"), (True, "bf16"),
+                                           (False, "fp8")])
 def test_decode_step_loop(paged, summary):
     import torch
     L0 = [62, 128, 300, 1, 63, 191]   # steps cross 64, 128 (first step), 192, and none
@@ -83,7 +84,7 @@ def test_decode_step_loop(paged, summary):
         torch.cuda.synchronize()
         kc_d = kc.view(torch.int16).cpu().numpy().view(np.uint16)
         vc_d = vc.view(torch.int16).cpu().numpy().view(np.uint16)
-        ks_h, sel_h = ksum.float().cpu().numpy(), sel.cpu().numpy()
+        ks_h, sel_h = summaries_f32(ksum), sel.cpu().numpy()
         o_h = out.float().cpu().numpy()
         for b in range(B):
             L = lens[b]

@@ -27,6 +27,7 @@
 
 #include "sas_device.h"
 #include "sas_launch.h"
+#include "select.h"
 #include "tile_stage.h"
 
 namespace sas {
@@ -40,11 +41,33 @@ __device__ inline const __bf16 *kv_row(const DecodeParams &p, const __bf16 *cach
   return cache + (((long)b * p.hkv + g) * p.max_seqlen + tok) * p.D;
 }
 
+// The fp8 e4m3 code of the nearest e4m3 value to x (1 sign bit, 4 exponent
+// bits with bias 7, 3 mantissa bits, no infinities, 0x7f = NaN): below 2^-6
+// the format's spacing is 2^-9, in [2^e, 2^(e+1)) it is 2^(e-3); x over its
+// spacing is rounded to the nearest integer, ties to even (exact in fp32);
+// 480 and beyond, infinities and NaN give NaN.
+__device__ inline uint8_t e4m3_code(float x) {
+  const uint8_t sgn = (__float_as_uint(x) >> 31) ? 0x80 : 0;
+  const float a = fabsf(x);
+  if (!(a < 480.f)) return sgn | 0x7f;  // NaN, infinities, >= 480
+  const int e = a >= 0x1p-6f ? (int)((__float_as_uint(a) >> 23) & 255u) - 127 : -7;
+  const float spacing = e >= -6 ? __uint_as_float((uint32_t)(e - 3 + 127) << 23) : 0x1p-9f;
+  const float n = rintf(a / spacing);  // ties to even
+  const float r = n * spacing;
+  if (r >= 480.f) return sgn | 0x7f;
+  if (r < 0x1p-6f) return sgn | (uint8_t)(int)n;  // subnormal (or zero): mantissa n
+  const int er = (int)((__float_as_uint(r) >> 23) & 255u) - 127;
+  const uint32_t mant = (__float_as_uint(r) >> 20) & 7u;
+  return sgn | (uint8_t)((er + 7) << 3) | (uint8_t)mant;
+}
+
 // A block summary (the fp32 mean) stored as fp32, or rounded to the nearest
-// bf16 (ties to even) when summaries are bf16.
+// bf16 / fp8 e4m3 value (ties to even).
 __device__ inline void store_summary(const DecodeParams &p, long idx, float v) {
-  if (p.sum_bf16)
+  if (p.sum_kind == kSumBf16)
     static_cast<__bf16 *>(p.ksum)[idx] = (__bf16)v;
+  else if (p.sum_kind == kSumFp8)
+    static_cast<uint8_t *>(p.ksum)[idx] = e4m3_code(v);
   else
     static_cast<float *>(p.ksum)[idx] = v;
 }
@@ -94,77 +117,308 @@ __global__ __launch_bounds__(128) void append_kernel(DecodeParams p, const __bf1
   }
 }
 
-// ------------------------------------------------------------------ scores
-template <typename TS>
-__global__ __launch_bounds__(256) void pooled_scores_kernel(DecodeParams p) {
-#pragma clang fp contract(off)
-  __shared__ float qbar[256];
-  const int bg = blockIdx.y;
-  const int b = bg / p.hkv, g = bg % p.hkv;
-  const int G = p.hq / p.hkv;
-  const __bf16 *q = static_cast<const __bf16 *>(p.q);
-  for (int e = threadIdx.x; e < p.D; e += blockDim.x) {
-    float acc = 0.f;
-    for (int hh = 0; hh < G; ++hh) acc = acc + (float)q[((long)b * p.hq + g * G + hh) * p.D + e];
-    qbar[e] = acc / (float)G;
-  }
-  __syncthreads();
-  const int nhist = (p.seqlens[b] - 1) / kBlock;
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= nhist) return;
-  const TS *ks =
-      static_cast<const TS *>(p.ksum) + ((long)b * p.hkv + g) * p.D * p.nblk_stride + j;
-  float acc = 0.f;
-  for (int e = 0; e < p.D; ++e) acc = fmaf(qbar[e], (float)ks[(long)e * p.nblk_stride], acc);
-  p.scores[((long)b * p.hkv + g) * p.nblk_stride + j] = acc / p.sqrt_d;
+// ------------------------------------------------------------------ select
+// The fp32 value of an fp8 e4m3 code (exact): (1 + m / 8) 2^(e - 7) for
+// exponent field e > 0, m 2^-9 for e = 0; 0x7f / 0xff are NaN.  The code's
+// exponent and mantissa fields placed at the top of an fp32 pattern are the
+// fp32 number 2^-120 times the value (a normal fp32 for e > 0, a subnormal
+// m 2^-129 for e = 0), so one exact multiplication by 2^120 decodes both.
+__device__ inline float e4m3_value(uint32_t b) {
+  const float v = __uint_as_float(((b & 0x80u) << 24) | ((b & 0x7fu) << 20)) * 0x1p120f;
+  return (b & 0x7fu) == 0x7fu ? __uint_as_float(0x7fc00000u) : v;
 }
 
-// V consecutive blocks per thread (4: 16-byte fp32 / 8-byte bf16 loads; 1 for short grids, so
-// that a single long sequence still spreads over every compute unit), V
-// independent chains each in channel order, so every score is bit-identical
-// to the one-block form; channels in batches of 64 / V loads in flight.  For
-// summary strides that are multiples of 4.
-template <int D, int V, typename TS>
-__global__ __launch_bounds__(256) void pooled_scores_vec_kernel(DecodeParams p) {
+// V consecutive summaries from an address aligned to their size, as one
+// non-temporal load (the scan reads every summary once per step).
+template <typename TS, int V>
+__device__ inline void load_summaries(const TS *src, TS (&w)[V]) {
+  constexpr int BYTES = V * (int)sizeof(TS);
+  if constexpr (BYTES == 4) {
+    const uint32_t x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(src));
+    __builtin_memcpy(&w[0], &x, 4);
+  } else if constexpr (BYTES > 4) {
+    typedef uint32_t words __attribute__((ext_vector_type(BYTES / 4)));
+    const words x = __builtin_nontemporal_load(reinterpret_cast<const words *>(src));
+    __builtin_memcpy(&w[0], &x, BYTES);
+  } else if constexpr (BYTES == 2) {
+    const uint16_t x = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(src));
+    __builtin_memcpy(&w[0], &x, 2);
+  } else {
+    const uint8_t x = __builtin_nontemporal_load(reinterpret_cast<const uint8_t *>(src));
+    __builtin_memcpy(&w[0], &x, 1);
+  }
+}
+
+template <typename TS>
+__device__ inline float summary_value(TS x) {
+  if constexpr (sizeof(TS) == 1)
+    return e4m3_value(x);
+  else
+    return (float)x;
+}
+
+// Decode selection, phase 1: workgroup (chunk c, row b * hkv + g) takes
+// history blocks [256 V c, 256 V (c + 1)) of the row, V consecutive blocks
+// per thread.  It computes their pooled scores in the fixed fp32 order
+//   qbar_e = (q_{gG} + ... + q_{gG+G-1})_e / G,
+//   s_j    = (fmaf chain over e of qbar_e * summary_je) / sqrtf(d)
+// (so every score is the one the oracle computes), writes them out, and
+// keeps the chunk's exact Top-K (the Kb - 1 largest scores, earlier block
+// on ties), in block order, with the chunk's max and sum of exp(s - max)
+// for the row's normaliser.  VEC: the summary stride allows V-wide loads.
+template <int D, int G, int V, typename TS, bool VEC>
+__global__ __launch_bounds__(256) void select_partial_kernel(DecodeParams p, SelectParams sp) {
 #pragma clang fp contract(off)
-  using vec = TS __attribute__((ext_vector_type(V)));
+  constexpr int NT = 256, NWV = NT / kWave;
+  // summaries requested per batch: at most 512 bytes per thread
+  constexpr int CB = 512 / (V * (int)sizeof(TS)) < D ? 512 / (V * (int)sizeof(TS)) : D;
+  static_assert(D % CB == 0, "channel batches");
   __shared__ float qbar[D];
-  const int bg = blockIdx.y;
-  const int b = bg / p.hkv, g = bg % p.hkv;
-  const int G = p.hq / p.hkv;
+  __shared__ float red[NWV];
+  __shared__ int cnt[NWV];
+  __shared__ SelectScratch sel;
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int b = row / p.hkv, g = row % p.hkv;
+  const int tid = threadIdx.x;
   const __bf16 *q = static_cast<const __bf16 *>(p.q);
-  for (int e = threadIdx.x; e < D; e += blockDim.x) {
+  if (tid < D) {
+    float qv[G];  // every head's value requested before the ordered sum
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) qv[hh] = (float)q[((long)b * p.hq + g * G + hh) * D + tid];
     float acc = 0.f;
-    for (int hh = 0; hh < G; ++hh) acc = acc + (float)q[((long)b * p.hq + g * G + hh) * D + e];
-    qbar[e] = acc / (float)G;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) acc = acc + qv[hh];
+    qbar[tid] = acc / (float)G;
   }
   __syncthreads();
   const int nhist = (p.seqlens[b] - 1) / kBlock;
-  const int j0 = V * (blockIdx.x * blockDim.x + threadIdx.x);
-  if (j0 >= nhist) return;
-  const TS *ks =
-      static_cast<const TS *>(p.ksum) + ((long)b * p.hkv + g) * D * p.nblk_stride + j0;
-  float a[V];
+  const int kh = p.Kb - 1;
+  const int j0 = 256 * V * c + V * tid;  // this thread's first block
+  const int lo = 256 * V * c, n = max(0, min(nhist - lo, 256 * V));  // valid blocks in the chunk
+
+  // scores of this thread's blocks (invalid ones: -inf, never kept)
+  float sv[V];
+  uint32_t valid = 0u;
 #pragma unroll
-  for (int c = 0; c < V; ++c) a[c] = 0.f;
-  constexpr int BATCH = 64 / V;
-#pragma unroll 1
-  for (int e0 = 0; e0 < D; e0 += BATCH) {
-    vec v[BATCH];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u)
-      v[u] = *reinterpret_cast<const vec *>(ks + (long)(e0 + u) * p.nblk_stride);
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const float w = qbar[e0 + u];
-#pragma unroll
-      for (int c = 0; c < V; ++c) a[c] = fmaf(w, (float)v[u][c], a[c]);
-    }
+  for (int v = 0; v < V; ++v) {
+    sv[v] = -INFINITY;
+    if (j0 + v < nhist) valid |= 1u << v;
   }
-  float *out = p.scores + ((long)b * p.hkv + g) * p.nblk_stride + j0;
+  if (valid) {
+    // the summaries of CB channels (512 bytes per thread) are requested
+    // before the first of them is used
+    const TS *ks = static_cast<const TS *>(p.ksum) + ((long)row * D) * p.nblk_stride + j0;
+    float a[V];
 #pragma unroll
-  for (int c = 0; c < V; ++c)
-    if (j0 + c < nhist) out[c] = a[c] / p.sqrt_d;
+    for (int v = 0; v < V; ++v) a[v] = 0.f;
+#pragma unroll 1
+    for (int e0 = 0; e0 < D; e0 += CB) {
+      TS w[CB][V];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const TS *src = ks + (long)(e0 + u) * p.nblk_stride;
+        if constexpr (VEC) {
+          load_summaries<TS, V>(src, w[u]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < V; ++v) w[u][v] = ((valid >> v) & 1u) ? src[v] : TS{};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const float qe = qbar[e0 + u];
+#pragma unroll
+        for (int v = 0; v < V; ++v) a[v] = fmaf(qe, summary_value<TS>(w[u][v]), a[v]);
+      }
+    }
+    float *out = p.scores + (long)row * p.nblk_stride + j0;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if ((valid >> v) & 1u) {
+        sv[v] = a[v] / p.sqrt_d;
+        out[v] = sv[v];
+      }
+  }
+  // the chunk's share of the normaliser
+  float mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < V; ++v) mx = fmaxf(mx, sv[v]);
+  mx = block_max<NWV>(mx, red);
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if ((valid >> v) & 1u) sum += expf(sv[v] - mx);
+  }
+  sum = block_sum<NWV>(sum, red);
+  // the chunk's Top-K
+  const int k = min(kh, n);
+  const bool keep_all = k == n;
+  Threshold th{0u, 0u, k};
+  if (!keep_all && k > 0)
+    th = radix_threshold<NT>(k, sel, [&](auto &&f) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if ((valid >> v) & 1u) f(order_key(sv[v]));
+    });
+  int2 *cand = sp.cand + ((long)row * sp.nchunk + c) * kh;
+  if (k > 0) {
+    int pos, total;
+    const uint32_t takem = kept_mask<V, NWV>(sv, valid, keep_all, th, cnt, pos, total);
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if ((takem >> v) & 1u) {
+        cand[pos] = make_int2(j0 + v, __float_as_int(sv[v]));
+        ++pos;
+      }
+  }
+  for (int x = k + tid; x < kh; x += NT) cand[x] = make_int2(-1, __float_as_int(-INFINITY));
+  if (tid == 0) sp.part[(long)row * sp.nchunk + c] = make_float2(mx, sum);
+}
+
+// Decode selection, phase 2: one workgroup per row merges the chunks'
+// candidates (in block order: chunk by chunk, each in block order).  The
+// row's Top-K is contained in the union of the chunks' Top-Ks, so an exact
+// Top-K over the candidates with the same order gives it.  The normaliser
+// combines the chunks' (max, sum) pairs in chunk order.  Writes the kept
+// blocks ascending with log g = s - lse, the current block (log g 0), then
+// -1 padding.
+template <int R>
+__global__ __launch_bounds__(256) void select_merge_kernel(DecodeParams p, SelectParams sp) {
+  constexpr int NT = 256, NWV = NT / kWave;
+  __shared__ float red[NWV];
+  __shared__ int cnt[NWV];
+  __shared__ SelectScratch sel;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int b = row / p.hkv;
+  const int cur = (p.seqlens[b] - 1) / kBlock;
+  const int kh = p.Kb - 1;
+  const int ncand = sp.nchunk * kh;
+  const int2 *cand = sp.cand + (long)row * ncand;
+  float sv[R];
+  int jv[R];
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int c = 0; c < R; ++c) {
+    const int x = R * tid + c;
+    const int2 e = x < ncand ? cand[x] : make_int2(-1, 0);
+    jv[c] = e.x;
+    sv[c] = __int_as_float(e.y);
+    if (e.x >= 0) valid |= 1u << c;
+  }
+  // the normaliser: the chunks' (max, sum) pairs combined, chunks tid,
+  // tid + 256, ... by thread tid (requested together), the sums added in a
+  // fixed order
+  constexpr int PC = 4;  // chunks per thread held at once
+  const float2 *part = sp.part + (long)row * sp.nchunk;
+  float M = -INFINITY;
+  for (int c0 = tid; c0 < sp.nchunk; c0 += PC * NT) {
+    float2 pv[PC];
+#pragma unroll
+    for (int u = 0; u < PC; ++u)
+      pv[u] = c0 + u * NT < sp.nchunk ? part[c0 + u * NT] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int u = 0; u < PC; ++u) M = fmaxf(M, pv[u].x);
+  }
+  M = block_max<NWV>(M, red);
+  float Lt = 0.f;
+  for (int c = tid; c < sp.nchunk; c += NT) {
+    const float2 pv = part[c];
+    if (pv.y > 0.f) Lt += pv.y * expf(pv.x - M);
+  }
+  const float Lsum = block_sum<NWV>(Lt, red);
+  const float lse = (cur == 0 || M == -INFINITY) ? -INFINITY : M + logf(Lsum);
+  int nvalid_local = __popc(valid), nvalid;
+  block_scan_int<NWV>(nvalid_local, nvalid, cnt);
+  const int k = min(kh, cur);
+  const bool keep_all = k >= nvalid;
+  Threshold th{0u, 0u, k};
+  if (!keep_all && k > 0)
+    th = radix_threshold<NT>(k, sel, [&](auto &&f) {
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+        if ((valid >> c) & 1u) f(order_key(sv[c]));
+    });
+  int32_t *oidx = sp.sel_idx + (long)row * p.Kb;
+  float *olg = sp.sel_lg + (long)row * p.Kb;
+  if (k > 0) {
+    int pos, total;
+    const uint32_t takem = kept_mask<R, NWV>(sv, valid, keep_all, th, cnt, pos, total);
+#pragma unroll
+    for (int c = 0; c < R; ++c)
+      if ((takem >> c) & 1u) {
+        oidx[pos] = jv[c];
+        olg[pos] = lse == -INFINITY ? -INFINITY : sv[c] - lse;
+        ++pos;
+      }
+  }
+  if (tid == 0) {
+    oidx[k] = cur;
+    olg[k] = 0.f;
+    sp.gate_lse[row] = lse;
+  }
+  for (int x = k + 1 + tid; x < p.Kb; x += NT) {
+    oidx[x] = -1;
+    olg[x] = -INFINITY;
+  }
+}
+
+template <int D, int G, int V, typename TS>
+static void launch_partial(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
+  const dim3 grid(sp.nchunk, p.batch * p.hkv);
+  if (p.nblk_stride % V == 0)
+    hipLaunchKernelGGL((select_partial_kernel<D, G, V, TS, true>), grid, dim3(256), 0, stream, p,
+                       sp);
+  else
+    hipLaunchKernelGGL((select_partial_kernel<D, G, V, TS, false>), grid, dim3(256), 0, stream,
+                       p, sp);
+}
+
+template <int D, int G, typename TS>
+static void launch_partial_v(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
+  switch (sp.chunk_v) {
+    case 1: launch_partial<D, G, 1, TS>(p, sp, stream); break;
+    case 2: launch_partial<D, G, 2, TS>(p, sp, stream); break;
+    case 4: launch_partial<D, G, 4, TS>(p, sp, stream); break;
+    default: launch_partial<D, G, 8, TS>(p, sp, stream); break;
+  }
+}
+
+template <int D, typename TS>
+static void launch_partial_g(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
+  switch (p.hq / p.hkv) {
+    case 1: launch_partial_v<D, 1, TS>(p, sp, stream); break;
+    case 2: launch_partial_v<D, 2, TS>(p, sp, stream); break;
+    case 4: launch_partial_v<D, 4, TS>(p, sp, stream); break;
+    default: launch_partial_v<D, 8, TS>(p, sp, stream); break;
+  }
+}
+
+hipError_t launch_decode_select(const DecodeParams &p, const SelectParams &sp,
+                                hipStream_t stream) {
+  if (p.D == 128) {
+    if (p.sum_kind == kSumBf16) launch_partial_g<128, __bf16>(p, sp, stream);
+    else if (p.sum_kind == kSumFp8) launch_partial_g<128, uint8_t>(p, sp, stream);
+    else launch_partial_g<128, float>(p, sp, stream);
+  } else {
+    if (p.sum_kind == kSumBf16) launch_partial_g<64, __bf16>(p, sp, stream);
+    else if (p.sum_kind == kSumFp8) launch_partial_g<64, uint8_t>(p, sp, stream);
+    else launch_partial_g<64, float>(p, sp, stream);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ncand = sp.nchunk * (p.Kb - 1);
+  const dim3 grid(p.batch * p.hkv);
+  if (ncand <= 256) hipLaunchKernelGGL((select_merge_kernel<1>), grid, dim3(256), 0, stream, p, sp);
+  else if (ncand <= 512)
+    hipLaunchKernelGGL((select_merge_kernel<2>), grid, dim3(256), 0, stream, p, sp);
+  else if (ncand <= 1024)
+    hipLaunchKernelGGL((select_merge_kernel<4>), grid, dim3(256), 0, stream, p, sp);
+  else if (ncand <= 2048)
+    hipLaunchKernelGGL((select_merge_kernel<8>), grid, dim3(256), 0, stream, p, sp);
+  else
+    hipLaunchKernelGGL((select_merge_kernel<16>), grid, dim3(256), 0, stream, p, sp);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ attend
@@ -552,35 +806,6 @@ hipError_t launch_decode_append(const DecodeParams &p, const void *k_new, const 
                      static_cast<const __bf16 *>(k_new), static_cast<const __bf16 *>(v_new),
                      static_cast<__bf16 *>(k_cache), static_cast<__bf16 *>(v_cache));
   return hipGetLastError();
-}
-
-template <typename TS>
-static hipError_t launch_pooled_scores_t(const DecodeParams &p, hipStream_t stream) {
-  if (p.nblk_stride % 4 == 0 && (p.D == 128 || p.D == 64)) {
-    const dim3 grid4((p.nblk_stride / 4 + 255) / 256, p.batch * p.hkv);
-    const dim3 grid1((p.nblk_stride + 255) / 256, p.batch * p.hkv);
-    const bool narrow = (long)grid4.x * grid4.y < 256;  // fewer workgroups than CUs
-    if (p.D == 128) {
-      if (narrow)
-        hipLaunchKernelGGL((pooled_scores_vec_kernel<128, 1, TS>), grid1, dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((pooled_scores_vec_kernel<128, 4, TS>), grid4, dim3(256), 0, stream, p);
-    } else {
-      if (narrow)
-        hipLaunchKernelGGL((pooled_scores_vec_kernel<64, 1, TS>), grid1, dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((pooled_scores_vec_kernel<64, 4, TS>), grid4, dim3(256), 0, stream, p);
-    }
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(pooled_scores_kernel<TS>, dim3((p.nblk_stride + 255) / 256, p.batch * p.hkv),
-                     dim3(256), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_pooled_scores(const DecodeParams &p, hipStream_t stream) {
-  return p.sum_bf16 ? launch_pooled_scores_t<__bf16>(p, stream)
-                    : launch_pooled_scores_t<float>(p, stream);
 }
 
 template <int D, int G>

@@ -30,104 +30,23 @@
 constexpr int kGateSigmoid = 2, kGateRaw = 3, kGateSte = 4;  // the ablations
 #include "sas_device.h"
 #include "sas_launch.h"
+#include "select.h"
 
 namespace sas {
 
 constexpr int kGateThreads = 256;
 constexpr int kGateWaves = kGateThreads / kWave;
 
-__device__ inline uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;  // -0 sorts with +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Workgroup reductions / scans through a small LDS scratch.
-template <int NWV = kGateWaves>
-__device__ inline float block_max(float x, float *red) {
-  x = wave_max(x);
-  const int w = threadIdx.x / kWave;
-  __syncthreads();
-  if ((threadIdx.x % kWave) == 0) red[w] = x;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int k = 1; k < NWV; ++k) r = fmaxf(r, red[k]);
-  return r;
-}
-
-template <int NWV = kGateWaves>
-__device__ inline float block_sum(float x, float *red) {
-  x = wave_sum(x);
-  const int w = threadIdx.x / kWave;
-  __syncthreads();
-  if ((threadIdx.x % kWave) == 0) red[w] = x;
-  __syncthreads();
-  float r = 0.f;
-#pragma unroll
-  for (int k = 0; k < NWV; ++k) r += red[k];  // fixed order: deterministic
-  return r;
-}
-
-// Exclusive prefix sum of a non-negative count over the workgroup in
-// thread order, and the total.
-template <int NWV = kGateWaves>
-__device__ inline int block_scan_int(int x, int &total, int *cnt) {
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  int incl = x;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  __syncthreads();
-  if (lane == kWave - 1) cnt[w] = incl;
-  __syncthreads();
-  int off = 0;
-  total = 0;
-#pragma unroll
-  for (int k = 0; k < NWV; ++k) {
-    if (k < w) off += cnt[k];
-    total += cnt[k];
-  }
-  return off + incl - x;
-}
-
-// Exclusive prefix count of `flag` over the workgroup in thread order, and
-// the total.
-template <int NWV = kGateWaves>
-__device__ inline int block_scan_flag(bool flag, int &total, int *cnt) {
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const uint64_t m = __ballot(flag);
-  const int below = __popcll(m & ((1ull << lane) - 1ull));
-  __syncthreads();
-  if (lane == 0) cnt[w] = __popcll(m);
-  __syncthreads();
-  int off = 0;
-  total = 0;
-#pragma unroll
-  for (int k = 0; k < NWV; ++k) {
-    if (k < w) off += cnt[k];
-    total += cnt[k];
-  }
-  return off + below;
-}
-
 __device__ inline void row_geometry(const GateParams &p, int r, int &i) {
-  if (p.decode) {
-    const int b = r / p.hkv;
-    i = (p.seqlens[b] - 1) / kBlock;
-  } else {
-    const int Q = r % p.QB;
-    const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, Q);
-    i = Q - p.cu_qblocks[s];
-  }
+  const int Q = r % p.QB;
+  const int s = seq_of_qblock(p.cu_qblocks, p.num_seqs, Q);
+  i = Q - p.cu_qblocks[s];
 }
 
 // R > 0: the row's scores (at most NT * R) are read once into registers,
 // thread t holding the R consecutive entries R t .. R t + R - 1;
 // every pass below then works on registers instead of re-reading the row
-// (long decode rows have thousands of candidates), and the kept blocks are
+// (long sequences have thousands of candidate blocks), and the kept blocks are
 // placed with two workgroup scans in all (entries are in index order across
 // the threads).  R = 0 reads the row in each pass and places the kept
 // blocks chunk by chunk.
@@ -136,8 +55,7 @@ __global__ __launch_bounds__(NT) void gate_topk_kernel(GateParams p) {
   constexpr int NWV = NT / kWave;
   __shared__ float red[NWV];
   __shared__ int cnt[NWV];
-  __shared__ int hist[256];
-  __shared__ int s_bin, s_rem, s_cnt;
+  __shared__ SelectScratch sel;
 
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -183,54 +101,13 @@ __global__ __launch_bounds__(NT) void gate_topk_kernel(GateParams p) {
 
   // Exact k-th largest key (radix select), unless every candidate is kept.
   const bool keep_all = (k == i);
-  uint32_t prefix = 0u, pmask = 0u;
-  int remaining = k;
-  if (!keep_all && k > 0) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      each(i, [&](int, float x) {
-        const uint32_t key = order_key(x);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-      });
-      __syncthreads();
-      if (tid < kWave) {
-        const int lane = tid;
-        // lane owns bins 4*lane .. 4*lane+3; suffix sums run from the top bin
-        const int c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
-                  c3 = hist[4 * lane + 3];
-        const int local = c0 + c1 + c2 + c3;
-        int incl = local;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int y = __shfl_down(incl, o);
-          if (lane + o < kWave) incl += y;
-        }
-        int cum = incl - local;  // keys in bins above this lane's four
-        const int cs[4] = {c0, c1, c2, c3};
-#pragma unroll
-        for (int x = 3; x >= 0; --x) {
-          if (cum < remaining && cum + cs[x] >= remaining) {
-            s_bin = 4 * lane + x;
-            s_rem = remaining - cum;
-            s_cnt = cs[x];
-          }
-          cum += cs[x];
-        }
-      }
-      __syncthreads();
-      prefix |= (uint32_t)s_bin << shift;
-      pmask |= 255u << shift;
-      remaining = s_rem;
-      const bool whole_bin = s_rem == s_cnt;
-      __syncthreads();
-      // every key of the threshold bin is kept: the bits below it cannot
-      // change the kept set, so the select stops (keys then compare on the
-      // bits decided so far)
-      if (whole_bin) break;
-    }
-  }
+  Threshold th{0u, 0u, k};
+  if (!keep_all && k > 0)
+    th = radix_threshold<NT>(k, sel, [&](auto &&f) {
+      each(i, [&](int, float x) { f(order_key(x)); });
+    });
+  const uint32_t prefix = th.prefix, pmask = th.pmask;
+  const int remaining = th.remaining;
 
   // Emit kept blocks in index order: keys above the threshold, plus the
   // first `remaining` keys equal to it.
@@ -262,28 +139,14 @@ __global__ __launch_bounds__(NT) void gate_topk_kernel(GateParams p) {
   };
   if (k > 0) {
     if constexpr (R > 0) {
-      // this thread's keys above the threshold and equal to it (the first
-      // `remaining` equal keys in index order are kept)
-      // (bit c of a mask: this thread's entry R tid + c)
-      uint32_t gtm = 0u, eqm = 0u;
-#pragma unroll
-      for (int c = 0; c < R; ++c) {
-        const int j = R * tid + c;
-        const uint32_t key = order_key(sv[c]) & pmask;
-        if (j < i && (keep_all || key > prefix)) gtm |= 1u << c;
-        if (j < i && !keep_all && key == prefix) eqm |= 1u << c;
-      }
-      int eq_tot;
-      int eq_rank = block_scan_int<NWV>(__popc(eqm), eq_tot, cnt);
-      uint32_t takem = gtm;
+      // this thread's kept entries (the first `remaining` keys equal to the
+      // threshold in index order are kept), placed by two workgroup scans
+      uint32_t valid = 0u;
 #pragma unroll
       for (int c = 0; c < R; ++c)
-        if ((eqm >> c) & 1u) {
-          if (eq_rank < remaining) takem |= 1u << c;
-          ++eq_rank;
-        }
-      int take_tot;
-      int pos = block_scan_int<NWV>(__popc(takem), take_tot, cnt);
+        if (R * tid + c < i) valid |= 1u << c;
+      int pos, take_tot;
+      const uint32_t takem = kept_mask<R, NWV>(sv, valid, keep_all, th, cnt, pos, take_tot);
 #pragma unroll
       for (int c = 0; c < R; ++c)
         if ((takem >> c) & 1u) {
@@ -314,7 +177,7 @@ hipError_t launch_gate_topk(const GateParams &p, hipStream_t stream) {
   // rows hold at most ld scores (one more than the history in SAS_GATE_ALL
   // is still within ld): registers when they fit, else re-reads
   // (long rows take 1024 threads: 4x the threads on each pass of the few
-  // rows a long-context decode has)
+  // rows a long sequence has)
   const dim3 grid(p.nrows);
   if (p.ld <= 256) hipLaunchKernelGGL((gate_topk_kernel<1, 256>), grid, dim3(256), 0, stream, p);
   else if (p.ld <= 1024)

@@ -126,7 +126,6 @@ sas_status sas_gate_topk(const sas_problem *p, const float *logits, int64_t ld,
   sas::GateParams g{};
   g.scores = logits;
   g.ld = ld;
-  g.decode = 0;
   g.QB = p->total_qblocks;
   g.num_seqs = p->num_seqs;
   g.hkv = p->hkv;
@@ -405,7 +404,8 @@ sas_status check_decode(const sas_decode_problem *p) {
   REQUIRE(p->layout == SAS_KV_CONTIGUOUS || p->layout == SAS_KV_PAGED, SAS_ERR_SHAPE,
           "unknown layout %d", p->layout);
   REQUIRE(std::isfinite(p->scale), SAS_ERR_SHAPE, "scale is not finite");
-  REQUIRE(p->summary_dtype == SAS_SUMMARY_F32 || p->summary_dtype == SAS_SUMMARY_BF16,
+  REQUIRE(p->summary_dtype == SAS_SUMMARY_F32 || p->summary_dtype == SAS_SUMMARY_BF16 ||
+              p->summary_dtype == SAS_SUMMARY_FP8,
           SAS_ERR_DTYPE, "unknown summary_dtype %d", p->summary_dtype);
   REQUIRE(p->seqlens && p->seqlens_host, SAS_ERR_NULL, "seqlens (device and host) required");
   int maxL = 0;
@@ -498,7 +498,9 @@ sas::DecodeParams decode_params(const sas_decode_problem *p) {
   d.D = p->head_dim;
   d.Kb = p->budget_blocks;
   d.nblk_stride = p->nblk_stride;
-  d.sum_bf16 = p->summary_dtype == SAS_SUMMARY_BF16;
+  d.sum_kind = p->summary_dtype == SAS_SUMMARY_BF16  ? sas::kSumBf16
+               : p->summary_dtype == SAS_SUMMARY_FP8 ? sas::kSumFp8
+                                                     : sas::kSumF32;
   d.sqrt_d = sqrtf((float)p->head_dim);
   d.scale_log2 = p->scale * 1.4426950408889634f;
   d.out_bf16 = p->out_dtype == SAS_BF16;
@@ -520,7 +522,46 @@ size_t decode_ws_bytes(const sas_decode_problem *p) {
   return decode_partial_bytes(p, nsplit);
 }
 
+// Chunking of the decode selection over workgroups: V blocks per thread
+// (256 V blocks per chunk).  The fixed cost of a chunk's workgroup (the
+// query mean, one memory latency per 512 bytes of summaries a thread
+// requests, the Top-K passes) is paid once per round of workgroups, so V
+// grows (up to 8) while the grid would still hold more than 512
+// workgroups; the merge takes at most 4096 candidates (chunks x (Kb - 1)),
+// which also bounds the chunk count from below.
+struct SelectGeom {
+  int v, nchunk;
+};
+
+int summary_bytes(const sas_decode_problem *p) {
+  return p->summary_dtype == SAS_SUMMARY_F32 ? 4 : p->summary_dtype == SAS_SUMMARY_BF16 ? 2 : 1;
+}
+
+SelectGeom select_geom(const sas_decode_problem *p) {
+  int maxhist = 1;
+  for (int b = 0; b < p->batch; ++b)
+    if ((p->seqlens_host[b] - 1) / 64 > maxhist) maxhist = (p->seqlens_host[b] - 1) / 64;
+  const long rows = (long)p->batch * p->hkv;
+  const int kh = p->budget_blocks > 1 ? p->budget_blocks - 1 : 1;
+  auto chunks = [&](int v) { return (maxhist + 256 * v - 1) / (256 * v); };
+  int v = 1;
+  while (v < 8 && (rows * chunks(v) > 512 || chunks(v) * kh > 4096)) v *= 2;
+  return {v, chunks(v)};
+}
+
+constexpr int kMaxSelectCandidates = 4096;
+
+size_t select_ws_bytes(const sas_decode_problem *p, const SelectGeom &sg) {
+  const size_t n = (size_t)p->batch * p->hkv * sg.nchunk;
+  return align256(n * (p->budget_blocks - 1) * sizeof(int2)) + n * sizeof(float2);
+}
+
 }  // namespace
+
+size_t sas_decode_select_workspace_size(const sas_decode_problem *p) {
+  if (check_decode(p) != SAS_OK) return 0;
+  return select_ws_bytes(p, select_geom(p));
+}
 
 size_t sas_decode_workspace_size(const sas_decode_problem *p) {
   if (check_decode(p) != SAS_OK) return 0;
@@ -554,30 +595,36 @@ sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, con
 
 sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const void *ksum,
                              float *scores, int32_t *sel_idx, float *sel_loggate,
-                             float *gate_lse, void *stream) {
+                             float *gate_lse, void *workspace, size_t workspace_bytes,
+                             void *stream) {
   sas_status st = check_decode(p);
   if (st) return st;
   REQUIRE(q && ksum && scores && sel_idx && sel_loggate && gate_lse, SAS_ERR_NULL,
           "a tensor argument of sas_decode_select is NULL");
+  REQUIRE(aligned16(ksum), SAS_ERR_ALIGN, "ksum must be 16-byte aligned");
+  const SelectGeom sg = select_geom(p);
+  REQUIRE(sg.nchunk * (p->budget_blocks - 1) <= kMaxSelectCandidates, SAS_ERR_UNSUPPORTED,
+          "history of %d chunks x %d kept blocks exceeds the selection's %d candidates",
+          sg.nchunk, p->budget_blocks - 1, kMaxSelectCandidates);
+  const size_t need = select_ws_bytes(p, sg);
+  REQUIRE(workspace && workspace_bytes >= need, SAS_ERR_WORKSPACE,
+          "workspace has %zu bytes, needs %zu", workspace ? workspace_bytes : 0, need);
+  REQUIRE(aligned16(workspace), SAS_ERR_ALIGN, "workspace must be 16-byte aligned");
   sas::DecodeParams d = decode_params(p);
   d.q = q;
   d.ksum = const_cast<void *>(ksum);
   d.scores = scores;
-  hipError_t e = sas::launch_pooled_scores(d, (hipStream_t)stream);
-  if (e != hipSuccess) return from_hip(e, "pooled scores launch");
-  sas::GateParams g{};
-  g.scores = scores;
-  g.ld = p->nblk_stride;
-  g.decode = 1;
-  g.hkv = p->hkv;
-  g.seqlens = p->seqlens;
-  g.Kb = p->budget_blocks;
-  g.mode = SAS_GATE_HIST;
-  g.sel_idx = sel_idx;
-  g.sel_lg = sel_loggate;
-  g.gate_lse = gate_lse;
-  g.nrows = p->batch * p->hkv;
-  return from_hip(sas::launch_gate_topk(g, (hipStream_t)stream), "decode gate_topk launch");
+  sas::SelectParams s{};
+  s.nchunk = sg.nchunk;
+  s.chunk_v = sg.v;
+  s.sel_idx = sel_idx;
+  s.sel_lg = sel_loggate;
+  s.gate_lse = gate_lse;
+  char *ws = static_cast<char *>(workspace);
+  const size_t n = (size_t)p->batch * p->hkv * sg.nchunk;
+  s.cand = reinterpret_cast<int2 *>(ws);
+  s.part = reinterpret_cast<float2 *>(ws + align256(n * (p->budget_blocks - 1) * sizeof(int2)));
+  return from_hip(sas::launch_decode_select(d, s, (hipStream_t)stream), "decode select launch");
 }
 
 sas_status sas_decode(const sas_decode_problem *p, const void *q, const void *k_cache,

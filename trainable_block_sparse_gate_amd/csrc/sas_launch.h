@@ -10,15 +10,12 @@ constexpr int kMaxBudget = 256;  // largest budget_blocks a row may hold
 constexpr int kDecodeWgPerCu = 1;  // decode workgroups resident per compute unit
 
 struct GateParams {
-  // Row layout: training rows (decode == 0) are r = g * QB + Q with the
-  // query block Q of sequence s at local index i = Q - cu_qblocks[s];
-  // decode rows are r = b * hkv + g with i = (seqlens[b] - 1) / 64.
+  // Row layout: r = g * QB + Q with the query block Q of sequence s at
+  // local index i = Q - cu_qblocks[s].
   const float *scores;
   int64_t ld;
-  int decode;
   int QB, num_seqs, hkv;
   const int32_t *cu_qblocks;
-  const int32_t *seqlens;
   int Kb, mode;
   int32_t *sel_idx;
   float *sel_lg;
@@ -95,8 +92,8 @@ struct DecodeParams {
   const int32_t *page_table;   // [batch][max_pages] when paged
   int paged, max_pages, max_seqlen;
   int batch, hq, hkv, D, Kb, nblk_stride;
-  void *ksum;                  // [batch][hkv][D][nblk_stride], fp32 or bf16
-  int sum_bf16;                // summaries stored as bf16
+  void *ksum;                  // [batch][hkv][D][nblk_stride], fp32, bf16 or fp8
+  int sum_kind;                // kSumF32, kSumBf16 or kSumFp8
   float *scores;               // [batch][hkv][nblk_stride]
   float sqrt_d;                // sqrtf(D), for the pooled score
   const int32_t *sel_idx;      // [batch*hkv][Kb]
@@ -108,10 +105,22 @@ struct DecodeParams {
   int nsplit, per_split;       // split-K geometry
   float *partial;              // [batch*hkv][nsplit][G][D + 2]
 };
+// decode selection (pooled scores -> gate + Top-K) over chunks of each row:
+// scores and an exact local Top-K per chunk, then a merge per row
+struct SelectParams {
+  int nchunk, chunk_v;         // chunks per row; blocks per thread (chunk = 256 chunk_v)
+  int32_t *sel_idx;            // out [batch*hkv][Kb]
+  float *sel_lg;               // out [batch*hkv][Kb]
+  float *gate_lse;             // out [batch*hkv]
+  int2 *cand;                  // workspace [rows][nchunk][Kb - 1]: (block, score bits)
+  float2 *part;                // workspace [rows][nchunk]: chunk max, sum of exp
+};
+constexpr int kSumF32 = 0, kSumBf16 = 1, kSumFp8 = 2;
+hipError_t launch_decode_select(const DecodeParams &p, const SelectParams &s,
+                                hipStream_t stream);
 hipError_t launch_pool_keys(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_append(const DecodeParams &p, const void *k_new, const void *v_new,
                                void *k_cache, void *v_cache, hipStream_t stream);
-hipError_t launch_pooled_scores(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_attend(const DecodeParams &p, hipStream_t stream);
 // The fixed device scratch sas_decode_noalloc puts split partials in: its
 // address on the current device (looked up once per device).

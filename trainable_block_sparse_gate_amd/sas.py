@@ -21,9 +21,9 @@ SAS_BF16, SAS_F32 = 0, 1
 GATE_HIST, GATE_ALL, GATE_SIGMOID, GATE_RAW, GATE_STE = 0, 1, 2, 3, 4
 GATE_INNER, GATE_OUTER = 0, 1  # gate position
 KV_CONTIGUOUS, KV_PAGED = 0, 1
-SUMMARY_F32, SUMMARY_BF16 = 0, 1
+SUMMARY_F32, SUMMARY_BF16, SUMMARY_FP8 = 0, 1, 2
 BLOCK = 64
-ABI_VERSION = 3  # the header's SAS_ABI_VERSION these structs follow
+ABI_VERSION = 4  # the header's SAS_ABI_VERSION these structs follow
 
 STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTYPE",
           -4: "SAS_ERR_ALIGN", -5: "SAS_ERR_UNSUPPORTED", -6: "SAS_ERR_WORKSPACE",
@@ -32,7 +32,8 @@ STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTY
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = ["sas_gate_topk", "sas_fwd", "sas_bwd_workspace_size", "sas_bwd", "sas_bwd_prepare",
            "sas_bwd_dq", "sas_bwd_dkdv", "sas_gate_bwd",
-           "sas_pool_keys", "sas_decode_append", "sas_decode_select", "sas_decode_workspace_size",
+           "sas_pool_keys", "sas_decode_append", "sas_decode_select_workspace_size",
+           "sas_decode_select", "sas_decode_workspace_size",
            "sas_decode", "sas_decode_noalloc",
            "sas_status_string", "sas_last_error", "sas_abi_version"]
 
@@ -96,7 +97,8 @@ def lib():
             "sas_gate_bwd": [P, vp, i64, i32, vp, vp, vp, vp, vp],
             "sas_pool_keys": [DP, vp, vp, vp],
             "sas_decode_append": [DP, vp, vp, vp, vp, vp, vp],
-            "sas_decode_select": [DP, vp, vp, vp, vp, vp, vp, vp],
+            "sas_decode_select_workspace_size": [DP],
+            "sas_decode_select": [DP, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "sas_decode_workspace_size": [DP],
             "sas_decode": [DP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "sas_decode_noalloc": [DP, vp, vp, vp, vp, vp, vp, vp, vp],
@@ -110,6 +112,7 @@ def lib():
             fn.restype = i32
         L.sas_bwd_workspace_size.restype = sz
         L.sas_decode_workspace_size.restype = sz
+        L.sas_decode_select_workspace_size.restype = sz
         L.sas_status_string.restype = ctypes.c_char_p
         L.sas_last_error.restype = ctypes.c_char_p
         if L.sas_abi_version() != ABI_VERSION:
@@ -162,7 +165,7 @@ def _gpu(*tensors):
 
 def _torch_dtype(code):
     import torch
-    return torch.bfloat16 if code == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}[code]
 
 
 def _stream():
@@ -357,8 +360,9 @@ class Decode:
         self.batch = len(self.seqlens)
         self.paged = paged
         # summary row stride: history blocks of the longest sequence, rounded
-        # up to a multiple of 4 (the library then reads summaries as float4)
-        self.nblk_stride = -(-max(1, max((n - 1) // BLOCK for n in self.seqlens)) // 4) * 4
+        # up to a multiple of 16 (the library then reads summaries 16 bytes
+        # at a time in every summary dtype)
+        self.nblk_stride = -(-max(1, max((n - 1) // BLOCK for n in self.seqlens)) // 16) * 16
         if nblk_stride is not None:
             self.nblk_stride = int(nblk_stride)
         self.pt_dev = None
@@ -378,7 +382,7 @@ class Decode:
             KV_PAGED if paged else KV_CONTIGUOUS, max_seqlen, max_pages, num_pages,
             self.nblk_stride, self.scale, self.sl_dev.data_ptr(), self.sl_host.ctypes.data,
             self.pt_dev.data_ptr() if paged else None,
-            SUMMARY_BF16 if summary_dtype == "bf16" else SUMMARY_F32,
+            {"f32": SUMMARY_F32, "bf16": SUMMARY_BF16, "fp8": SUMMARY_FP8}[summary_dtype],
             self.pt_host.ctypes.data if paged else None, int(num_splits))
         self.summary_dtype = summary_dtype
 
@@ -414,8 +418,7 @@ def pool_keys(prob: Decode, k_cache):
     import torch
     prob.check_cache(k_cache, "k_cache")
     ksum = torch.empty((prob.batch, prob.hkv, prob.d, prob.nblk_stride),
-                       dtype=torch.bfloat16 if prob.summary_dtype == "bf16" else torch.float32,
-                       device=k_cache.device)
+                       dtype=_torch_dtype(prob.summary_dtype), device=k_cache.device)
     _gpu(k_cache, ksum)
     _check(lib().sas_pool_keys(prob.ref, _ptr(k_cache), _ptr(ksum), _stream()))
     return ksum
@@ -435,7 +438,11 @@ def decode_append(prob: Decode, k_new, v_new, k_cache, v_cache, ksum):
                                    _ptr(v_cache), _ptr(ksum), _stream()))
 
 
-def decode_select(prob: Decode, q, ksum, out=None):
+def decode_select_workspace_bytes(prob: Decode):
+    return int(lib().sas_decode_select_workspace_size(prob.ref))
+
+
+def decode_select(prob: Decode, q, ksum, out=None, workspace=None):
     """sas_decode_select -> (sel_idx, sel_loggate, gate_lse, scores)."""
     import torch
     prob.check_q(q)
@@ -452,9 +459,14 @@ def decode_select(prob: Decode, q, ksum, out=None):
     prob.check_selection(sel, lg)
     _need(lse, "gate_lse", torch.float32, (rows,))
     _need(scores, "scores", torch.float32, (prob.batch, prob.hkv, prob.nblk_stride))
-    _gpu(q, ksum, sel, lg, lse, scores)
+    if workspace is None:
+        workspace = torch.empty(max(decode_select_workspace_bytes(prob), 1), dtype=torch.uint8,
+                                device=dev)
+    _need(workspace, "workspace", torch.uint8, (None,))
+    _gpu(q, ksum, sel, lg, lse, scores, workspace)
     _check(lib().sas_decode_select(prob.ref, _ptr(q), _ptr(ksum), _ptr(scores), _ptr(sel),
-                                   _ptr(lg), _ptr(lse), _stream()))
+                                   _ptr(lg), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                   _stream()))
     return sel, lg, lse, scores
 
 

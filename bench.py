@@ -181,7 +181,10 @@ def kernel_label(n):
     if m:  # mangled, no template arguments
         return f"sas::{m.group(1)}"
     if short_kernel(n):
-        return re.sub(r"^void ", "", re.sub(r"\(sas::\w+\)$", "", n))
+        # the profiler's demangler prints the __bf16 template argument (and
+        # the one after it) as "bool _Accum, bool, E"
+        n = n.replace("bool _Accum, bool, E", "__bf16, ...")
+        return re.sub(r"^void ", "", re.sub(r"\(sas::\w+(, sas::\w+)*\)$", "", n))
     m = re.search(r"at::native::[A-Za-z_:]*", n)
     return (m.group(0) if m else n[:48]) + " (torch)"
 
@@ -193,19 +196,22 @@ def summarize_trace(d, cmd, out, skip):
     if not rows:
         sys.exit(f"no kernel_trace.csv under {d}")
     per = {}
-    for r in rows:
-        per.setdefault(r["Kernel_Name"], []).append(r)
+    for r in rows:  # one entry per kernel and launch shape (workloads differ in grid)
+        grid = int(r.get("Grid_Size_X", 0) or 0) * int(r.get("Grid_Size_Y", 1) or 1) * \
+            int(r.get("Grid_Size_Z", 1) or 1)
+        per.setdefault((r["Kernel_Name"], grid), []).append(r)
     total = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows)
     lines = ["# Kernel trace summary (rocprofv3 --kernel-trace --stats)", "", "```", cmd, "```",
-             "", f"Durations in us.  Steady state = every dispatch after each kernel's first "
+             "", f"Durations in us, one row per kernel and launch grid (the workloads of the "
+             f"command differ in grid).  Steady state = every dispatch after the row's first "
              f"{skip} (the warm-up steps of the command).", "",
-             "| kernel | calls | avg (all) | avg (steady) | min | max | % of GPU time | WGs | "
+             "| kernel | WGs | calls | avg (all) | avg (steady) | min | max | % of GPU time | "
              "WG size | LDS B | VGPR | AGPR |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     summary = {}
-    for n, rs in sorted(per.items(), key=lambda kv: -sum(int(r["End_Timestamp"]) -
-                                                         int(r["Start_Timestamp"])
-                                                         for r in kv[1])):
+    for (n, _), rs in sorted(per.items(), key=lambda kv: -sum(int(r["End_Timestamp"]) -
+                                                              int(r["Start_Timestamp"])
+                                                              for r in kv[1])):
         rs.sort(key=lambda r: int(r["Start_Timestamp"]))
         dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
         steady = dur[skip:] if len(dur) > skip else dur
@@ -215,11 +221,11 @@ def summarize_trace(d, cmd, out, skip):
             int(t.get("Grid_Size_Z", 1) or 1)
         nwg = grid // wg if wg else 0
         lab = kernel_label(n)
-        summary[lab] = {"calls": len(dur), "avg_us": sum(dur) / len(dur),
-                        "steady_avg_us": sum(steady) / len(steady)}
-        lines.append(f"| `{lab}` | {len(dur)} | {sum(dur) / len(dur):.1f} | "
+        summary[f"{lab} [{nwg} WGs]"] = {"calls": len(dur), "avg_us": sum(dur) / len(dur),
+                                         "steady_avg_us": sum(steady) / len(steady)}
+        lines.append(f"| `{lab}` | {nwg} | {len(dur)} | {sum(dur) / len(dur):.1f} | "
                      f"{sum(steady) / len(steady):.1f} | {min(dur):.1f} | {max(dur):.1f} | "
-                     f"{100.0 * sum(dur) * 1e3 / total:.1f} | {nwg} | {wg} | "
+                     f"{100.0 * sum(dur) * 1e3 / total:.1f} | {wg} | "
                      f"{t.get('LDS_Block_Size', '')} | {t.get('VGPR_Count', '')} | "
                      f"{t.get('Accum_VGPR_Count', '')} |")
     text = "\n".join(lines) + "\n"
@@ -231,22 +237,62 @@ def summarize_trace(d, cmd, out, skip):
     print(text)
 
 
+XCDS, SIMDS = 8, 1024  # MI355X: accelerator dies (GRBM_GUI_ACTIVE is summed over them), SIMDs
+
+
 def summarize_counters(d, cmd, out):
-    """Average of every counter per kernel (one --pmc pass)."""
-    per = {}
+    """Average of every counter per kernel over one --pmc pass, and what
+    follows from them: MFMA busy (% of the SIMDs' cycles), the clock the
+    kernel ran at, LDS bank-conflict share, L2 hit rate."""
+    per, dur = {}, {}
     for r in read_csvs(d, "counter_collection.csv"):
         if short_kernel(r["Kernel_Name"]) in (None, "copyBuffer"):
             continue
         k = kernel_label(r["Kernel_Name"])
         per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        dur.setdefault(k, {})[r["Dispatch_Id"]] = \
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     names = sorted({c for v in per.values() for c in v})
-    lines = ["# Hardware counters per dispatch (rocprofv3 --pmc)", "", "```", cmd, "```", "",
-             "Averages over the dispatches of each kernel.", "",
-             "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+
+    def derived(v, ns):
+        out = {}
+        g = v.get("GRBM_GUI_ACTIVE")
+        if g and v.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+            out["mfma_busy_pct"] = 100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / (g / XCDS * SIMDS)
+        if g and ns:
+            out["clock_ghz"] = g / XCDS / ns
+        if v.get("SQ_LDS_IDX_ACTIVE"):
+            out["lds_bank_conflict_pct"] = 100.0 * (v.get("SQ_LDS_BANK_CONFLICT") or 0.0) / \
+                v["SQ_LDS_IDX_ACTIVE"]
+        if v.get("TCC_HIT_sum") is not None and v.get("TCC_MISS_sum") is not None:
+            tot = v["TCC_HIT_sum"] + v["TCC_MISS_sum"]
+            out["l2_hit_pct"] = 100.0 * v["TCC_HIT_sum"] / tot if tot else None
+        if v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16") is not None and ns:
+            out["mfma_bf16_tflops"] = v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / ns / 1e3
+        return out
+
     rec = {}
     for k, c in sorted(per.items()):
         vals = {n: (sum(c[n]) / len(c[n]) if n in c else None) for n in names}
-        rec[k] = vals
+        ns = sum(dur[k].values()) / len(dur[k]) if dur.get(k) else None
+        rec[k] = {"counters": vals, "avg_ns_under_counters": ns, "derived": derived(vals, ns)}
+    dnames = sorted({n for v in rec.values() for n in v["derived"]})
+    lines = ["# Hardware counters per dispatch (rocprofv3 --pmc)", "", "```", cmd, "```", "",
+             "Averages over the dispatches of each kernel.  GRBM_GUI_ACTIVE is summed over the "
+             f"{XCDS} accelerator dies; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / "
+             f"{XCDS} x {SIMDS} SIMDs); clock = GRBM_GUI_ACTIVE / {XCDS} / dispatch duration; the "
+             "MFMA TFLOP/s counts 512 FLOPs per SQ_INSTS_VALU_MFMA_MOPS_BF16 over the dispatch "
+             "duration under the counters (which can run slower than unprofiled).", ""]
+    if dnames:
+        lines += ["| kernel | " + " | ".join(dnames) + " |", "|---|" + "---|" * len(dnames)]
+        for k, v in rec.items():
+            lines.append(f"| `{k}` | " + " | ".join(
+                "" if v["derived"].get(n) is None else f"{v['derived'][n]:.3g}" for n in dnames) +
+                " |")
+        lines.append("")
+    lines += ["| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for k, v in rec.items():
+        vals = v["counters"]
         lines.append(f"| `{k}` | " + " | ".join("" if vals[n] is None else f"{vals[n]:.4g}"
                                                  for n in names) + " |")
     text = "\n".join(lines) + "\n"

@@ -10,23 +10,32 @@
 namespace sas {
 
 // Row-major tiles in LDS, 64 rows x D columns, no padding, with the 16-byte
-// chunks of each row permuted by an XOR swizzle so that both access
-// patterns the kernels use are free of bank conflicts:
-//   - 16-byte operand reads where 16 lanes read the same column chunk of 16
-//     different rows (rows differ in their low 4 bits), and
-//   - transposed reads (ds_read_b64_tr_b16) where a 16-lane group reads
-//     8 bytes x 4 lanes of two adjacent chunks in 4 consecutive rows.
-// With 16 chunks per row the chunk c of row r is stored at
-// c ^ ((r & 7) << 1 | (r >> 3) & 1): 16 consecutive rows see 16 distinct
-// values, and rows 4a..4a+3 see 4 distinct even/odd pairs, so the 8 chunks
-// of a transposed read never share a bank.
+// chunks of each row permuted by an XOR swizzle so that the access patterns
+// the kernels use are free of bank conflicts.  The LDS serves 256 bytes (64
+// banks of 4 bytes) per cycle, and a 16-chunk row (256 bytes) spans every
+// bank once, so a chunk's banks are set by its stored position alone:
+//   - 16-byte operand reads: 16 lanes per cycle read the same column chunk
+//     of 16 different rows (an aligned group of 16), so the 16 rows must
+//     store it at 16 different positions;
+//   - transposed reads (ds_read_b64_tr_b16): 32 lanes per cycle read 4
+//     consecutive rows (4a .. 4a + 3) x 4 aligned consecutive chunks (two
+//     16-lane groups of two chunks each), so those 16 chunks must land at 16
+//     different positions.
+// With 16 chunks per row the chunk c of row r is stored at c ^ f(r),
+// f(r) = ((r & 3) << 2) | ((r >> 2) & 3): a bijection on each aligned group
+// of 16 rows, and on rows 4a .. 4a + 3 it takes 4 values with distinct
+// upper two bits, so XOR with the chunk's own lower two bits gives 16
+// different positions.  (An earlier map, ((r & 7) << 1) | ((r >> 3) & 1),
+// left the transposed reads 2-way conflicted: measured half of their LDS
+// cycles.)  f(r + 16) = f(r), and XOR acts on the chunk bits only, so an
+// offset can be moved by 16 rows or XORed with a chunk offset directly.
 template <typename T, int D>
 struct Swz {
   static constexpr int VEC = 16 / sizeof(T);  // elements per chunk
   static constexpr int CPR = D / VEC;         // chunks per row
   __device__ static inline int f(int r) {
     if constexpr (CPR >= 16)
-      return ((r & 7) << 1) | ((r >> 3) & 1);
+      return ((r & 3) << 2) | ((r >> 2) & 3);
     else
       return (r >> 1) & (CPR - 1);
   }

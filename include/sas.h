@@ -40,7 +40,8 @@
  *     range are skipped by the kernels, NaN inputs give unspecified values.
  *   - Layouts are row-major and contiguous; tensors must be 16-byte aligned.
  *     block = 64 tokens; head_dim in {64, 128}; hq a multiple of hkv, and the
- *     query heads h of one KV head g are h = g*G .. g*G+G-1 (G = hq/hkv).
+ *     query heads h of one KV head g are h = g*G .. g*G+G-1 (G = hq/hkv);
+ *     hq * head_dim at most 2^20 (varlen entry points: SAS_ERR_UNSUPPORTED).
  *   - Varlen ("packed") tensors: tokens of all sequences back to back,
  *     cu_seqlens[s] = first token of sequence s.  Query block i of sequence s
  *     covers tokens [cu_seqlens[s] + 64 i, min(+64, cu_seqlens[s+1])).

@@ -64,6 +64,7 @@ def call_fwd(lib, p, q=FAKE):
 @pytest.mark.parametrize("kwargs,status", [
     (dict(d=96), -5), (dict(block=32), -5), (dict(hq=6, hkv=4), -2), (dict(Kb=0), -5),
     (dict(Kb=300), -5), (dict(dtype=7), -3), (dict(dtype=1, out=0), -5), (dict(bad_cuq=True), -2),
+    (dict(hq=16384, hkv=16384), -5),  # hq * head_dim above 2^20
 ])
 def test_fwd_rejects_bad_problems(lib, kwargs, status):
     assert call_fwd(lib, problem(**kwargs)) == status

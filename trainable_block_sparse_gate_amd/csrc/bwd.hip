@@ -130,7 +130,11 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
   constexpr int NKS = D / KS, NDT = D / 32, SPT = 32 / KS;
   constexpr int TILE = RT::ELEMS;
 
-  __shared__ __attribute__((aligned(16))) T tiles[2 * 2 * TILE];  // [buf][K | V]
+  // K and V of the kept tiles, double buffered as two arrays ([K | V] each)
+  // so that the compiler can tell a read of one from a request in flight
+  // into the other
+  __shared__ __attribute__((aligned(16))) T tiles0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) T tiles1[2 * TILE];
   __shared__ float s_F[NWV][kMaxBudget];  // per tile: the wave's share of dlg
   __shared__ int s_slot[kMaxBudget];     // tiles in processing order
   __shared__ int s_j[kMaxBudget];
@@ -205,20 +209,34 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
 
   barrier_keep_requests();  // the tile list is visible; the loads above may be in flight
   const int ntiles = s_n;
-  const long kstride = (long)p.hkv * D;
-  RT kst, vst;
-  auto load_tile = [&](int it) {
-    const int j = s_j[it];
+  // Tile u of the list goes straight from global memory into LDS
+  // (global_load_lds, 16 bytes per lane, one request per 1 KB of rows),
+  // each 16-byte chunk at its swizzled position; rows past the block's end
+  // repeat its last row.  Each wave issues its share; completion is counted
+  // by vmcnt.
+  auto issue_tile = [&](T *buf, int u) {
+    constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+    constexpr int RPI = kWave / CPR;              // rows per request
+    constexpr int NREQ = kBlock / RPI;            // requests per K (or V) tile
+    static_assert(NREQ % NWV == 0, "requests split evenly over the waves");
+    const int j = __builtin_amdgcn_readfirstlane(s_j[u]);
     const long tok = seq_start + (long)j * kBlock;
     const int nv = min(kBlock, seq_len - j * kBlock);
-    rowtile_load<T, T, D, NT>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);
-    rowtile_load<T, T, D, NT>(vst, vv + (tok * p.hkv + g) * D, kstride, nv);
+    const char *kb = reinterpret_cast<const char *>(kk + (tok * p.hkv + g) * D);
+    const char *vb = reinterpret_cast<const char *>(vv + (tok * p.hkv + g) * D);
+    const unsigned rstride = (unsigned)(p.hkv * D * (int)sizeof(T));
+#pragma unroll
+    for (int q = 0; q < NREQ / NWV; ++q) {
+      const int req = q * NWV + wave;
+      const int row = req * RPI + lane / CPR;
+      const int rr = row < nv ? row : nv - 1;
+      const unsigned off =
+          (unsigned)rr * rstride + (unsigned)(((lane % CPR) ^ Swz<T, D>::f(row)) * 16);
+      load_lds16(kb + off, buf + req * RPI * D);
+      load_lds16(vb + off, buf + TILE + req * RPI * D);
+    }
   };
-  auto store_tile = [&](int b) {
-    rowtile_store<T, D, NT>(kst, tiles + (2 * b + 0) * TILE);
-    rowtile_store<T, D, NT>(vst, tiles + (2 * b + 1) * TILE);
-  };
-  if (ntiles > 0) load_tile(0);
+  if (ntiles > 0) issue_tile(tiles0, 0);
 
 #pragma unroll
   for (int nt = 0; nt < QT; ++nt) {
@@ -243,29 +261,108 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
     Dv[nt] = dacc;
   }
 
-  if (ntiles > 0) {
-    store_tile(0);
-    if (ntiles > 1) load_tile(1);
-  }
+  // the first tile (and the Q / dO / O loads before it) has landed
+  wait_vmem<0>();
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int b = it & 1;
-    const float lg2 = s_lg[it];
-    const bool diag = (s_j[it] == i);
-    const T *Ks = tiles + (2 * b + 0) * TILE;
-    const T *Vs = tiles + (2 * b + 1) * TILE;
+  // The tile loop as a sequence of steps, two per 32-key half h of the
+  // kept tiles (h = 0 .. 2 ntiles - 1, tile h / 2, key half h % 2):
+  //   step 2h      MFMA:  dQ^T += K^T dS^T of half h - 1, then S^T and
+  //                       dP^T of half h;
+  //   step 2h + 1  VALU:  P^T and dS^T of half h (the exponentials, the
+  //                       row sums for d log g), kept as MFMA operands;
+  // and a last MFMA step 4 ntiles for the dQ of the last half.  Every step
+  // ends with a workgroup barrier.  The second half of the waves (`lag`)
+  // passes one extra barrier before its first step and the first half one
+  // after its last, so the lagging waves run each step one barrier interval
+  // later: the two waves that share a SIMD are always in different kinds of
+  // step, one keeping the matrix core busy while the other computes
+  // exponentials.
+  //
+  // LDS buffers: tile u lives in tiles0 / tiles1 for u even / odd.  Its
+  // last reader is step 4u + 4 (the dQ of its second half), which the
+  // lagging waves run in interval 4u + 5; tile u + 2 is first read by the
+  // leading waves' step 4u + 8.  So each wave requests its share of tile
+  // u + 2 in interval 4u + 6 (leading: step 4u + 6; lagging: step 4u + 5)
+  // and waits for it at the end of interval 4u + 7 (leading: step 4u + 7;
+  // lagging: step 4u + 6), before that interval's barrier.  Two tiles per
+  // loop iteration keep each step's buffers known at compile time, and no
+  // request is in flight across an iteration's end.
+  const int lag = wave >= NWV / 2 ? 1 : 0;
+  f32x16 sacc[QT], pacc[QT];      // S^T, dP^T of the half in flight
+  typename M::Op dsop[QT][SPT];    // dS^T of the previous half (B operands)
+  float Fp[QT], Gp[QT];            // lane partials over a tile: sum P dP, sum P
+#pragma unroll
+  for (int nt = 0; nt < QT; ++nt) Fp[nt] = Gp[nt] = 0.f;
 
-    float Fp[QT], Gp[QT];  // lane partials: sum of P dP, of P
+  // dQ^T[d][query] += K^T[d][key] dS^T[key][query] over key half mt of the
+  // tile in Kp.
+  // bf16: per-lane base offsets of the operand reads; each step makes them
+  // opaque, so that the slices' addresses (one XOR each) are formed where
+  // they are used instead of being held in registers across the loop.
+  unsigned ob_s = 0, ob_ta = 0, ob_tb = 0;
+  if constexpr (sizeof(T) == 2) {
+    ob_s = op_base_bytes<D>(chain_key_of_row<T>(l32), hf);
+    rows_base_bytes<D>(ob_ta, ob_tb);
+  }
+  auto dq_half = [&](const T *Kp, int mt) {
+    if constexpr (sizeof(T) == 2) {
+      // every operand read first (they complete in order; each MFMA waits
+      // for its own), then the products
+      __asm__ volatile("" : "+v"(ob_ta), "+v"(ob_tb));
+      bf16x8 ops[NDT][SPT];
 #pragma unroll
-    for (int nt = 0; nt < QT; ++nt) Fp[nt] = Gp[nt] = 0.f;
-    // one 32-key half at a time (not unrolled: keeps both halves' live
-    // ranges from overlapping)
-#pragma unroll 1
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x16 sacc[QT], pacc[QT];
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int nt = 0; nt < QT; ++nt) sacc[nt] = pacc[nt] = f32x16{};
+        for (int kc = 0; kc < SPT; ++kc)
+          ops[dt][kc] = tile_op_rows_x<D>(Kp, ob_ta, ob_tb, 32 * mt + kc * KS, dt);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int kc = 0; kc < SPT; ++kc)
+#pragma unroll
+          for (int nt = 0; nt < QT; ++nt)
+            dqacc[dt][nt] = M::run(ops[dt][kc], dsop[nt][kc], dqacc[dt][nt]);
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int kc = 0; kc < SPT; ++kc) {
+          const typename M::Op a = tile_op_rows<T, D>(Kp, 32 * mt + kc * KS, 32 * dt);
+#pragma unroll
+          for (int nt = 0; nt < QT; ++nt) dqacc[dt][nt] = M::run(a, dsop[nt][kc], dqacc[dt][nt]);
+        }
+      }
+    }
+  };
+  // S^T and dP^T of key half mt of the tile in Ks (K, then V).  bf16: the
+  // K and V operands run LA slices ahead of the products.
+  auto sdp_half = [&](const T *Ks, int mt) {
+    const T *Vs = Ks + TILE;
+    if constexpr (sizeof(T) == 2) {
+      constexpr int LA = 3;
+      __asm__ volatile("" : "+v"(ob_s));
+      bf16x8 ka[LA + 1], va[LA + 1];
+#pragma unroll
+      for (int ks = 0; ks < LA; ++ks) {
+        ka[ks] = tile_op_x<D>(Ks, ob_s, mt, ks);
+        va[ks] = tile_op_x<D>(Vs, ob_s, mt, ks);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + LA < NKS) {
+          ka[(ks + LA) % (LA + 1)] = tile_op_x<D>(Ks, ob_s, mt, ks + LA);
+          va[(ks + LA) % (LA + 1)] = tile_op_x<D>(Vs, ob_s, mt, ks + LA);
+        }
+#pragma unroll
+        for (int nt = 0; nt < QT; ++nt) {
+          sacc[nt] = M::run(ka[ks % (LA + 1)], qreg[nt][ks], ks == 0 ? f32x16{} : sacc[nt]);
+          pacc[nt] = M::run(va[ks % (LA + 1)], doreg[nt][ks], ks == 0 ? f32x16{} : pacc[nt]);
+        }
+      }
+    } else {
       const int krow = 32 * mt + chain_key_of_row<T>(l32);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -273,74 +370,104 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
         const typename M::Op bb = tile_op<T, D>(Vs, krow, hf * E + ks * KS);
 #pragma unroll
         for (int nt = 0; nt < QT; ++nt) {
-          sacc[nt] = M::run(a, qreg[nt][ks], sacc[nt]);
-          pacc[nt] = M::run(bb, doreg[nt][ks], pacc[nt]);
-        }
-      }
-      // dS^T = P^T (dP^T - D), P^T recomputed from the saved lse.  The sums
-      // of P dP and of P over the 16 values of a lane are pairwise trees
-      // (short dependency chains); the causal mask is only evaluated on the
-      // diagonal tile.
-#pragma unroll
-      for (int nt = 0; nt < QT; ++nt) {
-        const int ql = 32 * (nt0 + nt) + l32;
-        const float c = (OUTER ? 0.f : lg2) - lse2[nt];
-        const float gate = OUTER ? fast_exp2(lg2) : 1.f;
-        float pd[16], pp[16];
-        if (!diag) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) pp[r] = fast_exp2(fmaf(sacc[nt][r], p.scale_log2, c));
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(fmaf(sacc[nt][r], p.scale_log2, c));
-            pp[r] = 32 * mt + chain_slot<T>(r, hf) > ql ? 0.f : e;
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pd[r] = pp[r] * (OUTER ? gate * pacc[nt][r] : pacc[nt][r]);
-          sacc[nt][r] = fmaf(-pp[r], Dv[nt], pd[r]);
-        }
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-          for (int r = 0; r < w; ++r) {
-            pd[r] += pd[r + w];
-            pp[r] += pp[r + w];
-          }
-        Fp[nt] += pd[0];
-        Eacc[nt] += pd[0];
-        if constexpr (!OUTER) Gp[nt] += pp[0];  // outer: no D term in d log g
-      }
-      // dQ^T[d][query] += K^T[d][key] dS^T[key][query] over this 32-key half
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-        for (int kc = 0; kc < SPT; ++kc) {
-          const typename M::Op a = tile_op_rows<T, D>(Ks, 32 * mt + kc * KS, 32 * dt);
-#pragma unroll
-          for (int nt = 0; nt < QT; ++nt)
-            dqacc[dt][nt] = M::run(a, regs_op<T>(sacc[nt], kc * E), dqacc[dt][nt]);
+          sacc[nt] = M::run(a, qreg[nt][ks], ks == 0 ? f32x16{} : sacc[nt]);
+          pacc[nt] = M::run(bb, doreg[nt][ks], ks == 0 ? f32x16{} : pacc[nt]);
         }
       }
     }
-    // per query row (the two lane halves added); the sums over rows wait
-    // until after the loop, off the tile pipeline
+  };
+  // dS^T = P^T (dP^T - D) of key half mt of tile it, P^T recomputed from
+  // the saved lse, packed as the next MFMA step's operands as it is
+  // produced; the sums of P dP and of P over the 16 values of a lane run in
+  // two chains (even and odd registers), so no value outlives its own
+  // register.  The causal mask is only evaluated on the diagonal tile.
+  auto ds_half = [&](int it, int mt) {
+    const float lg2 = s_lg[it];
+    const bool diag = (s_j[it] == i);
 #pragma unroll
     for (int nt = 0; nt < QT; ++nt) {
-      const float fsum = Fp[nt] + __shfl_xor(Fp[nt], 32);
-      const float gsum = Gp[nt] + __shfl_xor(Gp[nt], 32);
-      if (hf == 0) {
-        s_Fq[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = fsum;
-        s_G[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = gsum;
+      const int ql = 32 * (nt0 + nt) + l32;
+      const float c = (OUTER ? 0.f : lg2) - lse2[nt];
+      const float gate = OUTER ? fast_exp2(lg2) : 1.f;
+      float f[2] = {0.f, 0.f}, gs[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < SPT; ++kc) {
+        float ds[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int r = kc * E + e;
+          float pr = fast_exp2(fmaf(sacc[nt][r], p.scale_log2, c));
+          if (diag && 32 * mt + chain_slot<T>(r, hf) > ql) pr = 0.f;
+          const float pd = pr * (OUTER ? gate * pacc[nt][r] : pacc[nt][r]);
+          ds[e] = fmaf(-pr, Dv[nt], pd);
+          f[r & 1] += pd;
+          gs[r & 1] += pr;
+        }
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 b;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b[e] = (__bf16)ds[e];
+          dsop[nt][kc] = b;
+        } else {
+          dsop[nt][kc] = ds[0];
+        }
+      }
+      const float fl = f[0] + f[1];
+      Fp[nt] += fl;
+      Eacc[nt] += fl;
+      if constexpr (!OUTER) Gp[nt] += gs[0] + gs[1];  // outer: no D term in d log g
+    }
+    if (mt == 1) {
+      // per query row (the two lane halves added); the sums over rows wait
+      // until after the loop
+#pragma unroll
+      for (int nt = 0; nt < QT; ++nt) {
+        const float fsum = Fp[nt] + __shfl_xor(Fp[nt], 32);
+        const float gsum = Gp[nt] + __shfl_xor(Gp[nt], 32);
+        if (hf == 0) {
+          s_Fq[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = fsum;
+          s_G[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = gsum;
+        }
+        Fp[nt] = Gp[nt] = 0.f;
       }
     }
-    if (it + 1 < ntiles) store_tile(b ^ 1);
-    if (it + 2 < ntiles) load_tile(it + 2);
-    __syncthreads();
+  };
+  // The four steps of tile u (in `cur`; tile u - 1 in `prev`, which then
+  // receives tile u + 1).
+  auto tile_steps = [&](T *cur, T *prev, int u) {
+    const bool next = u + 1 < ntiles;
+    // step 4u: dQ of tile u - 1's second half, S / dP of tile u's first
+    __builtin_amdgcn_s_setprio(1);
+    if (u > 0) dq_half(prev, 1);
+    sdp_half(cur, 0);
+    __builtin_amdgcn_s_setprio(0);
+    phase_barrier();
+    // step 4u + 1
+    ds_half(u, 0);
+    if (lag && next) issue_tile(prev, u + 1);
+    phase_barrier();
+    // step 4u + 2
+    __builtin_amdgcn_s_setprio(1);
+    dq_half(cur, 0);
+    sdp_half(cur, 1);
+    __builtin_amdgcn_s_setprio(0);
+    if (!lag && next) issue_tile(prev, u + 1);
+    if (lag) wait_vmem<0>();
+    phase_barrier();
+    // step 4u + 3
+    ds_half(u, 1);
+    if (!lag) wait_vmem<0>();
+    phase_barrier();
+  };
+  if (lag) phase_barrier();
+  for (int u = 0; u < ntiles; u += 2) {
+    tile_steps(tiles0, tiles1, u);
+    if (u + 1 < ntiles) tile_steps(tiles1, tiles0, u + 1);
   }
-
+  // step 4 ntiles: the dQ of the last half (nothing is in flight)
+  if (ntiles > 0) dq_half((ntiles & 1) ? tiles0 : tiles1, 1);
+  phase_barrier();
+  if (!lag) phase_barrier();
   // Exact D per query row, then dlg of each tile = sum P dP - sum_t D_t G_t.
   // Both row statistics are stored for all 64 rows of the block (rows past
   // its end: lse +inf, D 0) so the dk/dv phase can fetch them as a whole,
@@ -389,9 +516,11 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
   if (head_ok) {
     using SW = Swz<float, D / 2>;
     constexpr int ROWS = 32 * QT, HC = D / 8;  // rows, 16-byte chunks per half row
-    static_assert(NWV * ROWS * (D / 2) * 4 <= 2 * 2 * TILE * (int)sizeof(T),
-                  "all waves' half rows fit the tiles");
-    float *ob = reinterpret_cast<float *>(tiles) + wave * (ROWS * (D / 2));
+    constexpr int WPA = (NWV + 1) / 2;  // waves per tile array
+    static_assert(WPA * ROWS * (D / 2) * 4 <= 2 * TILE * (int)sizeof(T),
+                  "the waves' half rows fit the tile arrays");
+    float *ob = reinterpret_cast<float *>(wave < WPA ? tiles0 : tiles1) +
+                (wave % WPA) * (ROWS * (D / 2));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll

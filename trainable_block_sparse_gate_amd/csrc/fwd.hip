@@ -124,10 +124,10 @@ __global__ __launch_bounds__(NW * (2 / kFwdQT) * 64) void fwd_kernel(FwdParams p
   // overlaps the first tile's (storing that tile waits for both)
   barrier_keep_requests();
   const int ntiles = s_n;
-  const long kstride = (long)p.hkv * D;
+  const int kstride = p.hkv * D;
   RT kst, vst;
   auto load_tile = [&](int it) {
-    const int j = s_j[it];
+    const int j = __builtin_amdgcn_readfirstlane(s_j[it]);
     const long tok = seq_start + (long)j * kBlock;
     const int nv = min(kBlock, seq_len - j * kBlock);
     rowtile_load<T, T, D, NT>(kst, kk + (tok * p.hkv + g) * D, kstride, nv);

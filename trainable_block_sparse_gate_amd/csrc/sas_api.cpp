@@ -53,6 +53,9 @@ sas_status check_problem(const sas_problem *p, int *max_blocks) {
   REQUIRE(p->hq > 0 && p->hkv > 0, SAS_ERR_SHAPE, "head counts must be positive");
   REQUIRE(p->hq % p->hkv == 0, SAS_ERR_SHAPE, "hq (%d) is not a multiple of hkv (%d)", p->hq,
           p->hkv);
+  // tile loads address 64 rows from a uniform base with 32-bit byte offsets
+  REQUIRE((long)p->hq * p->head_dim <= (1L << 20), SAS_ERR_UNSUPPORTED,
+          "hq * head_dim must be at most 2^20 (got %ld)", (long)p->hq * p->head_dim);
   REQUIRE(p->budget_blocks >= 1 && p->budget_blocks <= sas::kMaxBudget, SAS_ERR_UNSUPPORTED,
           "budget_blocks must be in [1, %d] (got %d)", sas::kMaxBudget, p->budget_blocks);
   REQUIRE(p->dtype == SAS_BF16 || p->dtype == SAS_F32, SAS_ERR_DTYPE, "unknown dtype %d",

@@ -132,6 +132,18 @@ __device__ inline void barrier_keep_requests() {
   __asm__ volatile("" ::: "memory");
 }
 
+// Workgroup barrier between two steps of a software-pipelined loop: this
+// wave's LDS accesses are complete, and no instruction, arithmetic
+// included, is moved across it, so each step's work stays inside its step.
+__device__ inline void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // x as three bf16 parts [hi, mid, lo, 0, 0, 0, 0, 0] with hi + mid + lo = x
 // to within 2^-24 relative (each part is the rounding of what the previous
 // ones leave; the differences are exact in fp32).  Infinite x gives

@@ -74,18 +74,22 @@ struct RowTile {
 };
 
 // Rows >= nvalid are loaded from row nvalid - 1 (finite values; the kernels
-// mask those rows out of every product that could see them).
+// mask those rows out of every product that could see them).  base should
+// be wave-uniform: each lane then adds only a 32-bit byte offset to it
+// (64 rows of `stride` elements must span less than 2^31 bytes).
 template <typename TS, typename T, int D, int NT>
-__device__ inline void rowtile_load(RowTile<T, D, NT> &st, const TS *base, long stride,
+__device__ inline void rowtile_load(RowTile<T, D, NT> &st, const TS *base, int stride,
                                     int nvalid) {
   using F = RowTile<T, D, NT>;
+  const char *b = reinterpret_cast<const char *>(base);
 #pragma unroll
   for (int it = 0; it < F::CH; ++it) {
     const int c = threadIdx.x + it * NT;
     const int row = c / F::DC, dc = c % F::DC;
     if (F::TOT % NT == 0 || c < F::TOT) {
       const int r = row < nvalid ? row : nvalid - 1;
-      st.v[it] = load_chunk<TS, T>(base + r * stride + dc * F::VEC);
+      const unsigned off = (unsigned)((r * stride + dc * F::VEC) * (int)sizeof(TS));
+      st.v[it] = load_chunk<TS, T>(reinterpret_cast<const TS *>(b + off));
     }
   }
 }
@@ -204,6 +208,50 @@ __device__ inline bf16x8 tile_op_rows16(const __bf16 *X, int kb, int mb) {
   const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_v4i16 *)(const lds_short *)(X + Swz<__bf16, D>::off(row + 4, col)));
   const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+// bf16 tiles addressed from per-lane byte offsets.  Rows that differ by a
+// multiple of 16 share f, and XOR acts on the chunk bits of an offset only
+// (below the row bits, above the bytes within a chunk), so the offset of
+// (row + 16 m, chunk ^ x) is 16 m * D * 2 + (offset of (row, chunk)) ^ 16 x:
+// one base per lane serves every slice of a tile, the slice reached with a
+// single XOR and the row block folded into the instruction's immediate.
+//
+// Base of the k-contiguous operand reads (tile_op at row `row`, column
+// 8 hf): lane offset of (row, chunk hf).
+template <int D>
+__device__ inline unsigned op_base_bytes(int row, int hf) {
+  return (unsigned)(row * D * 2 + ((hf ^ Swz<__bf16, D>::f(row)) * 16));
+}
+// tile_op<bf16, D>(X, row + 32 m, 8 hf + 16 ks) given base = op_base_bytes.
+template <int D>
+__device__ inline bf16x8 tile_op_x(const __bf16 *X, unsigned base, int m, int ks) {
+  const char *p = reinterpret_cast<const char *>(X) + m * 32 * D * 2;
+  return *reinterpret_cast<const bf16x8 *>(p + (base ^ (unsigned)(32 * ks)));
+}
+// Bases of the transposed reads of tile_op_rows (rows kb .. kb + 15 with
+// kb a multiple of 16, columns from 0): the lane's first and second
+// (4 rows further) read.
+template <int D>
+__device__ inline void rows_base_bytes(unsigned &a, unsigned &b) {
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, s = lane % 16;
+  const int row = 8 * (g / 2) + s / 4;
+  const int col = 16 * (g % 2) + 4 * (s % 4);
+  a = (unsigned)(Swz<__bf16, D>::off(row, col) * 2);
+  b = (unsigned)(Swz<__bf16, D>::off(row + 4, col) * 2);
+}
+// tile_op_rows<bf16, D>(X, kb, 32 dt) given the bases (kb a multiple of 16).
+template <int D>
+__device__ inline bf16x8 tile_op_rows_x(const __bf16 *X, unsigned a, unsigned b, int kb, int dt) {
+  const char *p = reinterpret_cast<const char *>(X) + kb * D * 2;
+  const unsigned x = (unsigned)(64 * dt);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16 *)(const lds_short *)(p + (a ^ x)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16 *)(const lds_short *)(p + (b ^ x)));
+  const v8i16 ab = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, ab);
 }
 

@@ -269,6 +269,16 @@ def summarize_counters(d, cmd, out):
             out["l2_hit_pct"] = 100.0 * v["TCC_HIT_sum"] / tot if tot else None
         if v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16") is not None and ns:
             out["mfma_bf16_tflops"] = v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / ns / 1e3
+        if v.get("SQ_VALU_MFMA_COEXEC_CYCLES") is not None and v.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            out["valu_coexec_pct_of_mfma_busy"] = \
+                100.0 * v["SQ_VALU_MFMA_COEXEC_CYCLES"] / v["SQ_VALU_MFMA_BUSY_CYCLES"]
+        wc = v.get("SQ_WAVE_CYCLES")
+        if wc:
+            for n, key in (("SQ_ACTIVE_INST_VALU", "valu_active_pct_of_wave_cycles"),
+                           ("SQ_ACTIVE_INST_LDS", "lds_active_pct_of_wave_cycles"),
+                           ("SQ_WAIT_ANY", "wait_any_pct_of_wave_cycles")):
+                if v.get(n) is not None:
+                    out[key] = 100.0 * v[n] / wc
         return out
 
     rec = {}
@@ -571,6 +581,22 @@ def measured_peaks(torch, metrics):
     ms = timed(lambda: L.sas_peak_mfma_bf16(cus * 8, iters, ctypes.c_void_p(sink.data_ptr()), st))
     flops = cus * 8 * 4 * iters * chains * 32 * 32 * 16 * 2
     mfma_tf = flops / (ms * 1e-3) / 1e12
+    # on random operands, sustained: ten launches back to back as one interval
+    L.sas_peak_mfma_bf16_data.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p]
+    g = torch.Generator().manual_seed(7)
+    ops = torch.randn(1 << 16, generator=g).to(torch.bfloat16).cuda()
+    data_iters = 2048
+
+    def data_run():
+        for _ in range(10):
+            rc = L.sas_peak_mfma_bf16_data(cus * 8, data_iters, ctypes.c_void_p(ops.data_ptr()),
+                                           ops.numel() * 2, ctypes.c_void_p(sink.data_ptr()), st)
+            if rc != 0:
+                raise RuntimeError(f"sas_peak_mfma_bf16_data failed ({rc})")
+    ms_d = timed(data_run, reps=3)
+    data_tf = 10 * cus * 8 * 4 * data_iters * chains * 32 * 32 * 16 * 2 / (ms_d * 1e-3) / 1e12
+    del ops
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     rsink = torch.empty(cus * 32 * 256, dtype=torch.int32, device="cuda")
@@ -590,18 +616,24 @@ def measured_peaks(torch, metrics):
     mall_gbs = small / (mall * 1e-3) / 1e9
     del buf, rsink, sink
     torch.cuda.empty_cache()
-    log(f"[bench] measured peaks: bf16 MFMA {mfma_tf:.0f} TFLOP/s, streaming read "
+    log(f"[bench] measured peaks: bf16 MFMA {mfma_tf:.0f} TFLOP/s ({data_tf:.0f} on random "
+        f"operands, sustained), streaming read "
         f"{read_gbs:.0f} GB/s ({best}; {reads}), 64 MiB re-read {mall_gbs:.0f} GB/s "
         f"({cus} compute units)")
     return {"bf16_mfma_tflops": round(mfma_tf, 1),
             "bf16_mfma_frac_of_spec": round(mfma_tf / metrics.PEAK_BF16_TFLOPS, 4),
+            "bf16_mfma_random_operands_tflops": round(data_tf, 1),
+            "bf16_mfma_random_operands_frac_of_spec": round(data_tf / metrics.PEAK_BF16_TFLOPS, 4),
             "stream_read_gbs": round(read_gbs, 1),
             "stream_read_frac_of_spec": round(read_gbs / metrics.PEAK_HBM_GBS, 4),
             "stream_read_variants_gbs": reads,
             "cache_resident_read_gbs": round(mall_gbs, 1),
             "compute_units": cus,
             "how": (f"MFMA: {cus * 8} workgroups x 4 waves, each {iters} x {chains} "
-                    "independent 32x32x16 bf16 MFMAs on registers; read: 4 GiB, 16-byte loads, "
+                    "independent 32x32x16 bf16 MFMAs on registers (near-constant operands), best "
+                    f"of 5; random operands: the same grid, {data_iters} x {chains} MFMAs per wave "
+                    "on N(0,1) bf16 operands that change every instruction, ten launches timed "
+                    "as one interval, best of 3; read: 4 GiB, 16-byte loads, "
                     "grid-stride (mode0) or one contiguous chunk per workgroup with 8 / 16 "
                     "nontemporal loads in flight (mode1 / mode2), best of 5 launches each; "
                     "cache-resident: a 64 MiB buffer re-read (Infinity Cache), best of 10")}

@@ -123,9 +123,15 @@ __global__ __launch_bounds__(128) void append_kernel(DecodeParams p, const __bf1
 // exponent and mantissa fields placed at the top of an fp32 pattern are the
 // fp32 number 2^-120 times the value (a normal fp32 for e > 0, a subnormal
 // m 2^-129 for e = 0), so one exact multiplication by 2^120 decodes both.
+// The NaN codes are substituted by integer arithmetic, with no comparison
+// (a comparison per value leaves a lane mask per value in scalar registers
+// when many are decoded at once): nan = 1 exactly when the low seven bits
+// are all ones.
 __device__ inline float e4m3_value(uint32_t b) {
-  const float v = __uint_as_float(((b & 0x80u) << 24) | ((b & 0x7fu) << 20)) * 0x1p120f;
-  return (b & 0x7fu) == 0x7fu ? __uint_as_float(0x7fc00000u) : v;
+  const uint32_t v = __float_as_uint(
+      __uint_as_float(((b & 0x80u) << 24) | ((b & 0x7fu) << 20)) * 0x1p120f);
+  const uint32_t nan = ((b & 0x7fu) + 1u) >> 7;
+  return __uint_as_float(v ^ ((v ^ 0x7fc00000u) & (0u - nan)));
 }
 
 // V consecutive summaries from an address aligned to their size, as one
@@ -170,9 +176,19 @@ template <int D, int G, int V, typename TS, bool VEC>
 __global__ __launch_bounds__(256) void select_partial_kernel(DecodeParams p, SelectParams sp) {
 #pragma clang fp contract(off)
   constexpr int NT = 256, NWV = NT / kWave;
-  // summaries requested per batch: at most 512 bytes per thread
-  constexpr int CB = 512 / (V * (int)sizeof(TS)) < D ? 512 / (V * (int)sizeof(TS)) : D;
-  static_assert(D % CB == 0, "channel batches");
+  // Summaries of V blocks for one channel: BYTES per thread, one load.
+  // With V-wide loads the channels go in batches of 32 words per thread,
+  // two batches in flight (the first requested before the query mean is
+  // formed), each channel held in 32-bit words (a narrower one zero
+  // extended into a word) and decoded from them.  Without (a stride that
+  // is not a multiple of V) each element is loaded on its own.
+  constexpr int BYTES = V * (int)sizeof(TS);
+  constexpr bool WORDS = VEC;
+  constexpr int WPC = BYTES >= 4 ? BYTES / 4 : 1;  // 32-bit words per channel
+  constexpr int U = 32 / WPC < D / 2 ? 32 / WPC : D / 2;  // channels per batch (>= 2 batches)
+  constexpr int NB = D / U;
+  static_assert(D % U == 0, "channel batches");
+  typedef uint32_t chan_words __attribute__((ext_vector_type(WPC > 1 ? WPC : 2)));
   __shared__ float qbar[D];
   __shared__ float red[NWV];
   __shared__ int cnt[NWV];
@@ -180,6 +196,61 @@ __global__ __launch_bounds__(256) void select_partial_kernel(DecodeParams p, Sel
   const int c = blockIdx.x, row = blockIdx.y;
   const int b = row / p.hkv, g = row % p.hkv;
   const int tid = threadIdx.x;
+  const int nhist = (p.seqlens[b] - 1) / kBlock;
+  const int kh = p.Kb - 1;
+  const int j0 = 256 * V * c + V * tid;  // this thread's first block
+  const int lo = 256 * V * c, n = max(0, min(nhist - lo, 256 * V));  // valid blocks in the chunk
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (j0 + v < nhist) valid |= 1u << v;
+  const TS *ks = static_cast<const TS *>(p.ksum) + ((long)row * D) * p.nblk_stride + j0;
+
+  // channel e's words (V-wide loads are aligned and inside the row: j0 and
+  // the stride are multiples of V, and j0 < nhist <= stride), addressed as
+  // the row's uniform base plus a 32-bit byte offset per lane (a row of
+  // summaries spans D * stride elements, far below 4 GB)
+  const char *rbase = reinterpret_cast<const char *>(static_cast<const TS *>(p.ksum) +
+                                                     (long)row * D * p.nblk_stride);
+  const unsigned lane_off = (unsigned)j0 * (unsigned)sizeof(TS);
+  const unsigned cstride = (unsigned)p.nblk_stride * (unsigned)sizeof(TS);
+  auto load_chan = [&](int e) -> chan_words {
+    const char *src = rbase + (lane_off + (unsigned)e * cstride);
+    if constexpr (BYTES == 1) {
+      chan_words x{};
+      x[0] = __builtin_nontemporal_load(reinterpret_cast<const uint8_t *>(src));
+      return x;
+    } else if constexpr (BYTES == 2) {
+      chan_words x{};
+      x[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(src));
+      return x;
+    } else if constexpr (WPC == 1) {
+      chan_words x{};
+      x[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(src));
+      return x;
+    } else {
+      return __builtin_nontemporal_load(reinterpret_cast<const chan_words *>(src));
+    }
+  };
+  // element v of a channel's words
+  auto elem = [&](const chan_words &x, int v) -> float {
+    if constexpr (sizeof(TS) == 4) {
+      return __uint_as_float(x[v]);
+    } else if constexpr (sizeof(TS) == 2) {
+      const uint32_t w = x[v / 2];
+      return __uint_as_float((v % 2) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+      return e4m3_value((x[v / 4] >> (8 * (v % 4))) & 0xffu);
+    }
+  };
+  chan_words wb[2][U];
+  if constexpr (WORDS) {
+    if (valid) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) wb[0][u] = load_chan(u);
+    }
+  }
+
   const __bf16 *q = static_cast<const __bf16 *>(p.q);
   if (tid < D) {
     float qv[G];  // every head's value requested before the ordered sum
@@ -191,44 +262,61 @@ __global__ __launch_bounds__(256) void select_partial_kernel(DecodeParams p, Sel
     qbar[tid] = acc / (float)G;
   }
   __syncthreads();
-  const int nhist = (p.seqlens[b] - 1) / kBlock;
-  const int kh = p.Kb - 1;
-  const int j0 = 256 * V * c + V * tid;  // this thread's first block
-  const int lo = 256 * V * c, n = max(0, min(nhist - lo, 256 * V));  // valid blocks in the chunk
 
-  // scores of this thread's blocks (invalid ones: -inf, never kept)
+  // scores of this thread's blocks (invalid ones: -inf, never kept); each
+  // an fmaf chain over the channels in order
   float sv[V];
-  uint32_t valid = 0u;
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    sv[v] = -INFINITY;
-    if (j0 + v < nhist) valid |= 1u << v;
-  }
+  for (int v = 0; v < V; ++v) sv[v] = -INFINITY;
   if (valid) {
-    // the summaries of CB channels (512 bytes per thread) are requested
-    // before the first of them is used
-    const TS *ks = static_cast<const TS *>(p.ksum) + ((long)row * D) * p.nblk_stride + j0;
     float a[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) a[v] = 0.f;
-#pragma unroll 1
-    for (int e0 = 0; e0 < D; e0 += CB) {
-      TS w[CB][V];
+    if constexpr (WORDS) {
+      static_assert(NB % 2 == 0, "batches go in pairs");
+      auto load_batch = [&](chan_words (&dst)[U], int bi) {
 #pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const TS *src = ks + (long)(e0 + u) * p.nblk_stride;
-        if constexpr (VEC) {
-          load_summaries<TS, V>(src, w[u]);
-        } else {
+        for (int u = 0; u < U; ++u) dst[u] = load_chan(bi * U + u);
+      };
+      auto use_batch = [&](const chan_words (&src)[U], int bi) {
 #pragma unroll
-          for (int v = 0; v < V; ++v) w[u][v] = ((valid >> v) & 1u) ? src[v] : TS{};
+        for (int u = 0; u < U; ++u) {
+          const float qe = qbar[bi * U + u];
+#pragma unroll
+          for (int v = 0; v < V; ++v) a[v] = fmaf(qe, elem(src[u], v), a[v]);
         }
+      };
+      // batch bi + 1 is requested before batch bi is used; a loop over
+      // pairs keeps that to two batches in registers
+#pragma unroll 1
+      for (int bi = 0; bi < NB; bi += 2) {
+        load_batch(wb[1], bi + 1);
+        use_batch(wb[0], bi);
+        if (bi + 2 < NB) load_batch(wb[0], bi + 2);
+        use_batch(wb[1], bi + 1);
       }
+    } else {
+      constexpr int CB = 512 / BYTES < D ? 512 / BYTES : D;
+      static_assert(D % CB == 0, "channel batches");
+#pragma unroll 1
+      for (int e0 = 0; e0 < D; e0 += CB) {
+        TS w[CB][V];
 #pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const float qe = qbar[e0 + u];
+        for (int u = 0; u < CB; ++u) {
+          const TS *src = ks + (long)(e0 + u) * p.nblk_stride;
+          if constexpr (VEC) {
+            load_summaries<TS, V>(src, w[u]);
+          } else {
 #pragma unroll
-        for (int v = 0; v < V; ++v) a[v] = fmaf(qe, summary_value<TS>(w[u][v]), a[v]);
+            for (int v = 0; v < V; ++v) w[u][v] = ((valid >> v) & 1u) ? src[v] : TS{};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+          const float qe = qbar[e0 + u];
+#pragma unroll
+          for (int v = 0; v < V; ++v) a[v] = fmaf(qe, summary_value<TS>(w[u][v]), a[v]);
+        }
       }
     }
     float *out = p.scores + (long)row * p.nblk_stride + j0;

@@ -6,6 +6,9 @@
 //                        32x32x16 bf16 MFMAs on register operands, with
 //                        eight independent accumulators so the matrix core
 //                        never waits on a result;
+//   sas_peak_mfma_bf16_data  the same on operands taken from a buffer of
+//                        random values that change from one instruction to
+//                        the next (the rate under real data's power draw);
 //   sas_peak_read        a streaming read of a device buffer (16-byte loads,
 //                        grid-stride or one contiguous chunk per workgroup,
 //                        4 to 16 loads in flight per thread), folded into
@@ -36,6 +39,38 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float *sink) 
 #pragma unroll
     for (int c = 0; c < kChains; ++c)
       acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  if (s == 12345.f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;  // never true; keeps the work
+}
+
+// The same MFMA loop on data: eight A and eight B operands per lane from a
+// buffer of (random) bf16 values, B rotating over the chains each
+// iteration, so consecutive instructions see different operands.  The
+// matrix cores then draw the power real data makes them draw, and the chip
+// may lower its clock for it; the loop above on near-constant operands
+// does not show that.
+__global__ __launch_bounds__(256) void mfma_data_kernel(const u32x4 *src, int n16, int iters,
+                                                        float *sink) {
+  bf16x8 a[kChains], b[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) {
+    a[c] = __builtin_bit_cast(bf16x8, src[(c * 256 + threadIdx.x) % n16]);
+    b[c] = __builtin_bit_cast(bf16x8, src[(c * 256 + threadIdx.x + n16 / 2) % n16]);
+  }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
+  for (int it = 0; it < iters; it += kChains) {
+#pragma unroll
+    for (int j = 0; j < kChains; ++j)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[(c + j) % kChains], acc[c], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
@@ -98,6 +133,16 @@ int sas_peak_mfma_bf16(int grid_wgs, int iters, float *sink, void *stream) {
 }
 
 int sas_peak_mfma_chains(void) { return kChains; }
+
+// flops as above; iters a multiple of the chain count; src holds n_bytes
+// (a multiple of 16, at least 32) of bf16 operands.
+int sas_peak_mfma_bf16_data(int grid_wgs, int iters, const void *src, long n_bytes, float *sink,
+                            void *stream) {
+  if (iters % kChains != 0 || n_bytes < 32 || n_bytes % 16 != 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_data_kernel, dim3(grid_wgs), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const u32x4 *>(src), (int)(n_bytes / 16), iters, sink);
+  return (int)hipGetLastError();
+}
 
 // Reads n_bytes (a multiple of 16) from src; sink holds grid_wgs * 256 words.
 // mode 0: grid-stride, four loads in flight per thread; mode 1 / 2: one

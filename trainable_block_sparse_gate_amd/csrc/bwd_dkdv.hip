@@ -371,8 +371,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     // dV^T[d][key] += dO^T[d][query] P[query][key];  dK^T += Q^T dS
     if constexpr (kSplitD) {
       // this wave's d tiles over all four 16-row chunks: the transposed dO
-      // and Q operands (chunk c at 32 D c bytes), requested before the
-      // probabilities are formed so that their latency overlaps that work
+      // and Q operands (chunk c at 32 D c bytes), requested once the
+      // probabilities are formed (requesting the first half before them
+      // holds 32 more registers across the exponentials: it spilled and
+      // measured 20 % slower)
       constexpr int NC = 2 * SPT;
       auto trans_op = [&](const T *X, int c, int dt) -> bf16x8 {
         const char *tb = reinterpret_cast<const char *>(X) + c * 32 * D;

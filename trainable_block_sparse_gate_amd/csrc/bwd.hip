@@ -107,12 +107,15 @@ __global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p)
 
 // ------------------------------------------------------------------ dq
 // The forward's geometry: WPH waves per query head of one kv head, QT 32-row
-// query tiles per wave, Q and dO held in registers as B operands.  K and V tiles of the kept
-// blocks are double buffered in LDS (row-major); dQ^T = K^T dS^T reads K
-// transposed with ds_read_b64_tr_b16.  Per tile: compute from one buffer,
-// then store the next tile into the other, issue the loads of the one after,
-// and barrier (no LDS write of a wave in flight while its transposed reads
-// issue).
+// query tiles per wave, Q and dO held in registers as B operands.  K and V
+// tiles of the kept blocks go straight from global memory into two LDS
+// arrays (row-major, swizzled); dQ^T = K^T dS^T reads K transposed with
+// ds_read_b64_tr_b16.  The tile loop alternates MFMA and VALU steps with a
+// workgroup barrier after each (see the loop).  Transposed reads issued
+// while LDS writes of the same wave are in flight have returned wrong data
+// on gfx950: this wave's only LDS writes in the loop (the row sums of a
+// VALU step) complete at that step's barrier, before the next MFMA step
+// issues any transposed read.
 constexpr int kDqQT = 1;  // 32-query tiles per wave (1: two waves per head)
 
 // OUTER: the gate-position ablation.  P comes from the ungated logits,

@@ -112,10 +112,12 @@ __global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p)
 // arrays (row-major, swizzled); dQ^T = K^T dS^T reads K transposed with
 // ds_read_b64_tr_b16.  The tile loop alternates MFMA and VALU steps with a
 // workgroup barrier after each (see the loop).  Transposed reads issued
-// while LDS writes of the same wave are in flight have returned wrong data
-// on gfx950: this wave's only LDS writes in the loop (the row sums of a
-// VALU step) complete at that step's barrier, before the next MFMA step
-// issues any transposed read.
+// while LDS stores of the same wave are in flight have returned wrong data
+// on gfx950: this wave's LDS stores in the loop (the row sums of a VALU
+// step) complete at that step's barrier, before the next MFMA step issues
+// any transposed read.  The global-to-LDS requests into the other tile
+// array may be in flight during an MFMA step, as in the dK/dV kernel; the
+// full-size parity tests cover that overlap.
 constexpr int kDqQT = 1;  // 32-query tiles per wave (1: two waves per head)
 
 // OUTER: the gate-position ablation.  P comes from the ungated logits,

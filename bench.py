@@ -462,8 +462,7 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
         prob = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, False,
                           spec.max_len, summary_dtype=args.summary_dtype)
     ksum = sas.pool_keys(prob, t["k"])  # cache maintenance, not timed
-    sws = torch.empty(max(1, sas.decode_select_workspace_bytes(prob)), dtype=torch.uint8,
-                      device="cuda")
+    sws = sas.decode_select_workspace(prob)
     sel, lg, glse, scores = sas.decode_select(prob, t["q"], ksum, workspace=sws)
     ws = torch.empty(max(1, sas.decode_workspace_bytes(prob)), dtype=torch.uint8, device="cuda")
     o, lse = sas.decode(prob, t["q"], t["k"], t["v"], sel, lg, workspace=ws)
@@ -506,8 +505,7 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
                         spec.max_len, page_table=t["page_table"],
                         num_pages=t["k"].shape[0] if spec.paged else 0, summary_dtype=sd)
         ks2 = sas.pool_keys(p2, t["k"])
-        ws2 = torch.empty(max(1, sas.decode_select_workspace_bytes(p2)), dtype=torch.uint8,
-                          device="cuda")
+        ws2 = sas.decode_select_workspace(p2)
         out2 = sas.decode_select(p2, t["q"], ks2, workspace=ws2)
         tt = 0.0
         for it in range(n + 3):

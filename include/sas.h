@@ -148,9 +148,8 @@ typedef struct sas_decode_problem {
   int32_t max_seqlen;      /* contiguous: cache capacity per (batch, kv head) */
   int32_t max_pages;       /* paged: row stride of page_table */
   int32_t num_pages;       /* paged: physical pages in the cache */
-  int32_t nblk_stride;     /* summaries: row stride (>= largest history count);
-                              a multiple of 4 lets the pooled scores read the
-                              summaries 16 bytes at a time */
+  int32_t nblk_stride;     /* summaries and scores: blocks per row, a multiple
+                              of 64 (>= largest history count) */
   float scale;
   const int32_t *seqlens;       /* device [batch]: cache length L, query token included */
   const int32_t *seqlens_host;  /* host copy */
@@ -255,8 +254,11 @@ sas_status sas_gate_bwd(const sas_problem *p, const float *logits, int64_t ld,
  * sas_pool_keys -- cached block summaries for decode (review 3-7 step 1):
  * the mean key of each full history block j < (L_b - 1) / 64, summed in
  * token order in fp32 and divided by 64.
- *   k_cache in p->layout; ksum out [batch][hkv][head_dim][nblk_stride] in
- *   p->summary_dtype (fp32, or bf16 = the fp32 mean rounded to nearest even).
+ *   k_cache in p->layout; ksum out in p->summary_dtype (fp32, or the fp32 mean rounded to
+ *   the nearest bf16 / e4m3 value, ties to even), in tiles of 64 blocks:
+ *   element [b][g][j / 64][e / EPP][j % 64][e % EPP] is channel e of block j,
+ *   EPP = 16 / element size (4, 8 or 16 channels per 16 bytes), so the
+ *   16-byte pieces of 64 consecutive blocks lie side by side.
  */
 sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, void *ksum,
                          void *stream);
@@ -273,7 +275,7 @@ sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, void 
  *   k_new, v_new  [batch][hkv][head_dim] bf16 (the new token's key, value);
  *   k_cache, v_cache in p->layout (updated in place; paged: the page of
  *                 position L_b - 1 must be in the page table); ksum
- *                 [batch][hkv][head_dim][nblk_stride] in p->summary_dtype,
+ *                 (the tiled layout of sas_pool_keys) in p->summary_dtype,
  *                 updated in place.
  * The caller owns every buffer; NULL -> SAS_ERR_NULL, bad shapes as for
  * sas_pool_keys.  Steps are ordered on the stream; the summary read uses
@@ -289,14 +291,15 @@ sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, con
  *   qbar_e = (q_{gG} + ... + q_{gG+G-1})_e / G   (fp32, heads in order)
  *   s_j    = (fmaf chain over e of qbar_e * ksum_je) / sqrtf(head_dim)
  * then the gate + Top-K of sas_gate_topk with i = (L_b - 1) / 64 and
- * SAS_GATE_HIST.  q [batch][hq][d] bf16; ksum in p->summary_dtype, 16-byte
- * aligned.
+ * SAS_GATE_HIST.  q [batch][hq][d] bf16; ksum in the tiled layout of
+ * sas_pool_keys, p->summary_dtype, 16-byte aligned.
  *   sel_idx / sel_loggate out [batch*hkv][Kb]; gate_lse out [batch*hkv];
  *   scores out [batch][hkv][nblk_stride] fp32 (the pooled scores).
  * Each row's history is split into chunks taken by separate workgroups
  * (scores and an exact Top-K per chunk), merged per row by a second kernel;
  * the result is the whole row's Top-K.
- *   workspace: at least sas_decode_select_workspace_size(p) bytes.
+ *   workspace: at least sas_decode_select_workspace_size(p) bytes (any
+ *   contents; calls that share a workspace must not overlap in time).
  * A row's history is split into chunks of 256 to 2048 blocks; more than
  * 4096 candidates in the merge (chunks x (Kb - 1)) returns
  * SAS_ERR_UNSUPPORTED (at Kb = 32: histories beyond 270,336 blocks, 17M
@@ -353,7 +356,7 @@ const char *sas_last_error(void);
 /* ABI version of this header: bumped on any incompatible change. */
 int32_t sas_abi_version(void);
 
-#define SAS_ABI_VERSION 4
+#define SAS_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

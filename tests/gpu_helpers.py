@@ -52,10 +52,12 @@ def assert_close(name, got, want, tol):
 
 
 def summaries_f32(ksum):
-    """Block summaries as the fp32 values they stand for (fp8 summaries are
-    stored as e4m3 codes in uint8; torch's float8_e4m3fn decodes them
-    exactly)."""
+    """Block summaries as the fp32 values they stand for, indexed [batch][kv
+    head][block][channel] (fp8 summaries are stored as e4m3 codes in uint8;
+    torch's float8_e4m3fn decodes them exactly)."""
     import torch
+    from trainable_block_sparse_gate_amd import sas
+    ksum = sas.summaries_by_block(ksum)  # [batch][hkv][block][channel]
     if ksum.dtype == torch.uint8:
         return ksum.view(torch.float8_e4m3fn).float().cpu().numpy()
     return ksum.float().cpu().numpy()

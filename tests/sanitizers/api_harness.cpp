@@ -162,7 +162,7 @@ int main() {
   d.max_seqlen = 700;
   d.max_pages = max_pages;
   d.num_pages = 14;
-  d.nblk_stride = 12;
+  d.nblk_stride = 64;
   d.scale = 1.f / std::sqrt(128.f);
   d.seqlens = DI;
   d.seqlens_host = sl;
@@ -201,6 +201,9 @@ int main() {
   e = d;
   e.nblk_stride = 3;
   expect("stride", sas_decode_select(&e, D, D, DF, DI, DF, DF, D, sws, nullptr), SAS_ERR_SHAPE);
+  e.nblk_stride = 70;  // not whole 64-block summary tiles
+  expect("stride tiles", sas_decode_select(&e, D, D, DF, DI, DF, DF, D, sws, nullptr),
+         SAS_ERR_SHAPE);
   e = d;
   e.summary_dtype = SAS_SUMMARY_FP8;
   expect("fp8 select", sas_decode_select(&e, D, D, DF, DI, DF, DF, D,
@@ -226,7 +229,7 @@ int main() {
   e.hq = 32;
   e.hkv = 8;
   e.budget_blocks = 64;
-  e.nblk_stride = 100;
+  e.nblk_stride = 128;
   e.num_splits = 64;
   expect("noalloc too big", sas_decode_noalloc(&e, D, D, D, DI, DF, D, DF, nullptr),
          SAS_ERR_WORKSPACE);

@@ -39,7 +39,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sas_abi_version() == sas.ABI_VERSION == 4
+    assert lib.sas_abi_version() == sas.ABI_VERSION == 5
     assert lib.sas_status_string(0) == b"ok"
     assert b"unsupported" in lib.sas_status_string(-5)
 
@@ -105,7 +105,7 @@ def decode_problem(seqlens=(700, 129), hq=8, hkv=2, d=128, Kb=4, paged=True, max
                    num_pages=32):
     sl = np.array(seqlens, np.int32)
     mp = max_pages if max_pages is not None else (max(seqlens) + 63) // 64
-    nb = nblk if nblk is not None else max(1, (max(seqlens) - 1) // 64)
+    nb = nblk if nblk is not None else -(-max(1, (max(seqlens) - 1) // 64) // 64) * 64
     pth = None if page_table_host is None else np.ascontiguousarray(page_table_host, np.int32)
     p = sas.DecodeProblem(len(seqlens), hq, hkv, d, 64, Kb, 0, 0, 1 if paged else 0,
                           max_seqlen if max_seqlen is not None else max(seqlens), mp, num_pages,
@@ -122,8 +122,9 @@ def test_decode_checks(lib):
     bad = [decode_problem(hq=6, hkv=2),          # group of 3 heads
            decode_problem(max_pages=5),          # page table too short for 700 tokens
            decode_problem(nblk=3),               # summary stride too short
+           decode_problem(nblk=70),              # not whole 64-block summary tiles
            decode_problem(paged=False, max_seqlen=600)]
-    want = [-5, -2, -2, -2]
+    want = [-5, -2, -2, -2, -2]
     for p, w in zip(bad, want):
         assert lib.sas_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, *ws,
                               None) == w

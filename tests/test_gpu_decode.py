@@ -22,6 +22,10 @@ CASES = {
     "g2_d64": ([1000, 333], 4, 2, 64, 6),
     "g8_d128_bigK": ([64 * 40 + 5], 16, 2, 128, 64),
     "g1_d128": ([500, 129], 2, 2, 128, 3),
+    # several chunks of 256 blocks per row: 6 x 63 candidates in the merge
+    "chunks_g4_d128": ([64 * 1500 + 10, 64 * 700 + 1, 90], 8, 2, 128, 64),
+    # 17 chunks x 63 = 1071 candidates: the merge's widest form
+    "wide_merge_g2_d64": ([64 * 4300 + 7, 64 * 300 + 3], 2, 1, 64, 64),
 }
 
 
@@ -56,7 +60,7 @@ def run_decode(name, paged, out_dtype="bf16", gated=True, seed=7, summary="f32")
             V = wl.gather_row_cache(host["v"], host["page_table"], b, g, L)
             qg = host["q"][b, g * G:(g + 1) * G]
             kbar = oracle.pool_keys_row(K, summary=summary)
-            assert np.array_equal(ksum_h[b, g, :, :cur].T, kbar), (b, g, "summaries")
+            assert np.array_equal(ksum_h[b, g, :cur, :], kbar), (b, g, "summaries")
             ridx, rlg, rlse, rs = oracle.decode_select_row(qg, K, Kb, summary=summary)
             assert np.array_equal(scores_h[b, g, :cur], rs), (b, g, "scores")
             assert np.array_equal(sel_h[r], ridx), (b, g, sel_h[r], ridx)
@@ -126,13 +130,13 @@ def test_fp8_summary_codes_for_every_rounding_case():
     kct = torch.from_numpy(kc).to(torch.bfloat16).cuda()
     ksum = sas.pool_keys(prob, kct)
     torch.cuda.synchronize()
-    got = ksum[0, 0, 0, :nblk].cpu()
+    got = sas.summaries_by_block(ksum)[0, 0, :nblk, 0].cpu()
     ref = torch.from_numpy(want).to(torch.float8_e4m3fn).view(torch.uint8)
     # NaN has two codes (0x7f, 0xff) and torch writes 0x7f for either sign
     nan = (ref & 0x7f) == 0x7f
     assert torch.equal((got & 0x7f)[nan], ref[nan] & 0x7f)
     assert torch.equal(got[~nan], ref[~nan]), (want[~nan.numpy()][(got != ref)[~nan].numpy()])
-    assert np.array_equal(summaries_f32(ksum)[0, 0, 0, :nblk][~nan.numpy()],
+    assert np.array_equal(summaries_f32(ksum)[0, 0, :nblk, 0][~nan.numpy()],
                           oracle.round_e4m3(want)[~nan.numpy()])
     say(f"  {nblk} summaries: codes equal torch's conversion")
 
@@ -161,15 +165,14 @@ def test_paged_equals_contiguous_bitwise():
     assert torch.equal(o, o_p) and torch.equal(lse, lse_p)
 
 
-def test_unaligned_summary_stride_bitwise():
-    """A summary stride that is not a multiple of 4 takes the one-block
-    scoring kernel; summaries, scores, selection and output are the same
-    bits as with the padded stride."""
+def test_wider_summary_stride_bitwise():
+    """A summary / score row stride of two tiles instead of one: summaries,
+    scores, selection and output are the same bits."""
     import torch
     seqlens, hq, hkv, d, Kb = CASES["g8_d128_bigK"]
     host = wl.draw_decode_host_small(seqlens, hq, hkv, d, Kb, True, seed=11)
     res = []
-    for stride in (None, 41):  # padded default (40), and 41: 40 history blocks
+    for stride in (None, 128):  # one tile (the default for 40 history blocks), two
         prob = sas.Decode(seqlens, hq, hkv, d, Kb, True, max(seqlens),
                           page_table=host["page_table"], num_pages=host["k"].shape[0],
                           nblk_stride=stride)
@@ -182,7 +185,38 @@ def test_unaligned_summary_stride_bitwise():
         o, lse = sas.decode(prob, q, kc, vc, sel, lg)
         torch.cuda.synchronize()
         nh = (max(seqlens) - 1) // 64
-        res.append((ksum[..., :nh].cpu(), scores[..., :nh].cpu(), sel.cpu(), lg.cpu(), o.cpu(),
+        res.append((sas.summaries_by_block(ksum)[..., :nh, :].cpu(), scores[..., :nh].cpu(),
+                    sel.cpu(), lg.cpu(), o.cpu(),
                     lse.cpu()))
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+def test_select_workspace_reused_across_calls():
+    """One workspace serves repeated selections and a smaller problem in
+    between: every result equals that of a fresh workspace."""
+    import torch
+    seqlens, hq, hkv, d, Kb = CASES["chunks_g4_d128"]
+    host = wl.draw_decode_host_small(seqlens, hq, hkv, d, Kb, True, seed=17)
+    big = sas.Decode(seqlens, hq, hkv, d, Kb, True, max(seqlens),
+                     page_table=host["page_table"], num_pages=host["k"].shape[0])
+    small = sas.Decode(seqlens[1:], hq, hkv, d, Kb, True, max(seqlens),
+                       page_table=host["page_table"][1:], num_pages=host["k"].shape[0])
+    q = dev_tensor(host["q"], host["q_bits"], "bf16")
+    kc = dev_tensor(host["k"], host["k_bits"], "bf16")
+    ks_big, ks_small = sas.pool_keys(big, kc), sas.pool_keys(small, kc)
+    q_small = q[1:].contiguous()
+    fresh_big = [x.cpu() for x in sas.decode_select(big, q, ks_big)]
+    fresh_small = [x.cpu() for x in sas.decode_select(small, q_small, ks_small)]
+    ws = sas.decode_select_workspace(big)
+    assert ws.numel() >= sas.decode_select_workspace_bytes(small)
+    for prob, qq, ks, want in ((big, q, ks_big, fresh_big), (big, q, ks_big, fresh_big),
+                               (small, q_small, ks_small, fresh_small),
+                               (big, q, ks_big, fresh_big)):
+        got = [x.cpu() for x in sas.decode_select(prob, qq, ks, workspace=ws)]
+        for a, b in zip(got[:3], want[:3]):  # sel_idx, log gates, gate_lse
+            assert torch.equal(a, b)
+        for bi, L in enumerate(prob.seqlens):  # scores exist for history blocks only
+            nh = (L - 1) // 64
+            assert torch.equal(got[3][bi, :, :nh], want[3][bi, :, :nh])
+    say("  four calls on one workspace equal fresh ones")

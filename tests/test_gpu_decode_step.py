@@ -40,7 +40,7 @@ def test_decode_step_loop(paged, summary):
     kf, vf, qf = wl.bf16_bits_to_f32(kb), wl.bf16_bits_to_f32(vb), wl.bf16_bits_to_f32(qb)
     npg = [(n + 63) // 64 for n in Lfin]
     maxp = max(npg)
-    stride = -(-max(1, (cap - 1) // 64) // 4) * 4
+    stride = -(-max(1, (cap - 1) // 64) // 64) * 64
 
     # the prefilled prefix (tokens < L0) in the chosen layout; the rest zero
     if paged:
@@ -99,7 +99,7 @@ def test_decode_step_loop(paged, summary):
             cur = (L - 1) // 64
             for h in range(hkv):
                 K, V = kf[b, h, :L], vf[b, h, :L]
-                assert np.array_equal(ks_h[b, h, :, :cur].T,
+                assert np.array_equal(ks_h[b, h, :cur, :],
                                       oracle.pool_keys_row(K, summary=summary)), \
                     (s, b, h, "summaries")
                 qg = qf[s, b, h * G:(h + 1) * G]

@@ -69,7 +69,7 @@ def test_noalloc_rejects_partials_beyond_the_scratch():
     lib = sas.lib()
     FAKE = 0x10000
     sl = np.full(32, 64 * 100, np.int32)
-    p = sas.DecodeProblem(32, 32, 8, 128, 64, 64, 0, 0, 0, 64 * 100, 0, 0, 100,
+    p = sas.DecodeProblem(32, 32, 8, 128, 64, 64, 0, 0, 0, 64 * 100, 0, 0, 128,
                           1.0 / np.sqrt(128), FAKE, sl.ctypes.data, None, 0, None, 64)
     assert lib.sas_decode_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                   None) == -6

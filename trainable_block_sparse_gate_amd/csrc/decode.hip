@@ -4,13 +4,15 @@
 // selection).
 //
 //   pool:    summary of block j = mean of its 64 keys, summed in token order
-//            in fp32 (one thread per (block, channel), reads coalesced
-//            along the channel).
+//            in fp32 (one thread per (block, channel), reads and writes
+//            coalesced along the channel).
 //   scores:  s_j = (fmaf chain over channels of qbar * summary) / sqrt(d),
 //            qbar = sum of the group's query heads in head order / G, all
 //            in fp32 in exactly this order, so the Top-K decision is taken
 //            on values the oracle reproduces bit for bit.  Summaries are
-//            channel-major, so lanes (blocks) read consecutive addresses.
+//            tiled (summary_index), so a thread reads its block's channels
+//            as a few 16-byte pieces, all in flight at once, while each
+//            wave-wide read is 1 KB of contiguous memory.
 //   attend:  split-K over the kept blocks of every (sequence, kv head):
 //            each wave of a workgroup streams its own share of 64-token
 //            K/V blocks (16-byte coalesced loads, several passes in flight
@@ -61,6 +63,20 @@ __device__ inline uint8_t e4m3_code(float x) {
   return sgn | (uint8_t)((er + 7) << 3) | (uint8_t)mant;
 }
 
+// Element index of channel e of block j's summary in row `row`.  Summaries
+// are stored in tiles of 64 consecutive blocks; inside a tile, 16-byte piece
+// l (channels [l EPP, (l + 1) EPP), EPP = 16 / element size) of the 64 blocks
+// lies side by side in block order:
+//   [row][j / 64][e / EPP][j % 64][e % EPP]
+// so one wave reading piece l of 64 consecutive blocks (a block per lane)
+// reads 1 KB of contiguous memory.
+__device__ inline long summary_index(const DecodeParams &p, int row, int j, int e) {
+  const int epp = p.sum_kind == kSumBf16 ? 8 : p.sum_kind == kSumFp8 ? 16 : 4;
+  const int np = p.D / epp;
+  return (((long)row * (p.nblk_stride / 64) + j / 64) * np + e / epp) * (64 * epp) +
+         (j % 64) * epp + e % epp;
+}
+
 // A block summary (the fp32 mean) stored as fp32, or rounded to the nearest
 // bf16 / fp8 e4m3 value (ties to even).
 __device__ inline void store_summary(const DecodeParams &p, long idx, float v) {
@@ -85,7 +101,7 @@ __global__ __launch_bounds__(128) void pool_keys_kernel(DecodeParams p) {
   const __bf16 *row = kv_row(p, k, b, g, j * kBlock);  // a block never crosses a page
   float acc = 0.f;
   for (int t = 0; t < kBlock; ++t) acc = acc + (float)row[(long)t * p.D + e];
-  store_summary(p, (((long)b * p.hkv + g) * p.D + e) * p.nblk_stride + j, acc / (float)kBlock);
+  store_summary(p, summary_index(p, bg, j, e), acc / (float)kBlock);
 }
 
 // ------------------------------------------------------------------ append
@@ -112,8 +128,7 @@ __global__ __launch_bounds__(128) void append_kernel(DecodeParams p, const __bf1
     const __bf16 *row = kv_row(p, kc, b, g, j * kBlock);
     float acc = 0.f;
     for (int t = 0; t < kBlock; ++t) acc = acc + (float)row[(long)t * p.D + e];
-    store_summary(p, (((long)b * p.hkv + g) * p.D + e) * p.nblk_stride + j,
-                  acc / (float)kBlock);
+    store_summary(p, summary_index(p, bg, j, e), acc / (float)kBlock);
   }
 }
 
@@ -134,250 +149,31 @@ __device__ inline float e4m3_value(uint32_t b) {
   return __uint_as_float(v ^ ((v ^ 0x7fc00000u) & (0u - nan)));
 }
 
-// V consecutive summaries from an address aligned to their size, as one
-// non-temporal load (the scan reads every summary once per step).
-template <typename TS, int V>
-__device__ inline void load_summaries(const TS *src, TS (&w)[V]) {
-  constexpr int BYTES = V * (int)sizeof(TS);
-  if constexpr (BYTES == 4) {
-    const uint32_t x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(src));
-    __builtin_memcpy(&w[0], &x, 4);
-  } else if constexpr (BYTES > 4) {
-    typedef uint32_t words __attribute__((ext_vector_type(BYTES / 4)));
-    const words x = __builtin_nontemporal_load(reinterpret_cast<const words *>(src));
-    __builtin_memcpy(&w[0], &x, BYTES);
-  } else if constexpr (BYTES == 2) {
-    const uint16_t x = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(src));
-    __builtin_memcpy(&w[0], &x, 2);
-  } else {
-    const uint8_t x = __builtin_nontemporal_load(reinterpret_cast<const uint8_t *>(src));
-    __builtin_memcpy(&w[0], &x, 1);
-  }
-}
-
+// Element k of a 16-byte piece of summaries, as fp32 (bf16 widened, fp8
+// decoded; exact in every case).
 template <typename TS>
-__device__ inline float summary_value(TS x) {
-  if constexpr (sizeof(TS) == 1)
-    return e4m3_value(x);
-  else
-    return (float)x;
+__device__ inline float summary_elem(const u32x4 &w, int k) {
+  if constexpr (sizeof(TS) == 4) {
+    return __uint_as_float(w[k]);
+  } else if constexpr (sizeof(TS) == 2) {
+    const uint32_t x = w[k / 2];
+    return __uint_as_float((k % 2) ? (x & 0xffff0000u) : (x << 16));
+  } else {
+    return e4m3_value((w[k / 4] >> (8 * (k % 4))) & 0xffu);
+  }
 }
 
-// Decode selection, phase 1: workgroup (chunk c, row b * hkv + g) takes
-// history blocks [256 V c, 256 V (c + 1)) of the row, V consecutive blocks
-// per thread.  It computes their pooled scores in the fixed fp32 order
-//   qbar_e = (q_{gG} + ... + q_{gG+G-1})_e / G,
-//   s_j    = (fmaf chain over e of qbar_e * summary_je) / sqrtf(d)
-// (so every score is the one the oracle computes), writes them out, and
-// keeps the chunk's exact Top-K (the Kb - 1 largest scores, earlier block
-// on ties), in block order, with the chunk's max and sum of exp(s - max)
-// for the row's normaliser.  VEC: the summary stride allows V-wide loads.
-template <int D, int G, int V, typename TS, bool VEC>
-__global__ __launch_bounds__(256) void select_partial_kernel(DecodeParams p, SelectParams sp) {
-#pragma clang fp contract(off)
-  constexpr int NT = 256, NWV = NT / kWave;
-  // Summaries of V blocks for one channel: BYTES per thread, one load.
-  // With V-wide loads the channels go in batches of 32 words per thread,
-  // two batches in flight (the first requested before the query mean is
-  // formed), each channel held in 32-bit words (a narrower one zero
-  // extended into a word) and decoded from them.  Without (a stride that
-  // is not a multiple of V) each element is loaded on its own.
-  constexpr int BYTES = V * (int)sizeof(TS);
-  constexpr bool WORDS = VEC;
-  constexpr int WPC = BYTES >= 4 ? BYTES / 4 : 1;  // 32-bit words per channel
-  constexpr int U = 32 / WPC < D / 2 ? 32 / WPC : D / 2;  // channels per batch (>= 2 batches)
-  constexpr int NB = D / U;
-  static_assert(D % U == 0, "channel batches");
-  typedef uint32_t chan_words __attribute__((ext_vector_type(WPC > 1 ? WPC : 2)));
-  __shared__ float qbar[D];
-  __shared__ float red[NWV];
-  __shared__ int cnt[NWV];
-  __shared__ SelectScratch sel;
-  const int c = blockIdx.x, row = blockIdx.y;
-  const int b = row / p.hkv, g = row % p.hkv;
+// The row's merge: the chunks' candidates (in block order: chunk by chunk, each in block
+// order) hold the row's Top-K, since every block of it is among its own
+// chunk's Top-K; an exact Top-K over them with the same order gives the
+// row's.  The normaliser combines the chunks' (max, sum) pairs in chunk
+// order.  Writes the kept blocks ascending with log g = s - lse, the
+// current block (log g 0), then -1 padding.  R candidates per thread.
+template <int R, int NT>
+__device__ inline void merge_row(const DecodeParams &p, const SelectParams &sp, int row, float *red,
+                                 int *cnt, SelectScratch &sel) {
+  constexpr int NWV = NT / kWave;
   const int tid = threadIdx.x;
-  const int nhist = (p.seqlens[b] - 1) / kBlock;
-  const int kh = p.Kb - 1;
-  const int j0 = 256 * V * c + V * tid;  // this thread's first block
-  const int lo = 256 * V * c, n = max(0, min(nhist - lo, 256 * V));  // valid blocks in the chunk
-  uint32_t valid = 0u;
-#pragma unroll
-  for (int v = 0; v < V; ++v)
-    if (j0 + v < nhist) valid |= 1u << v;
-  const TS *ks = static_cast<const TS *>(p.ksum) + ((long)row * D) * p.nblk_stride + j0;
-
-  // channel e's words (V-wide loads are aligned and inside the row: j0 and
-  // the stride are multiples of V, and j0 < nhist <= stride), addressed as
-  // the row's uniform base plus a 32-bit byte offset per lane (a row of
-  // summaries spans D * stride elements, far below 4 GB)
-  const char *rbase = reinterpret_cast<const char *>(static_cast<const TS *>(p.ksum) +
-                                                     (long)row * D * p.nblk_stride);
-  const unsigned lane_off = (unsigned)j0 * (unsigned)sizeof(TS);
-  const unsigned cstride = (unsigned)p.nblk_stride * (unsigned)sizeof(TS);
-  auto load_chan = [&](int e) -> chan_words {
-    const char *src = rbase + (lane_off + (unsigned)e * cstride);
-    if constexpr (BYTES == 1) {
-      chan_words x{};
-      x[0] = __builtin_nontemporal_load(reinterpret_cast<const uint8_t *>(src));
-      return x;
-    } else if constexpr (BYTES == 2) {
-      chan_words x{};
-      x[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(src));
-      return x;
-    } else if constexpr (WPC == 1) {
-      chan_words x{};
-      x[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(src));
-      return x;
-    } else {
-      return __builtin_nontemporal_load(reinterpret_cast<const chan_words *>(src));
-    }
-  };
-  // element v of a channel's words
-  auto elem = [&](const chan_words &x, int v) -> float {
-    if constexpr (sizeof(TS) == 4) {
-      return __uint_as_float(x[v]);
-    } else if constexpr (sizeof(TS) == 2) {
-      const uint32_t w = x[v / 2];
-      return __uint_as_float((v % 2) ? (w & 0xffff0000u) : (w << 16));
-    } else {
-      return e4m3_value((x[v / 4] >> (8 * (v % 4))) & 0xffu);
-    }
-  };
-  chan_words wb[2][U];
-  if constexpr (WORDS) {
-    if (valid) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) wb[0][u] = load_chan(u);
-    }
-  }
-
-  const __bf16 *q = static_cast<const __bf16 *>(p.q);
-  if (tid < D) {
-    float qv[G];  // every head's value requested before the ordered sum
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) qv[hh] = (float)q[((long)b * p.hq + g * G + hh) * D + tid];
-    float acc = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) acc = acc + qv[hh];
-    qbar[tid] = acc / (float)G;
-  }
-  __syncthreads();
-
-  // scores of this thread's blocks (invalid ones: -inf, never kept); each
-  // an fmaf chain over the channels in order
-  float sv[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) sv[v] = -INFINITY;
-  if (valid) {
-    float a[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) a[v] = 0.f;
-    if constexpr (WORDS) {
-      static_assert(NB % 2 == 0, "batches go in pairs");
-      auto load_batch = [&](chan_words (&dst)[U], int bi) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) dst[u] = load_chan(bi * U + u);
-      };
-      auto use_batch = [&](const chan_words (&src)[U], int bi) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float qe = qbar[bi * U + u];
-#pragma unroll
-          for (int v = 0; v < V; ++v) a[v] = fmaf(qe, elem(src[u], v), a[v]);
-        }
-      };
-      // batch bi + 1 is requested before batch bi is used; a loop over
-      // pairs keeps that to two batches in registers
-#pragma unroll 1
-      for (int bi = 0; bi < NB; bi += 2) {
-        load_batch(wb[1], bi + 1);
-        use_batch(wb[0], bi);
-        if (bi + 2 < NB) load_batch(wb[0], bi + 2);
-        use_batch(wb[1], bi + 1);
-      }
-    } else {
-      constexpr int CB = 512 / BYTES < D ? 512 / BYTES : D;
-      static_assert(D % CB == 0, "channel batches");
-#pragma unroll 1
-      for (int e0 = 0; e0 < D; e0 += CB) {
-        TS w[CB][V];
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-          const TS *src = ks + (long)(e0 + u) * p.nblk_stride;
-          if constexpr (VEC) {
-            load_summaries<TS, V>(src, w[u]);
-          } else {
-#pragma unroll
-            for (int v = 0; v < V; ++v) w[u][v] = ((valid >> v) & 1u) ? src[v] : TS{};
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-          const float qe = qbar[e0 + u];
-#pragma unroll
-          for (int v = 0; v < V; ++v) a[v] = fmaf(qe, summary_value<TS>(w[u][v]), a[v]);
-        }
-      }
-    }
-    float *out = p.scores + (long)row * p.nblk_stride + j0;
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      if ((valid >> v) & 1u) {
-        sv[v] = a[v] / p.sqrt_d;
-        out[v] = sv[v];
-      }
-  }
-  // the chunk's share of the normaliser
-  float mx = -INFINITY;
-#pragma unroll
-  for (int v = 0; v < V; ++v) mx = fmaxf(mx, sv[v]);
-  mx = block_max<NWV>(mx, red);
-  float sum = 0.f;
-  if (mx != -INFINITY) {
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      if ((valid >> v) & 1u) sum += expf(sv[v] - mx);
-  }
-  sum = block_sum<NWV>(sum, red);
-  // the chunk's Top-K
-  const int k = min(kh, n);
-  const bool keep_all = k == n;
-  Threshold th{0u, 0u, k};
-  if (!keep_all && k > 0)
-    th = radix_threshold<NT>(k, sel, [&](auto &&f) {
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        if ((valid >> v) & 1u) f(order_key(sv[v]));
-    });
-  int2 *cand = sp.cand + ((long)row * sp.nchunk + c) * kh;
-  if (k > 0) {
-    int pos, total;
-    const uint32_t takem = kept_mask<V, NWV>(sv, valid, keep_all, th, cnt, pos, total);
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      if ((takem >> v) & 1u) {
-        cand[pos] = make_int2(j0 + v, __float_as_int(sv[v]));
-        ++pos;
-      }
-  }
-  for (int x = k + tid; x < kh; x += NT) cand[x] = make_int2(-1, __float_as_int(-INFINITY));
-  if (tid == 0) sp.part[(long)row * sp.nchunk + c] = make_float2(mx, sum);
-}
-
-// Decode selection, phase 2: one workgroup per row merges the chunks'
-// candidates (in block order: chunk by chunk, each in block order).  The
-// row's Top-K is contained in the union of the chunks' Top-Ks, so an exact
-// Top-K over the candidates with the same order gives it.  The normaliser
-// combines the chunks' (max, sum) pairs in chunk order.  Writes the kept
-// blocks ascending with log g = s - lse, the current block (log g 0), then
-// -1 padding.
-template <int R>
-__global__ __launch_bounds__(256) void select_merge_kernel(DecodeParams p, SelectParams sp) {
-  constexpr int NT = 256, NWV = NT / kWave;
-  __shared__ float red[NWV];
-  __shared__ int cnt[NWV];
-  __shared__ SelectScratch sel;
-  const int row = blockIdx.x, tid = threadIdx.x;
   const int b = row / p.hkv;
   const int cur = (p.seqlens[b] - 1) / kBlock;
   const int kh = p.Kb - 1;
@@ -394,26 +190,22 @@ __global__ __launch_bounds__(256) void select_merge_kernel(DecodeParams p, Selec
     sv[c] = __int_as_float(e.y);
     if (e.x >= 0) valid |= 1u << c;
   }
-  // the normaliser: the chunks' (max, sum) pairs combined, chunks tid,
-  // tid + 256, ... by thread tid (requested together), the sums added in a
-  // fixed order
-  constexpr int PC = 4;  // chunks per thread held at once
+  // the normaliser: chunks tid, tid + NT, ... by thread tid, the sums added
+  // in a fixed order
   const float2 *part = sp.part + (long)row * sp.nchunk;
+  constexpr int PC = 4;  // chunks per thread held at once
+  float2 pv[PC];
+#pragma unroll
+  for (int u = 0; u < PC; ++u)
+    pv[u] = tid + u * NT < sp.nchunk ? part[tid + u * NT] : make_float2(-INFINITY, 0.f);
   float M = -INFINITY;
-  for (int c0 = tid; c0 < sp.nchunk; c0 += PC * NT) {
-    float2 pv[PC];
 #pragma unroll
-    for (int u = 0; u < PC; ++u)
-      pv[u] = c0 + u * NT < sp.nchunk ? part[c0 + u * NT] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int u = 0; u < PC; ++u) M = fmaxf(M, pv[u].x);
-  }
+  for (int u = 0; u < PC; ++u) M = fmaxf(M, pv[u].x);
   M = block_max<NWV>(M, red);
   float Lt = 0.f;
-  for (int c = tid; c < sp.nchunk; c += NT) {
-    const float2 pv = part[c];
-    if (pv.y > 0.f) Lt += pv.y * expf(pv.x - M);
-  }
+#pragma unroll
+  for (int u = 0; u < PC; ++u)
+    if (pv[u].y > 0.f) Lt += pv[u].y * expf(pv[u].x - M);
   const float Lsum = block_sum<NWV>(Lt, red);
   const float lse = (cur == 0 || M == -INFINITY) ? -INFINITY : M + logf(Lsum);
   int nvalid_local = __popc(valid), nvalid;
@@ -451,47 +243,186 @@ __global__ __launch_bounds__(256) void select_merge_kernel(DecodeParams p, Selec
   }
 }
 
+// Decode selection: workgroup (chunk c, row b * hkv + g) takes history
+// blocks [256 V c, 256 V (c + 1)) of the row, V consecutive blocks per
+// thread.  A block's D values are NL 16-byte pieces (summary_index) that
+// its thread requests all at once (a block of fp32 summaries is 32
+// requests, bf16 16, fp8 8), before the query mean is formed; with one
+// block per thread a wave's request for piece l is 1 KB of contiguous
+// memory.  Each score is the fixed fp32
+// order
+//   qbar_e = (q_{gG} + ... + q_{gG+G-1})_e / G,
+//   s_j    = (fmaf chain over e of qbar_e * summary_je) / sqrtf(d)
+// (so every score is the one the oracle computes).  The workgroup writes the
+// scores and keeps the chunk's exact Top-K (the Kb - 1 largest scores,
+// earlier block on ties) in block order with the chunk's max and sum of
+// exp(s - max).  (A single launch whose last chunk merges its row needs a
+// device-scope release per workgroup, which writes back the L2 of its XCD:
+// measured 15 times slower than the second launch.)
 template <int D, int G, int V, typename TS>
-static void launch_partial(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
+__global__ __launch_bounds__(256) void select_kernel(DecodeParams p, SelectParams sp) {
+#pragma clang fp contract(off)
+  constexpr int NT = 256, NWV = NT / kWave;
+  constexpr int BB = D * (int)sizeof(TS);  // bytes of one block's summary
+  constexpr int NL = BB / 16;              // 16-byte pieces per block
+  constexpr int EPL = 16 / (int)sizeof(TS);
+  static_assert(BB % 16 == 0, "a block's summary is whole 16-byte pieces");
+  __shared__ __attribute__((aligned(16))) float qbar[D];
+  __shared__ float red[NWV];
+  __shared__ int cnt[NWV];
+  __shared__ SelectScratch sel;
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int b = row / p.hkv, g = row % p.hkv;
+  const int tid = threadIdx.x;
+  const int nhist = (p.seqlens[b] - 1) / kBlock;
+  const int kh = p.Kb - 1;
+  const int lo = 256 * V * c, n = max(0, min(nhist - lo, 256 * V));  // valid blocks in the chunk
+  const int j0 = lo + V * tid;  // this thread's first block
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (j0 + v < nhist) valid |= 1u << v;
+
+  float sv[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) sv[v] = -INFINITY;
+  if (n > 0) {  // uniform: the chunk holds blocks of this row
+    const __bf16 *q = static_cast<const __bf16 *>(p.q);
+    float qv[G];  // the heads' values requested before the summaries
+    if (tid < D) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) qv[hh] = (float)q[((long)b * p.hq + g * G + hh) * D + tid];
+    }
+    // block j's piece l at the row's uniform base plus a 32-bit byte offset
+    // (a row of summaries spans nblk_stride * BB bytes): tile j / 64 of NL
+    // KB, piece l's KB in it, the block's 16 bytes in that; blocks past the
+    // history re-read its last block (their scores are discarded), so every
+    // thread's requests issue without a branch
+    const char *rbase =
+        static_cast<const char *>(p.ksum) + (long)row * p.nblk_stride * (long)BB;
+    auto load_block = [&](int j, u32x4 (&w)[NL]) {
+      const int jj = min(j, nhist - 1);
+      const unsigned off = (unsigned)(jj / 64) * (unsigned)(NL * 1024) + 16u * (unsigned)(jj % 64);
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+        w[l] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(rbase + (off + 1024u * (unsigned)l)));
+    };
+    u32x4 w[NL];
+    load_block(j0, w);
+    if (tid < D) {
+      float acc = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) acc = acc + qv[hh];
+      qbar[tid] = acc / (float)G;
+    }
+    barrier_keep_requests();  // qbar visible; the summary requests stay in flight
+    float *out = p.scores + (long)row * p.nblk_stride;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      if (v > 0) load_block(j0 + v, w);
+      float a = 0.f;
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+#pragma unroll
+        for (int k4 = 0; k4 < EPL; k4 += 4) {
+          const float4 qe = *reinterpret_cast<const float4 *>(&qbar[l * EPL + k4]);
+          a = fmaf(qe.x, summary_elem<TS>(w[l], k4 + 0), a);
+          a = fmaf(qe.y, summary_elem<TS>(w[l], k4 + 1), a);
+          a = fmaf(qe.z, summary_elem<TS>(w[l], k4 + 2), a);
+          a = fmaf(qe.w, summary_elem<TS>(w[l], k4 + 3), a);
+        }
+      }
+      if ((valid >> v) & 1u) {
+        sv[v] = a / p.sqrt_d;
+        out[j0 + v] = sv[v];
+      }
+    }
+  }
+  // the chunk's share of the normaliser
+  float mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < V; ++v) mx = fmaxf(mx, sv[v]);
+  mx = block_max<NWV>(mx, red);
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if ((valid >> v) & 1u) sum += expf(sv[v] - mx);
+  }
+  sum = block_sum<NWV>(sum, red);
+  // the chunk's Top-K
+  const int k = min(kh, n);
+  const bool keep_all = k == n;
+  Threshold th{0u, 0u, k};
+  if (!keep_all && k > 0)
+    th = radix_threshold<NT>(k, sel, [&](auto &&f) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if ((valid >> v) & 1u) f(order_key(sv[v]));
+    });
+  int2 *cand = sp.cand + ((long)row * sp.nchunk + c) * kh;
+  if (k > 0) {
+    int pos, total;
+    const uint32_t takem = kept_mask<V, NWV>(sv, valid, keep_all, th, cnt, pos, total);
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if ((takem >> v) & 1u) {
+        cand[pos] = make_int2(j0 + v, __float_as_int(sv[v]));
+        ++pos;
+      }
+  }
+  for (int x = k + tid; x < kh; x += NT) cand[x] = make_int2(-1, __float_as_int(-INFINITY));
+  if (tid == 0) sp.part[(long)row * sp.nchunk + c] = make_float2(mx, sum);
+
+}
+
+// Decode selection, phase 2: one workgroup per row merges the chunks'
+// candidates (merge_row).
+template <int R>
+__global__ __launch_bounds__(256) void select_merge_kernel(DecodeParams p, SelectParams sp) {
+  __shared__ float red[256 / kWave];
+  __shared__ int cnt[256 / kWave];
+  __shared__ SelectScratch sel;
+  merge_row<R, 256>(p, sp, blockIdx.x, red, cnt, sel);
+}
+
+template <int D, int G, int V, typename TS>
+static void launch_select(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
   const dim3 grid(sp.nchunk, p.batch * p.hkv);
-  if (p.nblk_stride % V == 0)
-    hipLaunchKernelGGL((select_partial_kernel<D, G, V, TS, true>), grid, dim3(256), 0, stream, p,
-                       sp);
-  else
-    hipLaunchKernelGGL((select_partial_kernel<D, G, V, TS, false>), grid, dim3(256), 0, stream,
-                       p, sp);
+  hipLaunchKernelGGL((select_kernel<D, G, V, TS>), grid, dim3(256), 0, stream, p, sp);
 }
 
 template <int D, int G, typename TS>
-static void launch_partial_v(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
+static void launch_select_v(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
   switch (sp.chunk_v) {
-    case 1: launch_partial<D, G, 1, TS>(p, sp, stream); break;
-    case 2: launch_partial<D, G, 2, TS>(p, sp, stream); break;
-    case 4: launch_partial<D, G, 4, TS>(p, sp, stream); break;
-    default: launch_partial<D, G, 8, TS>(p, sp, stream); break;
+    case 1: launch_select<D, G, 1, TS>(p, sp, stream); break;
+    case 2: launch_select<D, G, 2, TS>(p, sp, stream); break;
+    case 4: launch_select<D, G, 4, TS>(p, sp, stream); break;
+    default: launch_select<D, G, 8, TS>(p, sp, stream); break;
   }
 }
 
 template <int D, typename TS>
-static void launch_partial_g(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
+static void launch_select_g(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
   switch (p.hq / p.hkv) {
-    case 1: launch_partial_v<D, 1, TS>(p, sp, stream); break;
-    case 2: launch_partial_v<D, 2, TS>(p, sp, stream); break;
-    case 4: launch_partial_v<D, 4, TS>(p, sp, stream); break;
-    default: launch_partial_v<D, 8, TS>(p, sp, stream); break;
+    case 1: launch_select_v<D, 1, TS>(p, sp, stream); break;
+    case 2: launch_select_v<D, 2, TS>(p, sp, stream); break;
+    case 4: launch_select_v<D, 4, TS>(p, sp, stream); break;
+    default: launch_select_v<D, 8, TS>(p, sp, stream); break;
   }
 }
 
 hipError_t launch_decode_select(const DecodeParams &p, const SelectParams &sp,
                                 hipStream_t stream) {
   if (p.D == 128) {
-    if (p.sum_kind == kSumBf16) launch_partial_g<128, __bf16>(p, sp, stream);
-    else if (p.sum_kind == kSumFp8) launch_partial_g<128, uint8_t>(p, sp, stream);
-    else launch_partial_g<128, float>(p, sp, stream);
+    if (p.sum_kind == kSumBf16) launch_select_g<128, __bf16>(p, sp, stream);
+    else if (p.sum_kind == kSumFp8) launch_select_g<128, uint8_t>(p, sp, stream);
+    else launch_select_g<128, float>(p, sp, stream);
   } else {
-    if (p.sum_kind == kSumBf16) launch_partial_g<64, __bf16>(p, sp, stream);
-    else if (p.sum_kind == kSumFp8) launch_partial_g<64, uint8_t>(p, sp, stream);
-    else launch_partial_g<64, float>(p, sp, stream);
+    if (p.sum_kind == kSumBf16) launch_select_g<64, __bf16>(p, sp, stream);
+    else if (p.sum_kind == kSumFp8) launch_select_g<64, uint8_t>(p, sp, stream);
+    else launch_select_g<64, float>(p, sp, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

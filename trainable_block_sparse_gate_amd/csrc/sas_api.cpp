@@ -440,7 +440,10 @@ sas_status check_decode(const sas_decode_problem *p) {
   REQUIRE(p->num_splits >= 0 && p->num_splits <= p->budget_blocks, SAS_ERR_SHAPE,
           "num_splits (%d) must be in [0, budget_blocks = %d]", p->num_splits,
           p->budget_blocks);
-  REQUIRE(p->nblk_stride >= 1 && p->nblk_stride >= (maxL - 1) / 64, SAS_ERR_SHAPE,
+  REQUIRE(p->nblk_stride >= 1 && p->nblk_stride % 64 == 0, SAS_ERR_SHAPE,
+          "nblk_stride (%d) must be a positive multiple of 64 (whole summary tiles)",
+          p->nblk_stride);
+  REQUIRE(p->nblk_stride >= (maxL - 1) / 64, SAS_ERR_SHAPE,
           "nblk_stride (%d) < history blocks of the longest sequence (%d)", p->nblk_stride,
           (maxL - 1) / 64);
   return SAS_OK;
@@ -526,12 +529,9 @@ size_t decode_ws_bytes(const sas_decode_problem *p) {
 }
 
 // Chunking of the decode selection over workgroups: V blocks per thread
-// (256 V blocks per chunk).  The fixed cost of a chunk's workgroup (the
-// query mean, one memory latency per 512 bytes of summaries a thread
-// requests, the Top-K passes) is paid once per round of workgroups, so V
-// grows (up to 8) while the grid would still hold more than 512
-// workgroups; the merge takes at most 4096 candidates (chunks x (Kb - 1)),
-// which also bounds the chunk count from below.
+// (256 V blocks per chunk).  One block per thread keeps every thread's
+// summary requests in flight at once; V grows (up to 8) only while the
+// row's merge would take more than 4096 candidates (chunks x (Kb - 1)).
 struct SelectGeom {
   int v, nchunk;
 };
@@ -544,16 +544,16 @@ SelectGeom select_geom(const sas_decode_problem *p) {
   int maxhist = 1;
   for (int b = 0; b < p->batch; ++b)
     if ((p->seqlens_host[b] - 1) / 64 > maxhist) maxhist = (p->seqlens_host[b] - 1) / 64;
-  const long rows = (long)p->batch * p->hkv;
   const int kh = p->budget_blocks > 1 ? p->budget_blocks - 1 : 1;
   auto chunks = [&](int v) { return (maxhist + 256 * v - 1) / (256 * v); };
   int v = 1;
-  while (v < 8 && (rows * chunks(v) > 512 || chunks(v) * kh > 4096)) v *= 2;
+  while (v < 8 && chunks(v) * kh > 4096) v *= 2;
   return {v, chunks(v)};
 }
 
 constexpr int kMaxSelectCandidates = 4096;
 
+// [rows][nchunk][Kb - 1] candidates | [rows][nchunk] (max, sum)
 size_t select_ws_bytes(const sas_decode_problem *p, const SelectGeom &sg) {
   const size_t n = (size_t)p->batch * p->hkv * sg.nchunk;
   return align256(n * (p->budget_blocks - 1) * sizeof(int2)) + n * sizeof(float2);

@@ -92,7 +92,7 @@ struct DecodeParams {
   const int32_t *page_table;   // [batch][max_pages] when paged
   int paged, max_pages, max_seqlen;
   int batch, hq, hkv, D, Kb, nblk_stride;
-  void *ksum;                  // [batch][hkv][D][nblk_stride], fp32, bf16 or fp8
+  void *ksum;                  // [batch][hkv][nblk_stride/64][D/EPP][64][EPP] (EPP = 16 / element size), fp32, bf16 or fp8
   int sum_kind;                // kSumF32, kSumBf16 or kSumFp8
   float *scores;               // [batch][hkv][nblk_stride]
   float sqrt_d;                // sqrtf(D), for the pooled score

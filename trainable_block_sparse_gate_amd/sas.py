@@ -23,7 +23,7 @@ GATE_INNER, GATE_OUTER = 0, 1  # gate position
 KV_CONTIGUOUS, KV_PAGED = 0, 1
 SUMMARY_F32, SUMMARY_BF16, SUMMARY_FP8 = 0, 1, 2
 BLOCK = 64
-ABI_VERSION = 4  # the header's SAS_ABI_VERSION these structs follow
+ABI_VERSION = 5  # the header's SAS_ABI_VERSION these structs follow
 
 STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTYPE",
           -4: "SAS_ERR_ALIGN", -5: "SAS_ERR_UNSUPPORTED", -6: "SAS_ERR_WORKSPACE",
@@ -359,10 +359,9 @@ class Decode:
         self.hq, self.hkv, self.d, self.Kb = hq, hkv, head_dim, budget_blocks
         self.batch = len(self.seqlens)
         self.paged = paged
-        # summary row stride: history blocks of the longest sequence, rounded
-        # up to a multiple of 16 (the library then reads summaries 16 bytes
-        # at a time in every summary dtype)
-        self.nblk_stride = -(-max(1, max((n - 1) // BLOCK for n in self.seqlens)) // 16) * 16
+        # blocks per summary / score row: history blocks of the longest
+        # sequence, rounded up to whole 64-block summary tiles
+        self.nblk_stride = -(-max(1, max((n - 1) // BLOCK for n in self.seqlens)) // 64) * 64
         if nblk_stride is not None:
             self.nblk_stride = int(nblk_stride)
         self.pt_dev = None
@@ -398,9 +397,14 @@ class Decode:
         else:
             _need(cache, name, torch.bfloat16, (self.batch, self.hkv, self.max_seqlen, self.d))
 
+    def summary_shape(self):
+        """The tiled summary layout: [batch][hkv][tile of 64 blocks][16-byte
+        piece][block in tile][channel in piece]."""
+        epp = 16 // {"f32": 4, "bf16": 2, "fp8": 1}[self.summary_dtype]
+        return (self.batch, self.hkv, self.nblk_stride // 64, self.d // epp, 64, epp)
+
     def check_summaries(self, ksum):
-        _need(ksum, "ksum", _torch_dtype(self.summary_dtype),
-              (self.batch, self.hkv, self.d, self.nblk_stride))
+        _need(ksum, "ksum", _torch_dtype(self.summary_dtype), self.summary_shape())
 
     def check_selection(self, sel_idx, sel_lg, lg_optional=False):
         import torch
@@ -417,11 +421,19 @@ class Decode:
 def pool_keys(prob: Decode, k_cache):
     import torch
     prob.check_cache(k_cache, "k_cache")
-    ksum = torch.empty((prob.batch, prob.hkv, prob.d, prob.nblk_stride),
+    ksum = torch.empty(prob.summary_shape(),
                        dtype=_torch_dtype(prob.summary_dtype), device=k_cache.device)
     _gpu(k_cache, ksum)
     _check(lib().sas_pool_keys(prob.ref, _ptr(k_cache), _ptr(ksum), _stream()))
     return ksum
+
+
+def summaries_by_block(ksum):
+    """A [batch][hkv][block][channel] view (copy) of tiled summaries, for
+    inspection: the library's layout is [batch][hkv][tile][piece][block in
+    tile][channel in piece]."""
+    B, hkv, nt, npc, bt, epp = ksum.shape
+    return ksum.permute(0, 1, 2, 4, 3, 5).reshape(B, hkv, nt * bt, npc * epp)
 
 
 def decode_append(prob: Decode, k_new, v_new, k_cache, v_cache, ksum):
@@ -442,6 +454,13 @@ def decode_select_workspace_bytes(prob: Decode):
     return int(lib().sas_decode_select_workspace_size(prob.ref))
 
 
+def decode_select_workspace(prob: Decode, device="cuda"):
+    """A workspace for sas_decode_select (any contents; reusable)."""
+    import torch
+    return torch.empty(max(decode_select_workspace_bytes(prob), 1), dtype=torch.uint8,
+                       device=device)
+
+
 def decode_select(prob: Decode, q, ksum, out=None, workspace=None):
     """sas_decode_select -> (sel_idx, sel_loggate, gate_lse, scores)."""
     import torch
@@ -460,8 +479,7 @@ def decode_select(prob: Decode, q, ksum, out=None, workspace=None):
     _need(lse, "gate_lse", torch.float32, (rows,))
     _need(scores, "scores", torch.float32, (prob.batch, prob.hkv, prob.nblk_stride))
     if workspace is None:
-        workspace = torch.empty(max(decode_select_workspace_bytes(prob), 1), dtype=torch.uint8,
-                                device=dev)
+        workspace = decode_select_workspace(prob, dev)
     _need(workspace, "workspace", torch.uint8, (None,))
     _gpu(q, ksum, sel, lg, lse, scores, workspace)
     _check(lib().sas_decode_select(prob.ref, _ptr(q), _ptr(ksum), _ptr(scores), _ptr(sel),

@@ -171,7 +171,7 @@ __device__ inline float summary_elem(const u32x4 &w, int k) {
 // current block (log g 0), then -1 padding.  R candidates per thread.
 template <int R, int NT>
 __device__ inline void merge_row(const DecodeParams &p, const SelectParams &sp, int row, float *red,
-                                 int *cnt, SelectScratch &sel) {
+                                 int *cnt, SelectScratch &sel, uint64_t *runs) {
   constexpr int NWV = NT / kWave;
   const int tid = threadIdx.x;
   const int b = row / p.hkv;
@@ -190,10 +190,11 @@ __device__ inline void merge_row(const DecodeParams &p, const SelectParams &sp, 
     sv[c] = __int_as_float(e.y);
     if (e.x >= 0) valid |= 1u << c;
   }
-  // the normaliser: chunks tid, tid + NT, ... by thread tid, the sums added
-  // in a fixed order
+  // the normaliser: chunks tid, tid + NT, ... by thread tid (the first PC
+  // held in registers across the max, the rest, if any, read again), the
+  // sums added in a fixed order
   const float2 *part = sp.part + (long)row * sp.nchunk;
-  constexpr int PC = 4;  // chunks per thread held at once
+  constexpr int PC = 4;
   float2 pv[PC];
 #pragma unroll
   for (int u = 0; u < PC; ++u)
@@ -201,36 +202,55 @@ __device__ inline void merge_row(const DecodeParams &p, const SelectParams &sp, 
   float M = -INFINITY;
 #pragma unroll
   for (int u = 0; u < PC; ++u) M = fmaxf(M, pv[u].x);
+  for (int c = tid + PC * NT; c < sp.nchunk; c += NT) M = fmaxf(M, part[c].x);
   M = block_max<NWV>(M, red);
   float Lt = 0.f;
 #pragma unroll
   for (int u = 0; u < PC; ++u)
     if (pv[u].y > 0.f) Lt += pv[u].y * expf(pv[u].x - M);
+  for (int c = tid + PC * NT; c < sp.nchunk; c += NT) {
+    const float2 q = part[c];
+    if (q.y > 0.f) Lt += q.y * expf(q.x - M);
+  }
   const float Lsum = block_sum<NWV>(Lt, red);
   const float lse = (cur == 0 || M == -INFINITY) ? -INFINITY : M + logf(Lsum);
   int nvalid_local = __popc(valid), nvalid;
   block_scan_int<NWV>(nvalid_local, nvalid, cnt);
   const int k = min(kh, cur);
   const bool keep_all = k >= nvalid;
-  Threshold th{0u, 0u, k};
-  if (!keep_all && k > 0)
-    th = radix_threshold<NT>(k, sel, [&](auto &&f) {
-#pragma unroll
-      for (int c = 0; c < R; ++c)
-        if ((valid >> c) & 1u) f(order_key(sv[c]));
-    });
   int32_t *oidx = sp.sel_idx + (long)row * p.Kb;
   float *olg = sp.sel_lg + (long)row * p.Kb;
-  if (k > 0) {
-    int pos, total;
-    const uint32_t takem = kept_mask<R, NWV>(sv, valid, keep_all, th, cnt, pos, total);
-#pragma unroll
-    for (int c = 0; c < R; ++c)
-      if ((takem >> c) & 1u) {
-        oidx[pos] = jv[c];
-        olg[pos] = lse == -INFINITY ? -INFINITY : sv[c] - lse;
-        ++pos;
+  if constexpr (R == 1) {
+    // one candidate per thread: the Top-K by ranks (entry order = thread
+    // order = block order)
+    if (k > 0) {
+      const bool keep = keep_all ? (valid & 1u) != 0 : rank_keep<NT>(sv[0], valid & 1u, k, runs);
+      int total;
+      const int pos = block_scan_flag<NWV>(keep, total, cnt);
+      if (keep) {
+        oidx[pos] = jv[0];
+        olg[pos] = lse == -INFINITY ? -INFINITY : sv[0] - lse;
       }
+    }
+  } else {
+    Threshold th{0u, 0u, k};
+    if (!keep_all && k > 0)
+      th = radix_threshold<NT>(k, sel, [&](auto &&f) {
+#pragma unroll
+        for (int c = 0; c < R; ++c)
+          if ((valid >> c) & 1u) f(order_key(sv[c]));
+      });
+    if (k > 0) {
+      int pos, total;
+      const uint32_t takem = kept_mask<R, NWV>(sv, valid, keep_all, th, cnt, pos, total);
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+        if ((takem >> c) & 1u) {
+          oidx[pos] = jv[c];
+          olg[pos] = lse == -INFINITY ? -INFINITY : sv[c] - lse;
+          ++pos;
+        }
+    }
   }
   if (tid == 0) {
     oidx[k] = cur;
@@ -260,7 +280,8 @@ __device__ inline void merge_row(const DecodeParams &p, const SelectParams &sp, 
 // device-scope release per workgroup, which writes back the L2 of its XCD:
 // measured 15 times slower than the second launch.)
 template <int D, int G, int V, typename TS>
-__global__ __launch_bounds__(256) void select_kernel(DecodeParams p, SelectParams sp) {
+__global__ __launch_bounds__(256) void select_kernel(
+    DecodeParams p, SelectParams sp) {
 #pragma clang fp contract(off)
   constexpr int NT = 256, NWV = NT / kWave;
   constexpr int BB = D * (int)sizeof(TS);  // bytes of one block's summary
@@ -271,6 +292,7 @@ __global__ __launch_bounds__(256) void select_kernel(DecodeParams p, SelectParam
   __shared__ float red[NWV];
   __shared__ int cnt[NWV];
   __shared__ SelectScratch sel;
+  __shared__ uint64_t runs[NT];
   const int c = blockIdx.x, row = blockIdx.y;
   const int b = row / p.hkv, g = row % p.hkv;
   const int tid = threadIdx.x;
@@ -320,7 +342,10 @@ __global__ __launch_bounds__(256) void select_kernel(DecodeParams p, SelectParam
     float *out = p.scores + (long)row * p.nblk_stride;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      if (v > 0) load_block(j0 + v, w);
+      if (v > 0) {  // one block's pieces in registers at a time
+        __builtin_amdgcn_sched_barrier(0);
+        load_block(j0 + v, w);
+      }
       float a = 0.f;
 #pragma unroll
       for (int l = 0; l < NL; ++l) {
@@ -351,40 +376,51 @@ __global__ __launch_bounds__(256) void select_kernel(DecodeParams p, SelectParam
       if ((valid >> v) & 1u) sum += expf(sv[v] - mx);
   }
   sum = block_sum<NWV>(sum, red);
-  // the chunk's Top-K
+  // the chunk's Top-K: by ranks for one block per thread, else by a radix
+  // select; the candidates go out in block order
   const int k = min(kh, n);
   const bool keep_all = k == n;
-  Threshold th{0u, 0u, k};
-  if (!keep_all && k > 0)
-    th = radix_threshold<NT>(k, sel, [&](auto &&f) {
+  int2 *cand = sp.cand + ((long)row * sp.nchunk + c) * kh;
+  if constexpr (V == 1) {
+    if (k > 0) {
+      const bool keep = keep_all ? (valid & 1u) != 0 : rank_keep<NT>(sv[0], valid & 1u, k, runs);
+      int total;
+      const int pos = block_scan_flag<NWV>(keep, total, cnt);
+      if (keep) cand[pos] = make_int2(j0, __float_as_int(sv[0]));
+    }
+  } else {
+    Threshold th{0u, 0u, k};
+    if (!keep_all && k > 0)
+      th = radix_threshold<NT>(k, sel, [&](auto &&f) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          if ((valid >> v) & 1u) f(order_key(sv[v]));
+      });
+    if (k > 0) {
+      int pos, total;
+      const uint32_t takem = kept_mask<V, NWV>(sv, valid, keep_all, th, cnt, pos, total);
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        if ((valid >> v) & 1u) f(order_key(sv[v]));
-    });
-  int2 *cand = sp.cand + ((long)row * sp.nchunk + c) * kh;
-  if (k > 0) {
-    int pos, total;
-    const uint32_t takem = kept_mask<V, NWV>(sv, valid, keep_all, th, cnt, pos, total);
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      if ((takem >> v) & 1u) {
-        cand[pos] = make_int2(j0 + v, __float_as_int(sv[v]));
-        ++pos;
-      }
+        if ((takem >> v) & 1u) {
+          cand[pos] = make_int2(j0 + v, __float_as_int(sv[v]));
+          ++pos;
+        }
+    }
   }
   for (int x = k + tid; x < kh; x += NT) cand[x] = make_int2(-1, __float_as_int(-INFINITY));
   if (tid == 0) sp.part[(long)row * sp.nchunk + c] = make_float2(mx, sum);
 
 }
 
-// Decode selection, phase 2: one workgroup per row merges the chunks'
-// candidates (merge_row).
-template <int R>
-__global__ __launch_bounds__(256) void select_merge_kernel(DecodeParams p, SelectParams sp) {
-  __shared__ float red[256 / kWave];
-  __shared__ int cnt[256 / kWave];
+// Decode selection, phase 2: one workgroup of NT threads per row merges the
+// chunks' candidates (merge_row), R per thread.
+template <int R, int NT>
+__global__ __launch_bounds__(NT) void select_merge_kernel(DecodeParams p, SelectParams sp) {
+  __shared__ float red[NT / kWave];
+  __shared__ int cnt[NT / kWave];
   __shared__ SelectScratch sel;
-  merge_row<R, 256>(p, sp, blockIdx.x, red, cnt, sel);
+  __shared__ uint64_t runs[R == 1 ? NT : 1];
+  merge_row<R, NT>(p, sp, blockIdx.x, red, cnt, sel, runs);
 }
 
 template <int D, int G, int V, typename TS>
@@ -428,15 +464,19 @@ hipError_t launch_decode_select(const DecodeParams &p, const SelectParams &sp,
   if (e != hipSuccess) return e;
   const int ncand = sp.nchunk * (p.Kb - 1);
   const dim3 grid(p.batch * p.hkv);
-  if (ncand <= 256) hipLaunchKernelGGL((select_merge_kernel<1>), grid, dim3(256), 0, stream, p, sp);
+  // up to 256 candidates: one per thread, Top-K by ranks; more: R per thread
+  // of 256, radix select (one candidate per thread of 1024 with the ranks'
+  // 16 runs measured slower than the radix select with 4 per thread)
+  if (ncand <= 256)
+    hipLaunchKernelGGL((select_merge_kernel<1, 256>), grid, dim3(256), 0, stream, p, sp);
   else if (ncand <= 512)
-    hipLaunchKernelGGL((select_merge_kernel<2>), grid, dim3(256), 0, stream, p, sp);
+    hipLaunchKernelGGL((select_merge_kernel<2, 256>), grid, dim3(256), 0, stream, p, sp);
   else if (ncand <= 1024)
-    hipLaunchKernelGGL((select_merge_kernel<4>), grid, dim3(256), 0, stream, p, sp);
+    hipLaunchKernelGGL((select_merge_kernel<4, 256>), grid, dim3(256), 0, stream, p, sp);
   else if (ncand <= 2048)
-    hipLaunchKernelGGL((select_merge_kernel<8>), grid, dim3(256), 0, stream, p, sp);
+    hipLaunchKernelGGL((select_merge_kernel<8, 256>), grid, dim3(256), 0, stream, p, sp);
   else
-    hipLaunchKernelGGL((select_merge_kernel<16>), grid, dim3(256), 0, stream, p, sp);
+    hipLaunchKernelGGL((select_merge_kernel<16, 256>), grid, dim3(256), 0, stream, p, sp);
   return hipGetLastError();
 }
 

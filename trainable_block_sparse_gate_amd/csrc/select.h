@@ -187,4 +187,49 @@ __device__ inline uint32_t kept_mask(const float (&sv)[R], uint32_t valid, bool 
   return takem;
 }
 
+// Exact Top-K of one candidate per thread (entry order = thread order), by
+// ranks instead of a radix select: a candidate's 64-bit key is its order key
+// above the complement of its thread index, so all keys differ and, of two
+// candidates, the one with the larger key is kept first (larger score, the
+// earlier one on ties).  Each wave sorts its 64 keys in descending order
+// (a bitonic network over lane shuffles, no LDS), the sorted runs go to LDS
+// (runs[NT]), and a candidate is kept when fewer than k keys of all runs
+// exceed its own (a binary search per run, the runs searched side by side).
+// Invalid candidates take key 0, below every valid key.  One workgroup
+// barrier; requires NT threads, a multiple of the wave size.
+template <int NT>
+__device__ inline bool rank_keep(float s, bool valid, int k, uint64_t *runs) {
+  constexpr int NR = NT / kWave;
+  const int lane = threadIdx.x % kWave;
+  const uint64_t key =
+      valid ? ((uint64_t)order_key(s) << 32) | (uint64_t)(~(uint32_t)threadIdx.x) : 0ull;
+  uint64_t x = key;
+#pragma unroll
+  for (int kk = 2; kk <= kWave; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      const uint64_t o = __shfl_xor(x, j);
+      // pairs in a descending block keep the larger key in the lower lane
+      const bool keep_max = ((lane & j) == 0) == ((lane & kk) == 0);
+      x = keep_max ? (x > o ? x : o) : (x < o ? x : o);
+    }
+  }
+  runs[threadIdx.x] = x;
+  __syncthreads();
+  // keys above this one in each run: 6 halving steps, then the last entry
+  int pos[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) pos[r] = 0;
+#pragma unroll
+  for (int b = kWave / 2; b >= 1; b >>= 1) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      if (runs[kWave * r + pos[r] + b - 1] > key) pos[r] += b;
+  }
+  int rank = 0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) rank += pos[r] + (runs[kWave * r + kWave - 1] > key ? 1 : 0);
+  return valid && rank < k;
+}
+
 }  // namespace sas

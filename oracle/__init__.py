@@ -244,6 +244,56 @@ def decode_select_row(q, K, Kb, mode=GATE_HIST, blk=64, summary="f32"):
     return idx, sl, lse, s
 
 
+COARSE_BLOCKS = 8  # history blocks per super-block of the hierarchical selection
+
+
+def coarse_summaries_row(kbar, summary="f32", F=COARSE_BLOCKS):
+    """Super-block summaries [nhist // F, d] from the stored block summaries
+    kbar [nhist, d]: the fp32 mean of each F consecutive blocks (summed in
+    block order), rounded like the block summaries (bf16 / fp8 e4m3)."""
+    kb = _f32(kbar)
+    nhist, d = kb.shape
+    nsup = nhist // F
+    out = np.empty((max(nsup, 1), d), np.float32)
+    _load().sas_oracle_coarse_summaries(nhist, d, F, _p(kb), _p(out))
+    out = out[:nsup]
+    if summary == "bf16":
+        return round_bf16(out)
+    if summary == "fp8":
+        return round_e4m3(out)
+    return out
+
+
+def decode_select_row_hier(q, K, Kb, coarse_keep, blk=64, summary="f32", F=COARSE_BLOCKS):
+    """Hierarchical (coarse-to-fine) selection of one decode row (review
+    7-2): score the super-block summaries, keep the coarse_keep best
+    super-blocks (earlier on ties), then take the gate + Top-K over the
+    candidate blocks only: every block of a kept super-block and the
+    trailing history blocks that form no complete super-block, in block
+    order.  The gates are normalised over the candidates.  Returns
+    (sel_idx, log gates, gate lse, fine scores of every history block,
+    candidate blocks)."""
+    L = K.shape[0]
+    cur = (L - 1) // blk
+    kbar = pool_keys_row(K, blk, summary)
+    nhist = kbar.shape[0]
+    cbar = coarse_summaries_row(kbar, summary, F)
+    nsup = cbar.shape[0]
+    S = decode_scores_row(q, cbar)
+    cidx, _, _ = gate_row(S, nsup, coarse_keep + 1)  # the coarse_keep best, ascending
+    kept = cidx[:min(coarse_keep, nsup)]
+    parts = [F * int(J) + np.arange(F) for J in kept] + [np.arange(F * nsup, nhist)]
+    cand = np.concatenate(parts).astype(np.int32)
+    s = decode_scores_row(q, kbar)
+    n = cand.size
+    idx_c, lg, lse = gate_row(s[cand], n, Kb)
+    idx = idx_c.copy()
+    hist = (idx_c >= 0) & (idx_c < n)
+    idx[hist] = cand[idx_c[hist]]
+    idx[idx_c == n] = cur
+    return idx, lg, lse, s, cand
+
+
 def decode_row(q, K, V, sel_idx, sel_lg, Kb, scale, blk=64):
     """Decode attention of one row: (o float64 [G,d], lse float64 [G])."""
     q, K, V = _f64(q), _f64(K), _f64(V)

@@ -761,6 +761,26 @@ int sas_oracle_pool_keys_row(int L, int blk, int d, const float *K, float *kbar)
 }
 
 /*
+ * Coarse summaries for the hierarchical selection (review 7-2: a coarse
+ * retrieval narrows the candidate blocks before the selector's final
+ * Top-K): super-block J covers history blocks F J .. F J + F - 1, and its
+ * summary is the mean of those F block summaries, summed in block order in
+ * fp32 and divided by F.  Only complete super-blocks (F J + F - 1 < nhist)
+ * have one.  kbar: [nhist][d] (the stored block summaries); cbar:
+ * [nhist / F][d].  Returns the number of super-blocks.
+ */
+int sas_oracle_coarse_summaries(int nhist, int d, int F, const float *kbar, float *cbar) {
+  int nsup = nhist / F;
+  for (int J = 0; J < nsup; ++J)
+    for (int e = 0; e < d; ++e) {
+      float acc = 0.0f;
+      for (int b = 0; b < F; ++b) acc = acc + kbar[(long)(J * F + b) * d + e];
+      cbar[(long)J * d + e] = acc / (float)F;
+    }
+  return nsup;
+}
+
+/*
  * Pooled decode scores of one (sequence, kv head): the group's mean query
  * dotted with each summary, divided by sqrt(d), all in fp32 in the fixed
  * order stated in the header.  q: [G][d]; kbar: [nhist][d]; scores: [nhist].

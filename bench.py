@@ -521,6 +521,40 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
         by_summary[sd] = {"us": round(tt / n * 1e3, 2), "summary_bytes": b2,
                           "GB/s": round(b2 / (tt / n * 1e-3) / 1e9, 1)}
         del ks2, ws2, out2
+    # the hierarchical selection (opt-in approximation): coarse_keep = Kb - 1
+    # super-blocks of 8 blocks, then the fine Top-K over their blocks; its
+    # time per summary dtype and its recall of the exact kept blocks
+    C = spec.budget_blocks - 1
+    hier = {"coarse_keep": C, "coarse_blocks": sas.COARSE_BLOCKS}
+    for sd in ("f32", "bf16", "fp8"):
+        p2 = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, spec.paged,
+                        spec.max_len, page_table=t["page_table"],
+                        num_pages=t["k"].shape[0] if spec.paged else 0, summary_dtype=sd)
+        ks2 = sas.pool_keys(p2, t["k"])
+        cs2 = sas.pool_coarse(p2, ks2)
+        exact = sas.decode_select(p2, t["q"], ks2)[0]
+        ws2 = torch.empty(max(1, sas.decode_select_hier_workspace_bytes(p2, C)),
+                          dtype=torch.uint8, device="cuda")
+        out2 = sas.decode_select_hier(p2, t["q"], ks2, cs2, C, workspace=ws2)
+        tt = 0.0
+        for it in range(n + 3):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            sas.decode_select_hier(p2, t["q"], ks2, cs2, C, out=out2, workspace=ws2)
+            e1.record()
+            torch.cuda.synchronize()
+            if it >= 3:
+                tt += e0.elapsed_time(e1)
+        # recall: kept history blocks of the exact selection also kept here
+        cur = torch.tensor([(L - 1) // 64 for L in spec.seqlens], device="cuda").repeat_interleave(
+            spec.hkv)[:, None]
+        ex = exact.long().masked_fill((exact < 0) | (exact == cur), -1)
+        hi = out2[0].long().masked_fill((out2[0] < 0) | (out2[0] == cur), -2)
+        hits = (ex[:, :, None] == hi[:, None, :]).any(-1).sum().item()
+        total = (ex >= 0).sum().item()
+        hier[sd] = {"us": round(tt / n * 1e3, 2), "recall": round(hits / max(total, 1), 4)}
+        del ks2, cs2, ws2, out2, exact
     kv = metrics.decode_kv_bytes(spec.seqlens, spec.hkv, spec.d, spec.budget_blocks)
     scan = metrics.decode_scan_bytes(spec.seqlens, spec.hkv, spec.d,
                                      SUMMARY_BYTES[args.summary_dtype])
@@ -540,7 +574,8 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
             "traffic": traffic_for("decode_attend_kernel", spec.name),
             "selection": {"us": round(t_sel / n * 1e3, 2), "summary_bytes": scan,
                           "summary_dtype": args.summary_dtype,
-                          "GB/s": round(scan_gbs, 1), "other_summary_dtypes": by_summary},
+                          "GB/s": round(scan_gbs, 1), "other_summary_dtypes": by_summary,
+                          "hierarchical": hier},
             "append_us": round(t_app / n * 1e3, 2),
             "step_us": round((t_app + t_sel + t_dec) / n * 1e3, 2)}
 

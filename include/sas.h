@@ -280,9 +280,15 @@ sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, void 
  * The caller owns every buffer; NULL -> SAS_ERR_NULL, bad shapes as for
  * sas_pool_keys.  Steps are ordered on the stream; the summary read uses
  * tokens written by earlier steps only.
+ *   csum: the super-block summaries of the hierarchical selection
+ *         (sas_pool_coarse), or NULL when they are not kept; when the
+ *         summary written completes a super-block (its index + 1 a multiple
+ *         of SAS_COARSE_BLOCKS), that super-block's summary is written too,
+ *         with exactly the value sas_pool_coarse gives it.
  */
 sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, const void *v_new,
-                             void *k_cache, void *v_cache, void *ksum, void *stream);
+                             void *k_cache, void *v_cache, void *ksum, void *csum,
+                             void *stream);
 
 /*
  * sas_decode_select -- decode-time selection (review 3-7 steps 1-2; GQA
@@ -310,6 +316,47 @@ sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const v
                              float *scores, int32_t *sel_idx, float *sel_loggate,
                              float *gate_lse, void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/*
+ * Hierarchical (coarse-to-fine) selection (review 7-2: a coarse retrieval
+ * narrows the candidate blocks, then the selector picks its Top-K among
+ * them, so the scan reads far fewer summaries on long contexts).  An
+ * approximation of sas_decode_select, opt-in: it equals sas_decode_select
+ * whenever every super-block is kept.
+ *
+ * A super-block is SAS_COARSE_BLOCKS consecutive history blocks; only
+ * complete super-blocks (all their blocks history) have a summary.
+ *
+ * sas_pool_coarse -- super-block summaries from the block summaries: the
+ * mean of the SAS_COARSE_BLOCKS stored block summaries (their fp32 values,
+ * summed in block order in fp32, divided by SAS_COARSE_BLOCKS), stored in
+ * p->summary_dtype like them.  ksum as written by sas_pool_keys; csum out
+ * in the same tiled layout with cstride = ceil(nblk_stride /
+ * SAS_COARSE_BLOCKS / 64) * 64 super-blocks per row:
+ * [batch][hkv][cstride / 64][head_dim / EPP][64][EPP].
+ */
+#define SAS_COARSE_BLOCKS 8
+sas_status sas_pool_coarse(const sas_decode_problem *p, const void *ksum, void *csum,
+                           void *stream);
+
+/*
+ * sas_decode_select_hier -- per (batch b, kv head g) row: the pooled score
+ * of every super-block summary (the fmaf chain of sas_decode_select); the
+ * coarse_keep best super-blocks (earlier on ties); the candidates are all
+ * blocks of those super-blocks and the trailing history blocks that form no
+ * complete super-block, in block order; then the gate and Top-K of
+ * sas_decode_select over the candidates only (the normaliser gate_lse runs
+ * over the candidates).  Outputs as sas_decode_select; scores are written
+ * for the candidate blocks only.  1 <= coarse_keep <= 127 (SAS_ERR_SHAPE
+ * otherwise).  Three launches (coarse chunks, coarse merge, fine pass).
+ *   workspace: at least sas_decode_select_hier_workspace_size(p, coarse_keep)
+ *   bytes (any contents; calls sharing one must not overlap in time).
+ */
+size_t sas_decode_select_hier_workspace_size(const sas_decode_problem *p, int32_t coarse_keep);
+sas_status sas_decode_select_hier(const sas_decode_problem *p, const void *q, const void *ksum,
+                                  const void *csum, int32_t coarse_keep, float *scores,
+                                  int32_t *sel_idx, float *sel_loggate, float *gate_lse,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sas_decode -- block-sparse decode attention (review 3-7 steps 3-4) for
@@ -356,7 +403,7 @@ const char *sas_last_error(void);
 /* ABI version of this header: bumped on any incompatible change. */
 int32_t sas_abi_version(void);
 
-#define SAS_ABI_VERSION 5
+#define SAS_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

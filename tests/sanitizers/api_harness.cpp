@@ -50,6 +50,14 @@ hipError_t launch_decode_attend(const DecodeParams &, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_decode_select_fine(const DecodeParams &, const HierParams &, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_pool_coarse(const DecodeParams &, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 static float g_scratch_standin[16];
 hipError_t decode_scratch_address(float **out) {
   *out = g_scratch_standin;
@@ -173,7 +181,24 @@ int main() {
   const size_t dws = sas_decode_workspace_size(&d);
   if (dws == 0) { std::printf("FAIL decode workspace size 0\n"); ++g_failures; }
   expect("pool ok", sas_pool_keys(&d, D, D, nullptr), SAS_OK);
-  expect("append ok", sas_decode_append(&d, D, D, D, D, D, nullptr), SAS_OK);
+  expect("append ok", sas_decode_append(&d, D, D, D, D, D, nullptr, nullptr), SAS_OK);
+  expect("append coarse", sas_decode_append(&d, D, D, D, D, D, D, nullptr), SAS_OK);
+  expect("pool coarse", sas_pool_coarse(&d, D, D, nullptr), SAS_OK);
+  expect("pool coarse null", sas_pool_coarse(&d, D, nullptr, nullptr), SAS_ERR_NULL);
+  const size_t hws = sas_decode_select_hier_workspace_size(&d, 4);
+  if (hws == 0) { std::printf("FAIL hier workspace size 0\n"); ++g_failures; }
+  expect("hier ok", sas_decode_select_hier(&d, D, D, D, 4, DF, DI, DF, DF, D, hws, nullptr),
+         SAS_OK);
+  expect("hier ws", sas_decode_select_hier(&d, D, D, D, 4, DF, DI, DF, DF, D, hws - 1, nullptr),
+         SAS_ERR_WORKSPACE);
+  expect("hier keep 0", sas_decode_select_hier(&d, D, D, D, 0, DF, DI, DF, DF, D, hws, nullptr),
+         SAS_ERR_SHAPE);
+  expect("hier keep 128",
+         sas_decode_select_hier(&d, D, D, D, 128, DF, DI, DF, DF, D, hws, nullptr),
+         SAS_ERR_SHAPE);
+  expect("hier null", sas_decode_select_hier(&d, D, D, nullptr, 4, DF, DI, DF, DF, D, hws,
+                                             nullptr),
+         SAS_ERR_NULL);
   const size_t sws = sas_decode_select_workspace_size(&d);
   if (sws == 0) { std::printf("FAIL select workspace size 0\n"); ++g_failures; }
   expect("select ok", sas_decode_select(&d, D, D, DF, DI, DF, DF, D, sws, nullptr), SAS_OK);

@@ -39,7 +39,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sas_abi_version() == sas.ABI_VERSION == 5
+    assert lib.sas_abi_version() == sas.ABI_VERSION == 6
     assert lib.sas_status_string(0) == b"ok"
     assert b"unsupported" in lib.sas_status_string(-5)
 
@@ -159,7 +159,8 @@ def test_decode_page_table_host_checked(lib):
         assert lib.sas_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, *ws,
                               None) == -2
         assert b"page_table" in lib.sas_last_error()
-        assert lib.sas_decode_append(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+        assert lib.sas_decode_append(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                     None) == -2
         assert lib.sas_pool_keys(ctypes.byref(p), FAKE, FAKE, None) == -2
 
 

@@ -70,22 +70,60 @@ __device__ inline uint8_t e4m3_code(float x) {
 //   [row][j / 64][e / EPP][j % 64][e % EPP]
 // so one wave reading piece l of 64 consecutive blocks (a block per lane)
 // reads 1 KB of contiguous memory.
-__device__ inline long summary_index(const DecodeParams &p, int row, int j, int e) {
+__device__ inline long summary_index(const DecodeParams &p, int stride, int row, int j, int e) {
   const int epp = p.sum_kind == kSumBf16 ? 8 : p.sum_kind == kSumFp8 ? 16 : 4;
   const int np = p.D / epp;
-  return (((long)row * (p.nblk_stride / 64) + j / 64) * np + e / epp) * (64 * epp) +
+  return (((long)row * (stride / 64) + j / 64) * np + e / epp) * (64 * epp) +
          (j % 64) * epp + e % epp;
+}
+__device__ inline long summary_index(const DecodeParams &p, int row, int j, int e) {
+  return summary_index(p, p.nblk_stride, row, j, e);
 }
 
 // A block summary (the fp32 mean) stored as fp32, or rounded to the nearest
-// bf16 / fp8 e4m3 value (ties to even).
-__device__ inline void store_summary(const DecodeParams &p, long idx, float v) {
+// bf16 / fp8 e4m3 value (ties to even), into `dst` (block or super-block
+// summaries).
+__device__ inline void store_summary(const DecodeParams &p, void *dst, long idx, float v) {
   if (p.sum_kind == kSumBf16)
-    static_cast<__bf16 *>(p.ksum)[idx] = (__bf16)v;
+    static_cast<__bf16 *>(dst)[idx] = (__bf16)v;
   else if (p.sum_kind == kSumFp8)
-    static_cast<uint8_t *>(p.ksum)[idx] = e4m3_code(v);
+    static_cast<uint8_t *>(dst)[idx] = e4m3_code(v);
   else
-    static_cast<float *>(p.ksum)[idx] = v;
+    static_cast<float *>(dst)[idx] = v;
+}
+__device__ inline void store_summary(const DecodeParams &p, long idx, float v) {
+  store_summary(p, p.ksum, idx, v);
+}
+
+__device__ inline float e4m3_value(uint32_t b);
+
+// The stored block summary at idx as fp32 (exact).
+__device__ inline float load_summary(const DecodeParams &p, long idx) {
+  if (p.sum_kind == kSumBf16) return (float)static_cast<const __bf16 *>(p.ksum)[idx];
+  if (p.sum_kind == kSumFp8) return e4m3_value(static_cast<const uint8_t *>(p.ksum)[idx]);
+  return static_cast<const float *>(p.ksum)[idx];
+}
+
+// Summary of super-block J (hierarchical selection; review 7-2: a coarse
+// retrieval narrows the candidates): the mean of its kCoarseBlocks stored
+// block summaries, summed in block order in fp32, stored like them.
+__device__ inline void store_coarse(const DecodeParams &p, int row, int J, int e) {
+  float acc = 0.f;
+  for (int b = 0; b < kCoarseBlocks; ++b)
+    acc = acc + load_summary(p, summary_index(p, row, kCoarseBlocks * J + b, e));
+  store_summary(p, p.csum, summary_index(p, p.cstride, row, J, e), acc / (float)kCoarseBlocks);
+}
+
+// Super-block summaries of every complete super-block (kCoarseBlocks J +
+// kCoarseBlocks - 1 < the history count): one thread per (super-block,
+// channel).
+__global__ __launch_bounds__(128) void pool_coarse_kernel(DecodeParams p) {
+#pragma clang fp contract(off)
+  const int J = blockIdx.x, row = blockIdx.y;
+  const int e = threadIdx.x;
+  const int nsup = ((p.seqlens[row / p.hkv] - 1) / kBlock) / kCoarseBlocks;
+  if (J >= nsup || e >= p.D) return;
+  store_coarse(p, row, J, e);
 }
 
 // ------------------------------------------------------------------ pool
@@ -129,6 +167,9 @@ __global__ __launch_bounds__(128) void append_kernel(DecodeParams p, const __bf1
     float acc = 0.f;
     for (int t = 0; t < kBlock; ++t) acc = acc + (float)row[(long)t * p.D + e];
     store_summary(p, summary_index(p, bg, j, e), acc / (float)kBlock);
+    // block j completes super-block j / kCoarseBlocks (this thread wrote
+    // the channel's last summary itself, so it reads it back)
+    if (p.csum && (j + 1) % kCoarseBlocks == 0) store_coarse(p, bg, j / kCoarseBlocks, e);
   }
 }
 
@@ -175,7 +216,7 @@ __device__ inline void merge_row(const DecodeParams &p, const SelectParams &sp, 
   constexpr int NWV = NT / kWave;
   const int tid = threadIdx.x;
   const int b = row / p.hkv;
-  const int cur = (p.seqlens[b] - 1) / kBlock;
+  const int cur = ((p.seqlens[b] - 1) / kBlock) / p.coarse_div;  // history count
   const int kh = p.Kb - 1;
   const int ncand = sp.nchunk * kh;
   const int2 *cand = sp.cand + (long)row * ncand;
@@ -296,7 +337,7 @@ __global__ __launch_bounds__(256) void select_kernel(
   const int c = blockIdx.x, row = blockIdx.y;
   const int b = row / p.hkv, g = row % p.hkv;
   const int tid = threadIdx.x;
-  const int nhist = (p.seqlens[b] - 1) / kBlock;
+  const int nhist = ((p.seqlens[b] - 1) / kBlock) / p.coarse_div;  // blocks or super-blocks
   const int kh = p.Kb - 1;
   const int lo = 256 * V * c, n = max(0, min(nhist - lo, 256 * V));  // valid blocks in the chunk
   const int j0 = lo + V * tid;  // this thread's first block
@@ -421,6 +462,158 @@ __global__ __launch_bounds__(NT) void select_merge_kernel(DecodeParams p, Select
   __shared__ SelectScratch sel;
   __shared__ uint64_t runs[R == 1 ? NT : 1];
   merge_row<R, NT>(p, sp, blockIdx.x, red, cnt, sel, runs);
+}
+
+// Hierarchical selection, fine pass (review 7-2): one workgroup per row.
+// The candidates are every block of the row's kept super-blocks (the coarse
+// pass's Top-C, ascending) followed by the trailing history blocks that
+// form no complete super-block -- all in block order, R consecutive
+// candidates per thread (each candidate's summary requested as a whole).  Each candidate's pooled score is the same fixed
+// fp32 order as in select_kernel; the gate normaliser runs over the
+// candidates, and the kept set is their exact Top-K (radix select, earlier
+// block on ties).  Writes the candidates' scores, the kept blocks ascending
+// with log g = s - lse, the current block (log g 0), then -1 padding.
+template <int D, int G, typename TS>
+__global__ __launch_bounds__(512) void select_fine_kernel(DecodeParams p, HierParams h) {
+#pragma clang fp contract(off)
+  constexpr int NT = 512, NWV = NT / kWave, R = 2;
+  constexpr int BB = D * (int)sizeof(TS), NL = BB / 16, EPL = 16 / (int)sizeof(TS);
+  __shared__ __attribute__((aligned(16))) float qbar[D];
+  __shared__ float red[NWV];
+  __shared__ int cnt[NWV];
+  __shared__ SelectScratch sel;
+  __shared__ int ksup[NT * R / kCoarseBlocks];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int b = row / p.hkv, g = row % p.hkv;
+  const int nhist = (p.seqlens[b] - 1) / kBlock;
+  const int nsup = nhist / kCoarseBlocks;
+  const int kc = min(h.C, nsup);
+  const int ncand = kCoarseBlocks * kc + (nhist - kCoarseBlocks * nsup);
+  if (tid < kc) ksup[tid] = h.kept[(long)row * (h.C + 1) + tid];
+  if (tid < D) {
+    const __bf16 *q = static_cast<const __bf16 *>(p.q);
+    float qv[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) qv[hh] = (float)q[((long)b * p.hq + g * G + hh) * D + tid];
+    float acc = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) acc = acc + qv[hh];
+    qbar[tid] = acc / (float)G;
+  }
+  __syncthreads();
+  const char *rbase =
+      static_cast<const char *>(p.ksum) + (long)row * p.nblk_stride * (long)BB;
+  float *out = p.scores + (long)row * p.nblk_stride;
+  float sv[R];
+  int jv[R];
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int c = 0; c < R; ++c) {
+    const int x = R * tid + c;
+    sv[c] = -INFINITY;
+    jv[c] = -1;
+    if (x >= ncand) continue;
+    const int j = x < kCoarseBlocks * kc
+                      ? kCoarseBlocks * ksup[x / kCoarseBlocks] + x % kCoarseBlocks
+                      : kCoarseBlocks * nsup + (x - kCoarseBlocks * kc);
+    jv[c] = j;
+    valid |= 1u << c;
+    const unsigned off = (unsigned)(j / 64) * (unsigned)(NL * 1024) + 16u * (unsigned)(j % 64);
+    u32x4 w[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
+      w[l] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4 *>(rbase + (off + 1024u * (unsigned)l)));
+    float a = 0.f;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+#pragma unroll
+      for (int k4 = 0; k4 < EPL; k4 += 4) {
+        const float4 qe = *reinterpret_cast<const float4 *>(&qbar[l * EPL + k4]);
+        a = fmaf(qe.x, summary_elem<TS>(w[l], k4 + 0), a);
+        a = fmaf(qe.y, summary_elem<TS>(w[l], k4 + 1), a);
+        a = fmaf(qe.z, summary_elem<TS>(w[l], k4 + 2), a);
+        a = fmaf(qe.w, summary_elem<TS>(w[l], k4 + 3), a);
+      }
+    }
+    sv[c] = a / p.sqrt_d;
+    out[j] = sv[c];
+  }
+  // the normaliser over the candidates
+  float mx = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < R; ++c) mx = fmaxf(mx, sv[c]);
+  mx = block_max<NWV>(mx, red);
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int c = 0; c < R; ++c)
+      if ((valid >> c) & 1u) sum += expf(sv[c] - mx);
+  }
+  sum = block_sum<NWV>(sum, red);
+  const float lse = (ncand == 0 || mx == -INFINITY) ? -INFINITY : mx + logf(sum);
+  const int k = min(p.Kb - 1, ncand);
+  const bool keep_all = k == ncand;
+  Threshold th{0u, 0u, k};
+  if (!keep_all && k > 0)
+    th = radix_threshold<NT>(k, sel, [&](auto &&f) {
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+        if ((valid >> c) & 1u) f(order_key(sv[c]));
+    });
+  int32_t *oidx = h.sel_idx + (long)row * p.Kb;
+  float *olg = h.sel_lg + (long)row * p.Kb;
+  if (k > 0) {
+    int pos, total;
+    const uint32_t takem = kept_mask<R, NWV>(sv, valid, keep_all, th, cnt, pos, total);
+#pragma unroll
+    for (int c = 0; c < R; ++c)
+      if ((takem >> c) & 1u) {
+        oidx[pos] = jv[c];
+        olg[pos] = lse == -INFINITY ? -INFINITY : sv[c] - lse;
+        ++pos;
+      }
+  }
+  if (tid == 0) {
+    oidx[k] = nhist;  // the current block
+    olg[k] = 0.f;
+    h.gate_lse[row] = lse;
+  }
+  for (int x = k + 1 + tid; x < p.Kb; x += NT) {
+    oidx[x] = -1;
+    olg[x] = -INFINITY;
+  }
+}
+
+template <int D, typename TS>
+static void launch_fine_g(const DecodeParams &p, const HierParams &h, hipStream_t stream) {
+  const dim3 grid(p.batch * p.hkv);
+  switch (p.hq / p.hkv) {
+    case 1: hipLaunchKernelGGL((select_fine_kernel<D, 1, TS>), grid, dim3(512), 0, stream, p, h); break;
+    case 2: hipLaunchKernelGGL((select_fine_kernel<D, 2, TS>), grid, dim3(512), 0, stream, p, h); break;
+    case 4: hipLaunchKernelGGL((select_fine_kernel<D, 4, TS>), grid, dim3(512), 0, stream, p, h); break;
+    default: hipLaunchKernelGGL((select_fine_kernel<D, 8, TS>), grid, dim3(512), 0, stream, p, h); break;
+  }
+}
+
+hipError_t launch_decode_select_fine(const DecodeParams &p, const HierParams &h,
+                                     hipStream_t stream) {
+  if (p.D == 128) {
+    if (p.sum_kind == kSumBf16) launch_fine_g<128, __bf16>(p, h, stream);
+    else if (p.sum_kind == kSumFp8) launch_fine_g<128, uint8_t>(p, h, stream);
+    else launch_fine_g<128, float>(p, h, stream);
+  } else {
+    if (p.sum_kind == kSumBf16) launch_fine_g<64, __bf16>(p, h, stream);
+    else if (p.sum_kind == kSumFp8) launch_fine_g<64, uint8_t>(p, h, stream);
+    else launch_fine_g<64, float>(p, h, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_coarse(const DecodeParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL(pool_coarse_kernel, dim3(p.cstride, p.batch * p.hkv), dim3(128), 0, stream,
+                     p);
+  return hipGetLastError();
 }
 
 template <int D, int G, int V, typename TS>

@@ -491,6 +491,11 @@ void decode_split(const sas_decode_problem *p, int cu_count, int *nsplit_out,
   *nsplit_out = (p->budget_blocks + per_split - 1) / per_split;
 }
 
+// super-block summaries per row: nblk_stride / 8 rounded up to whole tiles
+int coarse_stride(const sas_decode_problem *p) {
+  return (p->nblk_stride / sas::kCoarseBlocks + 63) / 64 * 64;
+}
+
 sas::DecodeParams decode_params(const sas_decode_problem *p) {
   sas::DecodeParams d{};
   d.seqlens = p->seqlens;
@@ -511,6 +516,8 @@ sas::DecodeParams decode_params(const sas_decode_problem *p) {
   d.scale_log2 = p->scale * 1.4426950408889634f;
   d.out_bf16 = p->out_dtype == SAS_BF16;
   decode_split(p, p->num_splits ? 0 : device_cu_count(), &d.nsplit, &d.per_split);
+  d.coarse_div = 1;
+  d.cstride = coarse_stride(p);
   return d;
 }
 
@@ -540,16 +547,20 @@ int summary_bytes(const sas_decode_problem *p) {
   return p->summary_dtype == SAS_SUMMARY_F32 ? 4 : p->summary_dtype == SAS_SUMMARY_BF16 ? 2 : 1;
 }
 
-SelectGeom select_geom(const sas_decode_problem *p) {
+// div = 1: blocks; div = kCoarseBlocks: super-blocks (kh = kept per row)
+SelectGeom select_geom(const sas_decode_problem *p, int div = 1, int kh = 0) {
   int maxhist = 1;
-  for (int b = 0; b < p->batch; ++b)
-    if ((p->seqlens_host[b] - 1) / 64 > maxhist) maxhist = (p->seqlens_host[b] - 1) / 64;
-  const int kh = p->budget_blocks > 1 ? p->budget_blocks - 1 : 1;
+  for (int b = 0; b < p->batch; ++b) {
+    const int n = ((p->seqlens_host[b] - 1) / 64) / div;
+    if (n > maxhist) maxhist = n;
+  }
+  if (kh <= 0) kh = p->budget_blocks > 1 ? p->budget_blocks - 1 : 1;
   auto chunks = [&](int v) { return (maxhist + 256 * v - 1) / (256 * v); };
   int v = 1;
   while (v < 8 && chunks(v) * kh > 4096) v *= 2;
   return {v, chunks(v)};
 }
+
 
 constexpr int kMaxSelectCandidates = 4096;
 
@@ -583,14 +594,30 @@ sas_status sas_pool_keys(const sas_decode_problem *p, const void *k_cache, void 
   return from_hip(sas::launch_pool_keys(d, (hipStream_t)stream), "pool_keys launch");
 }
 
+sas_status sas_pool_coarse(const sas_decode_problem *p, const void *ksum, void *csum,
+                           void *stream) {
+  sas_status st = check_decode(p);
+  if (st) return st;
+  REQUIRE(ksum && csum, SAS_ERR_NULL, "ksum / csum is NULL");
+  REQUIRE(aligned16(ksum) && aligned16(csum), SAS_ERR_ALIGN,
+          "ksum and csum must be 16-byte aligned");
+  sas::DecodeParams d = decode_params(p);
+  d.ksum = const_cast<void *>(ksum);
+  d.csum = csum;
+  return from_hip(sas::launch_pool_coarse(d, (hipStream_t)stream), "pool_coarse launch");
+}
+
 sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, const void *v_new,
-                             void *k_cache, void *v_cache, void *ksum, void *stream) {
+                             void *k_cache, void *v_cache, void *ksum, void *csum,
+                             void *stream) {
   sas_status st = check_decode(p);
   if (st) return st;
   REQUIRE(k_new && v_new && k_cache && v_cache && ksum, SAS_ERR_NULL,
           "a tensor argument of sas_decode_append is NULL");
+  REQUIRE(!csum || aligned16(csum), SAS_ERR_ALIGN, "csum must be 16-byte aligned");
   sas::DecodeParams d = decode_params(p);
   d.ksum = ksum;
+  d.csum = csum;
   return from_hip(sas::launch_decode_append(d, k_new, v_new, k_cache, v_cache,
                                             (hipStream_t)stream),
                   "decode_append launch");
@@ -628,6 +655,91 @@ sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const v
   s.cand = reinterpret_cast<int2 *>(ws);
   s.part = reinterpret_cast<float2 *>(ws + align256(n * (p->budget_blocks - 1) * sizeof(int2)));
   return from_hip(sas::launch_decode_select(d, s, (hipStream_t)stream), "decode select launch");
+}
+
+namespace {
+
+constexpr int kMaxCoarseKeep = 127;  // 8 C + 7 candidates <= 1024 in the fine pass
+
+// [rows][nchunk][C] coarse candidates | [rows][nchunk] (max, sum) |
+// [rows][C + 1] kept super-blocks | [rows][C + 1] their log gates (unused) |
+// [rows] coarse lse (unused) | [rows][cstride] coarse scores
+struct HierLayout {
+  size_t cand, part, kept, kept_lg, kept_lse, cscores, total;
+};
+
+HierLayout hier_layout(const sas_decode_problem *p, const SelectGeom &sg, int C) {
+  const size_t rows = (size_t)p->batch * p->hkv, n = rows * sg.nchunk;
+  HierLayout l{};
+  l.cand = 0;
+  l.part = l.cand + align256(n * C * sizeof(int2));
+  l.kept = l.part + align256(n * sizeof(float2));
+  l.kept_lg = l.kept + align256(rows * (C + 1) * sizeof(int32_t));
+  l.kept_lse = l.kept_lg + align256(rows * (C + 1) * sizeof(float));
+  l.cscores = l.kept_lse + align256(rows * sizeof(float));
+  l.total = l.cscores + rows * coarse_stride(p) * sizeof(float);
+  return l;
+}
+
+}  // namespace
+
+size_t sas_decode_select_hier_workspace_size(const sas_decode_problem *p, int32_t coarse_keep) {
+  if (check_decode(p) != SAS_OK || coarse_keep < 1 || coarse_keep > kMaxCoarseKeep) return 0;
+  return hier_layout(p, select_geom(p, sas::kCoarseBlocks, coarse_keep), coarse_keep).total;
+}
+
+sas_status sas_decode_select_hier(const sas_decode_problem *p, const void *q, const void *ksum,
+                                  const void *csum, int32_t coarse_keep, float *scores,
+                                  int32_t *sel_idx, float *sel_loggate, float *gate_lse,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  sas_status st = check_decode(p);
+  if (st) return st;
+  REQUIRE(q && ksum && csum && scores && sel_idx && sel_loggate && gate_lse, SAS_ERR_NULL,
+          "a tensor argument of sas_decode_select_hier is NULL");
+  REQUIRE(coarse_keep >= 1 && coarse_keep <= kMaxCoarseKeep, SAS_ERR_SHAPE,
+          "coarse_keep (%d) must be in [1, %d]", coarse_keep, kMaxCoarseKeep);
+  REQUIRE(aligned16(ksum) && aligned16(csum), SAS_ERR_ALIGN,
+          "ksum and csum must be 16-byte aligned");
+  const SelectGeom sg = select_geom(p, sas::kCoarseBlocks, coarse_keep);
+  REQUIRE(sg.nchunk * coarse_keep <= kMaxSelectCandidates, SAS_ERR_UNSUPPORTED,
+          "history of %d super-block chunks x %d kept exceeds the selection's %d candidates",
+          sg.nchunk, coarse_keep, kMaxSelectCandidates);
+  const HierLayout l = hier_layout(p, sg, coarse_keep);
+  REQUIRE(workspace && workspace_bytes >= l.total, SAS_ERR_WORKSPACE,
+          "workspace has %zu bytes, needs %zu", workspace ? workspace_bytes : 0, l.total);
+  REQUIRE(aligned16(workspace), SAS_ERR_ALIGN, "workspace must be 16-byte aligned");
+  char *ws = static_cast<char *>(workspace);
+  // coarse pass: the chunked selection over super-blocks, coarse_keep kept per row
+  sas::DecodeParams c = decode_params(p);
+  c.q = q;
+  c.ksum = const_cast<void *>(csum);
+  c.nblk_stride = c.cstride;
+  c.scores = reinterpret_cast<float *>(ws + l.cscores);
+  c.Kb = coarse_keep + 1;
+  c.coarse_div = sas::kCoarseBlocks;
+  sas::SelectParams s{};
+  s.nchunk = sg.nchunk;
+  s.chunk_v = sg.v;
+  s.sel_idx = reinterpret_cast<int32_t *>(ws + l.kept);
+  s.sel_lg = reinterpret_cast<float *>(ws + l.kept_lg);
+  s.gate_lse = reinterpret_cast<float *>(ws + l.kept_lse);
+  s.cand = reinterpret_cast<int2 *>(ws + l.cand);
+  s.part = reinterpret_cast<float2 *>(ws + l.part);
+  st = from_hip(sas::launch_decode_select(c, s, (hipStream_t)stream), "coarse select launch");
+  if (st) return st;
+  // fine pass over the candidate blocks
+  sas::DecodeParams d = decode_params(p);
+  d.q = q;
+  d.ksum = const_cast<void *>(ksum);
+  d.scores = scores;
+  sas::HierParams h{};
+  h.C = coarse_keep;
+  h.kept = s.sel_idx;
+  h.sel_idx = sel_idx;
+  h.sel_lg = sel_loggate;
+  h.gate_lse = gate_lse;
+  return from_hip(sas::launch_decode_select_fine(d, h, (hipStream_t)stream),
+                  "fine select launch");
 }
 
 sas_status sas_decode(const sas_decode_problem *p, const void *q, const void *k_cache,

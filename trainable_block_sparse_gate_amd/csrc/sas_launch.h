@@ -104,7 +104,13 @@ struct DecodeParams {
   int out_bf16;
   int nsplit, per_split;       // split-K geometry
   float *partial;              // [batch*hkv][nsplit][G][D + 2]
+  // hierarchical selection: super-block summaries (the tiled layout with
+  // cstride super-blocks per row), NULL when not kept; coarse_div = 8 when
+  // the selection kernels run over super-blocks, else 1
+  void *csum;
+  int cstride, coarse_div;
 };
+constexpr int kCoarseBlocks = 8;  // history blocks per super-block
 // decode selection (pooled scores -> gate + Top-K) over chunks of each row:
 // scores and an exact local Top-K per chunk, then a merge per row
 struct SelectParams {
@@ -118,6 +124,18 @@ struct SelectParams {
 constexpr int kSumF32 = 0, kSumBf16 = 1, kSumFp8 = 2;
 hipError_t launch_decode_select(const DecodeParams &p, const SelectParams &s,
                                 hipStream_t stream);
+// hierarchical selection: the coarse pass (launch_decode_select over the
+// super-block summaries, C kept per row into `kept`) and the fine pass
+struct HierParams {
+  int C;                       // super-blocks kept per row
+  const int32_t *kept;         // [batch*hkv][C + 1]: kept super-blocks ascending
+  int32_t *sel_idx;            // out [batch*hkv][Kb]
+  float *sel_lg;               // out [batch*hkv][Kb]
+  float *gate_lse;             // out [batch*hkv]
+};
+hipError_t launch_decode_select_fine(const DecodeParams &p, const HierParams &h,
+                                     hipStream_t stream);
+hipError_t launch_pool_coarse(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_pool_keys(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_append(const DecodeParams &p, const void *k_new, const void *v_new,
                                void *k_cache, void *v_cache, hipStream_t stream);

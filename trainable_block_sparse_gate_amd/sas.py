@@ -23,7 +23,7 @@ GATE_INNER, GATE_OUTER = 0, 1  # gate position
 KV_CONTIGUOUS, KV_PAGED = 0, 1
 SUMMARY_F32, SUMMARY_BF16, SUMMARY_FP8 = 0, 1, 2
 BLOCK = 64
-ABI_VERSION = 5  # the header's SAS_ABI_VERSION these structs follow
+ABI_VERSION = 6  # the header's SAS_ABI_VERSION these structs follow
 
 STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTYPE",
           -4: "SAS_ERR_ALIGN", -5: "SAS_ERR_UNSUPPORTED", -6: "SAS_ERR_WORKSPACE",
@@ -33,7 +33,8 @@ STATUS = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_DTY
 EXPORTS = ["sas_gate_topk", "sas_fwd", "sas_bwd_workspace_size", "sas_bwd", "sas_bwd_prepare",
            "sas_bwd_dq", "sas_bwd_dkdv", "sas_gate_bwd",
            "sas_pool_keys", "sas_decode_append", "sas_decode_select_workspace_size",
-           "sas_decode_select", "sas_decode_workspace_size",
+           "sas_decode_select", "sas_pool_coarse", "sas_decode_select_hier_workspace_size",
+           "sas_decode_select_hier", "sas_decode_workspace_size",
            "sas_decode", "sas_decode_noalloc",
            "sas_status_string", "sas_last_error", "sas_abi_version"]
 
@@ -96,7 +97,10 @@ def lib():
             "sas_bwd_dkdv": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "sas_gate_bwd": [P, vp, i64, i32, vp, vp, vp, vp, vp],
             "sas_pool_keys": [DP, vp, vp, vp],
-            "sas_decode_append": [DP, vp, vp, vp, vp, vp, vp],
+            "sas_decode_append": [DP, vp, vp, vp, vp, vp, vp, vp],
+            "sas_pool_coarse": [DP, vp, vp, vp],
+            "sas_decode_select_hier_workspace_size": [DP, i32],
+            "sas_decode_select_hier": [DP, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "sas_decode_select_workspace_size": [DP],
             "sas_decode_select": [DP, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "sas_decode_workspace_size": [DP],
@@ -113,6 +117,7 @@ def lib():
         L.sas_bwd_workspace_size.restype = sz
         L.sas_decode_workspace_size.restype = sz
         L.sas_decode_select_workspace_size.restype = sz
+        L.sas_decode_select_hier_workspace_size.restype = sz
         L.sas_status_string.restype = ctypes.c_char_p
         L.sas_last_error.restype = ctypes.c_char_p
         if L.sas_abi_version() != ABI_VERSION:
@@ -403,6 +408,16 @@ class Decode:
         epp = 16 // {"f32": 4, "bf16": 2, "fp8": 1}[self.summary_dtype]
         return (self.batch, self.hkv, self.nblk_stride // 64, self.d // epp, 64, epp)
 
+    def coarse_shape(self):
+        """Super-block summaries: the tiled layout with cstride super-blocks
+        per row (nblk_stride / 8 rounded up to whole 64-entry tiles)."""
+        epp = 16 // {"f32": 4, "bf16": 2, "fp8": 1}[self.summary_dtype]
+        cstride = -(-(self.nblk_stride // COARSE_BLOCKS) // 64) * 64
+        return (self.batch, self.hkv, cstride // 64, self.d // epp, 64, epp)
+
+    def check_coarse(self, csum):
+        _need(csum, "csum", _torch_dtype(self.summary_dtype), self.coarse_shape())
+
     def check_summaries(self, ksum):
         _need(ksum, "ksum", _torch_dtype(self.summary_dtype), self.summary_shape())
 
@@ -436,18 +451,70 @@ def summaries_by_block(ksum):
     return ksum.permute(0, 1, 2, 4, 3, 5).reshape(B, hkv, nt * bt, npc * epp)
 
 
-def decode_append(prob: Decode, k_new, v_new, k_cache, v_cache, ksum):
+def decode_append(prob: Decode, k_new, v_new, k_cache, v_cache, ksum, csum=None):
     """sas_decode_append: write the new token (prob.seqlens count it) into
-    the caches and, when it opens a block, the finished block's summary."""
+    the caches and, when it opens a block, the finished block's summary (and,
+    with csum, the summary of a super-block that block completes)."""
     import torch
     _need(k_new, "k_new", torch.bfloat16, (prob.batch, prob.hkv, prob.d))
     _need(v_new, "v_new", torch.bfloat16, (prob.batch, prob.hkv, prob.d))
     prob.check_cache(k_cache, "k_cache")
     prob.check_cache(v_cache, "v_cache")
     prob.check_summaries(ksum)
-    _gpu(k_new, v_new, k_cache, v_cache, ksum)
+    if csum is not None:
+        prob.check_coarse(csum)
+    _gpu(k_new, v_new, k_cache, v_cache, ksum, csum)
     _check(lib().sas_decode_append(prob.ref, _ptr(k_new), _ptr(v_new), _ptr(k_cache),
-                                   _ptr(v_cache), _ptr(ksum), _stream()))
+                                   _ptr(v_cache), _ptr(ksum), _ptr(csum), _stream()))
+
+
+COARSE_BLOCKS = 8  # the header's SAS_COARSE_BLOCKS
+
+
+def pool_coarse(prob: Decode, ksum):
+    """sas_pool_coarse -> super-block summaries (the tiled layout)."""
+    import torch
+    prob.check_summaries(ksum)
+    csum = torch.empty(prob.coarse_shape(), dtype=_torch_dtype(prob.summary_dtype),
+                       device=ksum.device)
+    _gpu(ksum, csum)
+    _check(lib().sas_pool_coarse(prob.ref, _ptr(ksum), _ptr(csum), _stream()))
+    return csum
+
+
+def decode_select_hier_workspace_bytes(prob: Decode, coarse_keep):
+    return int(lib().sas_decode_select_hier_workspace_size(prob.ref, int(coarse_keep)))
+
+
+def decode_select_hier(prob: Decode, q, ksum, csum, coarse_keep, out=None, workspace=None):
+    """sas_decode_select_hier -> (sel_idx, sel_loggate, gate_lse, scores);
+    scores are written for the candidate blocks only."""
+    import torch
+    prob.check_q(q)
+    prob.check_summaries(ksum)
+    prob.check_coarse(csum)
+    dev = q.device
+    rows = prob.batch * prob.hkv
+    if out is None:
+        out = (torch.empty((rows, prob.Kb), dtype=torch.int32, device=dev),
+               torch.empty((rows, prob.Kb), dtype=torch.float32, device=dev),
+               torch.empty((rows,), dtype=torch.float32, device=dev),
+               torch.empty((prob.batch, prob.hkv, prob.nblk_stride), dtype=torch.float32,
+                           device=dev))
+    sel, lg, lse, scores = out
+    prob.check_selection(sel, lg)
+    _need(lse, "gate_lse", torch.float32, (rows,))
+    _need(scores, "scores", torch.float32, (prob.batch, prob.hkv, prob.nblk_stride))
+    if workspace is None:
+        workspace = torch.empty(max(decode_select_hier_workspace_bytes(prob, coarse_keep), 1),
+                                dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, (None,))
+    _gpu(q, ksum, csum, sel, lg, lse, scores, workspace)
+    _check(lib().sas_decode_select_hier(prob.ref, _ptr(q), _ptr(ksum), _ptr(csum),
+                                        int(coarse_keep), _ptr(scores), _ptr(sel), _ptr(lg),
+                                        _ptr(lse), _ptr(workspace), workspace.numel(),
+                                        _stream()))
+    return sel, lg, lse, scores
 
 
 def decode_select_workspace_bytes(prob: Decode):

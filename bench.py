@@ -81,16 +81,28 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CALIBRATION_BYTES = 1 << 30
 
 
+def _code_only(text, python=False):
+    """Source text without comments and whitespace, so that edits to
+    comments alone leave the hash unchanged."""
+    if python:
+        text = re.sub(r"(?m)^\s*#.*$", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def source_hash():
-    """Hash of everything the library is built from (kernels, headers, build)."""
+    """Hash of the code the library is built from (kernels, headers, build),
+    comments and whitespace left out."""
     pkg = os.path.join(ROOT, "trainable_block_sparse_gate_amd")
     files = sorted(glob.glob(os.path.join(pkg, "csrc", "*")) +
                    [os.path.join(pkg, "build.py"), os.path.join(ROOT, "include", "sas.h")])
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read(), python=f.endswith(".py")).encode())
     return h.hexdigest()[:16]
 
 

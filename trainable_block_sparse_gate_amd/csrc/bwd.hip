@@ -119,6 +119,11 @@ __global__ __launch_bounds__(kScanThreads) void bwd_seg_scan_kernel(BwdParams p)
 // array may be in flight during an MFMA step, as in the dK/dV kernel; the
 // full-size parity tests cover that overlap.
 constexpr int kDqQT = 1;  // 32-query tiles per wave (1: two waves per head)
+// floats per (wave, tile) record of per-row sums: 32 QT rows and one of
+// padding, so the lanes reading one row of consecutive tiles hit distinct
+// LDS banks (an unpadded stride of 32 floats put every other lane on the
+// same bank)
+constexpr int kDqRec = 32 * kDqQT + 1;
 
 // OUTER: the gate-position ablation.  P comes from the ungated logits,
 // dP is scaled by the tile's gate, and the tile's d log g is the sum of
@@ -145,10 +150,10 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
   __shared__ int s_j[kMaxBudget];
   __shared__ float s_lg[kMaxBudget];     // log gate * log2(e)
   __shared__ int s_n;
-  // [2][NWV][Kb][32 QT]: per tile and query row, the sums over the tile's
+  // [2][NWV][Kb][kDqRec]: per tile and query row, the sums over the tile's
   // keys of P (s_G) and of P dP (s_Fq)
   extern __shared__ float s_G[];
-  float *s_Fq = s_G + NWV * p.Kb * 32 * QT;
+  float *s_Fq = s_G + NWV * p.Kb * kDqRec;
 
   const T *q = static_cast<const T *>(p.q);
   const T *kk = static_cast<const T *>(p.k);
@@ -430,8 +435,8 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
         const float fsum = Fp[nt] + __shfl_xor(Fp[nt], 32);
         const float gsum = Gp[nt] + __shfl_xor(Gp[nt], 32);
         if (hf == 0) {
-          s_Fq[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = fsum;
-          s_G[(wave * p.Kb + it) * (32 * QT) + 32 * nt + l32] = gsum;
+          s_Fq[(wave * p.Kb + it) * kDqRec + 32 * nt + l32] = fsum;
+          s_G[(wave * p.Kb + it) * kDqRec + 32 * nt + l32] = gsum;
         }
         Fp[nt] = Gp[nt] = 0.f;
       }
@@ -507,7 +512,7 @@ __global__ __launch_bounds__(NW * (2 / kDqQT) * 64) void bwd_dq_kernel(BwdParams
       for (int q = 0; q < 32; ++q) {
         const float e = lane_value(Ex[nt], q);
         if (t < ntiles) {
-          const int at = (wave * p.Kb + t) * (32 * QT) + 32 * nt + q;
+          const int at = (wave * p.Kb + t) * kDqRec + 32 * nt + q;
           val += s_Fq[at] - e * s_G[at];
         }
       }
@@ -587,7 +592,7 @@ constexpr int dq_static_lds() {
 
 template <typename T, int D, int NW>
 static size_t dq_dynamic_lds(const BwdParams &p) {
-  return 2 * sizeof(float) * NW * p.Kb * kBlock;  // s_G, s_Fq: NW (2/QT) waves x 32 QT rows
+  return 2 * sizeof(float) * NW * (2 / kDqQT) * p.Kb * kDqRec;  // s_G, s_Fq
 }
 
 template <typename T, typename TO, int D, int NW>

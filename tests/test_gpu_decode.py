@@ -140,7 +140,19 @@ def test_fp8_summary_codes_for_every_rounding_case():
     assert torch.equal(got[~nan], ref[~nan]), (want[~nan.numpy()][(got != ref)[~nan].numpy()])
     assert np.array_equal(summaries_f32(ksum)[0, 0, :nblk, 0][~nan.numpy()],
                           oracle.round_e4m3(want)[~nan.numpy()])
-    say(f"  {nblk} summaries: codes equal torch's conversion")
+    # the selection decodes every code to the same value: pooled scores of
+    # these summaries equal the oracle's bit for bit (NaN summaries: NaN)
+    qh = wl.round_bf16(wl.normal(g, (1, hq, d)))
+    q = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).cuda()
+    scores = sas.decode_select(prob, q, ksum)[3]
+    torch.cuda.synchronize()
+    kbar = np.repeat(oracle.round_e4m3(want)[:, None], d, axis=1)
+    rs = oracle.decode_scores_row(wl.bf16_bits_to_f32(qh)[0], kbar)
+    gs = scores[0, 0, :nblk].cpu().numpy()
+    fin = ~np.isnan(rs)
+    assert np.array_equal(np.isnan(gs), ~fin)
+    assert np.array_equal(gs[fin].view(np.uint32), rs[fin].view(np.uint32))
+    say(f"  {nblk} summaries: codes equal torch's conversion, scores equal the oracle's")
 
 
 def test_paged_equals_contiguous_bitwise():

@@ -190,17 +190,40 @@ __device__ inline float e4m3_value(uint32_t b) {
   return __uint_as_float(v ^ ((v ^ 0x7fc00000u) & (0u - nan)));
 }
 
-// Element k of a 16-byte piece of summaries, as fp32 (bf16 widened, fp8
-// decoded; exact in every case).
+// The EPL values of a 16-byte piece of summaries, as fp32 (bf16 widened,
+// fp8 decoded; exact in every case).  fp8 goes through the hardware
+// conversion of code pairs, which decodes gfx950's e4m3 (bias 7, no
+// infinities) to the same fp32 value as e4m3_value for every non-NaN code
+// (checked for all 256 codes on the device); it returns a negative NaN for
+// the two NaN codes, which are mapped to the positive quiet NaN e4m3_value
+// gives them.
 template <typename TS>
-__device__ inline float summary_elem(const u32x4 &w, int k) {
+__device__ inline void piece_values(const u32x4 &w, float (&out)[16 / sizeof(TS)]) {
   if constexpr (sizeof(TS) == 4) {
-    return __uint_as_float(w[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = __uint_as_float(w[k]);
   } else if constexpr (sizeof(TS) == 2) {
-    const uint32_t x = w[k / 2];
-    return __uint_as_float((k % 2) ? (x & 0xffff0000u) : (x << 16));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[2 * k] = __uint_as_float(w[k] << 16);
+      out[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
   } else {
-    return e4m3_value((w[k / 4] >> (8 * (k % 4))) & 0xffu);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+      const float v[4] = {lo[0], lo[1], hi[0], hi[1]};
+      // bit 7 of byte e set exactly when code e has its low seven bits all
+      // ones (NaN); that bit moved to the sign flips the NaN to positive
+      // (integer arithmetic: a comparison per value would leave a lane mask
+      // per value in scalar registers)
+      const uint32_t nan = ((w[k] & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[4 * k + e] = __uint_as_float(__float_as_uint(v[e]) ^ ((nan << (24 - 8 * e)) & 0x80000000u));
+    }
   }
 }
 
@@ -390,13 +413,15 @@ __global__ __launch_bounds__(256) void select_kernel(
       float a = 0.f;
 #pragma unroll
       for (int l = 0; l < NL; ++l) {
+        float x[EPL];
+        piece_values<TS>(w[l], x);
 #pragma unroll
         for (int k4 = 0; k4 < EPL; k4 += 4) {
           const float4 qe = *reinterpret_cast<const float4 *>(&qbar[l * EPL + k4]);
-          a = fmaf(qe.x, summary_elem<TS>(w[l], k4 + 0), a);
-          a = fmaf(qe.y, summary_elem<TS>(w[l], k4 + 1), a);
-          a = fmaf(qe.z, summary_elem<TS>(w[l], k4 + 2), a);
-          a = fmaf(qe.w, summary_elem<TS>(w[l], k4 + 3), a);
+          a = fmaf(qe.x, x[k4 + 0], a);
+          a = fmaf(qe.y, x[k4 + 1], a);
+          a = fmaf(qe.z, x[k4 + 2], a);
+          a = fmaf(qe.w, x[k4 + 3], a);
         }
       }
       if ((valid >> v) & 1u) {
@@ -527,13 +552,15 @@ __global__ __launch_bounds__(512) void select_fine_kernel(DecodeParams p, HierPa
     float a = 0.f;
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
+      float x[EPL];
+      piece_values<TS>(w[l], x);
 #pragma unroll
       for (int k4 = 0; k4 < EPL; k4 += 4) {
         const float4 qe = *reinterpret_cast<const float4 *>(&qbar[l * EPL + k4]);
-        a = fmaf(qe.x, summary_elem<TS>(w[l], k4 + 0), a);
-        a = fmaf(qe.y, summary_elem<TS>(w[l], k4 + 1), a);
-        a = fmaf(qe.z, summary_elem<TS>(w[l], k4 + 2), a);
-        a = fmaf(qe.w, summary_elem<TS>(w[l], k4 + 3), a);
+        a = fmaf(qe.x, x[k4 + 0], a);
+        a = fmaf(qe.y, x[k4 + 1], a);
+        a = fmaf(qe.z, x[k4 + 2], a);
+        a = fmaf(qe.w, x[k4 + 3], a);
       }
     }
     sv[c] = a / p.sqrt_d;

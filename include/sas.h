@@ -306,7 +306,8 @@ sas_status sas_decode_append(const sas_decode_problem *p, const void *k_new, con
  * the result is the whole row's Top-K.
  *   workspace: at least sas_decode_select_workspace_size(p) bytes (any
  *   contents; calls that share a workspace must not overlap in time).
- * A row's history is split into chunks of 256 to 2048 blocks; more than
+ * A row's history is split into chunks of 256 to 2048 blocks (512 for a
+ * many-row batch with bf16 or fp8 summaries); more than
  * 4096 candidates in the merge (chunks x (Kb - 1)) returns
  * SAS_ERR_UNSUPPORTED (at Kb = 32: histories beyond 270,336 blocks, 17M
  * tokens).

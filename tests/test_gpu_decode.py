@@ -24,9 +24,9 @@ CASES = {
     "g1_d128": ([500, 129], 2, 2, 128, 3),
     # several chunks of 256 blocks per row: 6 x 63 candidates in the merge
     "chunks_g4_d128": ([64 * 1500 + 10, 64 * 700 + 1, 90], 8, 2, 128, 64),
-    # 17 chunks x 63 = 1071 candidates: the merge takes 4 per thread
+    # 17 chunks x 63 = 1071 candidates: the merge takes 8 per thread
     "wide_merge_g2_d64": ([64 * 4300 + 7, 64 * 300 + 3], 2, 1, 64, 64),
-    # 17 chunks x 127 = 2159 candidates: the merge takes 8 per thread
+    # 17 chunks x 127 = 2159 candidates: the merge takes 16 per thread
     "widest_merge_g2_d64": ([64 * 4300 + 7, 64 * 300 + 3], 2, 1, 64, 128),
 }
 

@@ -218,7 +218,8 @@ def decode_rows_check(spec, t, prob, out_rows):
         for g in range(spec.hkv):
             K = bits_f32(wl.gather_row_cache(kb, t["page_table"], b, g, L))
             qg = q_h[b, g * G:(g + 1) * G]
-            ridx, rlg, rlse, rs = oracle.decode_select_row(qg, K, spec.budget_blocks)
+            ridx, rlg, rlse, rs = oracle.decode_select_row(qg, K, spec.budget_blocks,
+                                                           summary=prob.summary_dtype)
             r = b * spec.hkv + g
             assert np.array_equal(sc_h[b, g, :cur], rs), (b, g, "pooled scores")
             assert np.array_equal(sel_h[r], ridx), (b, g, "selection")
@@ -265,5 +266,23 @@ def test_decode_paged_full_size():
                       spec.max_len, page_table=t["page_table"], num_pages=t["k"].shape[0])
     every = {(b, g) for b in range(spec.batch) for g in range(spec.hkv)}
     decode_rows_check(spec, t, prob, every)
+    del t
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("summary", ["bf16", "fp8"])
+def test_decode_paged_full_size_reduced_summaries(summary):
+    """The paged batch with bf16 / fp8 block summaries (its selection runs in
+    512-thread chunks): every row's scores, selection and log gates against
+    the oracle's reading of the rounded summaries, the output of 32 rows."""
+    import torch
+    spec = wl.paged_spec()
+    say(f"[full {spec.name} summaries {summary}]")
+    t = wl.draw_decode_device(spec)
+    prob = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, True,
+                      spec.max_len, page_table=t["page_table"], num_pages=t["k"].shape[0],
+                      summary_dtype=summary)
+    some = {(b, b % spec.hkv) for b in range(spec.batch)}
+    decode_rows_check(spec, t, prob, some)
     del t
     torch.cuda.empty_cache()

@@ -343,11 +343,10 @@ __device__ inline void merge_row(const DecodeParams &p, const SelectParams &sp, 
 // exp(s - max).  (A single launch whose last chunk merges its row needs a
 // device-scope release per workgroup, which writes back the L2 of its XCD:
 // measured 15 times slower than the second launch.)
-template <int D, int G, int V, typename TS>
-__global__ __launch_bounds__(256) void select_kernel(
-    DecodeParams p, SelectParams sp) {
+template <int D, int G, int V, typename TS, int NT>
+__global__ __launch_bounds__(NT) void select_kernel(DecodeParams p, SelectParams sp) {
 #pragma clang fp contract(off)
-  constexpr int NT = 256, NWV = NT / kWave;
+  constexpr int NWV = NT / kWave;
   constexpr int BB = D * (int)sizeof(TS);  // bytes of one block's summary
   constexpr int NL = BB / 16;              // 16-byte pieces per block
   constexpr int EPL = 16 / (int)sizeof(TS);
@@ -362,7 +361,7 @@ __global__ __launch_bounds__(256) void select_kernel(
   const int tid = threadIdx.x;
   const int nhist = ((p.seqlens[b] - 1) / kBlock) / p.coarse_div;  // blocks or super-blocks
   const int kh = p.Kb - 1;
-  const int lo = 256 * V * c, n = max(0, min(nhist - lo, 256 * V));  // valid blocks in the chunk
+  const int lo = NT * V * c, n = max(0, min(nhist - lo, NT * V));  // valid blocks in the chunk
   const int j0 = lo + V * tid;  // this thread's first block
   uint32_t valid = 0u;
 #pragma unroll
@@ -643,19 +642,26 @@ hipError_t launch_pool_coarse(const DecodeParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int G, int V, typename TS>
+template <int D, int G, int V, typename TS, int NT>
 static void launch_select(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
   const dim3 grid(sp.nchunk, p.batch * p.hkv);
-  hipLaunchKernelGGL((select_kernel<D, G, V, TS>), grid, dim3(256), 0, stream, p, sp);
+  hipLaunchKernelGGL((select_kernel<D, G, V, TS, NT>), grid, dim3(NT), 0, stream, p, sp);
 }
 
 template <int D, int G, typename TS>
 static void launch_select_v(const DecodeParams &p, const SelectParams &sp, hipStream_t stream) {
+  // 512-thread chunks only for one block per thread and 1- or 2-byte
+  // summaries (fp32 ones hold too many registers for 8 waves of a workgroup
+  // beside other workgroups)
+  if (sizeof(TS) < 4 && sp.chunk_threads == 512 && sp.chunk_v == 1) {
+    launch_select<D, G, 1, TS, 512>(p, sp, stream);
+    return;
+  }
   switch (sp.chunk_v) {
-    case 1: launch_select<D, G, 1, TS>(p, sp, stream); break;
-    case 2: launch_select<D, G, 2, TS>(p, sp, stream); break;
-    case 4: launch_select<D, G, 4, TS>(p, sp, stream); break;
-    default: launch_select<D, G, 8, TS>(p, sp, stream); break;
+    case 1: launch_select<D, G, 1, TS, 256>(p, sp, stream); break;
+    case 2: launch_select<D, G, 2, TS, 256>(p, sp, stream); break;
+    case 4: launch_select<D, G, 4, TS, 256>(p, sp, stream); break;
+    default: launch_select<D, G, 8, TS, 256>(p, sp, stream); break;
   }
 }
 

@@ -540,7 +540,7 @@ size_t decode_ws_bytes(const sas_decode_problem *p) {
 // summary requests in flight at once; V grows (up to 8) only while the
 // row's merge would take more than 4096 candidates (chunks x (Kb - 1)).
 struct SelectGeom {
-  int v, nchunk;
+  int v, nchunk, nt;  // blocks per thread, chunks per row, threads per chunk
 };
 
 int summary_bytes(const sas_decode_problem *p) {
@@ -555,10 +555,17 @@ SelectGeom select_geom(const sas_decode_problem *p, int div = 1, int kh = 0) {
     if (n > maxhist) maxhist = n;
   }
   if (kh <= 0) kh = p->budget_blocks > 1 ? p->budget_blocks - 1 : 1;
-  auto chunks = [&](int v) { return (maxhist + 256 * v - 1) / (256 * v); };
+  const long rows = (long)p->batch * p->hkv;
+  auto chunks = [&](int nt, int v) { return (maxhist + nt * v - 1) / (nt * v); };
+  // 512-thread chunks (half the workgroups and of the merge's candidates)
+  // when 256-thread ones would put more than two workgroups on each of 256
+  // compute units, for 1- or 2-byte summaries: measured faster for the
+  // many-row paged batch, slower for a few long rows
+  if (summary_bytes(p) < 4 && rows * chunks(256, 1) > 512 && chunks(512, 1) * kh <= 4096)
+    return {1, chunks(512, 1), 512};
   int v = 1;
-  while (v < 8 && chunks(v) * kh > 4096) v *= 2;
-  return {v, chunks(v)};
+  while (v < 8 && chunks(256, v) * kh > 4096) v *= 2;
+  return {v, chunks(256, v), 256};
 }
 
 
@@ -647,6 +654,7 @@ sas_status sas_decode_select(const sas_decode_problem *p, const void *q, const v
   sas::SelectParams s{};
   s.nchunk = sg.nchunk;
   s.chunk_v = sg.v;
+  s.chunk_threads = sg.nt;
   s.sel_idx = sel_idx;
   s.sel_lg = sel_loggate;
   s.gate_lse = gate_lse;
@@ -720,6 +728,7 @@ sas_status sas_decode_select_hier(const sas_decode_problem *p, const void *q, co
   sas::SelectParams s{};
   s.nchunk = sg.nchunk;
   s.chunk_v = sg.v;
+  s.chunk_threads = sg.nt;
   s.sel_idx = reinterpret_cast<int32_t *>(ws + l.kept);
   s.sel_lg = reinterpret_cast<float *>(ws + l.kept_lg);
   s.gate_lse = reinterpret_cast<float *>(ws + l.kept_lse);

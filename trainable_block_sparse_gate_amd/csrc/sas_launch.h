@@ -114,7 +114,9 @@ constexpr int kCoarseBlocks = 8;  // history blocks per super-block
 // decode selection (pooled scores -> gate + Top-K) over chunks of each row:
 // scores and an exact local Top-K per chunk, then a merge per row
 struct SelectParams {
-  int nchunk, chunk_v;         // chunks per row; blocks per thread (chunk = 256 chunk_v)
+  int nchunk, chunk_v;         // chunks per row; blocks per thread
+  int chunk_threads;           // threads per chunk (256, or 512 with chunk_v 1 and
+                               // 1- or 2-byte summaries); chunk = chunk_threads chunk_v
   int32_t *sel_idx;            // out [batch*hkv][Kb]
   float *sel_lg;               // out [batch*hkv][Kb]
   float *gate_lse;             // out [batch*hkv]

@@ -826,6 +826,20 @@ def main():
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
+    line["config"]["seeds"] = ("1000 * workload + stream; workloads tiny 1, layer16k 2, varlen 3, "
+                               "decode 4, paged 5; streams q 0, k 1, v 2, logits 3, dO 4, "
+                               "lengths 5, page permutation 6, boosted columns 7")
+    if peaks:
+        # the same fractions against the peaks measured in this run
+        mf, hb = peaks["bf16_mfma_random_operands_tflops"], peaks["stream_read_gbs"]
+        line["frac_of_measured_peaks"] = {
+            "mfma_peak_tflops": mf, "hbm_peak_gbs": hb,
+            "step": round(tr["tflops"] / mf, 4),
+            "kernels": {k: round(v["algorithmic_tflops"] / mf, 4)
+                        for k, v in tr["kernels"].items()},
+            "backward": round(tr["backward"]["tflops"] / mf, 4),
+            "decode": round(dec["value"] / hb, 4) if dec else None,
+        }
     print(json.dumps(line), flush=True)
 
 

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 CASES = {
     # name: (seqlens, hq, hkv, d, Kb, coarse_keep)
     "mixed_g4_d128": ([64 * 300 + 5, 64 * 90 + 1, 64 * 17, 70], 8, 2, 128, 16, 4),
-    "keep1_g2_d64": ([64 * 200 + 40, 64 * 33 + 2], 4, 2, 64, 6, 1),
+    "keep1_g2_d64": ([64 * 200 + 40, 64 * 33 + 2, 1], 4, 2, 64, 6, 1),
     "keep127_g2_d64": ([64 * 1100 + 3], 2, 1, 64, 64, 127),
     "many_chunks_g8_d128": ([64 * 9000 + 9], 8, 1, 128, 32, 31),
 }

@@ -28,6 +28,9 @@ CASES = {
     "wide_merge_g2_d64": ([64 * 4300 + 7, 64 * 300 + 3], 2, 1, 64, 64),
     # 17 chunks x 127 = 2159 candidates: the merge takes 16 per thread
     "widest_merge_g2_d64": ([64 * 4300 + 7, 64 * 300 + 3], 2, 1, 64, 128),
+    # 256-block chunks would give 17 x 255 candidates, more than the merge
+    # takes: two blocks per scoring thread (9 chunks of 512)
+    "two_per_thread_g2_d64": ([64 * 4200 + 1], 2, 1, 64, 256),
 }
 
 
@@ -92,7 +95,7 @@ def test_decode_ungated_and_fp32_output():
 
 
 @pytest.mark.parametrize("paged", [False, True])
-@pytest.mark.parametrize("name", ["mixed_g4_d128", "g2_d64"])
+@pytest.mark.parametrize("name", ["mixed_g4_d128", "g2_d64", "two_per_thread_g2_d64"])
 @pytest.mark.parametrize("summary", ["bf16", "fp8"])
 def test_decode_reduced_precision_summaries(name, paged, summary):
     """Summaries stored as bf16 or fp8 e4m3 (the fp32 means rounded to

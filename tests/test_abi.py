@@ -229,6 +229,24 @@ def test_binding_checks_decode_tensors():
         sas.decode(prob, q, cache, cache, torch.zeros(2, 5, dtype=torch.int32), None,
                    workspace=torch.zeros(16, dtype=torch.uint8))
     assert e.value.status == -2
+    # summaries: the tiled layout [batch][hkv][tiles][pieces][64][channels per piece]
+    ksum = torch.zeros(prob.summary_shape())
+    assert prob.summary_shape() == (1, 2, 1, 32, 64, 4)
+    with pytest.raises(sas.SasError) as e:
+        sas.decode_select(prob, q, ksum.view(1, 2, 64, 128))  # block-major, not tiled
+    assert e.value.status == -2
+    with pytest.raises(sas.SasError) as e:
+        sas.pool_coarse(prob, ksum.to(bf))  # bf16 summaries for an fp32 problem
+    assert e.value.status == -3
+    csum = torch.zeros(prob.coarse_shape())
+    assert prob.coarse_shape() == (1, 2, 1, 32, 64, 4)
+    with pytest.raises(sas.SasError) as e:
+        sas.decode_select_hier(prob, q, ksum, csum[:, :1], 4)  # one kv head short
+    assert e.value.status == -2
+    with pytest.raises(sas.SasError) as e:
+        sas.decode_append(prob, torch.zeros(1, 2, 128, dtype=bf), torch.zeros(1, 2, 128, dtype=bf),
+                          cache, cache, ksum, csum.to(bf))
+    assert e.value.status == -3
 
 
 def test_decode_select_workspace_and_limits(lib):

@@ -14,13 +14,15 @@
  *        equations), 1-2 (hard Top-K equation), 2-1 (g = phi(s), g0 = 1,
  *        broadcast), 2-2 (inner log-gate equation and the softmax/log identity),
  *        3-3 (softmax gate activation), 3-5 (sparse scope), 3-6 (fused kernel,
- *        backward keeps the selector gradient), 3-7 (decode path steps 1-4).
+ *        backward keeps the selector gradient), 3-7 (decode path steps 1-4),
+ *        7-2 (a coarse retrieval narrowing the candidates before the Top-K).
  *   [P]  the page titled "SAS: Simple Attention Sparsification via End-to-End
  *        Optimization of Context Ranking" holding the paper's own text: section 3 (standard attention,
  *        scaling factor omitted, block partition, Top-K selected index set),
  *        section 4 (current block singled out and unbiased, gate broadcast,
  *        gate-position/activation/scope design elements), ablation results
- *        (inner gate gradient "relative signal", normaliser shared by the
+ *        (the inner gate's gradient measures a block against the row's
+ *        mean, the normaliser is shared by the
  *        historical blocks and not applied to the current block, invariance
  *        to a global shift of the scores).
  *
@@ -57,6 +59,12 @@
  *       qbar[e]    = (((q0 + q1) + ... + q_{G-1})) / G          (fp32, in order)
  *       A          = fmaf(qbar[e], kbar[j][e], A)  for e = 0..d-1 (fp32)
  *       s_j        = A / sqrtf(d)                                (fp32)
+ *   - hierarchical selection (opt-in): super-blocks of F = 8 history blocks;
+ *     a complete super-block's summary is the mean of its F stored block
+ *     summaries (summed in block order in fp32, divided by F, rounded like
+ *     them); the best super-blocks by the same pooled score (earlier on
+ *     ties) and the trailing blocks of no complete super-block are the
+ *     candidates, and the gate and Top-K run over the candidates only.
  *
  * Layouts (all row-major, C order):
  *   q, o, dq        [T][hq][d]        k, v, dk, dv   [T][hkv][d]
@@ -303,8 +311,8 @@ int sas_oracle_fwd(int nseq, const int32_t *cu, int blk, int hq, int hkv, int d,
  * Backward: the gradients of the forward above with respect to q, k, v and
  * the per-block log gate, written out by the chain rule (the pages state
  * that the backward keeps the selector gradient, [R] 3-6, and describe the
- * inner gate's gradient as P_gated (dP - D) style "relative signal", [P]
- * ablation results):
+ * inner gate's gradient as P_gated (dP - D), each block measured against
+ * the row's mean, [P] ablation results):
  *   P_tu  = softmax_u(z_t)          D_t   = sum_e dO_te o_te
  *   dP_tu = dO_t . v_u              dS_tu = P_tu (dP_tu - D_t)
  *   dq_t  = scale sum_u dS_tu k_u   dk_u  = scale sum_t dS_tu q_t

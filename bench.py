@@ -740,7 +740,37 @@ def cpu_baseline(case, metrics):
                        f"fp64, algorithmic 14d FLOPs per pair and head; fwd {t2 - t1:.1f} s, "
                        f"bwd {t3 - t2:.1f} s; gate+Top-K of all rows {t1 - t0:.2f} s not "
                        "counted"),
-            "seconds": round(secs, 2)}
+            "seconds": round(secs, 2), "decode_sample": cpu_decode_sample(metrics)}
+
+
+def cpu_decode_sample(metrics):
+    """The oracle's decode path on a bounded sample: one 131072-token
+    sequence, 8 query / 2 kv heads (the workloads' group of 4), head_dim 128,
+    budget 64 blocks: summaries, pooled selection and decode attention of
+    both (sequence, kv head) rows, timed per phase."""
+    import oracle
+    from trainable_block_sparse_gate_amd import workloads as wl
+    L, hq, hkv, d, Kb = 131072, 8, 2, 128, 64
+    host = wl.draw_decode_host_small([L], hq, hkv, d, Kb, False, seed=5000)
+    G = hq // hkv
+    t_pool = t_sel = t_dec = 0.0
+    for g in range(hkv):
+        K, V = host["k"][0, g, :L], host["v"][0, g, :L]
+        qg = host["q"][0, g * G:(g + 1) * G]
+        t0 = time.perf_counter()
+        kbar = oracle.pool_keys_row(K)
+        t1 = time.perf_counter()
+        s = oracle.decode_scores_row(qg, kbar)
+        idx, lg, _ = oracle.gate_row(s, (L - 1) // 64, Kb)
+        t2 = time.perf_counter()
+        oracle.decode_row(qg, K, V, idx, lg, Kb, 1.0 / np.sqrt(d))
+        t3 = time.perf_counter()
+        t_pool, t_sel, t_dec = t_pool + t1 - t0, t_sel + t2 - t1, t_dec + t3 - t2
+    kv = metrics.decode_kv_bytes([L], hkv, d, Kb)
+    return {"rows": hkv, "context": L, "budget_blocks": Kb,
+            "pool_s": round(t_pool, 4), "select_s": round(t_sel, 4),
+            "decode_s": round(t_dec, 4), "decode_kv_GB/s": round(kv / t_dec / 1e9, 3),
+            "threads": 1, "note": "fp64 oracle (fp32 pooled scores), rows in turn on one host thread"}
 
 
 def main():

@@ -25,6 +25,8 @@ SMALL = {
     "g8_d128_ties": ([640, 100], 16, 2, 128, 5, "bf16", 2.0, {"logit_grid": 1.0}),
     "g4_d64_f32_out": ([333], 8, 2, 64, 6, "f32", 3.0, {}),
     "g2_d128_bigK": ([1030], 4, 2, 128, 40, "bf16", 2.0, {}),
+    # several thousand tokens: dozens of key blocks per sequence, ragged tails
+    "mid_g4_d128": ([2048, 1500, 700], 8, 2, 128, 8, "bf16", 2.0, {}),
 }
 
 
@@ -120,7 +122,7 @@ def test_bwd_all_softmax_mode():
 
 
 @pytest.mark.parametrize("mode", [sas.GATE_SIGMOID, sas.GATE_RAW, sas.GATE_STE])
-@pytest.mark.parametrize("name", ["ragged_g4_d128", "g2_d64_f32"])
+@pytest.mark.parametrize("name", ["ragged_g4_d128", "g2_d64_f32", "mid_g4_d128"])
 def test_activation_ablations_fwd_bwd(name, mode):
     """Independent sigmoid gates, raw-logit injection and the straight-
     through hard gate (the pages' activation and ranking-preservation
@@ -225,7 +227,7 @@ def test_full_scope_zero_gates_is_dense_causal_attention(dtype):
     assert_close("dlg", dlg.cpu().numpy(), rdlg, tol)
 
 
-@pytest.mark.parametrize("name", ["ragged_g4_d128", "g2_d64_f32", "g1_d64_bf16"])
+@pytest.mark.parametrize("name", ["ragged_g4_d128", "g2_d64_f32", "g1_d64_bf16", "mid_g4_d128"])
 def test_outer_gate_fwd_bwd(name):
     """The gate-position ablation (review 3-2; paper text section 4): the
     softmax over the ungated logits, the gate scaling each block's values.

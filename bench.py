@@ -197,7 +197,12 @@ def kernel_label(n):
         # the one after it) as "bool _Accum, bool, E"
         n = n.replace("bool _Accum, bool, E", "__bf16, ...")
         return re.sub(r"^void ", "", re.sub(r"\(sas::\w+(, sas::\w+)*\)$", "", n))
-    m = re.search(r"at::native::[A-Za-z_:]*", n)
+    m = re.match(r"(?:void )?\(anonymous namespace\)::(\w+_kernel)(<\d+>)?", n)
+    if m:  # the measured-peak kernels (csrc/peaks.hip)
+        return f"peaks::{m.group(1)}{m.group(2) or ''}"
+    if "__amd_rocclr" in n:
+        return re.search(r"__amd_rocclr_\w+", n).group(0) + " (HIP runtime)"
+    m = re.search(r"at::native::(?:\(anonymous namespace\)::)?[A-Za-z_:]*", n)
     return (m.group(0) if m else n[:48]) + " (torch)"
 
 

@@ -151,14 +151,17 @@ def test_bwd_fp32_output_and_dO():
     check_bwd(case, prob, dv, gpu, ref)
 
 
-def test_bwd_hot_key_blocks_split_over_segments():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_hot_key_blocks_split_over_segments(dtype):
     """A long sequence with a few columns boosted so that most rows keep the
-    same key blocks: those blocks are split over many segments."""
+    same key blocks: those blocks are split over many segments (the bf16 and
+    the fp32 instantiations of dK/dV and of the segment reduction)."""
     import torch
     lengths, hq, hkv, d, Kb = [8192 + 37], 8, 2, 128, 8
-    case = wl.make_varlen("hot", lengths, hq, hkv, d, Kb, dtype="bf16", logit_sigma=1.0,
+    say(f"[hot key blocks {dtype}]")
+    case = wl.make_varlen("hot", lengths, hq, hkv, d, Kb, dtype=dtype, logit_sigma=1.0,
                           workload_id=71, boost_frac=0.05, boost=6.0)
-    prob = sas.Varlen(lengths, hq, hkv, d, Kb)
+    prob = sas.Varlen(lengths, hq, hkv, d, Kb, dtype=dtype, out_dtype=dtype)
     dv = case_to_device(case)
     sel, lg, glse = sas.gate_topk(prob, dv["logits"])
     o, lse = sas.fwd(prob, dv["q"], dv["k"], dv["v"], sel, lg)
@@ -169,7 +172,7 @@ def test_bwd_hot_key_blocks_split_over_segments():
     say(f"  most-kept block count: {counts.max()}")
     assert counts.max() > 64  # at least two segments of 64 rows
     ro, rl = oracle.fwd(case.cu_seqlens, case.q, case.k, case.v, ridx, rlg, Kb, case.scale)
-    assert_close("o", o.float().cpu().numpy(), ro, TOL["bf16"])
+    assert_close("o", o.float().cpu().numpy(), ro, TOL[dtype])
     check_bwd(case, prob, dv, (sel, lg, glse, o, lse), (ridx, rlg, rlse, ro, rl))
 
 

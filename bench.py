@@ -16,7 +16,9 @@ Reported in the same JSON line:
                 against the 2.5 PFLOP/s dense bf16 MFMA peak;
   layer16k      the same step on the 16K-token single-layer workload;
   decode        paged batch-32 decode (budget 4096 tokens): append, pooled
-                selection, split-K attention; KV GB/s against 8 TB/s;
+                selection, split-K attention; KV GB/s against 8 TB/s; the
+                whole step also timed as one unit, launched eagerly and
+                replayed from a HIP graph;
   decode_long   one sequence at 131072 and at 524288 tokens (budget 2048);
   measured_peaks  a bf16 MFMA loop and a streaming read on this device;
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
@@ -513,6 +515,38 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
             t_sel += e0.elapsed_time(e1)
             t_dec += e1.elapsed_time(e2)
     n = args.decode_steps
+    # the whole step as one unit: launched eagerly, and replayed from a HIP
+    # graph captured once (its 4-5 kernels with no host launch between them;
+    # the step is idempotent, so every replay does the same work)
+    def step():
+        sas.decode_append(prob, k_new, v_new, t["k"], t["v"], ksum)
+        sas.decode_select(prob, t["q"], ksum, out=(sel, lg, glse, scores), workspace=sws)
+        sas.decode(prob, t["q"], t["k"], t["v"], sel, lg, workspace=ws, out=(o, lse))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    t_whole = [0.0, 0.0]  # eager, graph
+    for it in range(n + 3):
+        for mode in (0, 1):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if mode == 0:
+                step()
+            else:
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if it >= 3:
+                t_whole[mode] += e0.elapsed_time(e1)
+    del graph
     # the selection with the other summary storages (same cache, same query)
     by_summary = {}
     for sd in ("f32", "bf16", "fp8"):
@@ -579,7 +613,8 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
     scan_gbs = scan / (t_sel / n * 1e-3) / 1e9
     log(f"[bench] decode {t_dec / n * 1e3:.1f} us for {kv / 2**20:.1f} MiB -> {gbs:.0f} GB/s; "
         f"selection {t_sel / n * 1e3:.1f} us over {scan / 2**20:.1f} MiB summaries; "
-        f"append {t_app / n * 1e3:.1f} us")
+        f"append {t_app / n * 1e3:.1f} us; whole step {t_whole[0] / n * 1e3:.1f} us eager, "
+        f"{t_whole[1] / n * 1e3:.1f} us from a HIP graph")
     del t, flush
     torch.cuda.empty_cache()
     desc = (f"paged: batch {spec.batch}, lengths U[32768,131072]" if spec.paged else
@@ -594,7 +629,9 @@ def decode_bench(args, torch, sas, wl, metrics, spec):
                           "GB/s": round(scan_gbs, 1), "other_summary_dtypes": by_summary,
                           "hierarchical": hier},
             "append_us": round(t_app / n * 1e3, 2),
-            "step_us": round((t_app + t_sel + t_dec) / n * 1e3, 2)}
+            "step_us": round((t_app + t_sel + t_dec) / n * 1e3, 2),
+            "whole_step_us": {"eager": round(t_whole[0] / n * 1e3, 2),
+                              "hip_graph": round(t_whole[1] / n * 1e3, 2)}}
 
 
 def measured_peaks(torch, metrics):

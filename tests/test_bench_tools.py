@@ -129,3 +129,14 @@ def test_source_hash_ignores_comments_only():
     assert bench._code_only(c) != bench._code_only("int f(int x){return x+2;}")
     assert bench._code_only("x = 1  # one\n# note\n", python=True) == \
         bench._code_only("x = 1  # one\n", python=True)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """The benchmark measures one GPU: --gpus above 1 exits non-zero, before
+    touching any device, and says why."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)

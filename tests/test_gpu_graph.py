@@ -1,5 +1,6 @@
-"""One decode step (cache append, selection, attention) captured in a HIP
-graph and replayed, through the C ABI.
+"""One decode step (cache append, selection, attention), and one training
+step (gate, forward, backward, gate backward), captured in a HIP graph and
+replayed, through the C ABI.
 
 Once its outputs and workspaces are given, every entry point of the step only
 launches kernels on the caller's stream (no allocation, copy, fill or
@@ -125,3 +126,53 @@ def test_decode_step_graph_replays_match_eager(paged, noalloc):
             assert np.max(np.abs(o_h[b, gg * G:(gg + 1) * G] - ro)) <= TOL["bf16"]
             assert np.max(np.abs(lse_h[b, gg * G:(gg + 1) * G] - rl)) <= 1e-4
     say("  eager step: selection bit-exact, output at the bf16 bar")
+
+
+def test_training_step_graph_replays_match_eager():
+    """Gate + Top-K, forward, backward and gate backward captured in one
+    graph (outputs allocated once, inside the capture, from the graph's
+    pool): every replay gives the eager step's bits, the kernels being
+    deterministic; the eager selection and forward are held to the oracle."""
+    import torch
+    from tests.gpu_helpers import assert_close, case_to_device
+    lengths, hq, hkv, d, Kb = [700, 64 * 9 + 5, 300], 8, 2, 128, 4
+    say("[graph training step]")
+    case = wl.make_varlen("graph", lengths, hq, hkv, d, Kb, dtype="bf16", logit_sigma=2.0,
+                          workload_id=95)
+    prob = sas.Varlen(lengths, hq, hkv, d, Kb)
+    dv = case_to_device(case)
+    ws = torch.empty(max(1, sas.bwd_workspace_bytes(prob)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        sel, lg, glse = sas.gate_topk(prob, dv["logits"])
+        o, lse = sas.fwd(prob, dv["q"], dv["k"], dv["v"], sel, lg)
+        dq, dk, dvv, dlg = sas.bwd(prob, dv["q"], dv["k"], dv["v"], o, dv["dO"], lse, sel, lg,
+                                   workspace=ws)
+        dz = sas.gate_bwd(prob, dv["logits"], sel, glse, dlg)
+        return sel, lg, glse, o, lse, dq, dk, dvv, dlg, dz
+
+    ref = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    names = ["sel_idx", "sel_lg", "gate_lse", "o", "lse", "dq", "dk", "dv", "dlg", "d_logits"]
+    for r in range(3):
+        _garbage(outs)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for nm, a, b in zip(names, outs, ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (r, nm)
+    say("  3 replays: the eager step's bits")
+    ridx, rlg, _ = oracle.gate_topk(case.cu_seqlens, case.logits, hkv, Kb)
+    assert np.array_equal(ref[0].cpu().numpy(), ridx)
+    ro, rl = oracle.fwd(case.cu_seqlens, case.q, case.k, case.v, ridx, rlg, Kb, case.scale)
+    assert_close("o", ref[3].float().cpu().numpy(), ro, TOL["bf16"])
+    assert_close("lse", ref[4].cpu().numpy(), rl, TOL["bf16"])

@@ -276,3 +276,76 @@ def test_decode_paged_full_size_reduced_summaries(summary):
     decode_rows_check(spec, t, prob, some)
     del t
     torch.cuda.empty_cache()
+
+
+def test_decode_step_loop_paged_full_size():
+    """The paged batch as a step loop: each sequence prefilled to the largest
+    multiple of 64 below its length minus one (summaries by sas_pool_keys),
+    then two steps of sas_decode_append with new tokens, the first of which
+    opens a block in every sequence, so the append summarises the block it
+    closes.  After the steps: every row's summaries equal the oracle's of the
+    updated cache bit for bit, every row's selection the oracle's, and the
+    output of 32 rows is within the bf16 bar."""
+    import torch
+    from tests.gpu_helpers import summaries_f32
+    spec = wl.paged_spec()
+    t = wl.draw_decode_device(spec)
+    L0 = [64 * ((L - 2) // 64) for L in spec.seqlens]
+    say(f"[full {spec.name} step loop] prefix {min(L0)}..{max(L0)}, 2 steps")
+    B, hkv, d, G = spec.batch, spec.hkv, spec.d, spec.hq // spec.hkv
+
+    # one summary layout for every step (the stride of the longest history)
+    stride = -(-max((L - 1) // 64 for L in spec.seqlens) // 64) * 64
+
+    def problem(lens):
+        return sas.Decode(lens, spec.hq, hkv, d, spec.budget_blocks, True, spec.max_len,
+                          page_table=t["page_table"], num_pages=t["k"].shape[0],
+                          nblk_stride=stride)
+
+    ksum = sas.pool_keys(problem(L0), t["k"])
+    g = np.random.Generator(np.random.PCG64(97))
+    new = [{nm: wl.round_bf16(wl.normal(g, (B, hkv, d))) for nm in ("k", "v")}
+           for _ in range(2)]
+    for s in range(2):
+        lens = [n + s + 1 for n in L0]
+        k_new, v_new = (torch.from_numpy(new[s][nm].view(np.int16)).view(torch.bfloat16).cuda()
+                        for nm in ("k", "v"))
+        sas.decode_append(problem(lens), k_new, v_new, t["k"], t["v"], ksum)
+    prob = problem(lens)
+    sel, lg, _, _ = sas.decode_select(prob, t["q"], ksum)
+    o, lse = sas.decode(prob, t["q"], t["k"], t["v"], sel, lg)
+    torch.cuda.synchronize()
+    ks_h, sel_h, lg_h = summaries_f32(ksum), sel.cpu().numpy(), lg.cpu().numpy()
+    o_h, lse_h = o.float().cpu().numpy(), lse.cpu().numpy()
+    q_h = t["q"].float().cpu().numpy()
+    kb, vb = host_cache(t, "k"), host_cache(t, "v")
+    pt = t["page_table"]
+    for s in range(2):  # the host caches with the steps' tokens
+        for b in range(B):
+            pos = L0[b] + s
+            kb[pt[b, pos // 64], :, pos % 64] = new[s]["k"][b]
+            vb[pt[b, pos // 64], :, pos % 64] = new[s]["v"][b]
+    worst = 0.0
+    for b, L in enumerate(lens):
+        cur = (L - 1) // 64
+        for gg in range(hkv):
+            K = bits_f32(wl.gather_row_cache(kb, pt, b, gg, L))
+            assert np.array_equal(ks_h[b, gg, :cur], oracle.pool_keys_row(K)), (b, gg, "ksum")
+            qg = q_h[b, gg * G:(gg + 1) * G]
+            ridx, rlg, _, _ = oracle.decode_select_row(qg, K, spec.budget_blocks)
+            r = b * hkv + gg
+            assert np.array_equal(sel_h[r], ridx), (b, gg, "selection")
+            fin = np.isfinite(rlg)
+            assert np.max(np.abs(lg_h[r][fin] - rlg[fin]), initial=0.0) < 1e-5
+            if gg != b % hkv:
+                continue
+            V = bits_f32(wl.gather_row_cache(vb, pt, b, gg, L))
+            ro, rl = oracle.decode_row(qg, K, V, ridx, rlg, spec.budget_blocks, prob.scale)
+            err = float(np.max(np.abs(o_h[b, gg * G:(gg + 1) * G] - ro)))
+            worst = max(worst, err)
+            assert err <= TOL["bf16"], (b, gg, err)
+            assert np.max(np.abs(lse_h[b, gg * G:(gg + 1) * G] - rl)) <= 1e-4
+    say(f"  summaries and selection of all {B * hkv} rows bit-exact after the steps; "
+        f"output of {B} rows, max |o err| {worst:.3e}")
+    del t
+    torch.cuda.empty_cache()

@@ -349,3 +349,45 @@ def test_decode_step_loop_paged_full_size():
         f"output of {B} rows, max |o err| {worst:.3e}")
     del t
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("summary", ["f32", "fp8"])
+def test_hier_selection_paged_full_size(summary):
+    """The hierarchical selection on the paged batch (coarse_keep = budget - 1
+    super-blocks of 8 blocks): every row's super-block summaries, candidate
+    scores and index sets bit-exact against the oracle, log gates to 1e-5."""
+    import torch
+    from tests.gpu_helpers import summaries_f32
+    spec = wl.paged_spec()
+    say(f"[full {spec.name} hierarchical selection, summaries {summary}]")
+    t = wl.draw_decode_device(spec)
+    prob = sas.Decode(spec.seqlens, spec.hq, spec.hkv, spec.d, spec.budget_blocks, True,
+                      spec.max_len, page_table=t["page_table"], num_pages=t["k"].shape[0],
+                      summary_dtype=summary)
+    C, Kb, hkv, G = spec.budget_blocks - 1, spec.budget_blocks, spec.hkv, spec.hq // spec.hkv
+    ksum = sas.pool_keys(prob, t["k"])
+    csum = sas.pool_coarse(prob, ksum)
+    sel, lg, glse, scores = sas.decode_select_hier(prob, t["q"], ksum, csum, C)
+    torch.cuda.synchronize()
+    cs_h, sc_h = summaries_f32(csum), scores.cpu().numpy()
+    sel_h, lg_h, glse_h = sel.cpu().numpy(), lg.cpu().numpy(), glse.cpu().numpy()
+    q_h = t["q"].float().cpu().numpy()
+    kb, pt = host_cache(t, "k"), t["page_table"]
+    for b, L in enumerate(spec.seqlens):
+        for gg in range(hkv):
+            K = bits_f32(wl.gather_row_cache(kb, pt, b, gg, L))
+            qg = q_h[b, gg * G:(gg + 1) * G]
+            cbar = oracle.coarse_summaries_row(oracle.pool_keys_row(K, summary=summary), summary)
+            assert np.array_equal(cs_h[b, gg, :cbar.shape[0]], cbar), (b, gg, "coarse summaries")
+            ridx, rlg, rlse, rs, cand = oracle.decode_select_row_hier(qg, K, Kb, C,
+                                                                      summary=summary)
+            r = b * hkv + gg
+            assert np.array_equal(sc_h[b, gg, cand], rs[cand]), (b, gg, "candidate scores")
+            assert np.array_equal(sel_h[r], ridx), (b, gg, "selection")
+            fin = np.isfinite(rlg)
+            assert np.array_equal(np.isfinite(lg_h[r]), fin)
+            assert np.max(np.abs(lg_h[r][fin] - rlg[fin]), initial=0.0) < 1e-5
+            assert abs(glse_h[r] - rlse) < 1e-5
+    say(f"  all {spec.batch * hkv} rows bit-exact")
+    del t
+    torch.cuda.empty_cache()

@@ -30,7 +30,9 @@
  *     The caller owns all memory; the library never allocates, frees or
  *     synchronises.  Every call is asynchronous on `stream` (a hipStream_t,
  *     NULL = the default stream); pointers must stay valid until the stream
- *     reaches the work.
+ *     reaches the work.  A call only launches kernels on `stream` (no copy,
+ *     fill or memset), so calls can be captured into a HIP graph and
+ *     replayed; a replay redoes the same work on the same buffers.
  *   - Arguments are checked on the host before anything is launched.  On a
  *     failed check nothing is launched, no output is touched and a negative
  *     sas_status is returned; sas_last_error() then describes the failure
